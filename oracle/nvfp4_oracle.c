@@ -1,0 +1,285 @@
+/*
+ * nvfp4_oracle.c -- plain, slow CPU oracle for the NVFP4 KV-cache hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product library
+ * (decode_attention_nvfp4_amd/) never calls it and shares no code with it.
+ *
+ * Everything here is written from the definitions on the source pages, in
+ * the simplest form that can be checked by eye: scalar loops, exact
+ * threshold comparisons done in IEEE double where the operands are provably
+ * exact, and double accumulation for attention.  No blocking, no fusion,
+ * no fast-math.
+ *
+ * Sources (page titles; sections named where cited below):
+ *  [EXPL] "NVIDIA解説: NVFP4 KV Cacheで長コンテキストLLM推論を最適化 —
+ *          メモリ50%削減・TTFT 3倍高速化"
+ *  [GB10] "一個 Triton FP8 繞道補丁，為 DGX Spark 的 GB10 擠出多 17% 的 NVFP4 速度"
+ *  [RC17] "TensorRT-LLM rc17 が SM121（DGX Spark）向けに NVFP4 MoE バックエンドと
+ *          NVFP4 KV キャッシュを追加"
+ *  [TRTL] "Compilation d'inferences spécialisées en matériel FP8 et NVFP4 sur
+ *          Blackwell"
+ *
+ * Readings taken where the pages are silent (each is listed in the design
+ * notes of the repository):
+ *  - E2M1 grid: sign + 2-bit exponent (bias 1) + 1-bit mantissa, giving the
+ *    magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; the pages fix only the bit
+ *    widths and the ~[-6, 6] range ([EXPL] §E2M1 + 2レベルスケーリング).
+ *  - E4M3 is the OCP E4M3FN encoding (bias 7, no infinities, 0x7F/0xFF NaN,
+ *    largest finite 448).
+ *  - Tensor scale s_t = amax(|X|) / (6 * 448), computed in FP32, so that the
+ *    tensor's largest magnitude maps onto the largest block scale times the
+ *    largest E2M1 value.  The pages only say it is one FP32 value per tensor.
+ *  - Block scale: the E4M3 value nearest to (block amax) / (6 * s_t), ties to
+ *    the even code, clamped to 448 (never NaN).  The pages do not give the
+ *    selection rule; this maps each block's largest magnitude onto 6.
+ *  - Element code: the E2M1 value nearest to x / (s_block * s_t), computed in
+ *    exact real arithmetic, ties to the even code, clamped to 6.  The sign bit
+ *    is always the sign of x (so -0 and small negatives give code 0x8).
+ *    A zero block scale gives magnitude 0 for every element.
+ *  - Dequantization multiplies by s_t, which is dividing by the global
+ *    encode scale g = 1/s_t ([GB10] §這個 80 行的 Triton 繞道: the global
+ *    scale must divide, not multiply).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_D 128      /* head dimension */
+#define ORC_BLOCK 16   /* micro-block length ([EXPL] §E2M1 + 2レベルスケーリング, Level 1) */
+#define ORC_NBLK (ORC_D / ORC_BLOCK)
+
+/* ---------------------------------------------------------------- formats */
+
+/* E2M1 magnitudes, code order 0..7 ([EXPL] §E2M1 + 2レベルスケーリング). */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* Value of a 4-bit E2M1 code (bit 3 = sign). */
+double orc_e2m1_value(unsigned code) {
+  double m = kE2M1[code & 7u];
+  return (code & 8u) ? -m : m;
+}
+
+/* Value of an OCP E4M3FN byte: 1 sign, 4 exponent (bias 7), 3 mantissa
+ * bits; exponent field 0 is subnormal (m/8 * 2^-6); 0x7F and 0xFF are NaN. */
+double orc_e4m3_value(unsigned byte) {
+  unsigned s = (byte >> 7) & 1u, e = (byte >> 3) & 15u, m = byte & 7u;
+  double v;
+  if (e == 15u && m == 7u) return NAN;
+  if (e == 0u) v = ldexp((double)m / 8.0, -6);
+  else v = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+  return s ? -v : v;
+}
+
+/* ------------------------------------------------------- tensor scale (A0) */
+
+/* s_t = amax(|x|) / (6 * 448) in FP32. */
+float orc_tensor_scale(const float* x, size_t n) {
+  float amax = 0.0f;
+  for (size_t i = 0; i < n; ++i) {
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  return amax / 2688.0f;
+}
+
+float orc_abs_max(const float* x, size_t n) {
+  float amax = 0.0f;
+  for (size_t i = 0; i < n; ++i) {
+    float a = fabsf(x[i]);
+    if (a > amax) amax = a;
+  }
+  return amax;
+}
+
+/* ------------------------------------------------------------ block scale */
+
+/* Nearest non-negative finite E4M3 code to the exact quotient a / (6 s_t),
+ * ties to the even code, clamped to the largest finite code 0x7E (448).
+ * Walks the 126 midpoints between consecutive codes in increasing order.
+ * Each threshold 6 * s_t * mid is exact in double: 2 + 24 + 5 significant
+ * bits.  a is an FP32 magnitude, also exact in double. */
+unsigned orc_block_scale_code(float amax_block, float s_t) {
+  double a = (double)amax_block;
+  double six_st = 6.0 * (double)s_t;
+  unsigned code = 0;
+  for (unsigned k = 0; k < 126u; ++k) {
+    double mid = 0.5 * (orc_e4m3_value(k) + orc_e4m3_value(k + 1u));
+    double t = six_st * mid;
+    if (a > t) {
+      code = k + 1u;
+    } else {
+      if (a == t) code = (k % 2u == 0u) ? k : k + 1u;
+      break;
+    }
+  }
+  return code;
+}
+
+/* --------------------------------------------------------- element code */
+
+/* 4-bit code of x for block-scale byte sb and tensor scale s_t: the E2M1
+ * magnitude nearest to |x| / (sb * s_t), ties to the even code, clamped to 6;
+ * sign bit from x.  Thresholds sb * s_t * mid are exact in double
+ * (4 + 24 + 3 significant bits). */
+unsigned orc_element_code(float x, unsigned sb_code, float s_t) {
+  unsigned sign = signbit(x) ? 8u : 0u;
+  double sb = orc_e4m3_value(sb_code);
+  double d = sb * (double)s_t;
+  double ax = fabs((double)x);
+  unsigned mag = 0;
+  if (d > 0.0) {
+    for (unsigned k = 0; k < 7u; ++k) {
+      double mid = 0.5 * (kE2M1[k] + kE2M1[k + 1u]);
+      double t = d * mid;
+      if (ax > t) {
+        mag = k + 1u;
+      } else {
+        if (ax == t) mag = (k % 2u == 0u) ? k : k + 1u;
+        break;
+      }
+    }
+  }
+  return sign | mag;
+}
+
+/* Array forms of the two encoders above (used by the exhaustive checks). */
+void orc_element_codes(const float* x, size_t n, unsigned sb_code, float s_t, uint8_t* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = (uint8_t)orc_element_code(x[i], sb_code, s_t);
+}
+
+void orc_block_scale_codes(const float* amax, size_t n, float s_t, uint8_t* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = (uint8_t)orc_block_scale_code(amax[i], s_t);
+}
+
+/* ---------------------------------------------------- quantize rows (A1) */
+
+/* Quantize nrows rows of 128 FP32 values.  codes: one 4-bit code per byte,
+ * [nrows][128]; scales: E4M3 bytes, [nrows][8], block j covering elements
+ * 16j..16j+15 of the row ([EXPL] §量子化・逆量子化フロー, quantize in
+ * 16-element blocks on append). */
+void orc_quantize_rows(const float* x, size_t nrows, float s_t,
+                       uint8_t* codes, uint8_t* scales) {
+  for (size_t r = 0; r < nrows; ++r) {
+    const float* row = x + r * ORC_D;
+    for (unsigned j = 0; j < ORC_NBLK; ++j) {
+      float amax = 0.0f;
+      for (unsigned i = 0; i < ORC_BLOCK; ++i) {
+        float a = fabsf(row[j * ORC_BLOCK + i]);
+        if (a > amax) amax = a;
+      }
+      unsigned sb = orc_block_scale_code(amax, s_t);
+      scales[r * ORC_NBLK + j] = (uint8_t)sb;
+      for (unsigned i = 0; i < ORC_BLOCK; ++i) {
+        unsigned e = j * ORC_BLOCK + i;
+        codes[r * ORC_D + e] = (uint8_t)orc_element_code(row[e], sb, s_t);
+      }
+    }
+  }
+}
+
+/* -------------------------------------------------- dequantize rows (A10) */
+
+/* x_hat = FP32( e2m1(code) * sb * s_t ): the two-level product of [EXPL]
+ * §E2M1 + 2レベルスケーリング, with s_t the decode-direction tensor scale.
+ * The product e2m1 * sb * s_t is exact in double (3 + 4 + 24 bits), so the
+ * cast gives one FP32 rounding. */
+float orc_dequant_value(unsigned code, unsigned sb_code, float s_t) {
+  double v = orc_e2m1_value(code) * orc_e4m3_value(sb_code) * (double)s_t;
+  return (float)v;
+}
+
+void orc_dequant_rows(const uint8_t* codes, const uint8_t* scales, size_t nrows,
+                      float s_t, float* out) {
+  for (size_t r = 0; r < nrows; ++r)
+    for (unsigned e = 0; e < ORC_D; ++e)
+      out[r * ORC_D + e] =
+          orc_dequant_value(codes[r * ORC_D + e], scales[r * ORC_NBLK + e / ORC_BLOCK], s_t);
+}
+
+/* FP32 -> bfloat16 bits, round to nearest even (NaN kept quiet). */
+uint16_t orc_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+    return (uint16_t)((u >> 16) | 0x0040u);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+void orc_f32_to_bf16_array(const float* x, size_t n, uint16_t* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(x[i]);
+}
+
+/* ----------------------------------------------------------- attention */
+
+/* Softmax attention of Hq query rows of one sequence over its first L cached
+ * tokens, reading the dequantized cache ([EXPL] §量子化・逆量子化フロー:
+ * dequantize before the attention math; [TRTL] §Pourquoi FP8 est toujours le
+ * sol pour KV cache: FP32 accumulator -- here double).
+ *   q:       [Hq][128] FP32 (bf16 inputs widened exactly)
+ *   kcodes:  [L][Hkv][128] one code per byte;  kscales: [L][Hkv][8]
+ *   vcodes / vscales: same for V
+ *   out:     [Hq][128] FP32
+ * Query head h reads KV head h / (Hq / Hkv).  L == 0 gives zeros. */
+void orc_attend(const float* q, int Hq, int Hkv,
+                const uint8_t* kcodes, const uint8_t* kscales, float s_tk,
+                const uint8_t* vcodes, const uint8_t* vscales, float s_tv,
+                int L, double scale, double* work /* >= L doubles */,
+                float* out) {
+  int G = Hq / Hkv;
+  for (int h = 0; h < Hq; ++h) {
+    int kvh = h / G;
+    const float* qh = q + (size_t)h * ORC_D;
+    if (L <= 0) {
+      for (int d = 0; d < ORC_D; ++d) out[(size_t)h * ORC_D + d] = 0.0f;
+      continue;
+    }
+    double mx = -INFINITY;
+    for (int t = 0; t < L; ++t) {
+      size_t row = (size_t)t * Hkv + kvh;
+      double s = 0.0;
+      for (int d = 0; d < ORC_D; ++d) {
+        float kh = orc_dequant_value(kcodes[row * ORC_D + d],
+                                     kscales[row * ORC_NBLK + d / ORC_BLOCK], s_tk);
+        s += (double)qh[d] * (double)kh;
+      }
+      s *= scale;
+      work[t] = s;
+      if (s > mx) mx = s;
+    }
+    double den = 0.0;
+    double num[ORC_D];
+    for (int d = 0; d < ORC_D; ++d) num[d] = 0.0;
+    for (int t = 0; t < L; ++t) {
+      size_t row = (size_t)t * Hkv + kvh;
+      double p = exp(work[t] - mx);
+      den += p;
+      for (int d = 0; d < ORC_D; ++d) {
+        float vh = orc_dequant_value(vcodes[row * ORC_D + d],
+                                     vscales[row * ORC_NBLK + d / ORC_BLOCK], s_tv);
+        num[d] += p * (double)vh;
+      }
+    }
+    for (int d = 0; d < ORC_D; ++d) out[(size_t)h * ORC_D + d] = (float)(num[d] / den);
+  }
+}
+
+/* Causal chunk: query i of a chunk of T queries sits at absolute position
+ * prefix + i and attends to cached tokens 0 .. prefix + i.  Row i of q and
+ * out is [Hq][128].  Only the listed query indices are computed (rows[]),
+ * so a caller can sample a large chunk. */
+void orc_prefill_rows(const float* q /*[nrows][Hq][128]*/, const int* rows, int nrows,
+                      int Hq, int Hkv,
+                      const uint8_t* kcodes, const uint8_t* kscales, float s_tk,
+                      const uint8_t* vcodes, const uint8_t* vscales, float s_tv,
+                      int prefix, int causal, int total_len, double scale,
+                      double* work, float* out /*[nrows][Hq][128]*/) {
+  for (int r = 0; r < nrows; ++r) {
+    int L = causal ? prefix + rows[r] + 1 : total_len;
+    orc_attend(q + (size_t)r * Hq * ORC_D, Hq, Hkv, kcodes, kscales, s_tk,
+               vcodes, vscales, s_tv, L, scale, work, out + (size_t)r * Hq * ORC_D);
+  }
+}
