@@ -1,0 +1,337 @@
+"""Benchmark of the NVFP4 KV-cache hot path on one MI355X.
+
+A step is one decode iteration of the paged large-batch workload (batch 128,
+32 query / 8 KV heads, head_dim 128, context lengths U[1024, 8192], 16-token
+pages placed by a seeded permutation): quantize-and-append one new K/V token
+per sequence (nvfp4_kv_append), then decode attention over the whole NVFP4
+cache (nvfp4_decode_attn).  The cache, queries and new tokens are resident in
+HBM before timing starts.  Each step appends at the same position, so every
+step does identical work.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  `value` is the step's algorithmic bytes (cache bytes
+read by decode at 0.5625 B/element, plus the append's bf16 input and NVFP4
+output, plus queries and outputs) per second.  `roofline` is for the decode
+kernels, timed with HIP events on their stream.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.  `extra` holds the other
+measured paths (bulk append, prefill, the other decode workloads).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4-KV decode attention HBM GB/s (% of peak) + append quantize GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+BYTES_PER_TOKEN_HEAD = 2 * 128 * 0.5625   # K and V, codes + scales
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gen_decode(w, threads=16):
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(w.kv, range(w.B)))
+
+
+def build_cache(api, torch, w, data, s_tk, s_tv, chunk=16):
+    from decode_attention_nvfp4_amd.workloads import round_bf16  # noqa: F401  (inputs already bf16)
+    cache = api.KVCache(w.num_pages, w.Hkv, s_tk, s_tv, fill=0)
+    pt = torch.from_numpy(w.page_table).cuda()
+    for b0 in range(0, w.B, chunk):
+        idx = range(b0, min(w.B, b0 + chunk))
+        k = np.concatenate([data[b][0] for b in idx])
+        v = np.concatenate([data[b][1] for b in idx])
+        seq = np.concatenate([np.full(len(data[b][0]), b, np.int32) for b in idx])
+        pos = np.concatenate([np.arange(len(data[b][0]), dtype=np.int32) for b in idx])
+        api.append(cache, torch.from_numpy(k).to(torch.bfloat16).cuda(),
+                   torch.from_numpy(v).to(torch.bfloat16).cuda(),
+                   torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), pt)
+    torch.cuda.synchronize()
+    return cache, pt
+
+
+def device_scale(api, torch, arrays):
+    """Calibrate s_t on the device: exact amax of every chunk, then the max."""
+    amax = 0.0
+    for a in arrays:
+        t = torch.from_numpy(a).to(torch.bfloat16).cuda()
+        amax = max(amax, api.abs_max(t).item())
+    return api.tensor_scale_from_amax(amax), amax
+
+
+def time_region(torch, fn, iters, stream):
+    """Average milliseconds of fn() over iters launches, HIP events on stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline(w, data, s_tk, s_tv, q, threads):
+    """The oracle, untuned, on 16 seeded sequences of the same step."""
+    import oracle
+    rng = np.random.default_rng(7)
+    sample = sorted(rng.choice(w.B, 16, replace=False).tolist())
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        codes = list(ex.map(lambda b: (*oracle.quantize_rows(data[b][0], s_tk),
+                                       *oracle.quantize_rows(data[b][1], s_tv)), sample))
+    t0 = time.perf_counter()
+    oracle.decode_batch(q[sample], codes, w.Hkv, s_tk, s_tv, threads=threads)
+    dt = time.perf_counter() - t0
+    nbytes = sum(int(w.lens[b]) for b in sample) * w.Hkv * BYTES_PER_TOKEN_HEAD
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"decode attention of 16 of the 128 sequences (seeded), all heads, full length "
+                      f"({nbytes / 1e6:.1f} MB of NVFP4 cache)"}
+
+
+def bench_prefill(api, torch, stream, iters=3):
+    from decode_attention_nvfp4_amd import workloads as W
+    pw = W.PrefillWorkload()
+    kp, vp = pw.prefix_kv()
+    kc, vc = pw.chunk_kv()
+    s_tk, _ = device_scale(api, torch, [kp, kc])
+    s_tv, _ = device_scale(api, torch, [vp, vc])
+    cache = api.KVCache(pw.num_pages, pw.Hkv, s_tk, s_tv, fill=0)
+    pt = torch.from_numpy(pw.page_table()).cuda()
+    dev = lambda a: torch.from_numpy(a).to(torch.bfloat16).cuda()  # noqa: E731
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()  # noqa: E731
+    api.append(cache, dev(kp), dev(vp), i32(np.zeros(pw.prefix)), i32(np.arange(pw.prefix)), pt)
+    kcd, vcd = dev(kc), dev(vc)
+    seq, pos = i32(np.zeros(pw.T)), i32(pw.prefix + np.arange(pw.T))
+    q = dev(pw.q())
+    out = torch.empty((pw.T, pw.Hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.prefill_workspace_bytes(pw.T, pw.Hq, pw.Hkv, pw.prefix), dtype=torch.uint8,
+                     device="cuda")
+
+    def chunk_append():
+        api.append(cache, kcd, vcd, seq, pos, pt)
+
+    def attend():
+        api.prefill(cache, q, pt[0], pw.prefix, causal=True, workspace=ws, out=out)
+
+    chunk_append(); attend()
+    torch.cuda.synchronize()
+    t_app = time_region(torch, chunk_append, iters, stream)
+    t_att = time_region(torch, attend, iters, stream)
+    flops = 4.0 * 128 * pw.Hq * sum(pw.prefix + i + 1 for i in range(pw.T))
+    app_bytes = pw.T * pw.Hkv * 128 * 2 * (2 + 0.5625)
+    return {
+        "workload": "chunked prefill: 2048 causal queries after a 32768-token NVFP4 prefix, 64 q / 8 kv heads",
+        "attention_ms": round(t_att, 4), "tflops": round(flops / t_att / 1e9, 2),
+        "frac_fp8_peak": round(flops / t_att / 1e9 / FP8_PEAK_TFLOPS, 4),
+        "chunk_append_ms": round(t_app, 4), "chunk_append_gbs": round(app_bytes / t_app / 1e6, 1),
+    }
+
+
+def bench_small_decode(api, torch, stream, cfg, iters=20):
+    """Decode of configurations 2 (GQA batch 8, L 4096) and 3 (L 65536).  The
+    caches fit in the 256 MB last-level cache; to read from HBM the timing
+    rotates over 4 replicas (> 1 GB together with the flush buffer)."""
+    from decode_attention_nvfp4_amd import workloads as W
+    w = W.decode_workload(cfg)
+    data = gen_decode(w)
+    s_tk, _ = device_scale(api, torch, [d[0] for d in data])
+    s_tv, _ = device_scale(api, torch, [d[1] for d in data])
+    reps = [build_cache(api, torch, w, data, s_tk, s_tv) for _ in range(4)]
+    q = torch.from_numpy(w.q(0)).to(torch.bfloat16).cuda()
+    lens = torch.from_numpy(w.lens).cuda()
+    L = int(w.lens.max())
+    out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, api.decode_workspace_bytes(w.B, w.Hq, w.Hkv, L)), dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    state = {"i": 0}
+
+    def one():
+        c, pt = reps[state["i"] % 4]
+        state["i"] += 1
+        api.decode(c, q, pt, lens, L, workspace=ws, out=out)
+
+    one(); torch.cuda.synchronize()
+    # cold: flush the caches between launches; time only the decode launches
+    times = []
+    for _ in range(iters):
+        flush.fill_(1)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        one()
+        e.record(stream)
+        e.synchronize()
+        times.append(s.elapsed_time(e))
+    t_cold = float(np.median(times))
+    t_warm = time_region(torch, lambda: api.decode(reps[0][0], q, reps[0][1], lens, L, workspace=ws, out=out),
+                         iters, stream)
+    nbytes = int(w.lens.sum()) * w.Hkv * BYTES_PER_TOKEN_HEAD
+    return {"workload": f"decode config {cfg}: batch {w.B}, {w.Hq}/{w.Hkv} heads, L {L}",
+            "cache_mb": round(nbytes / 1e6, 2), "cold_us": round(t_cold * 1e3, 2),
+            "cold_gbs": round(nbytes / t_cold / 1e6, 1), "warm_us": round(t_warm * 1e3, 2),
+            "warm_gbs": round(nbytes / t_warm / 1e6, 1),
+            "splits": api.decode_num_splits(w.B, w.Hkv, L)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the NVFP4 KV hot path here is a "
+              "single-GPU build and no multi-GPU run is defined.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decode_attention_nvfp4_amd import api
+    from decode_attention_nvfp4_amd import workloads as W
+
+    api.lib()
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    threads = min(16, os.cpu_count() or 1)
+
+    # ---- workload: paged large-batch decode
+    t0 = time.time()
+    w = W.decode_workload(4)
+    data = gen_decode(w, threads)
+    log(f"generated {int(w.lens.sum())} tokens x {w.Hkv} heads in {time.time() - t0:.1f}s")
+    s_tk, amax_k = device_scale(api, torch, [d[0] for d in data])
+    s_tv, amax_v = device_scale(api, torch, [d[1] for d in data])
+
+    # bulk append of the whole cache: timed (HIP events) as the append GB/s
+    cache = api.KVCache(w.num_pages, w.Hkv, s_tk, s_tv, fill=0)
+    pt = torch.from_numpy(w.page_table).cuda()
+    kd = torch.from_numpy(np.concatenate([d[0] for d in data])).to(torch.bfloat16).cuda()
+    vd = torch.from_numpy(np.concatenate([d[1] for d in data])).to(torch.bfloat16).cuda()
+    seq = torch.from_numpy(np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(w.lens)])).cuda()
+    pos = torch.from_numpy(np.concatenate([np.arange(int(L), dtype=np.int32) for L in w.lens])).cuda()
+    ntok = kd.shape[0]
+
+    def bulk():
+        api.append(cache, kd, vd, seq, pos, pt)
+
+    bulk(); torch.cuda.synchronize()
+    t_bulk = time_region(torch, bulk, 3, stream)
+    bulk_bytes = ntok * w.Hkv * 128 * 2 * (2 + 0.5625) + ntok * 8
+    del kd, vd
+    q_np = w.q(0)
+    q = torch.from_numpy(q_np).to(torch.bfloat16).cuda()
+    knew, vnew = w.append_kv(0)
+    knew = torch.from_numpy(knew).to(torch.bfloat16).cuda()
+    vnew = torch.from_numpy(vnew).to(torch.bfloat16).cuda()
+    bidx = torch.arange(w.B, dtype=torch.int32, device="cuda")
+    newpos = torch.from_numpy(w.lens.astype(np.int32)).cuda()          # append at position L_b
+    lens1 = torch.from_numpy((w.lens + 1).astype(np.int32)).cuda()     # then attend L_b + 1 tokens
+    Lmax = int(w.lens.max()) + 1
+    out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
+    ws_bytes = api.decode_workspace_bytes(w.B, w.Hq, w.Hkv, Lmax)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def append_step():
+        api.append(cache, knew, vnew, bidx, newpos, pt)
+
+    def decode_step():
+        api.decode(cache, q, pt, lens1, Lmax, workspace=ws, out=out)
+
+    def step():
+        append_step()
+        decode_step()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronized on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    # per-kernel timing with HIP events on the launch stream
+    t_dec = time_region(torch, decode_step, args.steps, stream)
+    t_app = time_region(torch, append_step, args.steps, stream)
+
+    cache_bytes = int((w.lens + 1).sum()) * w.Hkv * BYTES_PER_TOKEN_HEAD
+    q_out_bytes = w.B * w.Hq * 128 * (2 + 4)
+    app_bytes = w.B * w.Hkv * 128 * 2 * (2 + 0.5625)
+    step_bytes = cache_bytes + q_out_bytes + app_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = cache_bytes / (t_dec * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/Q; no model weights)",
+        "config": {
+            "workload": "paged decode step: append 1 token/seq + decode attention; batch 128, 32 q / 8 kv "
+                        "heads, head_dim 128, context U[1024,8192] (seeded), 16-token pages by seeded "
+                        "permutation, NVFP4 cache",
+            "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": 128,
+            "total_context_tokens": int((w.lens + 1).sum()), "splits": api.decode_num_splits(w.B, w.Hkv, Lmax),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "nvfp4 decode_kernel + merge_kernel (one nvfp4_decode_attn call)",
+            "bytes_per_launch": cache_bytes, "avg_ms": round(t_dec, 5),
+        },
+        "extra": {
+            "decode_ms": round(t_dec, 5), "append_step_us": round(t_app * 1e3, 2),
+            "bulk_append": {"tokens": ntok, "ms": round(t_bulk, 3),
+                            "gbs": round(bulk_bytes / (t_bulk * 1e-3) / 1e9, 1),
+                            "frac_hbm_peak": round(bulk_bytes / (t_bulk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "tensor_amax": {"k": amax_k, "v": amax_v},
+        },
+    }
+    if not args.no_extra:
+        del cache
+        torch.cuda.empty_cache()
+        for cfg in (2, 3):
+            try:
+                res["extra"][f"decode_cfg{cfg}"] = bench_small_decode(api, torch, stream, cfg)
+            except Exception as e:  # noqa: BLE001
+                res["extra"][f"decode_cfg{cfg}"] = {"error": repr(e)}
+            log(f"decode config {cfg}: {res['extra'][f'decode_cfg{cfg}']}")
+        try:
+            res["extra"]["prefill_cfg5"] = bench_prefill(api, torch, stream)
+        except Exception as e:  # noqa: BLE001
+            res["extra"]["prefill_cfg5"] = {"error": repr(e)}
+        log(f"prefill: {res['extra']['prefill_cfg5']}")
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, data, s_tk, s_tv, q_np, threads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

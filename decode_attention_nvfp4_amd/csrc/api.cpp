@@ -1,0 +1,317 @@
+// api.cpp -- the C ABI declared in include/nvfp4kv.h: argument validation,
+// the decode split planner, workspace sizing and kernel launches.
+#include "nvfp4kv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "internal.h"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return NVFP4_OK;
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+
+int32_t check_cache(const nvfp4_kv_cache* c) {
+  if (!c) return fail(NVFP4_ERR_INVALID_ARG, "cache is NULL");
+  if (c->head_dim != NVFP4_HEAD_DIM)
+    return fail(NVFP4_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", c->head_dim);
+  if (c->page_size != NVFP4_PAGE_SIZE)
+    return fail(NVFP4_ERR_UNSUPPORTED, "page_size %d is not supported (only 16)", c->page_size);
+  if (c->num_pages <= 0 || c->num_kv_heads <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "num_pages (%d) and num_kv_heads (%d) must be > 0",
+                c->num_pages, c->num_kv_heads);
+  if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales)
+    return fail(NVFP4_ERR_INVALID_ARG, "a cache plane pointer is NULL");
+  if (!aligned16(c->k_codes) || !aligned16(c->k_scales) || !aligned16(c->v_codes) ||
+      !aligned16(c->v_scales))
+    return fail(NVFP4_ERR_INVALID_ARG, "cache planes must be 16-byte aligned");
+  if (!good_scale(c->k_tensor_scale) || !good_scale(c->v_tensor_scale))
+    return fail(NVFP4_ERR_INVALID_ARG, "tensor scales must be finite and > 0 (k %g, v %g)",
+                (double)c->k_tensor_scale, (double)c->v_tensor_scale);
+  return NVFP4_OK;
+}
+
+bool dtype_ok(int32_t d) { return d == NVFP4_DTYPE_F32 || d == NVFP4_DTYPE_BF16; }
+
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Decode split plan: pages per split starts at 64 and halves (down to 8)
+// until batch * kv_heads * splits reaches 4 workgroups per CU, so ragged and
+// short batches still fill the machine; splits = ceil(max_pages / pps).
+void plan_splits(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t num_splits, int cus,
+                 int32_t* splits, int32_t* pps) {
+  const int64_t max_pages = max_seq_len > 0 ? (max_seq_len + NVFP4_PAGE_SIZE - 1) / NVFP4_PAGE_SIZE : 1;
+  int64_t per;
+  if (num_splits > 0) {
+    per = (max_pages + num_splits - 1) / num_splits;
+  } else {
+    per = 64;
+    const int64_t units = (int64_t)batch * hkv;
+    while (per > 8 && units * ((max_pages + per - 1) / per) < 4LL * cus) per /= 2;
+  }
+  if (per < 1) per = 1;
+  *pps = (int32_t)per;
+  *splits = (int32_t)((max_pages + per - 1) / per);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int32_t status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARG: return "invalid argument";
+    case NVFP4_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+    case NVFP4_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* nvfp4_last_error(void) { return g_err; }
+
+size_t nvfp4_kv_plane_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t plane) {
+  if (num_pages <= 0 || num_kv_heads <= 0) return 0;
+  const size_t slabs = (size_t)num_pages * num_kv_heads;
+  switch (plane) {
+    case 0: case 2: return slabs * (NVFP4_PAGE_SIZE * NVFP4_HEAD_DIM / 2);
+    case 1: case 3: return slabs * (NVFP4_PAGE_SIZE * NVFP4_HEAD_DIM / NVFP4_BLOCK);
+    default: return 0;
+  }
+}
+
+size_t nvfp4_kv_cache_bytes(int32_t num_pages, int32_t num_kv_heads) {
+  size_t t = 0;
+  for (int p = 0; p < 4; ++p) t += nvfp4_kv_plane_bytes(num_pages, num_kv_heads, p);
+  return t;
+}
+
+float nvfp4_tensor_scale_from_amax(float amax) {
+  if (!std::isfinite(amax) || !(amax > 0.0f)) return 0.0f;
+  volatile float den = 2688.0f;   // 6 * 448, IEEE division
+  return amax / den;
+}
+
+int32_t nvfp4_abs_max(const void* x, int32_t dtype, int64_t n, float* amax_out, void* stream) {
+  g_err[0] = 0;
+  if (!dtype_ok(dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (n < 0) return fail(NVFP4_ERR_INVALID_ARG, "n < 0");
+  if (!amax_out || (n > 0 && !x)) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer");
+  return hip_status(launch_absmax(x, dtype == NVFP4_DTYPE_F32, n, amax_out, (hipStream_t)stream),
+                    "abs_max launch");
+}
+
+int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
+                        int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                        const int32_t* tok_pos, const int32_t* page_table,
+                        int32_t max_pages_per_seq, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  if (!dtype_ok(dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (n_tok < 0) return fail(NVFP4_ERR_INVALID_ARG, "n_tok < 0");
+  if (max_pages_per_seq <= 0) return fail(NVFP4_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
+  if (n_tok == 0) return NVFP4_OK;
+  if (!k_new || !v_new || !tok_seq || !tok_pos || !page_table)
+    return fail(NVFP4_ERR_INVALID_ARG, "NULL input pointer");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(NVFP4_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
+  AppendArgs a;
+  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
+  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
+  a.k_scale = cache->k_tensor_scale; a.v_scale = cache->v_tensor_scale;
+  a.k_six_st = 6.0 * (double)cache->k_tensor_scale;
+  a.v_six_st = 6.0 * (double)cache->v_tensor_scale;
+  a.k_new = k_new; a.v_new = v_new;
+  a.tok_seq = tok_seq; a.tok_pos = tok_pos; a.page_table = page_table;
+  a.max_pages = max_pages_per_seq; a.n_tok = n_tok; a.hkv = cache->num_kv_heads;
+  return hip_status(launch_append(a, dtype == NVFP4_DTYPE_F32, (hipStream_t)stream), "append launch");
+}
+
+int32_t nvfp4_kv_dequant(const nvfp4_kv_cache* cache, const int32_t* page_table_row,
+                         int32_t pos0, int32_t n, void* k_out, void* v_out,
+                         int32_t out_dtype, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  if (!dtype_ok(out_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "dtype %d", out_dtype);
+  if (pos0 < 0 || n < 0) return fail(NVFP4_ERR_INVALID_ARG, "pos0 and n must be >= 0");
+  if (n == 0) return NVFP4_OK;
+  if (!page_table_row) return fail(NVFP4_ERR_INVALID_ARG, "page_table_row is NULL");
+  if (!k_out && !v_out) return NVFP4_OK;
+  if ((k_out && !aligned16(k_out)) || (v_out && !aligned16(v_out)))
+    return fail(NVFP4_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  DequantArgs a;
+  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
+  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
+  a.k_scale = cache->k_tensor_scale; a.v_scale = cache->v_tensor_scale;
+  a.page_table_row = page_table_row; a.pos0 = pos0; a.n = n; a.hkv = cache->num_kv_heads;
+  a.k_out = k_out; a.v_out = v_out;
+  return hip_status(launch_dequant(a, out_dtype == NVFP4_DTYPE_F32, (hipStream_t)stream),
+                    "dequant launch");
+}
+
+int32_t nvfp4_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                                int32_t num_splits) {
+  if (batch <= 0 || num_kv_heads <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  int32_t s, pps;
+  plan_splits(batch, num_kv_heads, max_seq_len, num_splits, cu_count(), &s, &pps);
+  return s;
+}
+
+static size_t decode_ws(int32_t batch, int32_t hq, int32_t splits) {
+  if (splits <= 1) return 0;
+  const size_t n = (size_t)batch * hq * splits;
+  return align256(n * NVFP4_HEAD_DIM * sizeof(float)) + align256(n * sizeof(float));
+}
+
+size_t nvfp4_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t max_seq_len, int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 || num_splits < 0)
+    return 0;
+  int32_t s, pps;
+  plan_splits(batch, num_kv_heads, max_seq_len, num_splits, cu_count(), &s, &pps);
+  return decode_ws(batch, num_q_heads, s);
+}
+
+int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
+                          int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                          int32_t max_pages_per_seq, const int32_t* seq_lens,
+                          int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  if (!dtype_ok(q_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
+  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0 || max_pages_per_seq <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d, max_seq_len %d, splits %d, "
+                "max_pages %d)", batch, num_q_heads, max_seq_len, num_splits, max_pages_per_seq);
+  const int32_t hkv = cache->num_kv_heads;
+  if (num_q_heads % hkv != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, hkv);
+  const int32_t G = num_q_heads / hkv;
+  if (G > 16) return fail(NVFP4_ERR_UNSUPPORTED, "more than 16 query heads per KV head (%d)", G);
+  if ((int64_t)(max_seq_len + NVFP4_PAGE_SIZE - 1) / NVFP4_PAGE_SIZE > max_pages_per_seq)
+    return fail(NVFP4_ERR_INVALID_ARG, "max_seq_len %d needs more than max_pages_per_seq %d pages",
+                max_seq_len, max_pages_per_seq);
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(NVFP4_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (batch == 0) return NVFP4_OK;
+  if (!q || !page_table || !seq_lens || !out) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(NVFP4_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+  int32_t S, pps;
+  plan_splits(batch, hkv, max_seq_len, num_splits, cu_count(), &S, &pps);
+  const size_t need = decode_ws(batch, num_q_heads, S);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(NVFP4_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(NVFP4_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  DecodeArgs a;
+  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
+  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
+  a.q = q; a.page_table = page_table; a.seq_lens = seq_lens; a.out = out;
+  const size_t n = (size_t)batch * num_q_heads * S;
+  a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             align256(n * NVFP4_HEAD_DIM * sizeof(float)))
+                  : nullptr;
+  a.qk_scale = (float)((double)cache->k_tensor_scale * (double)softmax_scale * 1.4426950408889634);
+  a.v_scale = cache->v_tensor_scale;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch; a.hq = num_q_heads; a.hkv = hkv; a.group = G;
+  a.num_splits = S; a.pages_per_split = pps;
+  return hip_status(launch_decode(a, q_dtype == NVFP4_DTYPE_F32, (hipStream_t)stream), "decode launch");
+}
+
+static size_t prefill_ws(int32_t total, int32_t hkv) {
+  const size_t tiles = (size_t)(total + kPrefillTile - 1) / kPrefillTile;
+  return 2 * align256(tiles * kPrefillTile * NVFP4_HEAD_DIM * (size_t)hkv);
+}
+
+size_t nvfp4_prefill_workspace_bytes(int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t prefix_len) {
+  (void)num_q_heads;
+  if (num_tokens < 0 || num_kv_heads <= 0 || prefix_len < 0) return 0;
+  return prefill_ws(prefix_len + num_tokens, num_kv_heads);
+}
+
+int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
+                           int32_t num_tokens, int32_t num_q_heads,
+                           const int32_t* page_table_row, int32_t prefix_len, int32_t causal,
+                           float softmax_scale, void* workspace, size_t workspace_bytes,
+                           float* out, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  if (!dtype_ok(q_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
+  if (num_tokens < 0 || prefix_len < 0 || num_q_heads <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "bad sizes (tokens %d, prefix %d, heads %d)", num_tokens,
+                prefix_len, num_q_heads);
+  const int32_t hkv = cache->num_kv_heads;
+  if (num_q_heads % hkv != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, hkv);
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(NVFP4_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if ((int64_t)prefix_len + num_tokens > (int64_t)1 << 30)
+    return fail(NVFP4_ERR_INVALID_ARG, "context too long");
+  if (num_tokens == 0) return NVFP4_OK;
+  if (!q || !page_table_row || !out) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(NVFP4_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
+  const int32_t total = prefix_len + num_tokens;
+  const size_t need = prefill_ws(total, hkv);
+  if (!workspace || workspace_bytes < need)
+    return fail(NVFP4_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(NVFP4_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  PrefillArgs a;
+  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
+  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
+  a.q = q; a.page_table_row = page_table_row; a.out = out;
+  a.k8 = static_cast<uint8_t*>(workspace);
+  a.v8 = static_cast<uint8_t*>(workspace) + need / 2;
+  a.k_scale = cache->k_tensor_scale; a.v_scale = cache->v_tensor_scale;
+  a.softmax_scale = softmax_scale;
+  a.T = num_tokens; a.hq = num_q_heads; a.hkv = hkv; a.group = num_q_heads / hkv;
+  a.prefix = prefix_len; a.causal = causal ? 1 : 0; a.total = total;
+  a.num_tiles = (total + kPrefillTile - 1) / kPrefillTile;
+  return hip_status(launch_prefill(a, q_dtype == NVFP4_DTYPE_F32, (hipStream_t)stream),
+                    "prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+// codec.hip -- quantize-on-append, dequantize, and tensor amax kernels.
+//
+// Quantize-on-append follows the flow of "NVIDIA解説: NVFP4 KV Cacheで長コン
+// テキストLLM推論を最適化" (section 量子化・逆量子化フロー): each new K/V row is
+// quantized in 16-element blocks and written to the NVFP4 cache.  The block
+// scale and element rounding rules are stated in include/nvfp4kv.h.
+//
+// Thread mapping: 16 lanes own one (token, head) row of 128 elements; lane i
+// owns elements 8i..8i+7 (half of block i/2) and exchanges its half-block
+// amax with lane i^1.  A 256-thread workgroup handles 16 rows.
+#include "common.h"
+#include "internal.h"
+
+namespace nvfp4 {
+
+template <bool F32IN>
+__device__ __forceinline__ void load8(const void* base, size_t row, int lane16, float x[8]) {
+  if (F32IN) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + row * kD + lane16 * 8);
+    float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * kD + lane16 * 8);
+    uint4 a = *p;
+    x[0] = bf16_lo(a.x); x[1] = bf16_hi(a.x); x[2] = bf16_lo(a.y); x[3] = bf16_hi(a.y);
+    x[4] = bf16_lo(a.z); x[5] = bf16_hi(a.z); x[6] = bf16_lo(a.w); x[7] = bf16_hi(a.w);
+  }
+}
+
+// Returns the packed codes of this lane's 8 elements; *sb gets the block
+// scale code of its block.
+__device__ __forceinline__ uint32_t quantize_half_block(const float x[8], float s_t, double six_st,
+                                                        uint32_t* sb) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
+  a = fmaxf(a, __shfl_xor(a, 1));
+  uint32_t code = block_scale_code(a, six_st);
+  *sb = code;
+  return encode8(x, code, s_t);
+}
+
+template <bool F32IN>
+__global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
+  const int lane16 = threadIdx.x & 15;
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);     // (token, head)
+  if (row >= (size_t)p.n_tok * p.hkv) return;
+  const int tok = (int)(row / p.hkv);
+  const int h = (int)(row - (size_t)tok * p.hkv);
+  const int seq = p.tok_seq[tok];
+  const int pos = p.tok_pos[tok];
+  const int page = p.page_table[(size_t)seq * p.max_pages + pos / kPage];
+  const int slot = pos % kPage;
+  const size_t slab = (size_t)page * p.hkv + h;
+
+  float x[8];
+  uint32_t sb;
+  // K: token-major codes [16][64 B], token-major scales [16][8]
+  load8<F32IN>(p.k_new, row, lane16, x);
+  uint32_t w = quantize_half_block(x, p.k_scale, p.k_six_st, &sb);
+  *reinterpret_cast<uint32_t*>(p.k_codes + slab * kSlab + slot * 64 + lane16 * 4) = w;
+  if ((lane16 & 1) == 0) p.k_scales[slab * kScaleSlab + slot * kNBlk + (lane16 >> 1)] = (uint8_t)sb;
+
+  // V: codes [group 4][byte 64][token 4], scales [block 8][token 16]
+  load8<F32IN>(p.v_new, row, lane16, x);
+  w = quantize_half_block(x, p.v_scale, p.v_six_st, &sb);
+  uint8_t* vc = p.v_codes + slab * kSlab + (slot >> 2) * 256 + (slot & 3);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) vc[(lane16 * 4 + k) * 4] = (uint8_t)(w >> (8 * k));
+  if ((lane16 & 1) == 0) p.v_scales[slab * kScaleSlab + (lane16 >> 1) * kPage + slot] = (uint8_t)sb;
+}
+
+hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
+  size_t rows = (size_t)a.n_tok * a.hkv;
+  unsigned grid = (unsigned)((rows + 15) / 16);
+  if (f32) append_kernel<true><<<grid, 256, 0, s>>>(a);
+  else append_kernel<false><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- dequantize
+
+template <bool F32OUT>
+__global__ void __launch_bounds__(256) dequant_kernel(DequantArgs p) {
+  const int lane16 = threadIdx.x & 15;
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (row >= (size_t)p.n * p.hkv) return;
+  const int i = (int)(row / p.hkv);
+  const int h = (int)(row - (size_t)i * p.hkv);
+  const int pos = p.pos0 + i;
+  const int page = p.page_table_row[pos / kPage];
+  const int slot = pos % kPage;
+  const size_t slab = (size_t)page * p.hkv + h;
+  for (int kv = 0; kv < 2; ++kv) {
+    void* out = kv ? p.v_out : p.k_out;
+    if (!out) continue;
+    uint32_t w, sb;
+    float st;
+    if (kv == 0) {
+      w = *reinterpret_cast<const uint32_t*>(p.k_codes + slab * kSlab + slot * 64 + lane16 * 4);
+      sb = p.k_scales[slab * kScaleSlab + slot * kNBlk + (lane16 >> 1)];
+      st = p.k_scale;
+    } else {
+      const uint8_t* vc = p.v_codes + slab * kSlab + (slot >> 2) * 256 + (slot & 3);
+      w = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w |= (uint32_t)vc[(lane16 * 4 + k) * 4] << (8 * k);
+      sb = p.v_scales[slab * kScaleSlab + (lane16 >> 1) * kPage + slot];
+      st = p.v_scale;
+    }
+    float sbf = e4m3_to_float(sb);
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t c = (w >> (4 * j)) & 15u;
+      // E2M1 magnitude from its bit fields: exponent bias 1, field 0 subnormal
+      uint32_t e = (c >> 1) & 3u, m = c & 1u;
+      float mag = e == 0u ? 0.5f * (float)m : (1.0f + 0.5f * (float)m) * (float)(1u << (e - 1u));
+      float v = (mag * sbf) * st;            // mag * sbf is exact; one rounding
+      y[j] = (c & 8u) ? -v : v;
+    }
+    if (F32OUT) {
+      float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + row * kD + lane16 * 8);
+      o[0] = make_float4(y[0], y[1], y[2], y[3]);
+      o[1] = make_float4(y[4], y[5], y[6], y[7]);
+    } else {
+      uint4 o;
+      o.x = float_to_bf16_bits(y[0]) | (float_to_bf16_bits(y[1]) << 16);
+      o.y = float_to_bf16_bits(y[2]) | (float_to_bf16_bits(y[3]) << 16);
+      o.z = float_to_bf16_bits(y[4]) | (float_to_bf16_bits(y[5]) << 16);
+      o.w = float_to_bf16_bits(y[6]) | (float_to_bf16_bits(y[7]) << 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + row * kD + lane16 * 8) = o;
+    }
+  }
+}
+
+hipError_t launch_dequant(const DequantArgs& a, bool f32, hipStream_t s) {
+  size_t rows = (size_t)a.n * a.hkv;
+  unsigned grid = (unsigned)((rows + 15) / 16);
+  if (f32) dequant_kernel<true><<<grid, 256, 0, s>>>(a);
+  else dequant_kernel<false><<<grid, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- abs max
+
+__global__ void zero_float_kernel(float* p) { *p = 0.0f; }
+
+template <bool F32IN>
+__global__ void __launch_bounds__(256) absmax_kernel(const void* x, int64_t n, float* out) {
+  float m = 0.0f;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) {
+    float v = F32IN ? static_cast<const float*>(x)[i]
+                    : __uint_as_float((uint32_t) static_cast<const uint16_t*>(x)[i] << 16);
+    m = fmaxf(m, fabsf(v));
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  // non-negative floats order like their bit patterns
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+}
+
+hipError_t launch_absmax(const void* x, bool f32, int64_t n, float* out, hipStream_t s) {
+  zero_float_kernel<<<1, 1, 0, s>>>(out);
+  if (n > 0) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (f32) absmax_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
+    else absmax_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

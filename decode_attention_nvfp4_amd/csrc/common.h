@@ -1,0 +1,163 @@
+// common.h -- device helpers shared by the NVFP4 KV-cache kernels (gfx950).
+//
+// Format facts used here ("NVIDIA解説: NVFP4 KV Cacheで長コンテキストLLM推論を
+// 最適化", section E2M1 + 2レベルスケーリング): E2M1 element codes, one E4M3
+// scale per 16 elements, one FP32 scale per tensor.  The E4M3 variant is OCP
+// E4M3FN (bias 7, largest finite 448), which is also gfx950's FP8 format.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kD = 128;        // head dimension
+constexpr int kPage = 16;      // tokens per page
+constexpr int kBlock = 16;     // elements per micro-block
+constexpr int kNBlk = kD / kBlock;
+constexpr int kSlab = kPage * kD / 2;        // code bytes per (page, head): 1024
+constexpr int kScaleSlab = kPage * kNBlk;    // scale bytes per (page, head): 128
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------ E4M3 decode
+
+// Exact value of a non-negative E4M3FN byte (sign ignored; 0x7F never used).
+__device__ __forceinline__ float e4m3_to_float(uint32_t b) {
+  uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  if (e == 0u) return (float)m * 0x1p-9f;
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// Two E4M3 bytes (byte 0 and byte 1 of `w` when hi == false, bytes 2, 3 when
+// true) to two exact halves.  The conversion's scale operand only applies a
+// power of two; 1.0 leaves the values unchanged.
+__device__ __forceinline__ halfx2 e4m3x2_to_half(uint32_t w, bool hi) {
+  fp16x2 h = hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  return __builtin_bit_cast(halfx2, h);
+}
+
+// Two E2M1 codes (low nibble -> element 0, high nibble -> element 1) of byte
+// `sel` of `w` to two exact halves.
+template <int SEL>
+__device__ __forceinline__ halfx2 e2m1x2_to_half(uint32_t w) {
+  fp16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+  return __builtin_bit_cast(halfx2, h);
+}
+
+// ------------------------------------------------------ block scale (E4M3)
+
+// Nearest E4M3FN code to the exact quotient amax / (6 s_t), ties to the even
+// code, clamped to 448 (0x7E).  six_st = 6 * (double)s_t is exact.  The double
+// quotient q = RN(amax / six_st) cannot cross or land on an E4M3 midpoint
+// unless the exact quotient does: amax has 24 significant bits and
+// six_st * midpoint at most 2 + 24 + 5, so a non-zero distance from a midpoint
+// is at least ~2^-31 relative, far above double rounding (2^-53).
+__device__ __forceinline__ uint32_t block_scale_code(float amax, double six_st) {
+  double q = (double)amax / six_st;
+  if (!(q < 448.0)) return 0x7Eu;                 // also catches NaN / inf
+  if (q < 0x1p-6) return (uint32_t)rint(q * 512.0);   // subnormal spacing 2^-9
+  int e = ilogb(q);                                 // -6 .. 8
+  double r = rint(ldexp(q, 3 - e));                 // 8 .. 16, nearest-even
+  return (uint32_t)((e + 6) * 8 + (int)r);
+}
+
+// ------------------------------------------------------- element codes
+
+// Magnitude code (0..7) of |x| for exact step d = s_block * s_t (double):
+// the nearest E2M1 value to |x| / d, ties to the even code, clamped to 6.
+// Thresholds d * {1/4, 3/4, 5/4, 7/4, 5/2, 7/2, 5} are exact in double.
+__device__ __forceinline__ uint32_t e2m1_mag_exact(float x, double d) {
+  double ax = fabs((double)x);
+  uint32_t m = 0;
+  m += ax > d * 0.25;
+  m += ax >= d * 0.75;
+  m += ax > d * 1.25;
+  m += ax >= d * 1.75;
+  m += ax > d * 2.5;
+  m += ax >= d * 3.5;
+  m += ax > d * 5.0;
+  return m;
+}
+
+// Eight element codes of one half-block, packed as nibbles (element j in bits
+// 4j..4j+3).  Fast path: the hardware FP32->E2M1 conversion rounds to nearest
+// even (and saturates at 6) for every FP32 input; x * y_lo and x * y_hi
+// bracket the exact quotient x / d, so when both conversions agree the exact
+// code is that value (the rounding is monotone).  Otherwise the lane redoes
+// its eight elements with exact double thresholds.
+__device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t sb_code, float s_t) {
+  uint32_t signs = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) signs |= (__float_as_uint(x[j]) >> 31) << (4 * j + 3);
+  if (sb_code == 0u) return signs;                  // zero scale: magnitude 0
+  double d = (double)e4m3_to_float(sb_code) * (double)s_t;   // exact
+  double yd = 1.0 / d;
+  bool fast = yd < 1.0e37;
+  uint32_t lo = 0, hi = 0;
+  if (fast) {
+    float y_lo = (float)(yd * (1.0 - 0x1p-20));
+    float y_hi = (float)(yd * (1.0 + 0x1p-20));
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[0] * y_lo, x[1] * y_lo, 1.0f, 0);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[2] * y_lo, x[3] * y_lo, 1.0f, 1);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[4] * y_lo, x[5] * y_lo, 1.0f, 2);
+    lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[6] * y_lo, x[7] * y_lo, 1.0f, 3);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[0] * y_hi, x[1] * y_hi, 1.0f, 0);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[2] * y_hi, x[3] * y_hi, 1.0f, 1);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[4] * y_hi, x[5] * y_hi, 1.0f, 2);
+    hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[6] * y_hi, x[7] * y_hi, 1.0f, 3);
+  }
+  if (fast && lo == hi) return (lo & 0x77777777u) | signs;
+  uint32_t w = signs;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w |= e2m1_mag_exact(x[j], d) << (4 * j);
+  return w;
+}
+
+// bf16 bits -> float (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, nearest even (finite inputs)
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Cross-row reductions inside a wave64 (rows of 16 lanes).  permlane16_swap
+// with the same register on both sides yields, per lane, its own value and
+// the value of the lane 16 away in the paired row; permlane32_swap likewise
+// across the two halves.
+__device__ __forceinline__ float max_across_rows(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_across_rows(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float max_across_halves(float v) {
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float v) {
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,85 @@
+// internal.h -- argument blocks and launchers shared by the C-ABI layer
+// (api.cpp) and the kernels.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+struct AppendArgs {
+  uint8_t* k_codes;
+  uint8_t* k_scales;
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  float k_scale, v_scale;     // tensor scales s_t
+  double k_six_st, v_six_st;  // 6 * s_t, exact in double
+  const void* k_new;
+  const void* v_new;
+  const int32_t* tok_seq;
+  const int32_t* tok_pos;
+  const int32_t* page_table;
+  int32_t max_pages;
+  int32_t n_tok;
+  int32_t hkv;
+};
+
+struct DequantArgs {
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  float k_scale, v_scale;
+  const int32_t* page_table_row;
+  int32_t pos0, n, hkv;
+  void* k_out;
+  void* v_out;
+};
+
+struct DecodeArgs {
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const void* q;              // [B][Hq][128]
+  const int32_t* page_table;  // [B][max_pages]
+  const int32_t* seq_lens;    // [B]
+  float* out;                 // [B][Hq][128]
+  float* ws_o;                // [B][Hq][S][128]   (S > 1)
+  float* ws_lse;              // [B][Hq][S]        (S > 1)
+  float qk_scale;             // s_tK * softmax_scale * log2(e)
+  float v_scale;              // s_tV
+  int32_t max_pages;
+  int32_t batch, hq, hkv, group;
+  int32_t num_splits;
+  int32_t pages_per_split;
+};
+
+struct PrefillArgs {
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  const uint8_t* v_codes;
+  const uint8_t* v_scales;
+  const void* q;              // [T][Hq][128]
+  const int32_t* page_table_row;
+  float* out;                 // [T][Hq][128]
+  uint8_t* k8;                // workspace: FP8 K  [Hkv][tiles*64][128]
+  uint8_t* v8;                // workspace: FP8 V^T [Hkv][tiles][128][64]
+  float k_scale, v_scale;     // tensor scales
+  float softmax_scale;
+  int32_t T, hq, hkv, group;
+  int32_t prefix, causal;
+  int32_t total;              // prefix + T
+  int32_t num_tiles;          // ceil(total / 64)
+};
+
+hipError_t launch_append(const AppendArgs& a, bool f32_in, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, bool f32_out, hipStream_t s);
+hipError_t launch_absmax(const void* x, bool f32_in, int64_t n, float* out, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, bool f32_q, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s);
+
+constexpr int kPrefillTile = 64;   // keys per prefill tile
+
+}  // namespace nvfp4

@@ -47,9 +47,9 @@ S_Q, S_K, S_V, S_OUTLIER, S_DRIFT, S_LENS, S_PERM, S_APPEND = range(8)
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """FP32 -> nearest bfloat16 (ties to even), returned as FP32."""
     x = np.ascontiguousarray(x, np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    u = x.view(np.uint32)
+    u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return u.view(np.float32)
 
 
 def _streams(k: int):
@@ -176,6 +176,33 @@ def decode_workload(cfg: int, reserve_tokens: int = 16) -> DecodeWorkload:
                           page_table=pt, num_pages=num_pages, steps=steps,
                           outlier_channels=outliers, drift=drift,
                           _child_k=st[S_K].spawn(B), _child_v=st[S_V].spawn(B))
+
+
+def custom_decode(seed: int, B: int, Hq: int, Hkv: int, lens, dtype: str = "bf16",
+                  permute: bool = True, reserve_tokens: int = 16, steps: int = 0,
+                  outliers: bool = False) -> DecodeWorkload:
+    """A reduced decode workload for parity tests (seed streams 5000 + seed):
+    given sequence lengths, pages handed out from a seeded permutation (or
+    contiguously), optional x20 outlier channels."""
+    st = np.random.SeedSequence(5000 + seed).spawn(8)
+    lens = np.asarray(lens, np.int32)
+    pages_per_seq = [max(1, -(-(int(L) + reserve_tokens) // PAGE)) for L in lens]
+    total = int(sum(pages_per_seq))
+    order = (np.random.default_rng(st[S_PERM]).permutation(total) if permute
+             else np.arange(total)).astype(np.int32)
+    pt = np.zeros((B, max(pages_per_seq)), np.int32)
+    nxt = 0
+    for b in range(B):
+        pt[b, :pages_per_seq[b]] = order[nxt:nxt + pages_per_seq[b]]
+        nxt += pages_per_seq[b]
+    oc = None
+    if outliers:
+        rng = np.random.default_rng(st[S_OUTLIER])
+        oc = np.stack([rng.choice(D, 4, replace=False) for _ in range(Hkv)]).astype(np.int64)
+    w = DecodeWorkload(cfg=5000 + seed, name=f"custom{seed}", B=B, Hq=Hq, Hkv=Hkv, lens=lens, dtype=dtype,
+                       page_table=pt, num_pages=total, steps=steps, outlier_channels=oc,
+                       _child_k=st[S_K].spawn(B), _child_v=st[S_V].spawn(B))
+    return w
 
 
 @dataclass

@@ -1,0 +1,211 @@
+/*
+ * nvfp4kv.h -- C ABI of the NVFP4 KV-cache library for AMD Instinct MI355X
+ * (gfx950).  Plain C; no HIP, PyTorch or C++ types in any signature.
+ *
+ * The operations follow these source pages (cited by title and section):
+ *  [EXPL] "NVIDIA解説: NVFP4 KV Cacheで長コンテキストLLM推論を最適化 —
+ *          メモリ50%削減・TTFT 3倍高速化"
+ *  [GB10] "一個 Triton FP8 繞道補丁，為 DGX Spark 的 GB10 擠出多 17% 的 NVFP4 速度"
+ *  [RC17] "TensorRT-LLM rc17 が SM121（DGX Spark）向けに NVFP4 MoE バックエンドと
+ *          NVFP4 KV キャッシュを追加"
+ *  [TRTL] "Compilation d'inferences spécialisées en matériel FP8 et NVFP4 sur
+ *          Blackwell"
+ *
+ * Format ([EXPL] §E2M1 + 2レベルスケーリング): every K or V element is a 4-bit
+ * E2M1 code (1 sign, 2 exponent, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5,
+ * 2, 3, 4, 6); every 16 consecutive elements of one token's 128-wide head
+ * vector share one E4M3 (OCP E4M3FN) block scale; each of K and V has one
+ * FP32 tensor scale s_t, so x ~= e2m1 * s_block * s_t.
+ *
+ * Quantization rule (the pages leave it open; this library fixes it):
+ *   s_block = the E4M3 value nearest to amax16 / (6 * s_t), ties to the even
+ *             code, clamped to 448;
+ *   code    = the E2M1 value nearest to x / (s_block * s_t) in exact
+ *             arithmetic, ties to the even code, clamped to 6; the sign bit is
+ *             the sign of x; a zero block scale gives magnitude 0.
+ *   s_t is calibrated offline, e.g. amax(|X|) / (6 * 448)
+ *   (nvfp4_tensor_scale_from_amax); NVFP4 KV needs a calibrated scale rather
+ *   than a runtime switch ([RC17] §実務メモ).
+ * Dequantization multiplies by s_t, i.e. divides by the global encode scale
+ * 1/s_t ([GB10] §這個 80 行的 Triton 繞道).
+ *
+ * ---------------------------------------------------------------- layout
+ * The cache is paged: a page holds 16 consecutive tokens of one sequence for
+ * every KV head.  Four device planes, each [num_pages][num_kv_heads][slab]:
+ *
+ *   k_codes  slab 1024 B: [token 16][byte 64]; byte j of a token row holds
+ *            element 2j in its low nibble and element 2j+1 in its high nibble.
+ *   k_scales slab  128 B: [token 16][block 8]; block j covers elements
+ *            16j..16j+15.
+ *   v_codes  slab 1024 B: [token group 4][byte 64][token 4]; byte j of token
+ *            t (same nibble packing as K) sits at (t/4)*256 + j*4 + t%4.
+ *   v_scales slab  128 B: [block 8][token 16].
+ *
+ * Bytes per element: 0.5 (code) + 1/16 (scale) = 0.5625, i.e. 3.56x fewer
+ * than FP16 and 1.78x fewer than FP8 ([EXPL] §メモリ削減効果).
+ *
+ * ---------------------------------------------------------- conventions
+ *  - Every buffer is caller-owned device memory unless marked host.  The
+ *    library allocates nothing, keeps no pointer after a call returns and
+ *    holds no global state except a thread-local error string.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
+ *    work is enqueued on it; no call synchronizes.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    failed call enqueues nothing.  Device-resident indices (page tables,
+ *    sequence ids, positions, lengths) are trusted: they must lie within the
+ *    bounds stated below.
+ *  - Every entry returns an nvfp4_status.  nvfp4_last_error() describes the
+ *    most recent failure on the calling thread.
+ */
+#ifndef NVFP4KV_H
+#define NVFP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARG = 1,  /* null pointer, bad size, bad scale, misaligned plane */
+  NVFP4_ERR_UNSUPPORTED = 2,  /* head_dim != 128, page_size != 16, unknown dtype */
+  NVFP4_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+  NVFP4_ERR_HIP = 4           /* the HIP runtime reported an error */
+} nvfp4_status;
+
+typedef enum nvfp4_dtype {
+  NVFP4_DTYPE_F32 = 0,
+  NVFP4_DTYPE_BF16 = 1
+} nvfp4_dtype;
+
+#define NVFP4_HEAD_DIM 128
+#define NVFP4_PAGE_SIZE 16
+#define NVFP4_BLOCK 16
+
+/* Host description of a paged NVFP4 cache (one layer).  The four plane
+ * pointers are device memory laid out as in the header comment and must be
+ * 16-byte aligned.  Tensor scales must be finite and > 0. */
+typedef struct nvfp4_kv_cache {
+  uint8_t* k_codes;
+  uint8_t* k_scales;
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  float k_tensor_scale;
+  float v_tensor_scale;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t page_size;   /* must be 16 */
+  int32_t head_dim;    /* must be 128 */
+} nvfp4_kv_cache;
+
+/* Text of a status code (static storage). */
+const char* nvfp4_status_string(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+/* Bytes of one plane: plane 0 k_codes, 1 k_scales, 2 v_codes, 3 v_scales.
+ * Returns 0 for invalid arguments. */
+size_t nvfp4_kv_plane_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t plane);
+
+/* Bytes of all four planes: 2 * num_pages * 16 * num_kv_heads * 128 * 0.5625
+ * (the KV-memory formula of [EXPL] §KV Cacheのメモリボトルネック for one layer,
+ * 0.5625 bytes per element). */
+size_t nvfp4_kv_cache_bytes(int32_t num_pages, int32_t num_kv_heads);
+
+/* Tensor-scale calibration (step A0, host): amax / (6 * 448) in FP32.
+ * Returns 0 when amax is not finite or not > 0. */
+float nvfp4_tensor_scale_from_amax(float amax);
+
+/* amax_out[0] = max |x_i| over n elements of x (device), computed exactly on
+ * the device.  amax_out is one device float, overwritten.  n >= 0. */
+int32_t nvfp4_abs_max(const void* x, int32_t dtype, int64_t n, float* amax_out, void* stream);
+
+/* Quantize-on-append (step A1; [EXPL] §量子化・逆量子化フロー: new K/V are
+ * quantized in 16-element blocks and appended to the NVFP4 cache).
+ *   k_new, v_new : device [n_tok][num_kv_heads][128] of `dtype` (F32 or BF16)
+ *   tok_seq      : device int32 [n_tok], sequence index of each row, in
+ *                  [0, number of page-table rows)
+ *   tok_pos      : device int32 [n_tok], token position within its sequence;
+ *                  page_table[seq * max_pages_per_seq + pos / 16] must be a
+ *                  valid page (< num_pages), slot pos % 16
+ *   page_table   : device int32 [rows][max_pages_per_seq]
+ * Writes the 64 code bytes and 8 scale bytes of each (token, head) row of K
+ * and of V; nothing else in the cache changes.  Two rows of one call must
+ * not target the same (page, slot).  n_tok == 0 is a no-op. */
+int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
+                        int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                        const int32_t* tok_pos, const int32_t* page_table,
+                        int32_t max_pages_per_seq, void* stream);
+
+/* Dequantization (step A10, for checks and fallbacks): positions
+ * pos0 .. pos0+n-1 of the sequence whose page-table row is page_table_row
+ * (device int32, at least ceil((pos0+n)/16) entries) into k_out and v_out,
+ * each device [n][num_kv_heads][128] of out_dtype.  F32 output is
+ * FP32(e2m1 * s_block * s_t); BF16 output is that value rounded to nearest
+ * even.  Either output pointer may be NULL to skip it.  n == 0 is a no-op. */
+int32_t nvfp4_kv_dequant(const nvfp4_kv_cache* cache, const int32_t* page_table_row,
+                         int32_t pos0, int32_t n, void* k_out, void* v_out,
+                         int32_t out_dtype, void* stream);
+
+/* Number of context splits the decode planner uses (num_splits 0 = auto),
+ * on the current device. */
+int32_t nvfp4_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                                int32_t num_splits);
+
+/* Workspace bytes nvfp4_decode_attn needs for these arguments on the
+ * current device (0 if the plan uses a single split). */
+size_t nvfp4_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t max_seq_len, int32_t num_splits);
+
+/* Decode attention over the NVFP4 cache (steps A2-A8).  For each sequence b
+ * and query head h (KV head h / (num_q_heads / num_kv_heads)):
+ *   out[b][h] = softmax_t(q[b][h] . k_hat_t * softmax_scale) . v_hat_t,
+ *   t = 0 .. seq_lens[b]-1, with k_hat, v_hat the dequantized cache
+ * ([EXPL] §量子化・逆量子化フロー: dequantize, then attention; FP32
+ * accumulation as in [TRTL] §Pourquoi FP8 est toujours le sol pour KV cache).
+ *   q          : device [batch][num_q_heads][128], F32 or BF16
+ *   page_table : device int32 [batch][max_pages_per_seq]
+ *   seq_lens   : device int32 [batch], each in [0, max_seq_len];
+ *                ceil(seq_lens[b]/16) <= max_pages_per_seq
+ *   max_seq_len: host bound on seq_lens, used by the split planner
+ *   softmax_scale: > 0 and finite (1/sqrt(128) is the usual value)
+ *   num_splits : 0 = automatic, else the number of context splits
+ *   workspace  : device, >= nvfp4_decode_workspace_bytes(...) bytes (may be
+ *                NULL when that is 0)
+ *   out        : device FP32 [batch][num_q_heads][128]
+ * A sequence of length 0 yields zeros.  Results do not depend on the run:
+ * no atomics, fixed reduction order. */
+int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
+                          int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                          int32_t max_pages_per_seq, const int32_t* seq_lens,
+                          int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/* Workspace bytes nvfp4_prefill_attn needs. */
+size_t nvfp4_prefill_workspace_bytes(int32_t num_tokens, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t prefix_len);
+
+/* Chunked-prefill attention (step A9; [EXPL] §量子化・逆量子化フロー: the
+ * NVFP4 cache is expanded to FP8 and attention runs on FP8 operands with an
+ * FP32 accumulator).  The chunk's own K/V must already be appended.
+ *   q             : device [num_tokens][num_q_heads][128], F32 or BF16
+ *   page_table_row: device int32, ceil((prefix_len+num_tokens)/16) pages
+ *   causal != 0   : query i (absolute position prefix_len + i) attends to
+ *                   tokens 0 .. prefix_len + i; causal == 0: to all
+ *                   prefix_len + num_tokens tokens
+ *   out           : device FP32 [num_tokens][num_q_heads][128]
+ * num_tokens == 0 is a no-op. */
+int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
+                           int32_t num_tokens, int32_t num_q_heads,
+                           const int32_t* page_table_row, int32_t prefix_len, int32_t causal,
+                           float softmax_scale, void* workspace, size_t workspace_bytes,
+                           float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4KV_H */

@@ -44,6 +44,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_D 128      /* head dimension */
@@ -83,6 +84,9 @@ float orc_tensor_scale(const float* x, size_t n) {
   }
   return amax / 2688.0f;
 }
+
+/* s_t for a given amax (the same formula, for callers that reduce in pieces). */
+float orc_tensor_scale_from_amax(float amax) { return amax / 2688.0f; }
 
 float orc_abs_max(const float* x, size_t n) {
   float amax = 0.0f;
@@ -215,20 +219,12 @@ void orc_f32_to_bf16_array(const float* x, size_t n, uint16_t* out) {
 
 /* ----------------------------------------------------------- attention */
 
-/* Softmax attention of Hq query rows of one sequence over its first L cached
- * tokens, reading the dequantized cache ([EXPL] §量子化・逆量子化フロー:
- * dequantize before the attention math; [TRTL] §Pourquoi FP8 est toujours le
- * sol pour KV cache: FP32 accumulator -- here double).
- *   q:       [Hq][128] FP32 (bf16 inputs widened exactly)
- *   kcodes:  [L][Hkv][128] one code per byte;  kscales: [L][Hkv][8]
- *   vcodes / vscales: same for V
- *   out:     [Hq][128] FP32
- * Query head h reads KV head h / (Hq / Hkv).  L == 0 gives zeros. */
-void orc_attend(const float* q, int Hq, int Hkv,
-                const uint8_t* kcodes, const uint8_t* kscales, float s_tk,
-                const uint8_t* vcodes, const uint8_t* vscales, float s_tv,
-                int L, double scale, double* work /* >= L doubles */,
-                float* out) {
+/* Softmax attention of Hq query rows over L tokens of an already dequantized
+ * cache kh, vh ([L][Hkv][128] FP32).  Products and sums in double; query head
+ * h reads KV head h / (Hq / Hkv); L == 0 gives zeros. */
+static void attend_dequantized(const float* q, int Hq, int Hkv, const float* kh,
+                               const float* vh, int L, double scale, double* work,
+                               float* out) {
   int G = Hq / Hkv;
   for (int h = 0; h < Hq; ++h) {
     int kvh = h / G;
@@ -239,13 +235,9 @@ void orc_attend(const float* q, int Hq, int Hkv,
     }
     double mx = -INFINITY;
     for (int t = 0; t < L; ++t) {
-      size_t row = (size_t)t * Hkv + kvh;
+      const float* k = kh + ((size_t)t * Hkv + kvh) * ORC_D;
       double s = 0.0;
-      for (int d = 0; d < ORC_D; ++d) {
-        float kh = orc_dequant_value(kcodes[row * ORC_D + d],
-                                     kscales[row * ORC_NBLK + d / ORC_BLOCK], s_tk);
-        s += (double)qh[d] * (double)kh;
-      }
+      for (int d = 0; d < ORC_D; ++d) s += (double)qh[d] * (double)k[d];
       s *= scale;
       work[t] = s;
       if (s > mx) mx = s;
@@ -254,32 +246,64 @@ void orc_attend(const float* q, int Hq, int Hkv,
     double num[ORC_D];
     for (int d = 0; d < ORC_D; ++d) num[d] = 0.0;
     for (int t = 0; t < L; ++t) {
-      size_t row = (size_t)t * Hkv + kvh;
+      const float* v = vh + ((size_t)t * Hkv + kvh) * ORC_D;
       double p = exp(work[t] - mx);
       den += p;
-      for (int d = 0; d < ORC_D; ++d) {
-        float vh = orc_dequant_value(vcodes[row * ORC_D + d],
-                                     vscales[row * ORC_NBLK + d / ORC_BLOCK], s_tv);
-        num[d] += p * (double)vh;
-      }
+      for (int d = 0; d < ORC_D; ++d) num[d] += p * (double)v[d];
     }
     for (int d = 0; d < ORC_D; ++d) out[(size_t)h * ORC_D + d] = (float)(num[d] / den);
   }
 }
 
-/* Causal chunk: query i of a chunk of T queries sits at absolute position
- * prefix + i and attends to cached tokens 0 .. prefix + i.  Row i of q and
- * out is [Hq][128].  Only the listed query indices are computed (rows[]),
- * so a caller can sample a large chunk. */
-void orc_prefill_rows(const float* q /*[nrows][Hq][128]*/, const int* rows, int nrows,
-                      int Hq, int Hkv,
-                      const uint8_t* kcodes, const uint8_t* kscales, float s_tk,
-                      const uint8_t* vcodes, const uint8_t* vscales, float s_tv,
-                      int prefix, int causal, int total_len, double scale,
-                      double* work, float* out /*[nrows][Hq][128]*/) {
+/* Attention of Hq query rows of one sequence over its first L cached tokens:
+ * the cache is dequantized first, then attended ([EXPL] §量子化・逆量子化フロー:
+ * dequantize before the attention math; [TRTL] §Pourquoi FP8 est toujours le
+ * sol pour KV cache: FP32 accumulator -- here double).
+ *   q:       [Hq][128] FP32 (bf16 inputs widened exactly)
+ *   kcodes:  [L][Hkv][128] one code per byte;  kscales: [L][Hkv][8]
+ *   vcodes / vscales: same for V
+ *   work:    >= L doubles of scratch
+ *   out:     [Hq][128] FP32
+ * Returns 0, or -1 if scratch memory could not be allocated. */
+int orc_attend(const float* q, int Hq, int Hkv,
+               const uint8_t* kcodes, const uint8_t* kscales, float s_tk,
+               const uint8_t* vcodes, const uint8_t* vscales, float s_tv,
+               int L, double scale, double* work, float* out) {
+  size_t n = (size_t)(L > 0 ? L : 0) * Hkv;
+  float* kh = (float*)malloc((n ? n : 1) * ORC_D * sizeof(float));
+  float* vh = (float*)malloc((n ? n : 1) * ORC_D * sizeof(float));
+  if (!kh || !vh) { free(kh); free(vh); return -1; }
+  orc_dequant_rows(kcodes, kscales, n, s_tk, kh);
+  orc_dequant_rows(vcodes, vscales, n, s_tv, vh);
+  attend_dequantized(q, Hq, Hkv, kh, vh, L, scale, work, out);
+  free(kh);
+  free(vh);
+  return 0;
+}
+
+/* Causal chunk: query i of a chunk sits at absolute position prefix + i and
+ * attends to cached tokens 0 .. prefix + i (all total_len tokens when causal
+ * is 0).  Only the listed query indices rows[] are computed, so a caller can
+ * sample a large chunk.  q and out: [nrows][Hq][128]; the cache arrays hold
+ * total_len tokens.  Returns 0, or -1 on allocation failure. */
+int orc_prefill_rows(const float* q, const int* rows, int nrows, int Hq, int Hkv,
+                     const uint8_t* kcodes, const uint8_t* kscales, float s_tk,
+                     const uint8_t* vcodes, const uint8_t* vscales, float s_tv,
+                     int prefix, int causal, int total_len, double scale,
+                     double* work, float* out) {
+  size_t n = (size_t)total_len * Hkv;
+  float* kh = (float*)malloc((n ? n : 1) * ORC_D * sizeof(float));
+  float* vh = (float*)malloc((n ? n : 1) * ORC_D * sizeof(float));
+  if (!kh || !vh) { free(kh); free(vh); return -1; }
+  orc_dequant_rows(kcodes, kscales, n, s_tk, kh);
+  orc_dequant_rows(vcodes, vscales, n, s_tv, vh);
   for (int r = 0; r < nrows; ++r) {
     int L = causal ? prefix + rows[r] + 1 : total_len;
-    orc_attend(q + (size_t)r * Hq * ORC_D, Hq, Hkv, kcodes, kscales, s_tk,
-               vcodes, vscales, s_tv, L, scale, work, out + (size_t)r * Hq * ORC_D);
+    if (L > total_len) L = total_len;
+    attend_dequantized(q + (size_t)r * Hq * ORC_D, Hq, Hkv, kh, vh, L, scale, work,
+                       out + (size_t)r * Hq * ORC_D);
   }
+  free(kh);
+  free(vh);
+  return 0;
 }

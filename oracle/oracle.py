@@ -45,6 +45,8 @@ def lib():
             L.orc_e4m3_value.argtypes = [ctypes.c_uint]
             L.orc_tensor_scale.restype = ctypes.c_float
             L.orc_tensor_scale.argtypes = [_f32p, ctypes.c_size_t]
+            L.orc_tensor_scale_from_amax.restype = ctypes.c_float
+            L.orc_tensor_scale_from_amax.argtypes = [ctypes.c_float]
             L.orc_abs_max.restype = ctypes.c_float
             L.orc_abs_max.argtypes = [_f32p, ctypes.c_size_t]
             L.orc_block_scale_code.restype = ctypes.c_uint
@@ -64,12 +66,12 @@ def lib():
             L.orc_dequant_rows.argtypes = [_u8p, _u8p, ctypes.c_size_t, ctypes.c_float, _f32p]
             L.orc_f32_to_bf16_array.restype = None
             L.orc_f32_to_bf16_array.argtypes = [_f32p, ctypes.c_size_t, _u16p]
-            L.orc_attend.restype = None
+            L.orc_attend.restype = ctypes.c_int
             L.orc_attend.argtypes = [_f32p, ctypes.c_int, ctypes.c_int,
                                      _u8p, _u8p, ctypes.c_float,
                                      _u8p, _u8p, ctypes.c_float,
                                      ctypes.c_int, ctypes.c_double, _f64p, _f32p]
-            L.orc_prefill_rows.restype = None
+            L.orc_prefill_rows.restype = ctypes.c_int
             L.orc_prefill_rows.argtypes = [_f32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            _u8p, _u8p, ctypes.c_float,
                                            _u8p, _u8p, ctypes.c_float,
@@ -120,6 +122,10 @@ def tensor_scale(x) -> float:
     """s_t = amax(|x|) / (6 * 448), FP32."""
     x = _c(x, np.float32).reshape(-1)
     return float(np.float32(lib().orc_tensor_scale(_p(x, _f32p), x.size)))
+
+
+def tensor_scale_from_amax(amax: float) -> float:
+    return float(np.float32(lib().orc_tensor_scale_from_amax(float(amax))))
 
 
 def element_codes(x, sb_code: int, s_t: float) -> np.ndarray:
@@ -191,9 +197,11 @@ def attend(q, Hkv, kcodes, kscales, s_tk, vcodes, vscales, s_tv, scale=None):
         scale = 1.0 / np.sqrt(D)
     out = np.empty((Hq, D), np.float32)
     work = np.empty(max(L, 1), np.float64)
-    lib().orc_attend(_p(q, _f32p), Hq, Hkv, _p(kcodes, _u8p), _p(kscales, _u8p), float(s_tk),
-                     _p(vcodes, _u8p), _p(vscales, _u8p), float(s_tv), L, float(scale),
-                     _p(work, _f64p), _p(out, _f32p))
+    rc = lib().orc_attend(_p(q, _f32p), Hq, Hkv, _p(kcodes, _u8p), _p(kscales, _u8p), float(s_tk),
+                          _p(vcodes, _u8p), _p(vscales, _u8p), float(s_tv), L, float(scale),
+                          _p(work, _f64p), _p(out, _f32p))
+    if rc != 0:
+        raise MemoryError("oracle scratch allocation failed")
     return out
 
 
@@ -201,19 +209,24 @@ def decode_batch(q, seqs, Hkv, s_tk, s_tv, scale=None, threads=None):
     """Decode attention for a batch.
 
     q: [B][Hq][128] FP32; seqs: list of B tuples (kcodes [L][Hkv][128],
-    kscales [L][Hkv][8], vcodes, vscales), one per sequence.  Sequences run
-    on a thread pool (the C call releases the GIL).  Returns [B][Hq][128]."""
+    kscales [L][Hkv][8], vcodes, vscales), one per sequence.  The (sequence,
+    KV head) pairs run on a thread pool (the C call releases the GIL); each
+    pair is an independent call on that KV head's slice.  Returns
+    [B][Hq][128]."""
     q = _c(q, np.float32)
-    B = q.shape[0]
+    B, Hq = q.shape[0], q.shape[1]
+    G = Hq // Hkv
     out = np.empty(q.shape, np.float32)
     threads = threads or os.cpu_count() or 1
 
-    def one(b):
+    def one(unit):
+        b, h = divmod(unit, Hkv)
         kc, ks, vc, vs = seqs[b]
-        out[b] = attend(q[b], Hkv, kc, ks, s_tk, vc, vs, s_tv, scale)
+        out[b, h * G:(h + 1) * G] = attend(q[b, h * G:(h + 1) * G], 1, kc[:, h:h + 1], ks[:, h:h + 1],
+                                           s_tk, vc[:, h:h + 1], vs[:, h:h + 1], s_tv, scale)
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(one, range(B)))
+        list(ex.map(one, range(B * Hkv)))
     return out
 
 
@@ -224,7 +237,7 @@ def prefill_rows(q_rows, rows, Hkv, kcodes, kscales, s_tk, vcodes, vscales, s_tv
     q_rows: [n][Hq][128] FP32 (the selected rows of the chunk's queries);
     rows: their indices i within the chunk (query i sits at absolute
     position prefix + i); kcodes...: the whole cache [Ltot][Hkv][...].
-    Returns [n][Hq][128]."""
+    Rows are split over a thread pool.  Returns [n][Hq][128]."""
     q_rows = _c(q_rows, np.float32)
     rows = np.asarray(rows, np.int32)
     n, Hq = q_rows.shape[0], q_rows.shape[1]
@@ -236,20 +249,26 @@ def prefill_rows(q_rows, rows, Hkv, kcodes, kscales, s_tk, vcodes, vscales, s_tv
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     out = np.empty((n, Hq, D), np.float32)
-    threads = threads or os.cpu_count() or 1
+    threads = max(1, min(threads or os.cpu_count() or 1, n))
+    bounds = np.linspace(0, n, threads + 1).astype(int)
 
-    def one(i):
-        r = np.ascontiguousarray(rows[i:i + 1])
-        qi = np.ascontiguousarray(q_rows[i:i + 1])
-        o = np.empty((1, Hq, D), np.float32)
+    def one(c):
+        a, e = bounds[c], bounds[c + 1]
+        if a == e:
+            return
+        r = np.ascontiguousarray(rows[a:e])
+        qi = np.ascontiguousarray(q_rows[a:e])
+        o = np.empty((e - a, Hq, D), np.float32)
         work = np.empty(max(total, 1), np.float64)
-        lib().orc_prefill_rows(_p(qi, _f32p), _p(r, _i32p), 1, Hq, Hkv,
-                               _p(kcodes, _u8p), _p(kscales, _u8p), float(s_tk),
-                               _p(vcodes, _u8p), _p(vscales, _u8p), float(s_tv),
-                               int(prefix), int(bool(causal)), total, float(scale),
-                               _p(work, _f64p), _p(o, _f32p))
-        out[i] = o[0]
+        rc = lib().orc_prefill_rows(_p(qi, _f32p), _p(r, _i32p), e - a, Hq, Hkv,
+                                    _p(kcodes, _u8p), _p(kscales, _u8p), float(s_tk),
+                                    _p(vcodes, _u8p), _p(vscales, _u8p), float(s_tv),
+                                    int(prefix), int(bool(causal)), total, float(scale),
+                                    _p(work, _f64p), _p(o, _f32p))
+        if rc != 0:
+            raise MemoryError("oracle scratch allocation failed")
+        out[a:e] = o
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(one, range(n)))
+        list(ex.map(one, range(threads)))
     return out

@@ -1,0 +1,134 @@
+"""Helpers for the GPU parity tests: build caches through the C-ABI library,
+compute the oracle's answer on the same seeded inputs, compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from decode_attention_nvfp4_amd import api
+from decode_attention_nvfp4_amd import workloads as W
+from layout import Planes, sequence_tokens
+
+TOL = 2e-2   # pass iff |o - r| <= TOL * max(1, |r|) for every output element
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    t = t.to(torch.bfloat16) if dtype == "bf16" else t.to(torch.float32)
+    return t.to(dev())
+
+
+def i32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev())
+
+
+def planes(cache: api.KVCache) -> Planes:
+    torch.cuda.synchronize()
+    return Planes(cache.k_codes.cpu().numpy(), cache.k_scales.cpu().numpy(),
+                  cache.v_codes.cpu().numpy(), cache.v_scales.cpu().numpy(),
+                  cache.num_pages, cache.num_kv_heads)
+
+
+def compare(got: np.ndarray, ref: np.ndarray, tol: float = TOL):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    ratio = float((err / np.maximum(1.0, np.abs(ref))).max()) if err.size else 0.0
+    rel_l2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)) if err.size else 0.0
+    stats = {"max_abs": float(err.max()) if err.size else 0.0, "mixed": ratio, "rel_l2": rel_l2}
+    return ratio <= tol and np.all(np.isfinite(got)), stats
+
+
+def calibrate(w: W.DecodeWorkload, oracle, data=None):
+    """(s_tK, s_tV) over the whole K and V tensors of a workload, including
+    the tokens its decode steps append, with the oracle's definition."""
+    ka = va = 0.0
+    for b in range(w.B):
+        k, v = data[b] if data is not None else w.kv(b)
+        ka = max(ka, oracle.abs_max(k))
+        va = max(va, oracle.abs_max(v))
+    for s in range(w.steps):
+        k, v = w.append_kv(s)
+        ka = max(ka, oracle.abs_max(k))
+        va = max(va, oracle.abs_max(v))
+    return oracle.tensor_scale_from_amax(ka), oracle.tensor_scale_from_amax(va)
+
+
+class BuiltDecode:
+    """A decode workload appended into a device cache, plus the oracle's
+    logical codes for the sequences it may check."""
+
+    def __init__(self, w: W.DecodeWorkload, oracle, keep=None, fill=0xA5, chunk=16):
+        self.w = w
+        self.keep = set(range(w.B)) if keep is None else set(keep)
+        data = [w.kv(b) for b in range(w.B)]
+        # tensor scales: static calibration over the whole tensor (all
+        # sequences plus the appended steps), with the oracle's definition
+        self.s_tk, self.s_tv = calibrate(w, oracle, data)
+        self.cache = api.KVCache(w.num_pages, w.Hkv, self.s_tk, self.s_tv, fill=fill)
+        self.pt = i32(w.page_table)
+        self.codes = {}
+        for b0 in range(0, w.B, chunk):
+            ks, vs, seqs, poss = [], [], [], []
+            for b in range(b0, min(w.B, b0 + chunk)):
+                k, v = data[b]
+                ks.append(k)
+                vs.append(v)
+                seqs.append(np.full(len(k), b, np.int32))
+                poss.append(np.arange(len(k), dtype=np.int32))
+                if b in self.keep:
+                    self.codes[b] = (*oracle.quantize_rows(k, self.s_tk), *oracle.quantize_rows(v, self.s_tv))
+            k = np.concatenate(ks)
+            if len(k) == 0:
+                continue
+            api.append(self.cache, to_dev(k, w.dtype), to_dev(np.concatenate(vs), w.dtype),
+                       i32(np.concatenate(seqs)), i32(np.concatenate(poss)), self.pt)
+        del data
+        self.lens = w.lens.copy()
+        torch.cuda.synchronize()
+
+    def append_step(self, step, oracle=None):
+        w = self.w
+        k, v = w.append_kv(step)
+        pos = self.lens.copy()
+        api.append(self.cache, to_dev(k, w.dtype), to_dev(v, w.dtype), i32(np.arange(w.B)), i32(pos), self.pt)
+        if oracle is not None:
+            for b in self.keep:
+                kc, ksc = oracle.quantize_rows(k[b:b + 1], self.s_tk)
+                vc, vsc = oracle.quantize_rows(v[b:b + 1], self.s_tv)
+                c = self.codes[b]
+                self.codes[b] = (np.concatenate([c[0], kc]), np.concatenate([c[1], ksc]),
+                                 np.concatenate([c[2], vc]), np.concatenate([c[3], vsc]))
+        self.lens += 1
+
+    def decode(self, q: np.ndarray, num_splits=0, dtype=None):
+        qd = to_dev(q, dtype or self.w.dtype)
+        return api.decode(self.cache, qd, self.pt, i32(self.lens), int(self.lens.max()),
+                          num_splits=num_splits)
+
+    def oracle_decode(self, oracle, q: np.ndarray, seqs):
+        seqs = list(seqs)
+        out = oracle.decode_batch(q[seqs], [self.codes[b] for b in seqs], self.w.Hkv, self.s_tk, self.s_tv)
+        return out
+
+    def check_codes(self, seqs):
+        """Bit-exact comparison of the device planes with the oracle's codes."""
+        P = planes(self.cache)
+        for b in seqs:
+            pages, slots = sequence_tokens(self.w.page_table[b], int(self.lens[b]))
+            got = P.gather(pages, slots)
+            for g, e, nm in zip(got, self.codes[b], ("k codes", "k scales", "v codes", "v scales")):
+                if not np.array_equal(g, e):
+                    bad = np.argwhere(g != e)[:5]
+                    raise AssertionError(f"seq {b}: {nm} differ at {bad.tolist()}")

@@ -1,0 +1,194 @@
+"""The C-ABI library: it builds, loads, exports every declared entry point,
+and rejects bad arguments on the host before touching the device.  Also the
+byte-count pins of the format.  CPU only: no call here reaches a kernel."""
+import ctypes
+import json
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4kv.h")
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "format_facts.json")))
+
+
+@pytest.fixture(scope="module")
+def api():
+    from decode_attention_nvfp4_amd import api, build
+    if not os.path.exists(build.LIB):
+        build.build()
+    api.lib()
+    return api
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("nvfp4_kv_append", "nvfp4_kv_dequant", "nvfp4_decode_attn", "nvfp4_prefill_attn"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(api):
+    from decode_attention_nvfp4_amd import build
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (nvfp4_[a-z0-9_]+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    assert set(api.EXPORTS) == set(declared_functions())
+
+
+def test_status_strings(api):
+    L = api.lib()
+    for code, word in ((0, b"ok"), (1, b"invalid"), (2, b"unsupported"), (3, b"workspace"), (4, b"HIP")):
+        assert word in L.nvfp4_status_string(code)
+
+
+def _fake_cache(api, **kw):
+    c = api.CacheStruct(0x10000, 0x20000, 0x30000, 0x40000, 0.01, 0.02, 64, 8, 16, 128)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+FAKE = ctypes.c_void_p(0x50000)
+
+
+def _append(api, cache, dtype=1, n_tok=4, max_pages=8, ptrs=True):
+    p = FAKE if ptrs else None
+    return api.lib().nvfp4_kv_append(ctypes.byref(cache), p, p, dtype, n_tok, p, p, p, max_pages, None)
+
+
+def test_append_rejects_bad_arguments(api):
+    L = api.lib()
+    assert L.nvfp4_kv_append(None, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == 1
+    assert _append(api, _fake_cache(api, head_dim=64)) == 2
+    assert _append(api, _fake_cache(api, page_size=32)) == 2
+    assert _append(api, _fake_cache(api, k_tensor_scale=0.0)) == 1
+    assert _append(api, _fake_cache(api, v_tensor_scale=-1.0)) == 1
+    assert _append(api, _fake_cache(api, k_tensor_scale=float("nan"))) == 1
+    assert _append(api, _fake_cache(api, k_tensor_scale=float("inf"))) == 1
+    assert _append(api, _fake_cache(api, k_codes=0x10008)) == 1        # misaligned plane
+    assert _append(api, _fake_cache(api, v_scales=None)) == 1
+    assert _append(api, _fake_cache(api, num_pages=0)) == 1
+    assert _append(api, _fake_cache(api), dtype=7) == 2
+    assert _append(api, _fake_cache(api), n_tok=-1) == 1
+    assert _append(api, _fake_cache(api), max_pages=0) == 1
+    assert _append(api, _fake_cache(api), ptrs=False) == 1
+    assert _append(api, _fake_cache(api), n_tok=0, ptrs=False) == 0     # empty append: no-op
+
+
+def test_dequant_rejects_bad_arguments(api):
+    L = api.lib()
+    c = _fake_cache(api)
+    assert L.nvfp4_kv_dequant(ctypes.byref(c), FAKE, -1, 4, FAKE, FAKE, 0, None) == 1
+    assert L.nvfp4_kv_dequant(ctypes.byref(c), FAKE, 0, 4, FAKE, FAKE, 3, None) == 2
+    assert L.nvfp4_kv_dequant(ctypes.byref(c), None, 0, 4, FAKE, FAKE, 0, None) == 1
+    assert L.nvfp4_kv_dequant(ctypes.byref(c), FAKE, 0, 4, ctypes.c_void_p(0x50004), None, 0, None) == 1
+    assert L.nvfp4_kv_dequant(ctypes.byref(c), None, 0, 0, None, None, 0, None) == 0
+
+
+def _decode(api, cache, q_dtype=1, B=2, Hq=32, max_pages=64, max_len=1000, scale=0.088,
+            splits=0, ws=FAKE, ws_bytes=1 << 30):
+    return api.lib().nvfp4_decode_attn(ctypes.byref(cache), FAKE, q_dtype, B, Hq, FAKE, max_pages, FAKE,
+                                       max_len, scale, splits, ws, ws_bytes, FAKE, None)
+
+
+def test_decode_rejects_bad_arguments(api):
+    c = _fake_cache(api)
+    assert _decode(api, _fake_cache(api, head_dim=256)) == 2
+    assert _decode(api, c, q_dtype=5) == 2
+    assert _decode(api, c, Hq=12) == 1                  # not a multiple of Hkv = 8
+    assert _decode(api, c, Hq=8 * 17) == 2              # more than 16 heads per KV head
+    assert _decode(api, c, max_pages=10, max_len=1000) == 1
+    assert _decode(api, c, scale=0.0) == 1
+    assert _decode(api, c, scale=float("nan")) == 1
+    assert _decode(api, c, B=-1) == 1
+    assert _decode(api, c, splits=-2) == 1
+    assert _decode(api, c, splits=4, ws=None, ws_bytes=0) == 3
+    assert _decode(api, c, splits=4, ws_bytes=16) == 3
+    assert _decode(api, c, splits=4, ws=ctypes.c_void_p(0x50010)) == 1   # workspace alignment
+    assert _decode(api, c, B=0) == 0                    # empty batch: no-op
+
+
+def test_prefill_rejects_bad_arguments(api):
+    L = api.lib()
+    c = _fake_cache(api)
+
+    def pf(T=16, Hq=64, prefix=100, ws=FAKE, ws_bytes=1 << 30, q_dtype=1, cache=c):
+        return L.nvfp4_prefill_attn(ctypes.byref(cache), FAKE, q_dtype, T, Hq, FAKE, prefix, 1, 0.088, ws,
+                                    ws_bytes, FAKE, None)
+    assert pf(Hq=60) == 1
+    assert pf(T=-1) == 1
+    assert pf(prefix=-5) == 1
+    assert pf(q_dtype=9) == 2
+    assert pf(ws=None, ws_bytes=0) == 3
+    assert pf(ws_bytes=100) == 3
+    assert pf(cache=_fake_cache(api, page_size=8)) == 2
+    assert pf(T=0) == 0
+
+
+def test_split_planner_and_workspace(api):
+    for B, Hkv, L in ((1, 1, 1024), (8, 8, 4097), (1, 8, 65536), (128, 8, 8192), (3, 2, 0), (4, 4, 17)):
+        S = api.decode_num_splits(B, Hkv, L, 0)
+        assert S >= 1
+        max_pages = max(1, -(-L // 16))
+        assert S <= max_pages
+        for req in (1, 2, 7, 64):
+            s = api.decode_num_splits(B, Hkv, L, req)
+            assert 1 <= s <= max(req, 1)
+        ws = api.decode_workspace_bytes(B, 4 * Hkv, Hkv, L, 0)
+        assert (ws == 0) == (S == 1)
+        if S > 1:
+            assert ws >= B * 4 * Hkv * S * 129 * 4
+    # long single sequences split across the machine
+    assert api.decode_num_splits(1, 8, 65536, 0) >= 64
+
+
+def test_memory_footprint_matches_page_claims(api):
+    """0.5625 bytes per element: 3.56x below FP16 (the page's "3.5x", ~71%)
+    and 1.78x below FP8 (the page's "about 1.8x")."""
+    facts = GOLD["memory_reduction"]
+    for pages, hkv in ((1, 1), (64, 8), (2176, 8)):
+        nbytes = api.kv_cache_bytes(pages, hkv)
+        elems = 2 * pages * 16 * hkv * 128             # K and V
+        assert nbytes == elems * 0.5625
+        # the page's KV-memory formula, one layer: 2 * L * n_h * d_h * s * b * sizeof
+        assert nbytes == 2 * 1 * hkv * 128 * (pages * 16) * 1 * 0.5625
+    per = api.kv_cache_bytes(1, 1) / (2 * 16 * 128)
+    vs16, vs8 = 2.0 / per, 1.0 / per
+    assert abs(vs16 - facts["vs_fp16_factor"]) < 0.1
+    assert abs(vs8 - facts["vs_fp8_factor"]) < 0.05
+    assert abs(100 * (1 - per / 2.0) - facts["vs_fp16_percent"]) < 1.0
+    # "about 50%" vs FP8 is a rounded headline: the format gives 43.75%
+    assert abs(100 * (1 - per / 1.0) - facts["vs_fp8_percent"]) < 7.0
+    for p in range(4):
+        assert api.plane_bytes(3, 2, p) == 3 * 2 * (1024 if p in (0, 2) else 128)
+    assert api.plane_bytes(3, 2, 4) == 0 and api.kv_cache_bytes(0, 2) == 0
+
+
+def test_tensor_scale_matches_oracle(api, orc):
+    from decode_attention_nvfp4_amd import workloads
+    for seed in range(5):
+        x = workloads.random_rows(seed, 50, "mixed")
+        amax = float(np.abs(x).max())
+        assert api.tensor_scale_from_amax(amax) == orc.tensor_scale(x)
+    assert api.tensor_scale_from_amax(0.0) == 0.0
+    assert api.tensor_scale_from_amax(float("inf")) == 0.0
+
+
+def test_binding_refuses_host_tensors(api):
+    import torch
+    cache = type("C", (), {"num_kv_heads": 8})()
+    with pytest.raises(ValueError):
+        api.append(cache, torch.zeros(2, 8, 128), torch.zeros(2, 8, 128), torch.zeros(2, dtype=torch.int32),
+                   torch.zeros(2, dtype=torch.int32), torch.zeros(1, 4, dtype=torch.int32))

@@ -1,0 +1,370 @@
+"""GPU parity: the C-ABI library against the CPU oracle on the same seeded
+inputs.  Codes and scales must match bit for bit; attention must satisfy
+|o - r| <= 2e-2 * max(1, |r|) element-wise (the decode path is expected to
+sit far below that; its stricter internal bound is checked too)."""
+import numpy as np
+import pytest
+import torch
+
+from decode_attention_nvfp4_amd import api
+from decode_attention_nvfp4_amd import workloads as W
+from gpu_common import TOL, BuiltDecode, compare, i32, planes, say, to_dev
+from layout import sequence_tokens
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+DECODE_STRICT = 2e-3     # decode uses exact 16-bit operands; only P is rounded (f16)
+
+
+# ------------------------------------------------------------------ codec
+
+def test_abs_max_exact(orc):
+    for dtype in ("bf16", "f32"):
+        x = W.random_rows(1, 777, "mixed", dtype=dtype)
+        say(f"abs_max {dtype} n={x.size}")
+        got = api.abs_max(to_dev(x, dtype)).item()
+        assert got == orc.abs_max(x)
+        assert api.tensor_scale_from_amax(got) == orc.tensor_scale(x)
+    say("abs_max empty")
+    assert api.abs_max(torch.empty(0, device="cuda")).item() == 0.0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dist", ["normal", "outlier", "mixed", "tiny"])
+def test_append_bit_exact_and_sentinel(orc, dtype, dist):
+    """Random (sequence, position) scatter into a sentinel-filled cache: the
+    rows' bytes equal the oracle's codes, every other byte keeps 0xA5."""
+    rng = np.random.default_rng(["normal", "outlier", "mixed", "tiny"].index(dist) * 2 + (dtype == "f32"))
+    B, Hkv, max_pages, num_pages = 3, 4, 6, 24
+    pt = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    n = 150
+    slots = rng.choice(B * max_pages * 16, n, replace=False)
+    seq = (slots // (max_pages * 16)).astype(np.int32)
+    pos = (slots % (max_pages * 16)).astype(np.int32)
+    k = W.random_rows(10, n * Hkv, dist, dtype).reshape(n, Hkv, 128)
+    v = W.random_rows(11, n * Hkv, dist, dtype).reshape(n, Hkv, 128)
+    stk, stv = orc.tensor_scale(k) * 0.8, orc.tensor_scale(v)     # 0.8: some blocks saturate
+    cache = api.KVCache(num_pages, Hkv, stk, stv, fill=0xA5)
+    say(f"append {dtype} {dist} n={n}")
+    api.append(cache, to_dev(k, dtype), to_dev(v, dtype), i32(seq), i32(pos), i32(pt))
+    P = planes(cache)
+    pages = pt[seq, pos // 16]
+    got = P.gather(pages, pos % 16)
+    exp = (*orc.quantize_rows(k, stk), *orc.quantize_rows(v, stv))
+    for g, e, nm in zip(got, exp, ("k codes", "k scales", "v codes", "v scales")):
+        bad = np.argwhere(g != e)
+        assert bad.size == 0, (nm, bad[:5].tolist())
+    masks = P.touched_mask(pages, pos % 16)
+    for arr, m in zip(P.arrays(), masks):
+        assert np.all(arr[~m] == 0xA5)
+
+
+def test_append_edge_values(orc):
+    """Ties, exact grid points, zeros of both signs, saturation beyond the
+    calibrated amax, zero and subnormal block scales."""
+    st = float(np.float32(1.0 / 256))
+    rows = []
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    mids = np.array([.25, .75, 1.25, 1.75, 2.5, 3.5, 5], np.float32)
+    for sb in (0x38, 0x40, 0x01, 0x05, 0x7E, 0x30):
+        sbv = orc.e4m3_value(sb)
+        d = np.float32(sbv * st)
+        r = np.zeros(128, np.float32)
+        r[0] = np.float32(6 * d)                    # pins the block scale to sb
+        r[1:8] = mids * d                            # exact ties
+        r[8:15] = np.nextafter(mids * d, np.float32(np.inf))
+        r[15] = -0.0
+        r[16] = np.float32(6 * d)
+        r[17:24] = -np.nextafter(mids * d, np.float32(0))
+        r[24:32] = grid * d
+        r[32:48] = np.float32(1e-30)                 # underflowing block: scale 0
+        r[48] = np.float32(1e6)                      # beyond calibrated amax: saturates
+        r[49:64] = -np.float32(3e5)
+        r[64:80] = np.float32(6 * d * 0.9)
+        r[80:96] = -0.0
+        rows.append(r)
+    x = np.stack(rows).reshape(len(rows), 1, 128)
+    for dtype in ("f32", "bf16"):
+        xx = x if dtype == "f32" else W.round_bf16(x)
+        n = xx.shape[0]
+        cache = api.KVCache(4, 1, st, st, fill=0xA5)
+        pt = np.arange(4, dtype=np.int32)[None]
+        say(f"append edge values {dtype}")
+        api.append(cache, to_dev(xx, dtype), to_dev(-xx, dtype), i32(np.zeros(n)), i32(np.arange(n)), i32(pt))
+        P = planes(cache)
+        got = P.gather(np.zeros(n, int), np.arange(n))
+        exp = (*orc.quantize_rows(xx, st), *orc.quantize_rows(-xx, st))
+        for g, e, nm in zip(got, exp, ("k codes", "k scales", "v codes", "v scales")):
+            assert np.array_equal(g, e), (dtype, nm, np.argwhere(g != e)[:5].tolist())
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dequant_bit_exact(orc, out_dtype):
+    w = W.custom_decode(1, 2, 8, 4, [37, 70], dtype="bf16")
+    built = BuiltDecode(w, orc)
+    for b in range(2):
+        L = int(w.lens[b])
+        for pos0, n in ((0, L), (5, 17), (L - 1, 1)):
+            say(f"dequant seq {b} pos0={pos0} n={n} {out_dtype}")
+            k, v = api.dequant(built.cache, i32(w.page_table[b]), pos0, n, out_dtype)
+            kc, ks, vc, vs = built.codes[b]
+            ek = orc.dequant_rows(kc[pos0:pos0 + n], ks[pos0:pos0 + n], built.s_tk)
+            ev = orc.dequant_rows(vc[pos0:pos0 + n], vs[pos0:pos0 + n], built.s_tv)
+            if out_dtype == torch.float32:
+                assert np.array_equal(k.cpu().numpy().view(np.uint32), ek.view(np.uint32))
+                assert np.array_equal(v.cpu().numpy().view(np.uint32), ev.view(np.uint32))
+            else:
+                assert np.array_equal(k.cpu().view(torch.int16).numpy().view(np.uint16), orc.f32_to_bf16_bits(ek))
+                assert np.array_equal(v.cpu().view(torch.int16).numpy().view(np.uint16), orc.f32_to_bf16_bits(ev))
+
+
+# ----------------------------------------------------------------- decode
+
+DECODE_CASES = [
+    # seed, B, Hq, Hkv, lens, dtype
+    (2, 1, 1, 1, [1], "f32"),
+    (3, 3, 4, 1, [15, 16, 17], "f32"),
+    (4, 4, 32, 8, [1, 100, 257, 1000], "bf16"),
+    (5, 2, 64, 8, [3000, 513], "bf16"),
+    (6, 5, 16, 2, [0, 31, 64, 65, 700], "bf16"),
+    (7, 2, 12, 4, [129, 2049], "bf16"),
+    (8, 2, 16, 1, [400, 33], "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"s{c[0]}-B{c[1]}-G{c[2] // c[3]}")
+def test_decode_parity_small(orc, case):
+    seed, B, Hq, Hkv, lens, dtype = case
+    w = W.custom_decode(seed, B, Hq, Hkv, lens, dtype=dtype, outliers=(seed % 2 == 0))
+    built = BuiltDecode(w, orc)
+    built.check_codes(range(B))
+    q = w.q(0)
+    say(f"decode {case}")
+    out = built.decode(q).cpu().numpy()
+    ref = built.oracle_decode(orc, q, range(B))
+    ok, st = compare(out, ref)
+    say("   ", st)
+    assert ok, st
+    assert st["mixed"] <= DECODE_STRICT, st
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[b] == 0)
+
+
+def test_decode_split_sweep_and_determinism(orc):
+    w = W.custom_decode(9, 3, 32, 8, [1500, 77, 4000], dtype="bf16", outliers=True)
+    built = BuiltDecode(w, orc)
+    q = w.q(0)
+    ref = built.oracle_decode(orc, q, range(3))
+    outs = {}
+    for S in (1, 2, 7, 64, 0):
+        say(f"decode split sweep S={S}")
+        outs[S] = built.decode(q, num_splits=S).cpu().numpy()
+        ok, st = compare(outs[S], ref)
+        assert ok and st["mixed"] <= DECODE_STRICT, (S, st)
+    # splits change the running max each probability is taken against, so the
+    # FP16 rounding of P differs (relative 2^-11 per weight); each result is
+    # within DECODE_STRICT of the oracle, so two are within twice that
+    for S in (2, 7, 64, 0):
+        ok, st = compare(outs[S], outs[1], tol=2 * DECODE_STRICT)
+        assert ok, (S, st)
+    say("decode determinism")
+    again = built.decode(q, num_splits=0).cpu().numpy()
+    assert np.array_equal(again.view(np.uint32), outs[0].view(np.uint32))
+
+
+def test_decode_f32_query_bf16_cache(orc):
+    w = W.custom_decode(10, 2, 8, 2, [300, 1025], dtype="bf16")
+    built = BuiltDecode(w, orc)
+    q = np.random.default_rng(3).standard_normal((2, 8, 128)).astype(np.float32)
+    say("decode f32 q")
+    out = built.decode(q, dtype="f32").cpu().numpy()
+    ok, st = compare(out, built.oracle_decode(orc, q, range(2)))
+    assert ok and st["mixed"] <= DECODE_STRICT, st
+
+
+def test_decode_softmax_scale_and_large_logits(orc):
+    """Large logits (scaled-up queries and a custom softmax scale) stay finite
+    and match."""
+    w = W.custom_decode(11, 2, 8, 2, [200, 333], dtype="bf16", outliers=True)
+    built = BuiltDecode(w, orc)
+    q = w.q(0) * np.float32(8.0)
+    qd = to_dev(q, "bf16")
+    say("decode large logits")
+    out = api.decode(built.cache, qd, built.pt, i32(built.lens), int(built.lens.max()), softmax_scale=0.3)
+    ref = orc.decode_batch(q, [built.codes[b] for b in range(2)], 2, built.s_tk, built.s_tv, scale=0.3)
+    ok, st = compare(out.cpu().numpy(), ref)
+    assert ok, st
+
+
+# ---------------------------------------------------------------- prefill
+
+PREFILL_CASES = [
+    # prefix, T, Hq, Hkv, causal
+    (0, 1, 8, 8, True),
+    (0, 40, 8, 2, True),
+    (200, 70, 8, 2, True),
+    (5, 130, 16, 2, True),
+    (64, 64, 64, 8, True),
+    (1000, 33, 8, 1, True),
+    (150, 40, 8, 2, False),
+    (300, 129, 32, 4, True),
+]
+
+# The prefill path multiplies FP8 operands, as on the pages (K~, V~ = E4M3 of
+# the dequantized cache, Q and P rounded to E4M3).  Each rounding is at most
+# 2^-4 relative.  The V and P roundings move an output by at most
+# 2^-4 * A each, with A = sum_t w_t |v_t| the attention-weighted magnitude of
+# the values; the Q and K roundings perturb the scores and hence the weights,
+# typically by a few percent.  With attention spread over hundreds of keys
+# these errors average out and the 2e-2 mixed gate holds; rows that see only
+# a handful of keys carry the rounding directly, so they are held to
+# 2e-2 * max(1, |r|) + 0.2 * A.
+FP8_LOCAL = 0.2
+
+
+def _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, causal):
+    kc, ks = orc.quantize_rows(k, stk)
+    vc, vs = orc.quantize_rows(v, stv)
+    ref = orc.prefill_rows(q, np.arange(T), Hkv, kc, ks, stk, vc, vs, stv, prefix, causal=causal)
+    mag = orc.prefill_rows(q, np.arange(T), Hkv, kc, ks, stk, vc & 7, vs, stv, prefix, causal=causal)
+    return ref, mag
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"p{c[0]}-T{c[1]}-G{c[2] // c[3]}-c{int(c[4])}")
+def test_prefill_parity_small(orc, case):
+    prefix, T, Hq, Hkv, causal = case
+    pw = W.small_prefill(prefix, T, Hq, Hkv, seed_cfg=600 + prefix + T)
+    kp, vp = pw.prefix_kv()
+    kc_, vc_ = pw.chunk_kv()
+    k = np.concatenate([kp, kc_])
+    v = np.concatenate([vp, vc_])
+    stk, stv = orc.tensor_scale(k), orc.tensor_scale(v)
+    total = prefix + T
+    npages = -(-total // 16)
+    perm = np.random.default_rng(prefix + T).permutation(npages + 3)[:npages].astype(np.int32)
+    cache = api.KVCache(npages + 3, Hkv, stk, stv, fill=0xA5)
+    say(f"prefill {case}: append")
+    api.append(cache, to_dev(k, "bf16"), to_dev(v, "bf16"), i32(np.zeros(total)), i32(np.arange(total)),
+               i32(perm[None]))
+    q = pw.q()
+    say(f"prefill {case}: attention")
+    out = api.prefill(cache, to_dev(q, "bf16"), i32(perm), prefix, causal=causal).cpu().numpy()
+    ref, mag = _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, causal)
+    seen = (prefix + np.arange(T) + 1) if causal else np.full(T, total)
+    wide = seen >= 200                     # rows whose softmax spans >= 200 keys
+    ok, st = compare(out[wide], ref[wide]) if wide.any() else (True, {})
+    say("    rows with >= 200 keys:", st)
+    assert ok, st
+    err = np.abs(out.astype(np.float64) - ref)
+    bound = TOL * np.maximum(1.0, np.abs(ref)) + FP8_LOCAL * mag
+    assert np.all(np.isfinite(out)) and np.all(err <= bound), float((err - bound).max())
+    ok, st = compare(out, ref)
+    say("    all rows:", st)
+    assert st["rel_l2"] < 0.05, st
+
+
+# ------------------------------------------------ full-size configurations
+
+def test_config1_tiny(orc):
+    w = W.decode_workload(1)
+    built = BuiltDecode(w, orc)
+    built.check_codes(range(1))
+    q = w.q(0)
+    say("config 1 decode")
+    out = built.decode(q, dtype="f32").cpu().numpy()
+    ok, st = compare(out, built.oracle_decode(orc, q, range(1)))
+    say("   ", st)
+    assert ok and st["mixed"] <= DECODE_STRICT, st
+
+
+def test_config2_gqa_steps(orc):
+    """Batch 8, GQA 32/8, L 4096, outlier channels; 16 steps each appending
+    one token per sequence then decoding."""
+    w = W.decode_workload(2)
+    built = BuiltDecode(w, orc)
+    built.check_codes(range(w.B))
+    for step in range(w.steps):
+        say(f"config 2 step {step}")
+        built.append_step(step, orc)
+        q = w.q(step)
+        out = built.decode(q).cpu().numpy()
+        if step in (0, 7, 15):
+            built.check_codes(range(w.B))
+            ok, st = compare(out, built.oracle_decode(orc, q, range(w.B)))
+            say("   ", st)
+            assert ok and st["mixed"] <= DECODE_STRICT, (step, st)
+
+
+def test_config3_long_context(orc):
+    w = W.decode_workload(3)
+    built = BuiltDecode(w, orc)
+    built.check_codes(range(1))
+    q = w.q(0)
+    say("config 3 decode (auto splits)")
+    out = built.decode(q).cpu().numpy()
+    ref = built.oracle_decode(orc, q, range(1))
+    ok, st = compare(out, ref)
+    say("   ", st)
+    assert ok and st["mixed"] <= DECODE_STRICT, st
+    say("config 3 decode (1 split)")
+    one = built.decode(q, num_splits=1).cpu().numpy()
+    ok, st = compare(one, out, tol=2 * DECODE_STRICT)
+    assert ok, st
+
+
+def test_config4_paged_sampled(orc):
+    """Batch 128 with ragged lengths and permuted pages, built in full on the
+    device; the oracle checks 6 sequences (shortest, longest, 4 seeded)."""
+    w = W.decode_workload(4)
+    rng = np.random.default_rng(44)
+    sample = sorted(set([int(np.argmin(w.lens)), int(np.argmax(w.lens))] +
+                        rng.choice(w.B, 4, replace=False).tolist()))
+    built = BuiltDecode(w, orc, keep=sample)
+    built.check_codes(sample)
+    q = w.q(0)
+    say(f"config 4 decode, checking {sample}")
+    out = built.decode(q).cpu().numpy()
+    ref = built.oracle_decode(orc, q, sample)
+    ok, st = compare(out[sample], ref)
+    say("   ", st)
+    assert ok and st["mixed"] <= DECODE_STRICT, st
+    assert np.all(np.isfinite(out))
+
+
+def test_config5_prefill_sampled(orc):
+    """Prefix 32768 + causal chunk 2048, 64/8 heads; the chunk is bulk-appended
+    then attended; the oracle checks 12 query rows (first, last, seeded)."""
+    pw = W.PrefillWorkload()
+    kp, vp = pw.prefix_kv()
+    kc_, vc_ = pw.chunk_kv()
+    k = np.concatenate([kp, kc_])
+    v = np.concatenate([vp, vc_])
+    stk, stv = orc.tensor_scale(k), orc.tensor_scale(v)
+    pt = pw.page_table()
+    cache = api.KVCache(pw.num_pages, pw.Hkv, stk, stv, fill=0)
+    say("config 5: append prefix, then chunk")
+    api.append(cache, to_dev(kp, "bf16"), to_dev(vp, "bf16"), i32(np.zeros(pw.prefix)),
+               i32(np.arange(pw.prefix)), i32(pt))
+    api.append(cache, to_dev(kc_, "bf16"), to_dev(vc_, "bf16"), i32(np.zeros(pw.T)),
+               i32(pw.prefix + np.arange(pw.T)), i32(pt))
+    q = pw.q()
+    say("config 5: prefill")
+    out = api.prefill(cache, to_dev(q, "bf16"), i32(pt[0]), pw.prefix, causal=True).cpu().numpy()
+    rows = np.unique(np.concatenate([[0, 1, pw.T - 1], np.random.default_rng(55).choice(pw.T, 9, replace=False)]))
+    kc, ks = orc.quantize_rows(k, stk)
+    vc, vs = orc.quantize_rows(v, stv)
+    # the device codes of the chunk are the oracle's (bit-exact)
+    P = planes(cache)
+    pages, slots = sequence_tokens(pt[0], pw.total)
+    sel = np.concatenate([np.arange(0, 64), np.arange(pw.prefix - 8, pw.total)])
+    got = P.gather(pages[sel], slots[sel])
+    for g, e in zip(got, (kc[sel], ks[sel], vc[sel], vs[sel])):
+        assert np.array_equal(g, e)
+    ref = orc.prefill_rows(q[rows], rows, pw.Hkv, kc, ks, stk, vc, vs, stv, pw.prefix, causal=True)
+    ok, st = compare(out[rows], ref)
+    say("   ", st)
+    assert ok, st
