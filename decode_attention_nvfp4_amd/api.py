@@ -17,6 +17,7 @@ import torch
 from . import build as _build
 
 F32, BF16 = 0, 1
+PREFILL_FP8, PREFILL_F16 = 0, 1
 HEAD_DIM, PAGE_SIZE, BLOCK = 128, 16, 16
 
 _lib = None
@@ -55,8 +56,8 @@ _SIGS = {
     "nvfp4_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "nvfp4_decode_attn": (_I32, [_CP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _F, _I32,
                                  _VP, _SZ, _VP, _VP]),
-    "nvfp4_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
-    "nvfp4_prefill_attn": (_I32, [_CP, _VP, _I32, _I32, _I32, _VP, _I32, _I32, _F, _VP, _SZ,
+    "nvfp4_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "nvfp4_prefill_attn": (_I32, [_CP, _VP, _I32, _I32, _I32, _VP, _I32, _I32, _I32, _F, _VP, _SZ,
                                   _VP, _VP]),
 }
 EXPORTS = tuple(_SIGS)
@@ -137,8 +138,8 @@ def decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len, num_sp
     return lib().nvfp4_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len, num_splits)
 
 
-def prefill_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, prefix_len) -> int:
-    return lib().nvfp4_prefill_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, prefix_len)
+def prefill_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, prefix_len, mode=PREFILL_FP8) -> int:
+    return lib().nvfp4_prefill_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, prefix_len, mode)
 
 
 # ------------------------------------------------------------------- cache
@@ -243,8 +244,9 @@ def decode(cache: KVCache, q, page_table, seq_lens, max_seq_len: int, softmax_sc
 
 
 def prefill(cache: KVCache, q, page_table_row, prefix_len: int, causal: bool = True,
-            softmax_scale=None, workspace=None, out=None, stream=None):
-    """Chunked prefill: q [T][Hq][128] -> out [T][Hq][128] FP32."""
+            softmax_scale=None, workspace=None, out=None, stream=None, mode=PREFILL_FP8):
+    """Chunked prefill: q [T][Hq][128] -> out [T][Hq][128] FP32.  mode:
+    PREFILL_FP8 (FP8 operands) or PREFILL_F16 (exact 16-bit operands)."""
     _dev(q, "q")
     _dev(page_table_row, "page_table_row", torch.int32)
     T, Hq = q.shape[0], q.shape[1]
@@ -252,12 +254,12 @@ def prefill(cache: KVCache, q, page_table_row, prefix_len: int, causal: bool = T
         softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
     if out is None:
         out = torch.empty((T, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
-    need = prefill_workspace_bytes(T, Hq, cache.num_kv_heads, prefix_len)
+    need = prefill_workspace_bytes(T, Hq, cache.num_kv_heads, prefix_len, mode)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     cs = cache.struct()
     _check("nvfp4_prefill_attn", lib().nvfp4_prefill_attn(
         ctypes.byref(cs), _ptr(q), _dtype_code(q), T, Hq, _ptr(page_table_row), int(prefix_len),
-        int(bool(causal)), float(softmax_scale), _ptr(workspace),
+        int(bool(causal)), int(mode), float(softmax_scale), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _ptr(out), _stream(stream)))
     return out

@@ -257,27 +257,31 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
   return hip_status(launch_decode(a, q_dtype == NVFP4_DTYPE_F32, (hipStream_t)stream), "decode launch");
 }
 
-static size_t prefill_ws(int32_t total, int32_t hkv) {
+static size_t prefill_ws(int32_t total, int32_t hkv, int32_t mode) {
   const size_t tiles = (size_t)(total + kPrefillTile - 1) / kPrefillTile;
-  return 2 * align256(tiles * kPrefillTile * NVFP4_HEAD_DIM * (size_t)hkv);
+  const size_t eb = mode == NVFP4_PREFILL_F16 ? 2 : 1;
+  return 2 * align256(tiles * kPrefillTile * NVFP4_HEAD_DIM * (size_t)hkv * eb);
 }
 
 size_t nvfp4_prefill_workspace_bytes(int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
-                                     int32_t prefix_len) {
+                                     int32_t prefix_len, int32_t mode) {
   (void)num_q_heads;
   if (num_tokens < 0 || num_kv_heads <= 0 || prefix_len < 0) return 0;
-  return prefill_ws(prefix_len + num_tokens, num_kv_heads);
+  if (mode != NVFP4_PREFILL_FP8 && mode != NVFP4_PREFILL_F16) return 0;
+  return prefill_ws(prefix_len + num_tokens, num_kv_heads, mode);
 }
 
 int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
                            int32_t num_tokens, int32_t num_q_heads,
                            const int32_t* page_table_row, int32_t prefix_len, int32_t causal,
-                           float softmax_scale, void* workspace, size_t workspace_bytes,
-                           float* out, void* stream) {
+                           int32_t mode, float softmax_scale, void* workspace,
+                           size_t workspace_bytes, float* out, void* stream) {
   g_err[0] = 0;
   int32_t st = check_cache(cache);
   if (st) return st;
   if (!dtype_ok(q_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
+  if (mode != NVFP4_PREFILL_FP8 && mode != NVFP4_PREFILL_F16)
+    return fail(NVFP4_ERR_UNSUPPORTED, "prefill mode %d", mode);
   if (num_tokens < 0 || prefix_len < 0 || num_q_heads <= 0)
     return fail(NVFP4_ERR_INVALID_ARG, "bad sizes (tokens %d, prefix %d, heads %d)", num_tokens,
                 prefix_len, num_q_heads);
@@ -293,7 +297,7 @@ int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q
   if (!q || !page_table_row || !out) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(NVFP4_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
   const int32_t total = prefix_len + num_tokens;
-  const size_t need = prefill_ws(total, hkv);
+  const size_t need = prefill_ws(total, hkv, mode);
   if (!workspace || workspace_bytes < need)
     return fail(NVFP4_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -303,8 +307,9 @@ int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q
   a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
   a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
   a.q = q; a.page_table_row = page_table_row; a.out = out;
-  a.k8 = static_cast<uint8_t*>(workspace);
-  a.v8 = static_cast<uint8_t*>(workspace) + need / 2;
+  a.kx = static_cast<uint8_t*>(workspace);
+  a.vx = static_cast<uint8_t*>(workspace) + need / 2;
+  a.mode = mode;
   a.k_scale = cache->k_tensor_scale; a.v_scale = cache->v_tensor_scale;
   a.softmax_scale = softmax_scale;
   a.T = num_tokens; a.hq = num_q_heads; a.hkv = hkv; a.group = num_q_heads / hkv;

@@ -8,6 +8,10 @@
 
 namespace nvfp4 {
 
+constexpr int kPrefillTile = 64;   // keys per prefill tile
+constexpr int kPrefillFP8 = 0;     // operand precisions of the prefill path
+constexpr int kPrefillF16 = 1;
+
 struct AppendArgs {
   uint8_t* k_codes;
   uint8_t* k_scales;
@@ -64,14 +68,15 @@ struct PrefillArgs {
   const void* q;              // [T][Hq][128]
   const int32_t* page_table_row;
   float* out;                 // [T][Hq][128]
-  uint8_t* k8;                // workspace: FP8 K  [Hkv][tiles*64][128]
-  uint8_t* v8;                // workspace: FP8 V^T [Hkv][tiles][128][64]
+  uint8_t* kx;                // workspace: expanded K  [Hkv][tiles*64][128]
+  uint8_t* vx;                // workspace: expanded V^T [Hkv][tiles][128][64]
   float k_scale, v_scale;     // tensor scales
   float softmax_scale;
   int32_t T, hq, hkv, group;
   int32_t prefix, causal;
   int32_t total;              // prefix + T
   int32_t num_tiles;          // ceil(total / 64)
+  int32_t mode;               // kPrefillFP8 or kPrefillF16
 };
 
 hipError_t launch_append(const AppendArgs& a, bool f32_in, hipStream_t s);
@@ -79,7 +84,5 @@ hipError_t launch_dequant(const DequantArgs& a, bool f32_out, hipStream_t s);
 hipError_t launch_absmax(const void* x, bool f32_in, int64_t n, float* out, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, bool f32_q, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s);
-
-constexpr int kPrefillTile = 64;   // keys per prefill tile
 
 }  // namespace nvfp4

@@ -1,49 +1,72 @@
-// prefill.hip -- chunked-prefill attention over the NVFP4 cache with FP8
-// MFMA operands and FP32 accumulation.
+// prefill.hip -- chunked-prefill attention over the NVFP4 cache.
 //
 // Flow ("NVIDIA解説: NVFP4 KV Cacheで長コンテキストLLM推論を最適化", section
-// 量子化・逆量子化フロー): the NVFP4 cache is dequantized to FP8 and the
-// attention and context products run on FP8 operands.  Here the expansion is
-// a separate pass over the sequence's cache (expand_kernel) into an FP8
-// workspace laid out as MFMA operands; the attention kernel (fa_kernel) then
-// streams 64-key tiles through LDS.  Each K/V element is expanded once
-// instead of once per query tile, which keeps the attention loop's VALU
-// budget for the softmax.
+// 量子化・逆量子化フロー): the NVFP4 cache is dequantized and attention runs
+// on the dequantized operands with an FP32 accumulator.  Two operand
+// precisions share one kernel structure:
+//   FP8 (the pages' flow): K~, V~ = E4M3(e2m1 * s_block / 8) (<= 336, no
+//     overflow); Q = E4M3(q * 2^shift_row) with |q| 2^shift < 256; P =
+//     E4M3(p * 256) with p <= 2^0.5 (lazy max, below); 32x32x64 FP8 MFMAs.
+//   F16: K~, V~ = e2m1 * s_block exactly (at most 6 significant bits,
+//     magnitudes 2^-10 .. 2688); Q = F16(q * 2^shift_row) (exact for bf16
+//     input in range); P = F16(p); 32x32x16 f16 MFMAs at half the FP8 rate.
+// The scores and the output take the scale factors back in FP32.
 //
-// FP8 values: K~ = E4M3(e2m1 * s_block / 8) (<= 336, no overflow);
-// Q = E4M3(q * 2^shift_row) with |q| * 2^shift < 256 per row;
-// P = E4M3(p * 256) with p <= 2^0.5 (lazy max, below).  The scores and the
-// output take the factors back in FP32.
+// The expansion is a separate pass over the sequence's cache (expand_kernel)
+// into a workspace laid out as MFMA operands, so each K/V element is expanded
+// once instead of once per query tile; the attention kernel (fa_kernel) then
+// streams 64-key tiles through LDS, double-buffered.
 //
 // fa_kernel: a 256-thread workgroup owns 128 consecutive (query, head) rows of
-// one KV head (row r = query r / G, head r % G), 32 per wave.  Per 64-key
-// tile and wave:
-//   S^T[key][row] = K~ Q^T: two key blocks x two 32x32x64 FP8 MFMAs (the
-//     contraction over d is permuted identically in K~ and Q: lane half h
-//     holds d in [64h, 64h+64)).
-//   softmax over keys: each lane holds 32 keys of one row, the other 32 sit
-//     in the lane 32 away.
-//   O^T[d][row] += V~^T P^T: four 32x32x64 FP8 MFMAs; P^T is the S^T
-//     accumulator converted in place, so the key order inside a tile follows
-//     the accumulator layout (kappa below), which the V~ workspace matches.
+// one KV head (row r = query r / G, head r % G), 32 per wave (lane n = row,
+// lane half h).  Per 64-key tile and wave:
+//   S^T[key][row] = K~ Q^T over two 32-key blocks (the contraction over d is
+//     permuted identically in K~ and Q: lane half h holds d in [64h, 64h+64)).
+//   softmax over keys: each lane holds 32 keys of one row, the other 32 sit in
+//     the lane 32 away (one permlane swap per reduction).
+//   O^T[d][row] += V~^T P^T: P^T is the S^T accumulator converted in place,
+//     so the key order inside a tile follows the accumulator layout
+//     (vt_pos below), which the V~ workspace matches.
 #include "common.h"
 #include "internal.h"
 
 namespace nvfp4 {
 
 constexpr int kTile = kPrefillTile;      // 64 keys
-constexpr int kKRow = 144;                // LDS bytes per K~ row (128 + pad)
-constexpr int kVRow = 80;                 // LDS bytes per V~^T row (64 + pad)
 
-// Position of key kk (0..63) of a tile inside a V~^T row: lane half h and
-// element j of the P^T operand.  The S^T accumulator of key block kb gives
-// lane (n, h) element r the key kb*32 + 8(r/4) + 4h + r%4, and P^T element
-// j = 16 kb + r.
+template <int MODE> struct Prec;
+template <> struct Prec<kPrefillFP8> {
+  static constexpr int EB = 1;                       // bytes per operand element
+  static constexpr float kExpand = 0.125f;           // K~, V~ carry 2^-3
+  static constexpr int kQTop = 7;                    // |q| 2^shift in [2^7, 2^8)
+  static constexpr float kPScale = 256.0f;           // P carries 2^8
+};
+template <> struct Prec<kPrefillF16> {
+  static constexpr int EB = 2;
+  static constexpr float kExpand = 1.0f;
+  static constexpr int kQTop = 14;                   // |q| 2^shift in [2^14, 2^15)
+  static constexpr float kPScale = 1.0f;
+};
+
+// Position of key kk (0..63) of a tile inside a V~^T row.
+//  FP8 (K = 64 keys per MFMA): S^T key block kb gives lane half h, element r
+//    the key kb*32 + 8(r/4) + 4h + r%4; P^T element j = 16 kb + r; the row
+//    holds [h][j] for j = 0..31.
+//  F16 (K = 16 keys per MFMA u = 0..3): P^T element j = 0..7 of MFMA u is key
+//    16u + 8(j/4) + 4h + j%4; the row holds [u][h][j].
+template <int MODE>
 __device__ __forceinline__ int vt_pos(int kk) {
-  const int kb = kk >> 5, rem = kk & 31;
-  const int h = (rem >> 2) & 1;
-  const int j = 16 * kb + (rem >> 3) * 4 + (rem & 3);
-  return h * 32 + j;
+  if (MODE == kPrefillFP8) {
+    const int kb = kk >> 5, rem = kk & 31;
+    const int h = (rem >> 2) & 1;
+    const int j = 16 * kb + (rem >> 3) * 4 + (rem & 3);
+    return h * 32 + j;
+  } else {
+    const int u = kk >> 4, rem = kk & 15;
+    const int h = (rem >> 2) & 1;
+    const int j = (rem >> 3) * 4 + (rem & 3);
+    return (u * 2 + h) * 8 + j;
+  }
 }
 
 __device__ __forceinline__ float e2m1_value(uint32_t c) {
@@ -52,45 +75,47 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
   return (c & 8u) ? -mag : mag;
 }
 
-// E4M3 of a value already known to be < 448 in magnitude (nearest even).
-__device__ __forceinline__ uint32_t to_fp8(float v) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+// Operand encoding of a value: E4M3 (nearest even; |v| < 448 here) or F16.
+template <int MODE>
+__device__ __forceinline__ uint32_t encode(float v) {
+  if (MODE == kPrefillFP8) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+  _Float16 h = (_Float16)v;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
-// Expand one 64-key tile of one KV head to FP8.  K~: [Hkv][tiles*64][128];
+// Expand one 64-key tile of one KV head.  K~: [Hkv][tiles*64][128];
 // V~^T: [Hkv][tiles][128][64] (keys in vt_pos order).  Keys >= total are 0.
+template <int MODE>
 __global__ void __launch_bounds__(256) expand_kernel(PrefillArgs p) {
+  using P = Prec<MODE>;
   const int tile = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
-  __shared__ uint8_t vt[kD * kTile];
+  __shared__ uint8_t vt[kD * kTile * P::EB];
 
   // K: thread -> key tid/4, elements 32q..32q+31
   {
     const int kk = tid >> 2, q = tid & 3;
     const int t = tile * kTile + kk;
-    u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
+    uint32_t o[8 * P::EB];
+#pragma unroll
+    for (int i = 0; i < 8 * P::EB; ++i) o[i] = 0u;
     if (t < p.total) {
       const int page = p.page_table_row[t / kPage], slot = t % kPage;
       const size_t slab = (size_t)page * p.hkv + kvh;
       const u32x4 kq = *reinterpret_cast<const u32x4*>(p.k_codes + slab * kSlab + slot * 64 + q * 16);
       const uint32_t ksc = *reinterpret_cast<const uint16_t*>(p.k_scales + slab * kScaleSlab + slot * kNBlk + q * 2);
-      const float s0 = e4m3_to_float(ksc & 0xFFu) * 0.125f, s1 = e4m3_to_float(ksc >> 8) * 0.125f;
+      const float s0 = e4m3_to_float(ksc & 0xFFu) * P::kExpand, s1 = e4m3_to_float(ksc >> 8) * P::kExpand;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = i < 2 ? s0 : s1;
-        uint32_t word0 = 0, word1 = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t b8 = to_fp8(e2m1_value((kq[i] >> (4 * j)) & 15u) * sc);
-          if (j < 4) word0 |= b8 << (8 * j);
-          else word1 |= b8 << (8 * (j - 4));
-        }
-        if (i < 2) { o0[2 * i] = word0; o0[2 * i + 1] = word1; }
-        else { o1[2 * (i - 2)] = word0; o1[2 * (i - 2) + 1] = word1; }
+      for (int e = 0; e < 32; ++e) {
+        const float sc = e < 16 ? s0 : s1;
+        const uint32_t c = (kq[e >> 3] >> (4 * (e & 7))) & 15u;
+        const uint32_t b = encode<MODE>(e2m1_value(c) * sc);
+        if (P::EB == 1) o[e >> 2] |= b << (8 * (e & 3));
+        else o[e >> 1] |= b << (16 * (e & 1));
       }
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(p.k8 + (((size_t)kvh * p.num_tiles * kTile) + (size_t)t) * kD + q * 32);
-    dst[0] = o0;
-    dst[1] = o1;
+    u32x4* dst = reinterpret_cast<u32x4*>(p.kx + ((((size_t)kvh * p.num_tiles * kTile) + (size_t)t) * kD + q * 32) * P::EB);
+#pragma unroll
+    for (int i = 0; i < 2 * P::EB; ++i) dst[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
   }
   // V: dword (token group tg, byte b) holds byte b of 4 consecutive tokens
 #pragma unroll
@@ -109,25 +134,39 @@ __global__ void __launch_bounds__(256) expand_kernel(PrefillArgs p) {
     for (int j = 0; j < 4; ++j) {
       const int kk = 4 * tg + j;
       const bool live = t0 + j < p.total;
-      const float sc = e4m3_to_float((sc4 >> (8 * j)) & 0xFFu) * 0.125f;
+      const float sc = e4m3_to_float((sc4 >> (8 * j)) & 0xFFu) * P::kExpand;
       const uint32_t byte = (W >> (8 * j)) & 0xFFu;
-      const int pos = vt_pos(kk);
-      vt[(2 * b) * kTile + pos] = live ? (uint8_t)to_fp8(e2m1_value(byte & 15u) * sc) : 0;
-      vt[(2 * b + 1) * kTile + pos] = live ? (uint8_t)to_fp8(e2m1_value(byte >> 4) * sc) : 0;
+      const int pos = vt_pos<MODE>(kk);
+      const uint32_t lo = live ? encode<MODE>(e2m1_value(byte & 15u) * sc) : 0u;
+      const uint32_t hi = live ? encode<MODE>(e2m1_value(byte >> 4) * sc) : 0u;
+      if (P::EB == 1) {
+        vt[(2 * b) * kTile + pos] = (uint8_t)lo;
+        vt[(2 * b + 1) * kTile + pos] = (uint8_t)hi;
+      } else {
+        reinterpret_cast<uint16_t*>(vt)[(2 * b) * kTile + pos] = (uint16_t)lo;
+        reinterpret_cast<uint16_t*>(vt)[(2 * b + 1) * kTile + pos] = (uint16_t)hi;
+      }
     }
   }
   __syncthreads();
-  const u32x4* src = reinterpret_cast<const u32x4*>(vt) + tid * 2;
-  u32x4* dst = reinterpret_cast<u32x4*>(p.v8 + ((size_t)kvh * p.num_tiles + tile) * (kD * kTile)) + tid * 2;
-  dst[0] = src[0];
-  dst[1] = src[1];
+  const u32x4* src = reinterpret_cast<const u32x4*>(vt) + tid * 2 * P::EB;
+  u32x4* dst = reinterpret_cast<u32x4*>(p.vx + ((size_t)kvh * p.num_tiles + tile) * (kD * kTile * P::EB)) + tid * 2 * P::EB;
+#pragma unroll
+  for (int i = 0; i < 2 * P::EB; ++i) dst[i] = src[i];
 }
 
-template <bool F32Q>
+template <int MODE, bool F32Q>
 __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
+  using P = Prec<MODE>;
+  constexpr int EB = P::EB;
+  constexpr int KROW = kD * EB + 16;        // LDS bytes per K~ row (padded)
+  constexpr int VROW = kTile * EB + 16;     // LDS bytes per V~^T row (padded)
+  constexpr int NCH = 512 * EB;             // 16-byte chunks per operand tile
+  constexpr int CPT = NCH / 256;            // chunks per thread per operand
+
   const int nrows = p.T * p.group;
-  const int kvh = blockIdx.x % p.hkv;             // consecutive blocks spread over XCDs;
-  const int rt = blockIdx.x / p.hkv;              // one KV head's tiles share an XCD when Hkv divides 8
+  const int kvh = blockIdx.x % p.hkv;       // one KV head's row tiles land on the same XCD
+  const int rt = blockIdx.x / p.hkv;        // when Hkv divides the 8 XCDs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int n = lane & 31, h = lane >> 5;
   const int row0 = rt * 128;
@@ -137,11 +176,12 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
   const int head = kvh * p.group + (row_ok ? row % p.group : 0);
   const int lim = p.causal ? p.prefix + qi : p.total - 1;    // last key this row sees
 
-  __shared__ uint8_t ks[2][kTile * kKRow];
-  __shared__ uint8_t vs[2][kD * kVRow];
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2][kTile * KROW];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[2][kD * VROW];
 
-  // ---- Q^T operand: lane (row n, half h) holds q[64h + 32i + j] in byte j of qb[i]
-  intx8 qb[2];
+  // ---- Q^T operand: lane (row n, half h) holds q[64h + e], e = 0..63, in
+  // operand order (byte e for FP8, half e for F16)
+  uint32_t qw[16 * EB];
   float rowscale;
   {
     float qv[64];
@@ -173,18 +213,18 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(qv[i]));
     amax = max_across_halves(amax);
-    int shift = amax > 0.0f ? 7 - ilogbf(amax) : 0;      // amax * 2^shift in [128, 256)
+    int shift = amax > 0.0f ? P::kQTop - ilogbf(amax) : 0;
     shift = max(-120, min(120, shift));
-    // scores: S * 2^-shift * 8 (K~ carries 2^-3) * s_tK * softmax_scale * log2(e)
-    rowscale = ldexpf(1.0f, -shift) * 8.0f * p.k_scale * p.softmax_scale * 1.4426950408889634f;
+    rowscale = ldexpf(1.0f, -shift) / P::kExpand * p.k_scale * p.softmax_scale * 1.4426950408889634f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const float* v = qv + 32 * i + 4 * w;
+    for (int w = 0; w < 16 * EB; ++w) {
+      if (MODE == kPrefillFP8) {
+        const float* v = qv + 4 * w;
         int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], shift), ldexpf(v[1], shift), 0, false);
-        int both = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], shift), ldexpf(v[3], shift), lo, true);
-        qb[i][w] = both;
+        qw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], shift), ldexpf(v[3], shift), lo, true);
+      } else {
+        const float* v = qv + 2 * w;
+        qw[w] = encode<MODE>(ldexpf(v[0], shift)) | (encode<MODE>(ldexpf(v[1], shift)) << 16);
       }
     }
   }
@@ -196,24 +236,27 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
   const int ntiles = (kv_len + kTile - 1) / kTile;
   const int mask_from = p.causal ? (p.prefix + first_q + 1) / kTile : ntiles;   // tiles needing a mask
 
-  const uint8_t* k8 = p.k8 + (size_t)kvh * p.num_tiles * kTile * kD;
-  const uint8_t* v8 = p.v8 + (size_t)kvh * p.num_tiles * kD * kTile;
+  const uint8_t* kx = p.kx + (size_t)kvh * p.num_tiles * kTile * kD * EB;
+  const uint8_t* vx = p.vx + (size_t)kvh * p.num_tiles * kD * kTile * EB;
 
-  // tile loads: K~ chunk c (0..511) = key c/8, bytes 16(c%8); V~^T chunk c = d c/4, bytes 16(c%4)
-  auto gload = [&](int tile, u32x4 r[4]) {
-    const uint8_t* kt = k8 + (size_t)tile * kTile * kD;
-    const uint8_t* vt = v8 + (size_t)tile * kD * kTile;
-    r[0] = *reinterpret_cast<const u32x4*>(kt + tid * 16);
-    r[1] = *reinterpret_cast<const u32x4*>(kt + (tid + 256) * 16);
-    r[2] = *reinterpret_cast<const u32x4*>(vt + tid * 16);
-    r[3] = *reinterpret_cast<const u32x4*>(vt + (tid + 256) * 16);
+  // tile loads: K~ chunk c = key c/(8 EB), 16 bytes at (c % (8 EB)) * 16;
+  // V~^T chunk c = d c/(4 EB), 16 bytes at (c % (4 EB)) * 16
+  auto gload = [&](int tile, u32x4 r[2 * CPT]) {
+    const uint8_t* kt = kx + (size_t)tile * kTile * kD * EB;
+    const uint8_t* vt = vx + (size_t)tile * kD * kTile * EB;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      r[i] = *reinterpret_cast<const u32x4*>(kt + (tid + 256 * i) * 16);
+      r[CPT + i] = *reinterpret_cast<const u32x4*>(vt + (tid + 256 * i) * 16);
+    }
   };
-  auto sstore = [&](int buf, const u32x4 r[4]) {
-    const int c0 = tid, c1 = tid + 256;
-    *reinterpret_cast<u32x4*>(&ks[buf][(c0 >> 3) * kKRow + (c0 & 7) * 16]) = r[0];
-    *reinterpret_cast<u32x4*>(&ks[buf][(c1 >> 3) * kKRow + (c1 & 7) * 16]) = r[1];
-    *reinterpret_cast<u32x4*>(&vs[buf][(c0 >> 2) * kVRow + (c0 & 3) * 16]) = r[2];
-    *reinterpret_cast<u32x4*>(&vs[buf][(c1 >> 2) * kVRow + (c1 & 3) * 16]) = r[3];
+  auto sstore = [&](int buf, const u32x4 r[2 * CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(&ks[buf][(c / (8 * EB)) * KROW + (c % (8 * EB)) * 16]) = r[i];
+      *reinterpret_cast<u32x4*>(&vs[buf][(c / (4 * EB)) * VROW + (c % (4 * EB)) * 16]) = r[CPT + i];
+    }
   };
 
   floatx16 acc_o[4];
@@ -223,7 +266,7 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
     for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.0f;
   float m_ref = -INFINITY, l_run = 0.0f;
 
-  u32x4 pre[4];
+  u32x4 pre[2 * CPT];
   if (ntiles > 0) {
     gload(0, pre);
     sstore(0, pre);
@@ -237,15 +280,27 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
     floatx16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t* kr = &ks[buf][(kb * 32 + n) * kKRow + h * 64];
-      intx8 a0, a1;
-      *reinterpret_cast<u32x4*>(&a0) = *reinterpret_cast<const u32x4*>(kr);
-      *(reinterpret_cast<u32x4*>(&a0) + 1) = *reinterpret_cast<const u32x4*>(kr + 16);
-      *reinterpret_cast<u32x4*>(&a1) = *reinterpret_cast<const u32x4*>(kr + 32);
-      *(reinterpret_cast<u32x4*>(&a1) + 1) = *reinterpret_cast<const u32x4*>(kr + 48);
+      const uint8_t* kr = &ks[buf][(kb * 32 + n) * KROW + h * 64 * EB];
       floatx16 c = {};
-      c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, qb[0], c, 0, 0, 0, 127, 0, 127);
-      c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, qb[1], c, 0, 0, 0, 127, 0, 127);
+      if (MODE == kPrefillFP8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          intx8 a, b;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) b[w] = (int)qw[8 * i + w];
+          *reinterpret_cast<u32x4*>(&a) = *reinterpret_cast<const u32x4*>(kr + 32 * i);
+          *(reinterpret_cast<u32x4*>(&a) + 1) = *reinterpret_cast<const u32x4*>(kr + 32 * i + 16);
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const u32x4 av = *reinterpret_cast<const u32x4*>(kr + 16 * i);
+          const u32x4 bv = {qw[4 * i], qw[4 * i + 1], qw[4 * i + 2], qw[4 * i + 3]};
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, av),
+                                                      __builtin_bit_cast(halfx8, bv), c, 0, 0, 0);
+        }
+      }
       s[kb] = c;
     }
     // ---- scale, mask, row max
@@ -267,7 +322,7 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
     }
     mx = max_across_halves(mx);
     // lazy max: rescale only when the row max grows by more than 0.5 (log2),
-    // which keeps p <= 2^0.5 so p * 256 stays inside E4M3's range
+    // which keeps p <= 2^0.5 (p * 256 stays inside E4M3's range)
     const bool grow = mx > m_ref + 0.5f;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_ref;
@@ -277,36 +332,53 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc_o[i] *= alpha;
     }
-    // ---- P^T (FP8, x256) and the row sum
-    intx8 pb;
+    // ---- P^T and the row sum
+    uint32_t pw[8 * EB];
     float lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int kb = w >> 2, r0 = (w & 3) * 4;
-      float e0 = exp2f(s[kb][r0] - m_ref), e1 = exp2f(s[kb][r0 + 1] - m_ref);
-      float e2 = exp2f(s[kb][r0 + 2] - m_ref), e3 = exp2f(s[kb][r0 + 3] - m_ref);
+      const float e0 = exp2f(s[kb][r0] - m_ref), e1 = exp2f(s[kb][r0 + 1] - m_ref);
+      const float e2 = exp2f(s[kb][r0 + 2] - m_ref), e3 = exp2f(s[kb][r0 + 3] - m_ref);
       lsum += (e0 + e1) + (e2 + e3);
-      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e0 * 256.0f, e1 * 256.0f, 0, false);
-      pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(e2 * 256.0f, e3 * 256.0f, lo, true);
+      if (MODE == kPrefillFP8) {
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e0 * P::kPScale, e1 * P::kPScale, 0, false);
+        pw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e2 * P::kPScale, e3 * P::kPScale, lo, true);
+      } else {
+        pw[2 * w] = encode<MODE>(e0) | (encode<MODE>(e1) << 16);
+        pw[2 * w + 1] = encode<MODE>(e2) | (encode<MODE>(e3) << 16);
+      }
     }
     l_run += lsum;
     // ---- O^T += V~^T P^T
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const uint8_t* vr = &vs[buf][(db * 32 + n) * kVRow + h * 32];
-      intx8 a;
-      *reinterpret_cast<u32x4*>(&a) = *reinterpret_cast<const u32x4*>(vr);
-      *(reinterpret_cast<u32x4*>(&a) + 1) = *reinterpret_cast<const u32x4*>(vr + 16);
-      acc_o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pb, acc_o[db], 0, 0, 0, 127, 0, 127);
+      const uint8_t* vr = &vs[buf][(db * 32 + n) * VROW];
+      if (MODE == kPrefillFP8) {
+        intx8 a, b;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) b[w] = (int)pw[w];
+        *reinterpret_cast<u32x4*>(&a) = *reinterpret_cast<const u32x4*>(vr + h * 32);
+        *(reinterpret_cast<u32x4*>(&a) + 1) = *reinterpret_cast<const u32x4*>(vr + h * 32 + 16);
+        acc_o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc_o[db], 0, 0, 0, 127, 0, 127);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const u32x4 av = *reinterpret_cast<const u32x4*>(vr + (u * 2 + h) * 16);
+          const u32x4 bv = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, av),
+                                                              __builtin_bit_cast(halfx8, bv), acc_o[db], 0, 0, 0);
+        }
+      }
     }
     if (t + 1 < ntiles) sstore(buf ^ 1, pre);
     __syncthreads();
   }
 
-  // ---- epilogue: O / l * s_tV * 8 (V~ carries 2^-3) / 256 (P carries 2^8)
+  // ---- epilogue: O / l * s_tV, removing the operand scale factors
   const float l_tot = sum_across_halves(l_run);
   if (row_ok) {
-    const float f = l_tot > 0.0f ? p.v_scale * (8.0f / 256.0f) / l_tot : 0.0f;
+    const float f = l_tot > 0.0f ? p.v_scale / (P::kExpand * P::kPScale) / l_tot : 0.0f;
     float* o = p.out + ((size_t)qi * p.hq + head) * kD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -320,12 +392,18 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
   }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s) {
-  expand_kernel<<<dim3(a.num_tiles, a.hkv), 256, 0, s>>>(a);
+template <int MODE>
+static void launch_mode(const PrefillArgs& a, bool f32_q, hipStream_t s) {
+  expand_kernel<MODE><<<dim3(a.num_tiles, a.hkv), 256, 0, s>>>(a);
   const int nrows = a.T * a.group;
-  const unsigned rtiles = (unsigned)((nrows + 127) / 128);
-  if (f32_q) fa_kernel<true><<<rtiles * a.hkv, 256, 0, s>>>(a);
-  else fa_kernel<false><<<rtiles * a.hkv, 256, 0, s>>>(a);
+  const unsigned blocks = (unsigned)((nrows + 127) / 128) * a.hkv;
+  if (f32_q) fa_kernel<MODE, true><<<blocks, 256, 0, s>>>(a);
+  else fa_kernel<MODE, false><<<blocks, 256, 0, s>>>(a);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s) {
+  if (a.mode == kPrefillF16) launch_mode<kPrefillF16>(a, f32_q, s);
+  else launch_mode<kPrefillFP8>(a, f32_q, s);
   return hipGetLastError();
 }
 

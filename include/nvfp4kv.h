@@ -184,25 +184,38 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
                           int32_t max_seq_len, float softmax_scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, float* out, void* stream);
 
-/* Workspace bytes nvfp4_prefill_attn needs. */
+/* Operand precision of the prefill path. */
+typedef enum nvfp4_prefill_mode {
+  NVFP4_PREFILL_FP8 = 0,  /* the pages' flow: FP8 operands (E4M3 rounding of
+                             the dequantized cache, of Q and of P) */
+  NVFP4_PREFILL_F16 = 1   /* exact 16-bit operands (the dequantized cache is
+                             exact in FP16); half the FP8 MFMA rate */
+} nvfp4_prefill_mode;
+
+/* Workspace bytes nvfp4_prefill_attn needs (0 for invalid arguments): the
+ * expanded K and V of the sequence, 1 (FP8) or 2 (F16) bytes per element. */
 size_t nvfp4_prefill_workspace_bytes(int32_t num_tokens, int32_t num_q_heads,
-                                     int32_t num_kv_heads, int32_t prefix_len);
+                                     int32_t num_kv_heads, int32_t prefix_len, int32_t mode);
 
 /* Chunked-prefill attention (step A9; [EXPL] §量子化・逆量子化フロー: the
- * NVFP4 cache is expanded to FP8 and attention runs on FP8 operands with an
- * FP32 accumulator).  The chunk's own K/V must already be appended.
+ * NVFP4 cache is dequantized to FP8 and attention runs on FP8 operands with
+ * an FP32 accumulator; mode NVFP4_PREFILL_F16 keeps the dequantized values
+ * exact instead).  The chunk's own K/V must already be appended.
  *   q             : device [num_tokens][num_q_heads][128], F32 or BF16
  *   page_table_row: device int32, ceil((prefix_len+num_tokens)/16) pages
  *   causal != 0   : query i (absolute position prefix_len + i) attends to
  *                   tokens 0 .. prefix_len + i; causal == 0: to all
  *                   prefix_len + num_tokens tokens
+ *   mode          : an nvfp4_prefill_mode
+ *   workspace     : device, >= nvfp4_prefill_workspace_bytes(...), 256-byte
+ *                   aligned
  *   out           : device FP32 [num_tokens][num_q_heads][128]
  * num_tokens == 0 is a no-op. */
 int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
                            int32_t num_tokens, int32_t num_q_heads,
                            const int32_t* page_table_row, int32_t prefix_len, int32_t causal,
-                           float softmax_scale, void* workspace, size_t workspace_bytes,
-                           float* out, void* stream);
+                           int32_t mode, float softmax_scale, void* workspace,
+                           size_t workspace_bytes, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -124,9 +124,9 @@ def test_prefill_rejects_bad_arguments(api):
     L = api.lib()
     c = _fake_cache(api)
 
-    def pf(T=16, Hq=64, prefix=100, ws=FAKE, ws_bytes=1 << 30, q_dtype=1, cache=c):
-        return L.nvfp4_prefill_attn(ctypes.byref(cache), FAKE, q_dtype, T, Hq, FAKE, prefix, 1, 0.088, ws,
-                                    ws_bytes, FAKE, None)
+    def pf(T=16, Hq=64, prefix=100, ws=FAKE, ws_bytes=1 << 30, q_dtype=1, cache=c, mode=0):
+        return L.nvfp4_prefill_attn(ctypes.byref(cache), FAKE, q_dtype, T, Hq, FAKE, prefix, 1, mode, 0.088,
+                                    ws, ws_bytes, FAKE, None)
     assert pf(Hq=60) == 1
     assert pf(T=-1) == 1
     assert pf(prefix=-5) == 1
@@ -134,7 +134,11 @@ def test_prefill_rejects_bad_arguments(api):
     assert pf(ws=None, ws_bytes=0) == 3
     assert pf(ws_bytes=100) == 3
     assert pf(cache=_fake_cache(api, page_size=8)) == 2
+    assert pf(mode=2) == 2
     assert pf(T=0) == 0
+    # F16 operands need twice the FP8 workspace
+    assert api.prefill_workspace_bytes(2048, 64, 8, 32768, 1) == 2 * api.prefill_workspace_bytes(2048, 64, 8, 32768, 0)
+    assert api.prefill_workspace_bytes(16, 8, 2, 10, 5) == 0
 
 
 def test_split_planner_and_workspace(api):
