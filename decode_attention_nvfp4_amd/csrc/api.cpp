@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -64,23 +65,21 @@ int cu_count() {
   return n;
 }
 
-// Decode split plan: pages per split starts at 64 and halves (down to 8)
-// until batch * kv_heads * splits reaches 4 workgroups per CU, so ragged and
-// short batches still fill the machine; splits = ceil(max_pages / pps).
-void plan_splits(int32_t batch, int32_t hkv, int32_t max_seq_len, int32_t num_splits, int cus,
-                 int32_t* splits, int32_t* pps) {
-  const int64_t max_pages = max_seq_len > 0 ? (max_seq_len + NVFP4_PAGE_SIZE - 1) / NVFP4_PAGE_SIZE : 1;
-  int64_t per;
-  if (num_splits > 0) {
-    per = (max_pages + num_splits - 1) / num_splits;
-  } else {
-    per = 64;
-    const int64_t units = (int64_t)batch * hkv;
-    while (per > 8 && units * ((max_pages + per - 1) / per) < 4LL * cus) per /= 2;
-  }
-  if (per < 1) per = 1;
-  *pps = (int32_t)per;
-  *splits = (int32_t)((max_pages + per - 1) / per);
+// Decode work plan: the number of waves W that split the (sequence, KV head,
+// page) work into equal contiguous ranges.  Automatic: at most one wave per
+// resident wave slot of the device (CUs x decode waves per CU), so the grid
+// runs in a single round of residency, and at least kMinPagesPerWave pages
+// per wave (for the longest batch max_seq_len allows), so that each wave's
+// fixed cost (query load, partial write and merge) stays small next to its
+// page stream.  A requested count is used as given.
+constexpr int64_t kMinPagesPerWave = 16;
+
+int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, int32_t max_seq_len) {
+  if (num_splits > 0) return num_splits;
+  const int64_t slots = (int64_t)cu_count() * decode_occupancy(f32_q);
+  const int64_t units = (int64_t)batch * hkv * ((max_seq_len + NVFP4_PAGE_SIZE - 1) / NVFP4_PAGE_SIZE);
+  const int64_t want = (units + kMinPagesPerWave - 1) / kMinPagesPerWave;
+  return (int32_t)std::max<int64_t>(1, std::min(slots, want));
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -186,24 +185,24 @@ int32_t nvfp4_kv_dequant(const nvfp4_kv_cache* cache, const int32_t* page_table_
 int32_t nvfp4_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
                                 int32_t num_splits) {
   if (batch <= 0 || num_kv_heads <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
-  int32_t s, pps;
-  plan_splits(batch, num_kv_heads, max_seq_len, num_splits, cu_count(), &s, &pps);
-  return s;
+  return plan_waves(num_splits, false, batch, num_kv_heads, max_seq_len);
 }
 
-static size_t decode_ws(int32_t batch, int32_t hq, int32_t splits) {
-  if (splits <= 1) return 0;
-  const size_t n = (size_t)batch * hq * splits;
-  return align256(n * NVFP4_HEAD_DIM * sizeof(float)) + align256(n * sizeof(float));
+static size_t decode_ws(int32_t batch, int32_t group, int32_t waves) {
+  const size_t pieces = (size_t)waves * 2 * group;
+  return align256(pieces * NVFP4_HEAD_DIM * sizeof(float)) + align256(pieces * sizeof(float)) +
+         align256(((size_t)batch + 1) * sizeof(int32_t));
 }
 
 size_t nvfp4_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t max_seq_len, int32_t num_splits) {
-  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 || num_splits < 0)
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 || num_splits < 0 ||
+      num_q_heads % num_kv_heads != 0)
     return 0;
-  int32_t s, pps;
-  plan_splits(batch, num_kv_heads, max_seq_len, num_splits, cu_count(), &s, &pps);
-  return decode_ws(batch, num_q_heads, s);
+  // sized for the FP32-query kernel too (its occupancy is never higher)
+  const int32_t w = std::max(plan_waves(num_splits, false, batch, num_kv_heads, max_seq_len),
+                             plan_waves(num_splits, true, batch, num_kv_heads, max_seq_len));
+  return decode_ws(batch, num_q_heads / num_kv_heads, w);
 }
 
 int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
@@ -232,29 +231,30 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
   if (batch == 0) return NVFP4_OK;
   if (!q || !page_table || !seq_lens || !out) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(NVFP4_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
-  int32_t S, pps;
-  plan_splits(batch, hkv, max_seq_len, num_splits, cu_count(), &S, &pps);
-  const size_t need = decode_ws(batch, num_q_heads, S);
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  const bool f32q = q_dtype == NVFP4_DTYPE_F32;
+  const int32_t W = plan_waves(num_splits, f32q, batch, hkv, max_seq_len);
+  const size_t need = decode_ws(batch, G, W);
+  if (!workspace || workspace_bytes < need)
     return fail(NVFP4_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(NVFP4_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   DecodeArgs a;
   a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
   a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
   a.q = q; a.page_table = page_table; a.seq_lens = seq_lens; a.out = out;
-  const size_t n = (size_t)batch * num_q_heads * S;
-  a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
-  a.ws_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             align256(n * NVFP4_HEAD_DIM * sizeof(float)))
-                  : nullptr;
+  const size_t pieces = (size_t)W * 2 * G;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(ws);
+  a.ws_lse = reinterpret_cast<float*>(ws + align256(pieces * NVFP4_HEAD_DIM * sizeof(float)));
+  a.ws_prefix = reinterpret_cast<int32_t*>(ws + align256(pieces * NVFP4_HEAD_DIM * sizeof(float)) +
+                                           align256(pieces * sizeof(float)));
   a.qk_scale = (float)((double)cache->k_tensor_scale * (double)softmax_scale * 1.4426950408889634);
   a.v_scale = cache->v_tensor_scale;
   a.max_pages = max_pages_per_seq;
   a.batch = batch; a.hq = num_q_heads; a.hkv = hkv; a.group = G;
-  a.num_splits = S; a.pages_per_split = pps;
-  return hip_status(launch_decode(a, q_dtype == NVFP4_DTYPE_F32, (hipStream_t)stream), "decode launch");
+  a.num_splits = W;
+  return hip_status(launch_decode(a, f32q, (hipStream_t)stream), "decode launch");
 }
 
 static size_t prefill_ws(int32_t total, int32_t hkv, int32_t mode) {

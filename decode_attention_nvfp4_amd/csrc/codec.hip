@@ -41,39 +41,86 @@ __device__ __forceinline__ uint32_t quantize_half_block(const float x[8], float 
   return encode8(x, code, s_t);
 }
 
+// Eight nibbles (element e in bits 4e..4e+3) spread to the low nibbles of
+// eight bytes: elements 0..3 in *w0, 4..7 in *w1.
+__device__ __forceinline__ void spread_nibbles(uint32_t w, uint32_t* w0, uint32_t* w1) {
+  auto sp = [](uint32_t x) {
+    return (x & 0xFu) | ((x & 0xF0u) << 4) | ((x & 0xF00u) << 8) | ((x & 0xF000u) << 12);
+  };
+  *w0 = sp(w & 0xFFFFu);
+  *w1 = sp(w >> 16);
+}
+
+// Workgroup = 16 consecutive tokens of the call x one KV head (grid.y).  The
+// V codes of a token pair (2i, 2i+1) share bytes: when both tokens of a pair
+// sit in the same workgroup (consecutive rows, same sequence, positions 2i
+// and 2i+1) the even row writes the whole bytes; a token whose partner is
+// elsewhere updates its nibbles with atomic AND / OR, which commute with the
+// partner's own update of the other nibbles.
 template <bool F32IN>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
-  const int lane16 = threadIdx.x & 15;
-  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);     // (token, head)
-  if (row >= (size_t)p.n_tok * p.hkv) return;
-  const int tok = (int)(row / p.hkv);
-  const int h = (int)(row - (size_t)tok * p.hkv);
-  const int seq = p.tok_seq[tok];
-  const int pos = p.tok_pos[tok];
-  const int page = p.page_table[(size_t)seq * p.max_pages + pos / kPage];
-  const int slot = pos % kPage;
-  const size_t slab = (size_t)page * p.hkv + h;
-
-  float x[8];
-  uint32_t sb;
-  // K: token-major codes [16][64 B], token-major scales [16][8]
-  load8<F32IN>(p.k_new, row, lane16, x);
-  uint32_t w = quantize_half_block(x, p.k_scale, p.k_six_st, &sb);
-  *reinterpret_cast<uint32_t*>(p.k_codes + slab * kSlab + slot * 64 + lane16 * 4) = w;
-  if ((lane16 & 1) == 0) p.k_scales[slab * kScaleSlab + slot * kNBlk + (lane16 >> 1)] = (uint8_t)sb;
-
-  // V: codes [group 4][byte 64][token 4], scales [block 8][token 16]
-  load8<F32IN>(p.v_new, row, lane16, x);
-  w = quantize_half_block(x, p.v_scale, p.v_six_st, &sb);
-  uint8_t* vc = p.v_codes + slab * kSlab + (slot >> 2) * 256 + (slot & 3);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) vc[(lane16 * 4 + k) * 4] = (uint8_t)(w >> (8 * k));
-  if ((lane16 & 1) == 0) p.v_scales[slab * kScaleSlab + (lane16 >> 1) * kPage + slot] = (uint8_t)sb;
+  const int lane16 = threadIdx.x & 15, r = threadIdx.x >> 4;
+  const int tok = blockIdx.x * 16 + r;
+  const int h = blockIdx.y;
+  const bool valid = tok < p.n_tok;
+  __shared__ int s_seq[16], s_pos[16];
+  __shared__ uint32_t s_vw[16][16];
+  int seq = -1, pos = 0;
+  if (valid) {
+    seq = p.tok_seq[tok];
+    pos = p.tok_pos[tok];
+  }
+  if (lane16 == 0) {
+    s_seq[r] = seq;
+    s_pos[r] = pos;
+  }
+  const size_t row = (size_t)tok * p.hkv + h;
+  size_t slab = 0;
+  int slot = 0;
+  uint32_t vw = 0, vsb = 0;
+  if (valid) {
+    const int page = p.page_table[(size_t)seq * p.max_pages + pos / kPage];
+    slot = pos % kPage;
+    slab = (size_t)page * p.hkv + h;
+    float x[8];
+    uint32_t sb;
+    // K: token-major codes [16][64 B], token-major scales [16][8]
+    load8<F32IN>(p.k_new, row, lane16, x);
+    const uint32_t w = quantize_half_block(x, p.k_scale, p.k_six_st, &sb);
+    *reinterpret_cast<uint32_t*>(p.k_codes + slab * kSlab + slot * 64 + lane16 * 4) = w;
+    if ((lane16 & 1) == 0) p.k_scales[slab * kScaleSlab + slot * kNBlk + (lane16 >> 1)] = (uint8_t)sb;
+    // V: codes of elements 8 lane16 .. 8 lane16 + 7; scales [block 8][token 16]
+    load8<F32IN>(p.v_new, row, lane16, x);
+    vw = quantize_half_block(x, p.v_scale, p.v_six_st, &vsb);
+    if ((lane16 & 1) == 0) p.v_scales[slab * kScaleSlab + (lane16 >> 1) * kPage + slot] = (uint8_t)vsb;
+  }
+  s_vw[r][lane16] = vw;
+  __syncthreads();
+  if (!valid) return;
+  const int odd = pos & 1;
+  const int pr = odd ? r - 1 : r + 1;           // the partner's row, if it is here
+  const bool paired = pr >= 0 && pr < 16 && s_seq[pr] == seq && s_pos[pr] == (pos ^ 1);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(p.v_codes + slab * kSlab + (slot >> 2) * 256 + lane16 * 16 +
+                                              ((slot >> 1) & 1) * 8);
+  uint32_t a0, a1;
+  spread_nibbles(vw, &a0, &a1);
+  if (paired) {
+    if (odd) return;                            // written by the even row
+    uint32_t b0, b1;
+    spread_nibbles(s_vw[pr][lane16], &b0, &b1);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(a0 | (b0 << 4), a1 | (b1 << 4));
+  } else {
+    const uint32_t keep = odd ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
+    const int sh = odd ? 4 : 0;
+    atomicAnd(dst, keep);
+    atomicOr(dst, a0 << sh);
+    atomicAnd(dst + 1, keep);
+    atomicOr(dst + 1, a1 << sh);
+  }
 }
 
 hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
-  size_t rows = (size_t)a.n_tok * a.hkv;
-  unsigned grid = (unsigned)((rows + 15) / 16);
+  const dim3 grid((unsigned)((a.n_tok + 15) / 16), (unsigned)a.hkv);
   if (f32) append_kernel<true><<<grid, 256, 0, s>>>(a);
   else append_kernel<false><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
@@ -102,10 +149,16 @@ __global__ void __launch_bounds__(256) dequant_kernel(DequantArgs p) {
       sb = p.k_scales[slab * kScaleSlab + slot * kNBlk + (lane16 >> 1)];
       st = p.k_scale;
     } else {
-      const uint8_t* vc = p.v_codes + slab * kSlab + (slot >> 2) * 256 + (slot & 3);
+      // the nibble of this token in each of the 8 bytes of elements 8 lane16..
+      const uint2 b = *reinterpret_cast<const uint2*>(p.v_codes + slab * kSlab + (slot >> 2) * 256 +
+                                                      lane16 * 16 + ((slot >> 1) & 1) * 8);
+      const int sh = 4 * (slot & 1);
       w = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w |= (uint32_t)vc[(lane16 * 4 + k) * 4] << (8 * k);
+      for (int e = 0; e < 4; ++e) {
+        w |= ((b.x >> (8 * e + sh)) & 15u) << (4 * e);
+        w |= ((b.y >> (8 * e + sh)) & 15u) << (4 * (e + 4));
+      }
       sb = p.v_scales[slab * kScaleSlab + (lane16 >> 1) * kPage + slot];
       st = p.v_scale;
     }
@@ -158,15 +211,21 @@ __global__ void __launch_bounds__(256) absmax_kernel(const void* x, int64_t n, f
     m = fmaxf(m, fabsf(v));
   }
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  // non-negative floats order like their bit patterns
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  // one atomic per workgroup; non-negative floats order like their bit patterns
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+  }
 }
 
 hipError_t launch_absmax(const void* x, bool f32, int64_t n, float* out, hipStream_t s) {
   zero_float_kernel<<<1, 1, 0, s>>>(out);
   if (n > 0) {
     int64_t blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > 1024) blocks = 1024;
     if (f32) absmax_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
     else absmax_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
   }

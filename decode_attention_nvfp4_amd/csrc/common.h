@@ -123,6 +123,10 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t sb_code, 
   return w;
 }
 
+// 2^x with the hardware exponential (results below 2^-126 flush to zero,
+// which is harmless for softmax weights; exp2(-inf) = 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // bf16 bits -> float (exact)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

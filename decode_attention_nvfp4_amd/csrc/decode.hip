@@ -1,258 +1,549 @@
-// decode.hip -- decode attention over the paged NVFP4 cache, split over the
-// context, plus the log-sum-exp merge of the splits.
+// decode.hip -- decode attention over the paged NVFP4 cache.
 //
 // The cache is dequantized in registers right before the QK^T and PV
 // products ("NVIDIA解説: NVFP4 KV Cacheで長コンテキストLLM推論を最適化",
 // section 量子化・逆量子化フロー); softmax and accumulation run in FP32.
 //
-// Work decomposition: grid (split, kv head, sequence); a 256-thread
-// workgroup (4 wave64s) owns one split of one (sequence, kv head) and its
-// waves take every 4th page of the split.  Per page (16 tokens):
-//   * K: lane (t = lane%16, c = lane/16) loads 16 bytes = elements
-//     32c..32c+31 of token t (one coalesced 1 KiB wave load) and 2 block
-//     scales; the nibbles expand to halves e2m1 * s_block (exact in FP16:
-//     at most 6 significant bits, magnitudes 2^-10 .. 2688), and four
-//     16x16x32 f16 MFMAs give S^T[token][head] for the G query heads of the
-//     KV head (columns >= G are zero padding).  The contraction index order
-//     is permuted identically on the Q side, which is loaded once.
-//   * softmax: lane holds 4 tokens of one head; the page max reduces across
-//     the 4 lane rows with permlane swaps; running max / sum in FP32 (log2).
-//   * V: the cache stores V 4-token-interleaved so lane (m = lane%16, c)
-//     loads 16 bytes = bytes 4m..4m+3 of tokens 4c..4c+3; a bit-field
-//     transpose pairs the nibbles of 2 tokens per byte, which expand to the
-//     A operand of eight 16x16x16 f16 MFMAs O^T[d][head] += V^T P^T with
-//     d = 8m + tile.  P^T comes straight from the S^T accumulator layout.
-// The 4 waves merge in LDS; with one split the workgroup writes the output,
-// otherwise a normalized partial and its log2-sum-exp go to the workspace
-// and merge_kernel combines them.
+// Work decomposition (balanced stream): the work units are (sequence, KV
+// head, page) triples, ordered sequence-major, then KV head, then page.  The
+// grid is one wave64 per resident wave slot of the device; wave w takes the
+// contiguous unit range [w U / W, (w+1) U / W), so every wave streams the same
+// number of pages whatever the mix of sequence lengths (work counts that do
+// not divide the machine evenly waste it: "【CUDA 16GB向け】RTX 5090の長文推論
+// 遅延修正と…", section 利用者の報告).  A (sequence, KV head) segment that lies
+// inside one wave's range is finished by that wave; a segment cut by range
+// boundaries leaves one normalized partial per wave (at most two per wave: its
+// first and its last segment) and merge_kernel combines them with a
+// log-sum-exp merge.
+//
+// Per page (16 tokens), lane l = (col = l%16, kg = l/16):
+//   * K: 16-byte buffer load = elements 32kg..32kg+31 of token col (one
+//     coalesced 1 KiB wave load) plus 2 block scales; nibbles expand to FP16
+//     e2m1 * s_block (exact: at most 6 significant bits, magnitudes
+//     2^-10 .. 2688); four 16x16x32 f16 MFMAs give S^T[token][head] for the G
+//     query heads of the KV head (columns >= G are zero padding).  The
+//     contraction index order is permuted identically on the Q side.
+//   * softmax: lane holds 4 tokens of head col; the page max reduces across
+//     the 4 lane rows with permlane swaps; running max / sum in FP32 (log2),
+//     rescaled lazily.
+//   * V: the cache stores V with the two tokens of a pair in one byte, so
+//     lane (m = col, kg) loads 16 bytes = elements 8m..8m+7 of tokens
+//     4kg..4kg+3, which expand (one conversion per byte, then the block
+//     scale) to the A operand of eight 16x16x16 f16 MFMAs
+//     O^T[d][head] += V^T P^T with d = 8m + tile.  P^T comes straight from
+//     the S^T accumulator layout.
+// Pages stream through a 4-stage register pipeline (loads of page t+3 in
+// flight while page t is computed).
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
 namespace nvfp4 {
 
 struct PageRegs {
-  u32x4 kq;       // K codes: 32 nibbles of token lane%16
+  u32x4 kq;       // K codes: 32 nibbles of token col
   u32x4 vq;       // V codes: 4 tokens x 8 nibbles
-  uint32_t ksc;   // 2 K block scales (low 16 bits)
+  uint16_t ksc;   // 2 K block scales
   uint32_t vsc;   // 4 V block scales
 };
 
-__device__ __forceinline__ void load_page(const DecodeArgs& p, int pid, int kvh, int col, int kg,
+// Per-lane byte offsets of the four loads of a page (fixed per lane).
+struct LaneOffsets {
+  int k, ks, v, vs;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+// Buffer loads: the slab base lives in scalar registers and the lane offsets
+// are fixed, so a page load needs no vector address temporaries.
+__device__ __forceinline__ void load_page(const DecodeArgs& p, uint32_t slab, const LaneOffsets& o,
                                           PageRegs& r) {
-  const size_t slab = (size_t)pid * p.hkv + kvh;
-  r.kq = *reinterpret_cast<const u32x4*>(p.k_codes + slab * kSlab + col * 64 + kg * 16);
-  r.ksc = *reinterpret_cast<const uint16_t*>(p.k_scales + slab * kScaleSlab + col * kNBlk + kg * 2);
-  r.vq = *reinterpret_cast<const u32x4*>(p.v_codes + slab * kSlab + kg * 256 + col * 16);
-  r.vsc = *reinterpret_cast<const uint32_t*>(p.v_scales + slab * kScaleSlab + (col >> 1) * kPage + kg * 4);
+  r.kq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.k_codes + (size_t)slab * kSlab), o.k, 0, 0);
+  r.ksc = __builtin_amdgcn_raw_buffer_load_b16(page_rsrc(p.k_scales + (size_t)slab * kScaleSlab), o.ks, 0, 0);
+  r.vq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.v_codes + (size_t)slab * kSlab), o.v, 0, 0);
+  r.vsc = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(p.v_scales + (size_t)slab * kScaleSlab), o.vs, 0, 0);
+}
+
+struct WaveState {
+  floatx4 acc_o[8];   // O^T[d = 8(4kg + r) + i][head col] in acc_o[i][r]
+  float m_run;        // reference max (log2 domain) of head col
+  float l_run;        // this lane's share of the running sum
+};
+
+// Lazy rescaling: the accumulators are rescaled only when a head's max grows
+// by more than kLazy (log2 units) over the reference, so p = 2^(s - m_run)
+// stays <= 2^kLazy, well inside FP16.  The reference starts at a large
+// negative finite value so that fully masked pages give p = 0, never NaN.
+constexpr float kLazy = 8.0f;
+constexpr float kNoMax = -1.0e30f;
+
+__device__ __forceinline__ void reset_state(WaveState& st) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.acc_o[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  st.m_run = kNoMax;
+  st.l_run = 0.0f;
 }
 
 template <bool F32Q>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs p) {
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, kg = lane >> 4;
-  const int G = p.group;
-  const int L = p.seq_lens[b];
-  const int npages = (L + kPage - 1) / kPage;
-  const int pstart = split * p.pages_per_split;
-  const int pend = min(npages, pstart + p.pages_per_split);
-  const int S = p.num_splits;
-
-  if (pstart >= pend) {       // nothing of this sequence falls in the split
-    if (S > 1) {
-      for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-        const int g = idx / kD, d = idx % kD;
-        const size_t bh = (size_t)b * p.hq + kvh * G + g;
-        p.ws_o[(bh * S + split) * kD + d] = 0.0f;
-        if (d == 0) p.ws_lse[bh * S + split] = -INFINITY;
-      }
-    } else {
-      for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-        const int g = idx / kD, d = idx % kD;
-        p.out[((size_t)b * p.hq + kvh * G + g) * kD + d] = 0.0f;
-      }
-    }
-    return;
+__device__ __forceinline__ void process_page(const PageRegs& cur, int pg, int L, int kg, float qscale,
+                                             const halfx8 qh[4], const halfx8 ql[4], WaveState& st) {
+  // ---- S^T = K~ Q^T
+  const halfx2 ks = e4m3x2_to_half((uint32_t)cur.ksc, false);
+  const halfx2 sa = {ks[0], ks[0]}, sb = {ks[1], ks[1]};
+  floatx4 acc_s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = cur.kq[i];
+    const halfx2 sc = i < 2 ? sa : sb;
+    const halfx2 h0 = e2m1x2_to_half<0>(w) * sc;
+    const halfx2 h1 = e2m1x2_to_half<1>(w) * sc;
+    const halfx2 h2 = e2m1x2_to_half<2>(w) * sc;
+    const halfx2 h3 = e2m1x2_to_half<3>(w) * sc;
+    const halfx8 a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+    acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[i], acc_s, 0, 0, 0);
+    if (F32Q) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[i], acc_s, 0, 0, 0);
   }
-
-  // ---- Q (B operand of S^T = K~ Q^T): lane (head col, group kg) holds
-  // q[32kg + 8i + j] in element j of qh[i].  Scaled by 2^shift into FP16.
-  halfx8 qh[4], ql[4];
-  float qscale = 0.0f;
-  {
-    float qv[32];
-    if (col < G) {
-      const size_t qoff = ((size_t)b * p.hq + kvh * G + col) * kD + kg * 32;
-      if (F32Q) {
-        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qoff);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float4 v = src[i];
-          qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
-        }
-      } else {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint4 v = src[i];
-          qv[8 * i + 0] = bf16_lo(v.x); qv[8 * i + 1] = bf16_hi(v.x);
-          qv[8 * i + 2] = bf16_lo(v.y); qv[8 * i + 3] = bf16_hi(v.y);
-          qv[8 * i + 4] = bf16_lo(v.z); qv[8 * i + 5] = bf16_hi(v.z);
-          qv[8 * i + 6] = bf16_lo(v.w); qv[8 * i + 7] = bf16_hi(v.w);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) qv[i] = 0.0f;
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(qv[i]));
-    amax = max_across_rows(amax);
-    int shift = amax > 0.0f ? 14 - ilogbf(amax) : 0;
-    shift = max(-120, min(120, shift));
-    qscale = p.qk_scale * ldexpf(1.0f, -shift);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = ldexpf(qv[8 * i + j], shift);
-        _Float16 hv = (_Float16)v;
-        qh[i][j] = hv;
-        if (F32Q) ql[i][j] = (_Float16)(v - (float)hv);
-      }
-    }
-  }
-
-  floatx4 acc_o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc_o[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY, l_run = 0.0f;
-
-  const int32_t* pt = p.page_table + (size_t)b * p.max_pages;
-  int pg = pstart + wave;
-  PageRegs cur;
-  if (pg < pend) load_page(p, pt[pg], kvh, col, kg, cur);
-  while (pg < pend) {
-    const int pgn = pg + 4;
-    PageRegs nxt;
-    if (pgn < pend) load_page(p, pt[pgn], kvh, col, kg, nxt);
-
-    // ---- S^T = K~ Q^T
-    halfx2 ks = e4m3x2_to_half(cur.ksc, false);
-    halfx2 sa = {ks[0], ks[0]}, sb = {ks[1], ks[1]};
-    floatx4 acc_s = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w = cur.kq[i];
-      const halfx2 sc = i < 2 ? sa : sb;
-      halfx2 h0 = e2m1x2_to_half<0>(w) * sc;
-      halfx2 h1 = e2m1x2_to_half<1>(w) * sc;
-      halfx2 h2 = e2m1x2_to_half<2>(w) * sc;
-      halfx2 h3 = e2m1x2_to_half<3>(w) * sc;
-      halfx8 a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-      acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[i], acc_s, 0, 0, 0);
-      if (F32Q) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[i], acc_s, 0, 0, 0);
-    }
-
-    // ---- online softmax (log2 domain); lane holds tokens 4kg..4kg+3 of head col
+  // ---- softmax (log2 domain); lane holds tokens 4kg..4kg+3 of head col.
+  // Only a sequence's last page is partial (uniform test).  qscale > 0, so
+  // the max is taken on the raw products and scaled once.
+  if ((pg + 1) * kPage > L) {
     const int tbase = pg * kPage + kg * 4;
-    float s[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = (tbase + r < L) ? acc_s[r] * qscale : -INFINITY;
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = max_across_rows(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float pr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = exp2f(s[r] - m_new);
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc_o[i] *= alpha;
-    halfx4 bp = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
-
-    // ---- O^T += V~^T P^T
-    const halfx2 v01 = e4m3x2_to_half(cur.vsc, false);
-    const halfx2 v23 = e4m3x2_to_half(cur.vsc, true);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t W = cur.vq[k];
-      const uint32_t lo = (W & 0x000F000Fu) | ((W >> 4) & 0x00F000F0u);
-      const uint32_t hi = ((W >> 4) & 0x000F000Fu) | ((W >> 8) & 0x00F000F0u);
-      halfx2 a0 = e2m1x2_to_half<0>(lo) * v01, a1 = e2m1x2_to_half<2>(lo) * v23;
-      halfx2 b0 = e2m1x2_to_half<0>(hi) * v01, b1 = e2m1x2_to_half<2>(hi) * v23;
-      halfx4 alo = {a0[0], a0[1], a1[0], a1[1]};
-      halfx4 ahi = {b0[0], b0[1], b1[0], b1[1]};
-      acc_o[2 * k] = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bp, acc_o[2 * k], 0, 0, 0);
-      acc_o[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bp, acc_o[2 * k + 1], 0, 0, 0);
-    }
-    cur = nxt;
-    pg = pgn;
+    for (int r = 0; r < 4; ++r) acc_s[r] = (tbase + r < L) ? acc_s[r] : -INFINITY;
   }
-
-  // ---- merge the 4 waves in LDS
-  __shared__ float sm_o[4][16][kD];
-  __shared__ float sm_m[4][16], sm_l[4][16];
-  const float l_tot = sum_across_rows(l_run);
-  if (col < G) {
-    if (kg == 0) { sm_m[wave][col] = m_run; sm_l[wave][col] = l_tot; }
+  float mx = fmaxf(fmaxf(acc_s[0], acc_s[1]), fmaxf(acc_s[2], acc_s[3]));
+  mx = max_across_rows(mx) * qscale;
+  const bool grow = mx > st.m_run + kLazy;
+  if (__any(grow)) {
+    const float m_new = grow ? mx : st.m_run;
+    const float alpha = fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm_o[wave][col][8 * (4 * kg + r) + i] = acc_o[i][r];
+    for (int i = 0; i < 8; ++i) st.acc_o[i] *= alpha;
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kD; idx += 256) {
-    const int g = idx / kD, d = idx % kD;
-    float M = -INFINITY;
+  float pr[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][g]);
-    float o = 0.0f, l = 0.0f;
-    if (M > -INFINITY) {
+  for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(acc_s[r], qscale, -st.m_run));
+  st.l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  const halfx4 bp = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+  // ---- O^T += V~^T P^T.  Byte e of word j / 2 (j = token pair) holds
+  // element d = 8 col + e of tokens (4kg + 2j, 4kg + 2j + 1): one conversion
+  // gives the two tokens of a pair, the A operand's k order.
+  const halfx2 v01 = e4m3x2_to_half(cur.vsc, false);
+  const halfx2 v23 = e4m3x2_to_half(cur.vsc, true);
+  auto tile = [&](halfx2 a0, halfx2 a1, floatx4& acc) {
+    a0 *= v01;
+    a1 *= v23;
+    const halfx4 a = {a0[0], a0[1], a1[0], a1[1]};
+    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bp, acc, 0, 0, 0);
+  };
+  tile(e2m1x2_to_half<0>(cur.vq[0]), e2m1x2_to_half<0>(cur.vq[2]), st.acc_o[0]);
+  tile(e2m1x2_to_half<1>(cur.vq[0]), e2m1x2_to_half<1>(cur.vq[2]), st.acc_o[1]);
+  tile(e2m1x2_to_half<2>(cur.vq[0]), e2m1x2_to_half<2>(cur.vq[2]), st.acc_o[2]);
+  tile(e2m1x2_to_half<3>(cur.vq[0]), e2m1x2_to_half<3>(cur.vq[2]), st.acc_o[3]);
+  tile(e2m1x2_to_half<0>(cur.vq[1]), e2m1x2_to_half<0>(cur.vq[3]), st.acc_o[4]);
+  tile(e2m1x2_to_half<1>(cur.vq[1]), e2m1x2_to_half<1>(cur.vq[3]), st.acc_o[5]);
+  tile(e2m1x2_to_half<2>(cur.vq[1]), e2m1x2_to_half<2>(cur.vq[3]), st.acc_o[6]);
+  tile(e2m1x2_to_half<3>(cur.vq[1]), e2m1x2_to_half<3>(cur.vq[3]), st.acc_o[7]);
+}
+
+// Q of (sequence b, KV head kvh) as the B operand of S^T = K~ Q^T: lane
+// (head col, group kg) holds q[32kg + 8i + j] in element j of qh[i], scaled by
+// 2^shift into FP16 (the max |q| of the head lands in [2^14, 2^15)).
+template <bool F32Q>
+__device__ __forceinline__ void load_q(const DecodeArgs& p, int b, int kvh, int col, int kg,
+                                       halfx8 qh[4], halfx8 ql[4], float& qscale) {
+  float qv[32];
+  if (col < p.group) {
+    const size_t qoff = ((size_t)b * p.hq + kvh * p.group + col) * kD + kg * 32;
+    if (F32Q) {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qoff);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float c = exp2f(sm_m[w][g] - M);
-        o += c * sm_o[w][g][d];
-        l += c * sm_l[w][g];
+      for (int i = 0; i < 8; ++i) {
+        const float4 v = src[i];
+        qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
+      }
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = src[i];
+        qv[8 * i + 0] = bf16_lo(v.x); qv[8 * i + 1] = bf16_hi(v.x);
+        qv[8 * i + 2] = bf16_lo(v.y); qv[8 * i + 3] = bf16_hi(v.y);
+        qv[8 * i + 4] = bf16_lo(v.z); qv[8 * i + 5] = bf16_hi(v.z);
+        qv[8 * i + 6] = bf16_lo(v.w); qv[8 * i + 7] = bf16_hi(v.w);
       }
     }
-    const size_t bh = (size_t)b * p.hq + kvh * G + g;
-    if (S == 1) {
-      p.out[bh * kD + d] = l > 0.0f ? o / l * p.v_scale : 0.0f;
-    } else {
-      p.ws_o[(bh * S + split) * kD + d] = l > 0.0f ? o / l : 0.0f;
-      if (d == 0) p.ws_lse[bh * S + split] = l > 0.0f ? M + log2f(l) : -INFINITY;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) qv[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(qv[i]));
+  amax = max_across_rows(amax);
+  int shift = amax > 0.0f ? 14 - ilogbf(amax) : 0;
+  shift = max(-120, min(120, shift));
+  qscale = p.qk_scale * ldexpf(1.0f, -shift);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = ldexpf(qv[8 * i + j], shift);
+      const _Float16 hv = (_Float16)v;
+      qh[i][j] = hv;
+      ql[i][j] = F32Q ? (_Float16)(v - (float)hv) : (_Float16)0.0f;
     }
   }
 }
 
-// One workgroup per (sequence, query head); thread d combines the splits:
-// o = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), times s_tV.
-__global__ void __launch_bounds__(128) merge_kernel(DecodeArgs p) {
-  const size_t bh = blockIdx.x;
-  const int d = threadIdx.x;
-  const int S = p.num_splits;
-  const float* lse = p.ws_lse + bh * S;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lse[s]);
-  float num = 0.0f, den = 0.0f;
-  if (M > -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float w = exp2f(lse[s] - M);
-      num += w * p.ws_o[(bh * S + s) * kD + d];
-      den += w;
+// Write the state of (b, kvh): the final output when the piece is the whole
+// segment, else a normalized partial (o / l, log2-sum-exp) in workspace slot
+// (wave, slot).
+__device__ __forceinline__ void flush(const DecodeArgs& p, const WaveState& st, int b, int kvh,
+                                      int col, int kg, bool complete, int wave, int slot) {
+  const float l_tot = sum_across_rows(st.l_run);
+  if (col >= p.group) return;
+  float* dst;
+  float f;
+  if (complete) {
+    dst = p.out + ((size_t)b * p.hq + kvh * p.group + col) * kD;
+    f = l_tot > 0.0f ? p.v_scale / l_tot : 0.0f;
+  } else {
+    const size_t piece = ((size_t)wave * 2 + slot) * p.group + col;
+    dst = p.ws_o + piece * kD;
+    f = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (kg == 0) p.ws_lse[piece] = l_tot > 0.0f ? st.m_run + log2f(l_tot) : -INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[8 * (4 * kg + r) + i] = st.acc_o[i][r] * f;
+}
+
+__device__ __forceinline__ int pages_of(int len) { return (len + kPage - 1) / kPage; }
+
+// Sequence length clamped to what its page-table row can hold, so that a
+// length outside the documented range never reads past the row.
+__device__ __forceinline__ int seq_len(const DecodeArgs& p, int b) {
+  return min(max(p.seq_lens[b], 0), p.max_pages * kPage);
+}
+
+// Inclusive prefix sum across the wave.
+__device__ __forceinline__ int wave_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+// Sequence lengths of 64 consecutive sequences base .. base + 63, one per
+// lane (0 past the batch), so that walking to the next sequence is a
+// readlane rather than a memory round trip.
+struct LenWindow {
+  int base;
+  int len;
+};
+
+__device__ __forceinline__ int window_len(const DecodeArgs& p, LenWindow& w, int b, int lane) {
+  if (b - w.base >= 64) {                  // rare: move the window forward
+    w.base = b;
+    w.len = b + lane < p.batch ? seq_len(p, b + lane) : 0;
+  }
+  return __builtin_amdgcn_readlane(w.len, b - w.base);
+}
+
+// Position in the (sequence, KV head, page) order: the segment (b, kvh) of a
+// sequence of length L with np pages, and page pg inside it.  All fields are
+// wave-uniform.
+struct SegPos {
+  int b, kvh, L, np, pg;
+};
+
+// Move to the first page of the next non-empty segment.  The caller knows
+// that one exists (a unit of the wave's range lies beyond).
+__device__ __forceinline__ void next_segment(const DecodeArgs& p, SegPos& s, LenWindow& w, int lane) {
+  s.pg = 0;
+  if (++s.kvh == p.hkv) {
+    s.kvh = 0;
+    do {
+      ++s.b;
+      s.L = window_len(p, w, s.b, lane);
+      s.np = pages_of(s.L);
+    } while (s.np == 0);
+  }
+}
+
+// Slab ids (page * Hkv + head) of the next n = min(64, left) units of the
+// stream, lane j holding unit j; `w` advances past them.  Lanes j >= n are
+// left at 0 and never read.  The page-table loads are not waited for here:
+// their results are read a whole block later.
+__device__ __forceinline__ uint32_t prepare_block(const DecodeArgs& p, SegPos& w, LenWindow& win, int left,
+                                                  int lane) {
+  const int n = min(64, left);
+  int off = w.pg + lane;
+  SegPos s = w;
+  LenWindow sw = win;
+  uint32_t slab = 0;
+  bool need = lane < n;
+  while (true) {
+    const bool here = need && off < s.np;
+    if (here) slab = (uint32_t)p.page_table[(size_t)s.b * p.max_pages + off] * (uint32_t)p.hkv + (uint32_t)s.kvh;
+    need = need && !here;
+    if (!__any(need)) break;
+    off -= s.np;
+    next_segment(p, s, sw, lane);
+  }
+  // the walker moves to unit n (only needed while units remain)
+  w.pg += n;
+  if (left > n) {
+    while (w.pg >= w.np) {
+      const int rest = w.pg - w.np;
+      next_segment(p, w, win, lane);
+      w.pg = rest;
     }
   }
-  p.out[bh * kD + d] = den > 0.0f ? num / den * p.v_scale : 0.0f;
+  return slab;
+}
+
+template <bool F32Q>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecodeArgs p) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15, kg = lane >> 4;
+  const int wave = blockIdx.x, W = gridDim.x;
+  const int Hkv = p.hkv, B = p.batch;
+
+  // ---- total work U = Hkv * sum_b pages(b), and (wave 0) the page prefix
+  // sums for merge_kernel
+  int total_pages = 0;
+  for (int c = 0; c < B; c += 64) {
+    const int b = c + lane;
+    const int np = b < B ? pages_of(seq_len(p, b)) : 0;
+    const int incl = wave_scan(np, lane);
+    if (wave == 0 && b < B) p.ws_prefix[b] = total_pages + incl - np;
+    total_pages += __builtin_amdgcn_readlane(incl, 63);
+  }
+  if (wave == 0 && lane == 0) p.ws_prefix[B] = total_pages;
+  const long long U = (long long)total_pages * Hkv;
+  const long long u0 = (long long)wave * U / W, u1 = (long long)(wave + 1) * U / W;
+  if (u0 >= u1) return;
+  const int N = (int)(u1 - u0);            // units of this wave
+
+  // ---- the segment holding u0: sequence b0 (first sequence whose prefix
+  // passes u0), KV head and page inside it
+  int b0 = 0;
+  long long a_b0 = 0;
+  LenWindow win0 = {0, 0};
+  {
+    int carry = 0;
+    for (int c = 0; c < B; c += 64) {
+      const int b = c + lane;
+      const int len = b < B ? seq_len(p, b) : 0;
+      const int np = pages_of(len);
+      const int incl = wave_scan(np, lane);
+      const unsigned long long hit = __ballot(b < B && (long long)(carry + incl) * Hkv > u0);
+      if (hit) {
+        const int idx = __ffsll((long long)hit) - 1;
+        b0 = c + idx;
+        a_b0 = (long long)(carry + __builtin_amdgcn_readlane(incl - np, idx)) * Hkv;
+        win0.base = c;
+        win0.len = len;
+        break;
+      }
+      carry += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  win0.base = __builtin_amdgcn_readfirstlane(win0.base);
+  SegPos start;
+  start.b = __builtin_amdgcn_readfirstlane(b0);
+  start.L = __builtin_amdgcn_readlane(win0.len, start.b - win0.base);
+  start.np = pages_of(start.L);
+  {
+    const long long off0 = u0 - a_b0;
+    start.kvh = (int)(off0 / start.np);
+    start.pg = (int)(off0 % start.np);
+  }
+
+  // ---- issue side: the wave's units form one stream of pages; the slab ids
+  // of the current 64-unit block (cur, units base..) and of the next one
+  // (nxt) sit one per lane
+  SegPos walker = start;
+  LenWindow wwin = win0;
+  int prepared = 0, base = 0;
+  uint32_t cur = prepare_block(p, walker, wwin, N, lane);
+  prepared = min(64, N);
+  uint32_t nxt = cur;
+  if (prepared < N) {
+    nxt = prepare_block(p, walker, wwin, N - prepared, lane);
+    prepared += min(64, N - prepared);
+  }
+  const LaneOffsets lo = {col * 64 + kg * 16, col * kNBlk + kg * 2, kg * 256 + col * 16,
+                           (col >> 1) * kPage + kg * 4};
+  // units past the end reload the last one (never consumed)
+  auto issue = [&](PageRegs& r, int x) {
+    const int o = min(x, N - 1) - base;
+    const uint32_t slab = o < 64 ? __builtin_amdgcn_readlane(cur, o) : __builtin_amdgcn_readlane(nxt, o - 64);
+    load_page(p, slab, lo, r);
+  };
+
+  // ---- process side: one piece (the wave's part of one segment) at a time
+  SegPos seg = start;
+  LenWindow pwin = win0;
+  int piece_left = 0;                      // pages of the current piece still to process
+  bool whole = false, first_piece = true, started = false;
+  int done = 0;                            // units processed
+  halfx8 qh[4], ql[4];
+  float qscale = 0.0f;
+  WaveState st;
+  auto step = [&](const PageRegs& r) {
+    if (piece_left == 0) {                 // a new piece starts with this page
+      if (started) next_segment(p, seg, pwin, lane);
+      started = true;
+      piece_left = min(seg.np - seg.pg, N - done);
+      whole = seg.pg == 0 && piece_left == seg.np;
+      load_q<F32Q>(p, seg.b, seg.kvh, col, kg, qh, ql, qscale);
+      reset_state(st);
+    }
+    process_page<F32Q>(r, seg.pg, seg.L, kg, qscale, qh, ql, st);
+    ++seg.pg;
+    ++done;
+    if (--piece_left == 0) {
+      flush(p, st, seg.b, seg.kvh, col, kg, whole, wave, first_piece ? 0 : 1);
+      first_piece = false;
+    }
+  };
+
+  PageRegs r0, r1, r2, r3;
+  issue(r0, 0);
+  issue(r1, 1);
+  issue(r2, 2);
+  for (int t = 0; t < N; t += 4) {
+    if (t == base + 64) {                  // the next block becomes current
+      cur = nxt;
+      base += 64;
+      if (prepared < N) {
+        nxt = prepare_block(p, walker, wwin, N - prepared, lane);
+        prepared += min(64, N - prepared);
+      }
+    }
+    issue(r3, t + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    step(r0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 >= N) break;
+    issue(r0, t + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    step(r1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 2 >= N) break;
+    issue(r1, t + 5);
+    __builtin_amdgcn_sched_barrier(0);
+    step(r2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 3 >= N) break;
+    issue(r2, t + 6);
+    __builtin_amdgcn_sched_barrier(0);
+    step(r3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One workgroup (four waves) per (sequence, KV head) segment.  A segment cut
+// by wave ranges is combined from its pieces, per query head:
+//   o = sum_w 2^(lse_w - M) o_w / sum_w 2^(lse_w - M), times s_tV.
+// Wave w's range starts at start(w) = w U / W; unit u belongs to wave
+// floor(((u + 1) W - 1) / U); the piece of wave w sits in slot 0 when w's range
+// starts inside the segment, else in slot 1.  Waves between the first and the
+// last owner with an empty range (W > U) wrote nothing and are skipped.
+// Wave i of the workgroup merges heads i, i + 4, ...; lane l owns output
+// elements 2l, 2l + 1, and the partial loads of all pieces are independent.
+__global__ void __launch_bounds__(256) merge_kernel(DecodeArgs p) {
+  const int b = blockIdx.x / p.hkv, kvh = blockIdx.x % p.hkv;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int W = p.num_splits, G = p.group;
+  const int pb = p.ws_prefix[b], np = p.ws_prefix[b + 1] - pb;
+  const long long U = (long long)p.ws_prefix[p.batch] * p.hkv;
+  float* out = p.out + ((size_t)b * p.hq + (size_t)kvh * G) * kD;
+  if (np == 0) {
+    for (int i = threadIdx.x; i < G * kD; i += 256) out[i] = 0.0f;
+    return;
+  }
+  const long long a = (long long)pb * p.hkv + (long long)kvh * np;
+  const long long e = a + np;
+  const int w0 = (int)(((a + 1) * W - 1) / U);
+  const int w1 = (int)((e * W - 1) / U);
+  if (w0 == w1) return;                       // finished by one wave
+  const int n = w1 - w0 + 1;
+  auto start = [&](int w) { return (long long)w * U / W; };
+  for (int g = wid; g < G; g += 4) {
+    // pass 1: the largest log-sum-exp of the head's pieces
+    float M = -INFINITY;
+    for (int i = lane; i < n; i += 64) {
+      const int w = w0 + i;
+      if (start(w) < start(w + 1)) {
+        const int slot = start(w) >= a ? 0 : 1;
+        M = fmaxf(M, p.ws_lse[((size_t)w * 2 + slot) * G + g]);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    // pass 2: weights per piece (lane = piece within a chunk of 64), then
+    // the weighted sum of the partial outputs
+    float2 acc = {0.0f, 0.0f};
+    float den = 0.0f;
+    if (M > -INFINITY) {
+      for (int c = 0; c < n; c += 64) {
+        const int w = w0 + c + lane;
+        float cf = 0.0f;
+        int piece = 0;
+        if (c + lane < n && start(w) < start(w + 1)) {
+          const int slot = start(w) >= a ? 0 : 1;
+          piece = (w * 2 + slot) * G + g;
+          cf = exp2f(p.ws_lse[piece] - M);
+        }
+        den += cf;
+        const int cnt = min(64, n - c);
+#pragma unroll 8
+        for (int k = 0; k < cnt; ++k) {
+          const float ck = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cf), k));
+          const int pk = __builtin_amdgcn_readlane(piece, k);
+          const float2 v = *reinterpret_cast<const float2*>(p.ws_o + (size_t)pk * kD + 2 * lane);
+          // a skipped piece has weight 0 and its (stale) slot is not used
+          acc.x = ck != 0.0f ? fmaf(ck, v.x, acc.x) : acc.x;
+          acc.y = ck != 0.0f ? fmaf(ck, v.y, acc.y) : acc.y;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+    }
+    const float f = den > 0.0f ? p.v_scale / den : 0.0f;
+    *reinterpret_cast<float2*>(out + (size_t)g * kD + 2 * lane) = make_float2(acc.x * f, acc.y * f);
+  }
+}
+
+// Resident decode waves per CU, queried once per process (every device here
+// is gfx950, so the answer does not depend on the device).
+int decode_occupancy(bool f32_q) {
+  static std::atomic<int> cached[2] = {0, 0};
+  int n = cached[f32_q].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  hipError_t e = f32_q ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<true>, 64, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<false>, 64, 0);
+  if (e != hipSuccess || n <= 0) return 8;
+  cached[f32_q].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool f32_q, hipStream_t s) {
-  dim3 grid(a.num_splits, a.hkv, a.batch);
-  if (f32_q) decode_kernel<true><<<grid, 256, 0, s>>>(a);
-  else decode_kernel<false><<<grid, 256, 0, s>>>(a);
-  if (a.num_splits > 1) merge_kernel<<<(unsigned)(a.batch * a.hq), 128, 0, s>>>(a);
+  if (f32_q) decode_kernel<true><<<a.num_splits, 64, 0, s>>>(a);
+  else decode_kernel<false><<<a.num_splits, 64, 0, s>>>(a);
+  merge_kernel<<<(unsigned)(a.batch * a.hkv), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

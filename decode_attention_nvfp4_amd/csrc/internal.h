@@ -50,14 +50,14 @@ struct DecodeArgs {
   const int32_t* page_table;  // [B][max_pages]
   const int32_t* seq_lens;    // [B]
   float* out;                 // [B][Hq][128]
-  float* ws_o;                // [B][Hq][S][128]   (S > 1)
-  float* ws_lse;              // [B][Hq][S]        (S > 1)
+  float* ws_o;                // partials [W][2][G][128]
+  float* ws_lse;              // partial log2-sum-exp [W][2][G]
+  int32_t* ws_prefix;         // [B+1] exclusive prefix of pages per sequence
   float qk_scale;             // s_tK * softmax_scale * log2(e)
   float v_scale;              // s_tV
   int32_t max_pages;
   int32_t batch, hq, hkv, group;
-  int32_t num_splits;
-  int32_t pages_per_split;
+  int32_t num_splits;         // W: number of waves (work ranges)
 };
 
 struct PrefillArgs {
@@ -83,6 +83,7 @@ hipError_t launch_append(const AppendArgs& a, bool f32_in, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, bool f32_out, hipStream_t s);
 hipError_t launch_absmax(const void* x, bool f32_in, int64_t n, float* out, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, bool f32_q, hipStream_t s);
+int decode_occupancy(bool f32_q);   // resident decode waves per CU
 hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s);
 
 }  // namespace nvfp4

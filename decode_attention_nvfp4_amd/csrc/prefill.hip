@@ -117,34 +117,33 @@ __global__ void __launch_bounds__(256) expand_kernel(PrefillArgs p) {
 #pragma unroll
     for (int i = 0; i < 2 * P::EB; ++i) dst[i] = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
   }
-  // V: dword (token group tg, byte b) holds byte b of 4 consecutive tokens
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int idx = tid + 256 * r;
-    const int tg = idx >> 6, b = idx & 63;
-    const int t0 = tile * kTile + 4 * tg;
-    uint32_t W = 0, sc4 = 0;
+  // V: thread -> token quad tq (keys 4tq..4tq+3 of the tile) x element group
+  // m (elements 8m..8m+7): 16 bytes, byte 8j + e = element 8m + e of the
+  // token pair (4tq + 2j, 4tq + 2j + 1)
+  {
+    const int tq = tid >> 4, m = tid & 15;
+    const int t0 = tile * kTile + 4 * tq;
+    u32x4 W = {0u, 0u, 0u, 0u};
+    uint32_t sc4 = 0;
     if (t0 < p.total) {
       const int page = p.page_table_row[t0 / kPage], slot0 = t0 % kPage;
       const size_t slab = (size_t)page * p.hkv + kvh;
-      W = *reinterpret_cast<const uint32_t*>(p.v_codes + slab * kSlab + (slot0 >> 2) * 256 + b * 4);
-      sc4 = *reinterpret_cast<const uint32_t*>(p.v_scales + slab * kScaleSlab + (b >> 3) * kPage + slot0);
+      W = *reinterpret_cast<const u32x4*>(p.v_codes + slab * kSlab + (slot0 >> 2) * 256 + m * 16);
+      sc4 = *reinterpret_cast<const uint32_t*>(p.v_scales + slab * kScaleSlab + (m >> 1) * kPage + slot0);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = 4 * tg + j;
+    for (int j = 0; j < 4; ++j) {               // token 4tq + j
+      const int kk = 4 * tq + j;
       const bool live = t0 + j < p.total;
       const float sc = e4m3_to_float((sc4 >> (8 * j)) & 0xFFu) * P::kExpand;
-      const uint32_t byte = (W >> (8 * j)) & 0xFFu;
       const int pos = vt_pos<MODE>(kk);
-      const uint32_t lo = live ? encode<MODE>(e2m1_value(byte & 15u) * sc) : 0u;
-      const uint32_t hi = live ? encode<MODE>(e2m1_value(byte >> 4) * sc) : 0u;
-      if (P::EB == 1) {
-        vt[(2 * b) * kTile + pos] = (uint8_t)lo;
-        vt[(2 * b + 1) * kTile + pos] = (uint8_t)hi;
-      } else {
-        reinterpret_cast<uint16_t*>(vt)[(2 * b) * kTile + pos] = (uint16_t)lo;
-        reinterpret_cast<uint16_t*>(vt)[(2 * b + 1) * kTile + pos] = (uint16_t)hi;
+      const int sh = 4 * (j & 1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {             // element 8m + e
+        const uint32_t c = (W[(j >> 1) * 2 + (e >> 2)] >> (8 * (e & 3) + sh)) & 15u;
+        const uint32_t v = live ? encode<MODE>(e2m1_value(c) * sc) : 0u;
+        if (P::EB == 1) vt[(8 * m + e) * kTile + pos] = (uint8_t)v;
+        else reinterpret_cast<uint16_t*>(vt)[(8 * m + e) * kTile + pos] = (uint16_t)v;
       }
     }
   }

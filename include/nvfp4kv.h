@@ -37,8 +37,10 @@
  *            element 2j in its low nibble and element 2j+1 in its high nibble.
  *   k_scales slab  128 B: [token 16][block 8]; block j covers elements
  *            16j..16j+15.
- *   v_codes  slab 1024 B: [token group 4][byte 64][token 4]; byte j of token
- *            t (same nibble packing as K) sits at (t/4)*256 + j*4 + t%4.
+ *   v_codes  slab 1024 B: [token quad 4][element group 16][token pair 2]
+ *            [element 8]; the byte at (t/4)*256 + (d/8)*16 + ((t/2)%2)*8 + d%8
+ *            holds element d of the token pair (t & ~1, t | 1): the even
+ *            token in the low nibble, the odd token in the high nibble.
  *   v_scales slab  128 B: [block 8][token 16].
  *
  * Bytes per element: 0.5 (code) + 1/16 (scale) = 0.5625, i.e. 3.56x fewer
@@ -132,9 +134,10 @@ int32_t nvfp4_abs_max(const void* x, int32_t dtype, int64_t n, float* amax_out, 
  *                  page_table[seq * max_pages_per_seq + pos / 16] must be a
  *                  valid page (< num_pages), slot pos % 16
  *   page_table   : device int32 [rows][max_pages_per_seq]
- * Writes the 64 code bytes and 8 scale bytes of each (token, head) row of K
- * and of V; nothing else in the cache changes.  Two rows of one call must
- * not target the same (page, slot).  n_tok == 0 is a no-op. */
+ * Writes the 128 codes and 8 block scales of each (token, head) row of K and
+ * of V; nothing else in the cache changes (the V codes of the other token of
+ * a pair, which share bytes with this token's, are kept).  Two rows of one
+ * call must not target the same (page, slot).  n_tok == 0 is a no-op. */
 int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
                         int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
                         const int32_t* tok_pos, const int32_t* page_table,
@@ -150,13 +153,16 @@ int32_t nvfp4_kv_dequant(const nvfp4_kv_cache* cache, const int32_t* page_table_
                          int32_t pos0, int32_t n, void* k_out, void* v_out,
                          int32_t out_dtype, void* stream);
 
-/* Number of context splits the decode planner uses (num_splits 0 = auto),
- * on the current device. */
+/* Number of work ranges (waves) the decode planner uses on the current
+ * device: num_splits when > 0, else the smaller of the device's resident
+ * decode wave slots and ceil(batch * num_kv_heads * ceil(max_seq_len/16) / 16)
+ * (at least 16 pages per wave), and at least 1.  0 for invalid arguments. */
 int32_t nvfp4_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
                                 int32_t num_splits);
 
 /* Workspace bytes nvfp4_decode_attn needs for these arguments on the
- * current device (0 if the plan uses a single split). */
+ * current device (partial results of the work ranges; 0 for invalid
+ * arguments). */
 size_t nvfp4_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t max_seq_len, int32_t num_splits);
 
@@ -172,9 +178,11 @@ size_t nvfp4_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
  *                ceil(seq_lens[b]/16) <= max_pages_per_seq
  *   max_seq_len: host bound on seq_lens, used by the split planner
  *   softmax_scale: > 0 and finite (1/sqrt(128) is the usual value)
- *   num_splits : 0 = automatic, else the number of context splits
- *   workspace  : device, >= nvfp4_decode_workspace_bytes(...) bytes (may be
- *                NULL when that is 0)
+ *   num_splits : 0 = automatic, else the number of work ranges: the
+ *                (sequence, KV head, page) work is cut into that many equal
+ *                contiguous ranges, one per wave
+ *   workspace  : device, >= nvfp4_decode_workspace_bytes(...) bytes,
+ *                256-byte aligned
  *   out        : device FP32 [batch][num_q_heads][128]
  * A sequence of length 0 yields zeros.  Results do not depend on the run:
  * no atomics, fixed reduction order. */

@@ -50,6 +50,24 @@ def compare(got: np.ndarray, ref: np.ndarray, tol: float = TOL):
     return ratio <= tol and np.all(np.isfinite(got)), stats
 
 
+# The decode path multiplies exact 16-bit operands; its only rounding of note
+# is P to FP16 (relative 2^-11 per weight), which moves an output by at most
+# 2^-11 * A with A = sum_t w_t |v_t|.  The check allows twice that, plus FP32
+# accumulation noise.
+DECODE_P_BOUND = 2.0 ** -10
+
+
+def check_decode(out, ref, mag, factor=1.0):
+    """The 2e-2 gate plus the decode path's derived bound; returns stats."""
+    ok, st = compare(out, ref)
+    err = np.abs(np.asarray(out, np.float64) - ref)
+    bound = 1e-5 * np.maximum(1.0, np.abs(ref)) + factor * DECODE_P_BOUND * mag
+    st["worst_err_over_bound"] = float((err / bound).max()) if err.size else 0.0
+    assert ok, st
+    assert np.all(err <= bound), st
+    return st
+
+
 def calibrate(w: W.DecodeWorkload, oracle, data=None):
     """(s_tK, s_tV) over the whole K and V tensors of a workload, including
     the tokens its decode steps append, with the oracle's definition."""
@@ -117,10 +135,15 @@ class BuiltDecode:
         return api.decode(self.cache, qd, self.pt, i32(self.lens), int(self.lens.max()),
                           num_splits=num_splits)
 
-    def oracle_decode(self, oracle, q: np.ndarray, seqs):
+    def oracle_decode(self, oracle, q: np.ndarray, seqs, scale=None):
+        """(reference, magnitude): the oracle's output, and the same attention
+        over |v| (codes with the sign bit cleared), i.e. A = sum_t w_t |v_t|."""
         seqs = list(seqs)
-        out = oracle.decode_batch(q[seqs], [self.codes[b] for b in seqs], self.w.Hkv, self.s_tk, self.s_tv)
-        return out
+        codes = [self.codes[b] for b in seqs]
+        ref = oracle.decode_batch(q[seqs], codes, self.w.Hkv, self.s_tk, self.s_tv, scale=scale)
+        mag = oracle.decode_batch(q[seqs], [(c[0], c[1], c[2] & 7, c[3]) for c in codes], self.w.Hkv,
+                                  self.s_tk, self.s_tv, scale=scale)
+        return ref, mag
 
     def check_codes(self, seqs):
         """Bit-exact comparison of the device planes with the oracle's codes."""

@@ -21,8 +21,14 @@ class Planes:
     def __init__(self, k_codes, k_scales, v_codes, v_scales, num_pages, hkv):
         self.kc = np.asarray(k_codes).reshape(num_pages, hkv, PAGE, 64)
         self.ks = np.asarray(k_scales).reshape(num_pages, hkv, PAGE, NBLK)
-        # v codes: [page][head][group 4][byte 64][token 4]
-        self.vc = np.asarray(v_codes).reshape(num_pages, hkv, 4, 64, 4)
+        # v codes: [page][head][token quad 4][element group 16][token pair 2]
+        # [element 8]; each byte holds the even token of its pair in the low
+        # nibble and the odd token in the high nibble.  self.vc is the
+        # logical code array [page][head][token 16][element 128].
+        vb = np.asarray(v_codes).reshape(num_pages, hkv, 4, 16, 2, 8)
+        nib = np.stack([vb & 0xF, vb >> 4], axis=-1)        # [..][quad][group][pair][e][nibble]
+        nib = nib.transpose(0, 1, 2, 4, 6, 3, 5)             # [..][quad][pair][nibble][group][e]
+        self.vc = np.ascontiguousarray(nib).reshape(num_pages, hkv, PAGE, D)
         # v scales: [page][head][block 8][token 16]
         self.vs = np.asarray(v_scales).reshape(num_pages, hkv, NBLK, PAGE)
 
@@ -31,7 +37,7 @@ class Planes:
         return unpack_nibbles(self.kc[page, :, slot]), self.ks[page, :, slot]
 
     def v_row(self, page, slot):
-        return unpack_nibbles(self.vc[page, :, slot // 4, :, slot % 4]), self.vs[page, :, :, slot]
+        return self.vc[page, :, slot], self.vs[page, :, :, slot]
 
     def gather(self, pages, slots):
         """Logical (kcodes, kscales, vcodes, vscales) for token lists, each
@@ -40,25 +46,34 @@ class Planes:
         slots = np.asarray(slots)
         kc = unpack_nibbles(self.kc[pages, :, slots])
         ks = self.ks[pages, :, slots]
-        vb = self.vc[pages, :, slots // 4, :, slots % 4]       # [n][Hkv][64]
-        vc = unpack_nibbles(vb)
+        vc = self.vc[pages, :, slots]                          # [n][Hkv][128]
         vs = self.vs[pages, :, :, slots]                        # [n][Hkv][8]
         return kc, ks, vc, vs
 
     def touched_mask(self, pages, slots):
-        """Boolean masks over the four planes marking the bytes that the rows
-        (page, slot) own; everything else must keep its fill value."""
+        """Boolean masks over the four planes (V codes as the logical nibble
+        array) marking what the rows (page, slot) own; everything else must
+        keep its fill value (see untouched_fill)."""
         m = [np.zeros(self.kc.shape, bool), np.zeros(self.ks.shape, bool),
              np.zeros(self.vc.shape, bool), np.zeros(self.vs.shape, bool)]
         for p, s in zip(np.asarray(pages), np.asarray(slots)):
             m[0][p, :, s] = True
             m[1][p, :, s] = True
-            m[2][p, :, s // 4, :, s % 4] = True
+            m[2][p, :, s] = True
             m[3][p, :, :, s] = True
         return m
 
     def arrays(self):
         return self.kc, self.ks, self.vc, self.vs
+
+    def untouched_fill(self, fill: int):
+        """Per-plane arrays of what a byte fill value reads as: the byte for
+        three planes, its low (even token) or high (odd token) nibble for the
+        V codes."""
+        tok = np.arange(PAGE)[None, None, :, None]
+        vfill = np.where(tok % 2 == 0, fill & 0xF, fill >> 4) + np.zeros(self.vc.shape, np.uint8)
+        return (np.full(self.kc.shape, fill, np.uint8), np.full(self.ks.shape, fill, np.uint8),
+                vfill.astype(np.uint8), np.full(self.vs.shape, fill, np.uint8))
 
 
 def sequence_tokens(page_table_row, L):

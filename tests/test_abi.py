@@ -142,20 +142,26 @@ def test_prefill_rejects_bad_arguments(api):
 
 
 def test_split_planner_and_workspace(api):
+    """The decode work plan: W waves share the (sequence, KV head, page) work
+    in equal contiguous ranges.  A requested W is used as given; 0 asks for
+    one wave per resident wave slot of the device."""
     for B, Hkv, L in ((1, 1, 1024), (8, 8, 4097), (1, 8, 65536), (128, 8, 8192), (3, 2, 0), (4, 4, 17)):
-        S = api.decode_num_splits(B, Hkv, L, 0)
-        assert S >= 1
-        max_pages = max(1, -(-L // 16))
-        assert S <= max_pages
+        auto = api.decode_num_splits(B, Hkv, L, 0)
+        units = B * Hkv * -(-L // 16)
+        # at least 16 pages per wave, at most the device's wave slots
+        assert auto == max(1, min(auto, -(-units // 16)))
+        assert auto >= min(256, -(-units // 16))
         for req in (1, 2, 7, 64):
-            s = api.decode_num_splits(B, Hkv, L, req)
-            assert 1 <= s <= max(req, 1)
-        ws = api.decode_workspace_bytes(B, 4 * Hkv, Hkv, L, 0)
-        assert (ws == 0) == (S == 1)
-        if S > 1:
-            assert ws >= B * 4 * Hkv * S * 129 * 4
-    # long single sequences split across the machine
-    assert api.decode_num_splits(1, 8, 65536, 0) >= 64
+            assert api.decode_num_splits(B, Hkv, L, req) == req
+        for G in (1, 4, 8):
+            for req in (1, 7, 0):
+                W = req or auto
+                ws = api.decode_workspace_bytes(B, G * Hkv, Hkv, L, req)
+                # two partial (o, lse) slots per wave and head, plus B + 1 prefix entries
+                assert ws >= W * 2 * G * 129 * 4 + (B + 1) * 4
+                assert ws % 256 == 0
+    assert api.decode_num_splits(0, 8, 1024, 0) == 0
+    assert api.decode_workspace_bytes(1, 6, 4, 1024, 0) == 0     # 6 % 4 != 0
 
 
 def test_memory_footprint_matches_page_claims(api):

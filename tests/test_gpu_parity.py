@@ -8,16 +8,13 @@ import torch
 
 from decode_attention_nvfp4_amd import api
 from decode_attention_nvfp4_amd import workloads as W
-from gpu_common import TOL, BuiltDecode, compare, i32, planes, say, to_dev
+from gpu_common import TOL, BuiltDecode, check_decode, compare, i32, planes, say, to_dev
 from layout import sequence_tokens
 
 pytestmark = pytest.mark.gpu
 
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
-
-DECODE_STRICT = 2e-3     # decode uses exact 16-bit operands; only P is rounded (f16)
-
 
 # ------------------------------------------------------------------ codec
 
@@ -58,8 +55,40 @@ def test_append_bit_exact_and_sentinel(orc, dtype, dist):
         bad = np.argwhere(g != e)
         assert bad.size == 0, (nm, bad[:5].tolist())
     masks = P.touched_mask(pages, pos % 16)
-    for arr, m in zip(P.arrays(), masks):
-        assert np.all(arr[~m] == 0xA5)
+    for arr, m, f in zip(P.arrays(), masks, P.untouched_fill(0xA5)):
+        assert np.array_equal(arr[~m], f[~m])
+
+
+def test_append_token_pairs(orc):
+    """The two tokens of a V pair share bytes: written together (consecutive
+    rows of one call), one at a time across calls, in reverse order, and
+    across workgroup boundaries, the codes stay exact and the partner's
+    nibbles are kept."""
+    rng = np.random.default_rng(77)
+    Hkv, max_pages, num_pages = 2, 8, 10
+    pt = rng.permutation(num_pages)[:max_pages].reshape(1, max_pages).astype(np.int32)
+    n = 8 * 16
+    k = W.random_rows(20, n * Hkv, "mixed", "bf16").reshape(n, Hkv, 128)
+    v = W.random_rows(21, n * Hkv, "mixed", "bf16").reshape(n, Hkv, 128)
+    stk, stv = orc.tensor_scale(k), orc.tensor_scale(v)
+    cache = api.KVCache(num_pages, Hkv, stk, stv, fill=0xA5)
+    calls = [np.arange(1, 40), np.array([0]), np.arange(70, 40, -1), np.array([40]),
+             np.arange(71, 100), np.arange(100, n)[::2], np.arange(101, n)[::2]]
+    done = np.zeros(0, np.int64)
+    for c in calls:
+        say(f"append pairs: positions {c[:3].tolist()}.. ({len(c)})")
+        api.append(cache, to_dev(k[c], "bf16"), to_dev(v[c], "bf16"), i32(np.zeros(len(c))), i32(c), i32(pt))
+        done = np.concatenate([done, c])
+        P = planes(cache)
+        pages = pt[0, done // 16]
+        got = P.gather(pages, done % 16)
+        exp = (*orc.quantize_rows(k[done], stk), *orc.quantize_rows(v[done], stv))
+        for g, e, nm in zip(got, exp, ("k codes", "k scales", "v codes", "v scales")):
+            bad = np.argwhere(g != e)
+            assert bad.size == 0, (nm, bad[:5].tolist())
+        masks = P.touched_mask(pages, done % 16)
+        for arr, m, f in zip(P.arrays(), masks, P.untouched_fill(0xA5)):
+            assert np.array_equal(arr[~m], f[~m])
 
 
 def test_append_edge_values(orc):
@@ -144,11 +173,8 @@ def test_decode_parity_small(orc, case):
     q = w.q(0)
     say(f"decode {case}")
     out = built.decode(q).cpu().numpy()
-    ref = built.oracle_decode(orc, q, range(B))
-    ok, st = compare(out, ref)
-    say("   ", st)
-    assert ok, st
-    assert st["mixed"] <= DECODE_STRICT, st
+    ref, mag = built.oracle_decode(orc, q, range(B))
+    say("   ", check_decode(out, ref, mag))
     for b, L in enumerate(lens):
         if L == 0:
             assert np.all(out[b] == 0)
@@ -158,19 +184,19 @@ def test_decode_split_sweep_and_determinism(orc):
     w = W.custom_decode(9, 3, 32, 8, [1500, 77, 4000], dtype="bf16", outliers=True)
     built = BuiltDecode(w, orc)
     q = w.q(0)
-    ref = built.oracle_decode(orc, q, range(3))
+    ref, mag = built.oracle_decode(orc, q, range(3))
     outs = {}
-    for S in (1, 2, 7, 64, 0):
+    # 5000 waves exceed the 2800 (sequence, KV head, page) units: waves with
+    # empty ranges sit between the owners of a segment
+    for S in (1, 2, 7, 64, 5000, 0):
         say(f"decode split sweep S={S}")
         outs[S] = built.decode(q, num_splits=S).cpu().numpy()
-        ok, st = compare(outs[S], ref)
-        assert ok and st["mixed"] <= DECODE_STRICT, (S, st)
-    # splits change the running max each probability is taken against, so the
-    # FP16 rounding of P differs (relative 2^-11 per weight); each result is
-    # within DECODE_STRICT of the oracle, so two are within twice that
-    for S in (2, 7, 64, 0):
-        ok, st = compare(outs[S], outs[1], tol=2 * DECODE_STRICT)
-        assert ok, (S, st)
+        check_decode(outs[S], ref, mag)
+    # splits change the reference max each probability is taken against, so
+    # the FP16 rounding of P differs; each result is within the bound of the
+    # oracle, so two are within twice the bound of each other
+    for S in (2, 7, 64, 5000, 0):
+        check_decode(outs[S], outs[1], mag, factor=2.0)
     say("decode determinism")
     again = built.decode(q, num_splits=0).cpu().numpy()
     assert np.array_equal(again.view(np.uint32), outs[0].view(np.uint32))
@@ -182,8 +208,7 @@ def test_decode_f32_query_bf16_cache(orc):
     q = np.random.default_rng(3).standard_normal((2, 8, 128)).astype(np.float32)
     say("decode f32 q")
     out = built.decode(q, dtype="f32").cpu().numpy()
-    ok, st = compare(out, built.oracle_decode(orc, q, range(2)))
-    assert ok and st["mixed"] <= DECODE_STRICT, st
+    check_decode(out, *built.oracle_decode(orc, q, range(2)))
 
 
 def test_decode_softmax_scale_and_large_logits(orc):
@@ -195,9 +220,7 @@ def test_decode_softmax_scale_and_large_logits(orc):
     qd = to_dev(q, "bf16")
     say("decode large logits")
     out = api.decode(built.cache, qd, built.pt, i32(built.lens), int(built.lens.max()), softmax_scale=0.3)
-    ref = orc.decode_batch(q, [built.codes[b] for b in range(2)], 2, built.s_tk, built.s_tv, scale=0.3)
-    ok, st = compare(out.cpu().numpy(), ref)
-    assert ok, st
+    check_decode(out.cpu().numpy(), *built.oracle_decode(orc, q, range(2), scale=0.3))
 
 
 # ---------------------------------------------------------------- prefill
@@ -272,9 +295,7 @@ def test_config1_tiny(orc):
     q = w.q(0)
     say("config 1 decode")
     out = built.decode(q, dtype="f32").cpu().numpy()
-    ok, st = compare(out, built.oracle_decode(orc, q, range(1)))
-    say("   ", st)
-    assert ok and st["mixed"] <= DECODE_STRICT, st
+    say("   ", check_decode(out, *built.oracle_decode(orc, q, range(1))))
 
 
 def test_config2_gqa_steps(orc):
@@ -290,9 +311,7 @@ def test_config2_gqa_steps(orc):
         out = built.decode(q).cpu().numpy()
         if step in (0, 7, 15):
             built.check_codes(range(w.B))
-            ok, st = compare(out, built.oracle_decode(orc, q, range(w.B)))
-            say("   ", st)
-            assert ok and st["mixed"] <= DECODE_STRICT, (step, st)
+            say("   ", check_decode(out, *built.oracle_decode(orc, q, range(w.B))))
 
 
 def test_config3_long_context(orc):
@@ -302,14 +321,11 @@ def test_config3_long_context(orc):
     q = w.q(0)
     say("config 3 decode (auto splits)")
     out = built.decode(q).cpu().numpy()
-    ref = built.oracle_decode(orc, q, range(1))
-    ok, st = compare(out, ref)
-    say("   ", st)
-    assert ok and st["mixed"] <= DECODE_STRICT, st
-    say("config 3 decode (1 split)")
-    one = built.decode(q, num_splits=1).cpu().numpy()
-    ok, st = compare(one, out, tol=2 * DECODE_STRICT)
-    assert ok, st
+    ref, mag = built.oracle_decode(orc, q, range(1))
+    say("   ", check_decode(out, ref, mag))
+    say("config 3 decode (16 splits)")
+    few = built.decode(q, num_splits=16).cpu().numpy()
+    check_decode(few, ref, mag)
 
 
 def test_config4_paged_sampled(orc):
@@ -324,10 +340,8 @@ def test_config4_paged_sampled(orc):
     q = w.q(0)
     say(f"config 4 decode, checking {sample}")
     out = built.decode(q).cpu().numpy()
-    ref = built.oracle_decode(orc, q, sample)
-    ok, st = compare(out[sample], ref)
-    say("   ", st)
-    assert ok and st["mixed"] <= DECODE_STRICT, st
+    ref, mag = built.oracle_decode(orc, q, sample)
+    say("   ", check_decode(out[sample], ref, mag))
     assert np.all(np.isfinite(out))
 
 
