@@ -66,19 +66,25 @@ int cu_count() {
 }
 
 // Decode work plan: the number of waves W that split the (sequence, KV head,
-// page) work into equal contiguous ranges.  Automatic: at most one wave per
-// resident wave slot of the device (CUs x decode waves per CU), so the grid
-// runs in a single round of residency, and at least kMinPagesPerWave pages
-// per wave (for the longest batch max_seq_len allows), so that each wave's
-// fixed cost (query load, partial write and merge) stays small next to its
-// page stream.  A requested count is used as given.
+// page) work into equal contiguous ranges.  Automatic: at most 8 waves per
+// CU (two per SIMD: with more, the oldest waves take the issue slots and the
+// younger ones only stretch the tail, measured on MI355X), and at least
+// kMinPagesPerWave pages per wave for the longest batch max_seq_len allows, so
+// that each wave's fixed cost (query load, partial write and merge) stays
+// small next to its page stream, and at most about kMaxPiecesPerSegment waves
+// per (sequence, KV head) segment, since the merge of a segment's partials
+// grows with their number (few long sequences).  A requested count is used
+// as given.
 constexpr int64_t kMinPagesPerWave = 16;
+constexpr int64_t kWavesPerCu = 8;
+constexpr int64_t kMaxPiecesPerSegment = 128;
 
 int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, int32_t max_seq_len) {
   if (num_splits > 0) return num_splits;
-  const int64_t slots = (int64_t)cu_count() * decode_occupancy(f32_q);
+  const int64_t slots = (int64_t)cu_count() * std::min<int64_t>(kWavesPerCu, decode_occupancy(f32_q));
   const int64_t units = (int64_t)batch * hkv * ((max_seq_len + NVFP4_PAGE_SIZE - 1) / NVFP4_PAGE_SIZE);
-  const int64_t want = (units + kMinPagesPerWave - 1) / kMinPagesPerWave;
+  const int64_t want = std::min((units + kMinPagesPerWave - 1) / kMinPagesPerWave,
+                                 std::max<int64_t>(cu_count(), kMaxPiecesPerSegment * batch * hkv));
   return (int32_t)std::max<int64_t>(1, std::min(slots, want));
 }
 

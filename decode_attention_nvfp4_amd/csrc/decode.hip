@@ -313,7 +313,7 @@ __device__ __forceinline__ uint32_t prepare_block(const DecodeArgs& p, SegPos& w
 }
 
 template <bool F32Q>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) decode_kernel(DecodeArgs p) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(F32Q ? 3 : 4, 8))) decode_kernel(DecodeArgs p) {
   const int lane = threadIdx.x;
   const int col = lane & 15, kg = lane >> 4;
   const int wave = blockIdx.x, W = gridDim.x;
@@ -454,76 +454,98 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8)))
   }
 }
 
-// One workgroup (four waves) per (sequence, KV head) segment.  A segment cut
-// by wave ranges is combined from its pieces, per query head:
+// One workgroup per (sequence, KV head, query head).  A segment cut by wave
+// ranges is combined from its pieces:
 //   o = sum_w 2^(lse_w - M) o_w / sum_w 2^(lse_w - M), times s_tV.
 // Wave w's range starts at start(w) = w U / W; unit u belongs to wave
 // floor(((u + 1) W - 1) / U); the piece of wave w sits in slot 0 when w's range
 // starts inside the segment, else in slot 1.  Waves between the first and the
 // last owner with an empty range (W > U) wrote nothing and are skipped.
-// Wave i of the workgroup merges heads i, i + 4, ...; lane l owns output
-// elements 2l, 2l + 1, and the partial loads of all pieces are independent.
-__global__ void __launch_bounds__(256) merge_kernel(DecodeArgs p) {
-  const int b = blockIdx.x / p.hkv, kvh = blockIdx.x % p.hkv;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+// Thread (i, e) = (tid / 32, tid % 32) takes pieces i, i + PL, ... and output
+// elements 4e .. 4e + 3, so all partial loads are independent; the PL piece
+// lanes are combined in LDS.  PL = 8 when segments have many pieces (few
+// long sequences), else 2 (one wave per head).
+template <int PL>
+__global__ void __launch_bounds__(32 * PL) merge_kernel(DecodeArgs p) {
+  const int g = blockIdx.x % p.group;
+  const int seg = blockIdx.x / p.group;
+  const int b = seg / p.hkv, kvh = seg % p.hkv;
+  const int tid = threadIdx.x, pi = tid >> 5, e = tid & 31;
   const int W = p.num_splits, G = p.group;
   const int pb = p.ws_prefix[b], np = p.ws_prefix[b + 1] - pb;
   const long long U = (long long)p.ws_prefix[p.batch] * p.hkv;
-  float* out = p.out + ((size_t)b * p.hq + (size_t)kvh * G) * kD;
+  float* out = p.out + ((size_t)b * p.hq + (size_t)kvh * G + g) * kD;
   if (np == 0) {
-    for (int i = threadIdx.x; i < G * kD; i += 256) out[i] = 0.0f;
+    if (tid < 32) reinterpret_cast<float4*>(out)[tid] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     return;
   }
   const long long a = (long long)pb * p.hkv + (long long)kvh * np;
-  const long long e = a + np;
+  const long long end = a + np;
   const int w0 = (int)(((a + 1) * W - 1) / U);
-  const int w1 = (int)((e * W - 1) / U);
+  const int w1 = (int)((end * W - 1) / U);
   if (w0 == w1) return;                       // finished by one wave
   const int n = w1 - w0 + 1;
   auto start = [&](int w) { return (long long)w * U / W; };
-  for (int g = wid; g < G; g += 4) {
-    // pass 1: the largest log-sum-exp of the head's pieces
-    float M = -INFINITY;
-    for (int i = lane; i < n; i += 64) {
-      const int w = w0 + i;
-      if (start(w) < start(w + 1)) {
-        const int slot = start(w) >= a ? 0 : 1;
-        M = fmaxf(M, p.ws_lse[((size_t)w * 2 + slot) * G + g]);
-      }
+  // the piece of wave w0 + i: its workspace index, or -1 when w wrote none
+  auto piece = [&](int i) -> int {
+    const int w = w0 + i;
+    if (start(w) == start(w + 1)) return -1;
+    const int slot = start(w) >= a ? 0 : 1;
+    return (w * 2 + slot) * G + g;
+  };
+  // each thread merges its pieces online (running max m, rescaling as it
+  // grows); the 8 piece lanes are then combined once
+  __shared__ float4 s_acc[PL][32];
+  __shared__ float s_m[PL], s_den[PL];
+  float m = -INFINITY, den = 0.0f;
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int i = pi; i < n; i += PL) {
+    const int k = piece(i);
+    if (k < 0) continue;
+    const float l = p.ws_lse[k];
+    const float4 v = reinterpret_cast<const float4*>(p.ws_o + (size_t)k * kD)[e];
+    if (l == -INFINITY) continue;             // a piece with no weight
+    if (l > m) {
+      const float r = exp2f(m - l);           // 0 while m is -inf
+      acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
+      den *= r;
+      m = l;
     }
+    const float c = exp2f(l - m);
+    acc.x = fmaf(c, v.x, acc.x);
+    acc.y = fmaf(c, v.y, acc.y);
+    acc.z = fmaf(c, v.z, acc.z);
+    acc.w = fmaf(c, v.w, acc.w);
+    den += c;
+  }
+  s_acc[pi][e] = acc;
+  if (e == 0) {
+    s_m[pi] = m;
+    s_den[pi] = den;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    float M = s_m[0];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    // pass 2: weights per piece (lane = piece within a chunk of 64), then
-    // the weighted sum of the partial outputs
-    float2 acc = {0.0f, 0.0f};
-    float den = 0.0f;
+    for (int j = 1; j < PL; ++j) M = fmaxf(M, s_m[j]);
+    float4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+    float d = 0.0f;
     if (M > -INFINITY) {
-      for (int c = 0; c < n; c += 64) {
-        const int w = w0 + c + lane;
-        float cf = 0.0f;
-        int piece = 0;
-        if (c + lane < n && start(w) < start(w + 1)) {
-          const int slot = start(w) >= a ? 0 : 1;
-          piece = (w * 2 + slot) * G + g;
-          cf = exp2f(p.ws_lse[piece] - M);
-        }
-        den += cf;
-        const int cnt = min(64, n - c);
-#pragma unroll 8
-        for (int k = 0; k < cnt; ++k) {
-          const float ck = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cf), k));
-          const int pk = __builtin_amdgcn_readlane(piece, k);
-          const float2 v = *reinterpret_cast<const float2*>(p.ws_o + (size_t)pk * kD + 2 * lane);
-          // a skipped piece has weight 0 and its (stale) slot is not used
-          acc.x = ck != 0.0f ? fmaf(ck, v.x, acc.x) : acc.x;
-          acc.y = ck != 0.0f ? fmaf(ck, v.y, acc.y) : acc.y;
-        }
-      }
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+      for (int j = 0; j < PL; ++j) {
+        if (s_m[j] == -INFINITY) continue;
+        const float f = exp2f(s_m[j] - M);
+        const float4 u = s_acc[j][tid];
+        t.x = fmaf(f, u.x, t.x);
+        t.y = fmaf(f, u.y, t.y);
+        t.z = fmaf(f, u.z, t.z);
+        t.w = fmaf(f, u.w, t.w);
+        d = fmaf(f, s_den[j], d);
+      }
     }
-    const float f = den > 0.0f ? p.v_scale / den : 0.0f;
-    *reinterpret_cast<float2*>(out + (size_t)g * kD + 2 * lane) = make_float2(acc.x * f, acc.y * f);
+    const float f = d > 0.0f ? p.v_scale / d : 0.0f;
+    reinterpret_cast<float4*>(out)[tid] = make_float4(t.x * f, t.y * f, t.z * f, t.w * f);
   }
 }
 
@@ -543,7 +565,9 @@ int decode_occupancy(bool f32_q) {
 hipError_t launch_decode(const DecodeArgs& a, bool f32_q, hipStream_t s) {
   if (f32_q) decode_kernel<true><<<a.num_splits, 64, 0, s>>>(a);
   else decode_kernel<false><<<a.num_splits, 64, 0, s>>>(a);
-  merge_kernel<<<(unsigned)(a.batch * a.hkv), 256, 0, s>>>(a);
+  const unsigned heads = (unsigned)(a.batch * a.hkv * a.group);
+  if ((long long)a.num_splits > 8LL * a.batch * a.hkv) merge_kernel<8><<<heads, 256, 0, s>>>(a);
+  else merge_kernel<2><<<heads, 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -148,9 +148,10 @@ def test_split_planner_and_workspace(api):
     for B, Hkv, L in ((1, 1, 1024), (8, 8, 4097), (1, 8, 65536), (128, 8, 8192), (3, 2, 0), (4, 4, 17)):
         auto = api.decode_num_splits(B, Hkv, L, 0)
         units = B * Hkv * -(-L // 16)
-        # at least 16 pages per wave, at most the device's wave slots
+        # at least 16 pages per wave, at most 8 waves per CU
         assert auto == max(1, min(auto, -(-units // 16)))
         assert auto >= min(256, -(-units // 16))
+        assert auto <= 8 * 256 or auto == max(1, -(-units // 16))
         for req in (1, 2, 7, 64):
             assert api.decode_num_splits(B, Hkv, L, req) == req
         for G in (1, 4, 8):
