@@ -141,6 +141,18 @@ def bench_prefill(api, torch, stream, iters=3):
     }
 
 
+def stream_read_probe(torch, stream, gib=1, iters=10):
+    """Streaming-read reference: a sum over `gib` GiB of bf16 (torch's
+    reduction kernel reads each byte once; larger than the 256 MB LLC)."""
+    x = torch.ones((gib << 30) // 2, dtype=torch.bfloat16, device="cuda")
+    x.sum()
+    torch.cuda.synchronize()
+    t = time_region(torch, lambda: x.sum(), iters, stream)
+    del x
+    return {"what": f"torch sum over {gib} GiB of bf16", "ms": round(t, 4),
+            "gbs": round((gib << 30) / (t * 1e-3) / 1e9, 1)}
+
+
 def bench_small_decode(api, torch, stream, cfg, iters=20):
     """Decode of configurations 2 (GQA batch 8, L 4096) and 3 (L 65536).  The
     caches fit in the 256 MB last-level cache; to read from HBM the timing
@@ -187,6 +199,93 @@ def bench_small_decode(api, torch, stream, cfg, iters=20):
             "splits": api.decode_num_splits(w.B, w.Hkv, L)}
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_paged_b128_traffic.json")
+DECODE_SOURCES = [os.path.join(ROOT, "decode_attention_nvfp4_amd", "csrc", f)
+                  for f in ("decode.hip", "common.h", "internal.h", "api.cpp")]
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def decode_traffic():
+    """HBM bytes per decode call (decode_kernel + merge_kernel) from the
+    committed counter record, or None when the kernels changed since."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_digest():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def _pmc_per_kernel(d: str, counter: str):
+    """{kernel name: [value per dispatch]} of one rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = (r["Kernel_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def write_traffic_record(fetch_dir: str, write_dir: str):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of decode_kernel and
+    merge_kernel, each scaled by what the same counter reads for the plain
+    device copy of --copy-mib MiB (ideal: that many MiB read and written)."""
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(table, part):
+        vals = [v for k, vs in table.items() if part in k for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of {part} in the counter output")
+        return float(np.median(vals))
+
+    # the calibration copy is the largest device-to-device copy dispatch
+    def largest(table, part):
+        vals = [v for k, vs in table.items() if part in k for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of {part} in the counter output")
+        return max(vals)
+
+    copy_f, copy_w = largest(fetch, "copyBuffer"), largest(write, "copyBuffer")
+    mib = int(os.environ.get("COPY_MIB", "512"))
+    ideal_kib = mib * 1024.0
+    fk, wk = ideal_kib / copy_f, ideal_kib / copy_w
+    dec_f, dec_w = pick(fetch, "decode_kernel"), pick(write, "decode_kernel")
+    mer_f, mer_w = pick(fetch, "merge_kernel"), pick(write, "merge_kernel")
+    rec = {
+        "workload": "paged decode, batch 128, 32/8 heads, context U[1024, 8192] (bench.py)",
+        "copy_mib": mib, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+        "fetch_factor": fk, "write_factor": wk,
+        "decode_kernel_kib": {"fetch": dec_f, "write": dec_w},
+        "merge_kernel_kib": {"fetch": mer_f, "write": mer_w},
+        "bytes_per_call": round(((dec_f + mer_f) * fk + (dec_w + mer_w) * wk) * 1024.0),
+        "sources_sha256": sources_digest(),
+    }
+    with open(TRAFFIC_RECORD, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,7 +293,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed steps, copy this many MiB device to device three times "
+                         "(the calibration kernel of the HBM traffic counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the decode traffic record from two rocprofv3 --pmc outputs "
+                         "(FETCH_SIZE, then WRITE_SIZE) of a run with --copy-mib, then exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic_record(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the NVFP4 KV hot path here is a "
               "single-GPU build and no multi-GPU run is defined.", file=sys.stderr)
@@ -273,6 +381,14 @@ def main():
     t_dec = time_region(torch, decode_step, args.steps, stream)
     t_app = time_region(torch, append_step, args.steps, stream)
 
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cache_bytes = int((w.lens + 1).sum()) * w.Hkv * BYTES_PER_TOKEN_HEAD
     q_out_bytes = w.B * w.Hq * 128 * (2 + 4)
     app_bytes = w.B * w.Hkv * 128 * 2 * (2 + 0.5625)
@@ -302,7 +418,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": decode_traffic(),
             "kernel": "nvfp4 decode_kernel + merge_kernel (one nvfp4_decode_attn call)",
             "bytes_per_launch": cache_bytes, "avg_ms": round(t_dec, 5),
         },
@@ -317,6 +433,13 @@ def main():
     if not args.no_extra:
         del cache
         torch.cuda.empty_cache()
+        try:
+            probe = stream_read_probe(torch, stream)
+            probe["decode_frac"] = round(achieved / probe["gbs"], 4)
+            res["extra"]["stream_read"] = probe
+        except Exception as e:  # noqa: BLE001
+            res["extra"]["stream_read"] = {"error": repr(e)}
+        log(f"stream read: {res['extra']['stream_read']}")
         for cfg in (2, 3):
             try:
                 res["extra"][f"decode_cfg{cfg}"] = bench_small_decode(api, torch, stream, cfg)
