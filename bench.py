@@ -141,15 +141,16 @@ def bench_prefill(api, torch, stream, iters=3):
     }
 
 
-def stream_read_probe(torch, stream, gib=1, iters=10):
-    """Streaming-read reference: a sum over `gib` GiB of bf16 (torch's
-    reduction kernel reads each byte once; larger than the 256 MB LLC)."""
+def stream_read_probe(api, torch, stream, gib=1, iters=10):
+    """Streaming-read reference: nvfp4_abs_max over `gib` GiB of bf16 (one
+    16-byte load per lane per step, each byte read once; larger than the
+    256 MB LLC)."""
     x = torch.ones((gib << 30) // 2, dtype=torch.bfloat16, device="cuda")
-    x.sum()
+    api.abs_max(x)
     torch.cuda.synchronize()
-    t = time_region(torch, lambda: x.sum(), iters, stream)
+    t = time_region(torch, lambda: api.abs_max(x, stream=stream), iters, stream)
     del x
-    return {"what": f"torch sum over {gib} GiB of bf16", "ms": round(t, 4),
+    return {"what": f"nvfp4_abs_max over {gib} GiB of bf16", "ms": round(t, 4),
             "gbs": round((gib << 30) / (t * 1e-3) / 1e9, 1)}
 
 
@@ -434,7 +435,7 @@ def main():
         del cache
         torch.cuda.empty_cache()
         try:
-            probe = stream_read_probe(torch, stream)
+            probe = stream_read_probe(api, torch, stream)
             probe["decode_frac"] = round(achieved / probe["gbs"], 4)
             res["extra"]["stream_read"] = probe
         except Exception as e:  # noqa: BLE001

@@ -159,6 +159,11 @@ int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const vo
   a.k_scale = cache->k_tensor_scale; a.v_scale = cache->v_tensor_scale;
   a.k_six_st = 6.0 * (double)cache->k_tensor_scale;
   a.v_six_st = 6.0 * (double)cache->v_tensor_scale;
+  // the FP32 fast path of the block scale needs 6 s_t well inside the
+  // normal FP32 range; 0 turns it off (the exact path then decides)
+  auto inv6 = [](double six) { return (six > 0x1p-100 && six < 0x1p100) ? (float)(1.0 / six) : 0.0f; };
+  a.k_inv6 = inv6(a.k_six_st);
+  a.v_inv6 = inv6(a.v_six_st);
   a.k_new = k_new; a.v_new = v_new;
   a.tok_seq = tok_seq; a.tok_pos = tok_pos; a.page_table = page_table;
   a.max_pages = max_pages_per_seq; a.n_tok = n_tok; a.hkv = cache->num_kv_heads;

@@ -13,30 +13,49 @@
 
 namespace nvfp4 {
 
+// A lane's 8 input elements (half of one block) as raw bits: 32 bytes of
+// FP32 or 16 bytes of BF16.  Converted to float only when quantized, so that
+// the loads of a row can all be in flight together.
+struct Raw8 {
+  uint4 a, b;
+};
+
 template <bool F32IN>
-__device__ __forceinline__ void load8(const void* base, size_t row, int lane16, float x[8]) {
+__device__ __forceinline__ Raw8 load_raw8(const void* base, size_t row, int lane16) {
+  Raw8 r;
   if (F32IN) {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + row * kD + lane16 * 8);
-    float4 a = p[0], b = p[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + row * kD + lane16 * 8);
+    r.a = p[0];
+    r.b = p[1];
   } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * kD + lane16 * 8);
-    uint4 a = *p;
-    x[0] = bf16_lo(a.x); x[1] = bf16_hi(a.x); x[2] = bf16_lo(a.y); x[3] = bf16_hi(a.y);
-    x[4] = bf16_lo(a.z); x[5] = bf16_hi(a.z); x[6] = bf16_lo(a.w); x[7] = bf16_hi(a.w);
+    r.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * kD + lane16 * 8);
+    r.b = uint4{0u, 0u, 0u, 0u};
+  }
+  return r;
+}
+
+template <bool F32IN>
+__device__ __forceinline__ void unpack8(const Raw8& r, float x[8]) {
+  if (F32IN) {
+    x[0] = __uint_as_float(r.a.x); x[1] = __uint_as_float(r.a.y);
+    x[2] = __uint_as_float(r.a.z); x[3] = __uint_as_float(r.a.w);
+    x[4] = __uint_as_float(r.b.x); x[5] = __uint_as_float(r.b.y);
+    x[6] = __uint_as_float(r.b.z); x[7] = __uint_as_float(r.b.w);
+  } else {
+    x[0] = bf16_lo(r.a.x); x[1] = bf16_hi(r.a.x); x[2] = bf16_lo(r.a.y); x[3] = bf16_hi(r.a.y);
+    x[4] = bf16_lo(r.a.z); x[5] = bf16_hi(r.a.z); x[6] = bf16_lo(r.a.w); x[7] = bf16_hi(r.a.w);
   }
 }
 
 // Returns the packed codes of this lane's 8 elements; *sb gets the block
 // scale code of its block.
-__device__ __forceinline__ uint32_t quantize_half_block(const float x[8], float s_t, double six_st,
+__device__ __forceinline__ uint32_t quantize_half_block(const float x[8], float s_t, float inv6, double six_st,
                                                         uint32_t* sb) {
   float a = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
   a = fmaxf(a, __shfl_xor(a, 1));
-  uint32_t code = block_scale_code(a, six_st);
+  uint32_t code = block_scale_code_fast(a, inv6, six_st);
   *sb = code;
   return encode8(x, code, s_t);
 }
@@ -65,33 +84,39 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
   const bool valid = tok < p.n_tok;
   __shared__ int s_seq[16], s_pos[16];
   __shared__ uint32_t s_vw[16][16];
+  // all of the row's loads go out first (position, then the K and V data),
+  // so their latencies overlap; the page-table lookup waits only for the
+  // position, and the quantization only for the data
   int seq = -1, pos = 0;
+  Raw8 rk = {}, rv = {};
+  const size_t row = (size_t)tok * p.hkv + h;
   if (valid) {
     seq = p.tok_seq[tok];
     pos = p.tok_pos[tok];
+    rk = load_raw8<F32IN>(p.k_new, row, lane16);
+    rv = load_raw8<F32IN>(p.v_new, row, lane16);
   }
   if (lane16 == 0) {
     s_seq[r] = seq;
     s_pos[r] = pos;
   }
-  const size_t row = (size_t)tok * p.hkv + h;
   size_t slab = 0;
   int slot = 0;
   uint32_t vw = 0, vsb = 0;
   if (valid) {
     const int page = p.page_table[(size_t)seq * p.max_pages + pos / kPage];
     slot = pos % kPage;
-    slab = (size_t)page * p.hkv + h;
+    uint32_t ksb;
     float x[8];
-    uint32_t sb;
+    unpack8<F32IN>(rk, x);
+    const uint32_t kw = quantize_half_block(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
+    unpack8<F32IN>(rv, x);
+    vw = quantize_half_block(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
+    slab = (size_t)page * p.hkv + h;
     // K: token-major codes [16][64 B], token-major scales [16][8]
-    load8<F32IN>(p.k_new, row, lane16, x);
-    const uint32_t w = quantize_half_block(x, p.k_scale, p.k_six_st, &sb);
-    *reinterpret_cast<uint32_t*>(p.k_codes + slab * kSlab + slot * 64 + lane16 * 4) = w;
-    if ((lane16 & 1) == 0) p.k_scales[slab * kScaleSlab + slot * kNBlk + (lane16 >> 1)] = (uint8_t)sb;
-    // V: codes of elements 8 lane16 .. 8 lane16 + 7; scales [block 8][token 16]
-    load8<F32IN>(p.v_new, row, lane16, x);
-    vw = quantize_half_block(x, p.v_scale, p.v_six_st, &vsb);
+    *reinterpret_cast<uint32_t*>(p.k_codes + slab * kSlab + slot * 64 + lane16 * 4) = kw;
+    if ((lane16 & 1) == 0) p.k_scales[slab * kScaleSlab + slot * kNBlk + (lane16 >> 1)] = (uint8_t)ksb;
+    // V scales [block 8][token 16]; the V codes follow below
     if ((lane16 & 1) == 0) p.v_scales[slab * kScaleSlab + (lane16 >> 1) * kPage + slot] = (uint8_t)vsb;
   }
   s_vw[r][lane16] = vw;
@@ -200,34 +225,75 @@ hipError_t launch_dequant(const DequantArgs& a, bool f32, hipStream_t s) {
 
 __global__ void zero_float_kernel(float* p) { *p = 0.0f; }
 
-template <bool F32IN>
-__global__ void __launch_bounds__(256) absmax_kernel(const void* x, int64_t n, float* out) {
-  float m = 0.0f;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; i < n; i += stride) {
-    float v = F32IN ? static_cast<const float*>(x)[i]
-                    : __uint_as_float((uint32_t) static_cast<const uint16_t*>(x)[i] << 16);
-    m = fmaxf(m, fabsf(v));
-  }
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  __shared__ float wmax[4];
+// Wave max, then one atomic per workgroup; non-negative floats order like
+// their bit patterns, so the maximum is taken on |x|'s bits.
+__device__ __forceinline__ void absmax_publish(uint32_t m, float* out) {
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  __shared__ uint32_t wmax[4];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  // one atomic per workgroup; non-negative floats order like their bit patterns
   if (threadIdx.x == 0) {
-    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    atomicMax(reinterpret_cast<unsigned int*>(out), __float_as_uint(m));
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(out), m);
   }
+}
+
+// |x| bits of one element: FP32 without its sign, or BF16 widened to FP32.
+template <bool F32IN>
+__device__ __forceinline__ uint32_t abs_bits(const void* x, int64_t i) {
+  return F32IN ? (static_cast<const uint32_t*>(x)[i] & 0x7FFFFFFFu)
+               : ((uint32_t)(static_cast<const uint16_t*>(x)[i] & 0x7FFFu) << 16);
+}
+
+// Any alignment: one element per thread per step.
+template <bool F32IN>
+__global__ void __launch_bounds__(256) absmax_kernel(const void* x, int64_t n, float* out) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    m = max(m, abs_bits<F32IN>(x, i));
+  absmax_publish(m, out);
+}
+
+// 16-byte aligned input: 16 bytes per thread per step (a streaming read),
+// then the elements past the last whole 16 bytes.
+template <bool F32IN>
+__global__ void __launch_bounds__(256) absmax_vec_kernel(const void* x, int64_t n, float* out) {
+  constexpr int kPer = F32IN ? 4 : 8;
+  const int64_t nvec = n / kPer;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const u32x4* v = static_cast<const u32x4*>(x);
+  uint32_t m = 0;
+  for (int64_t i = gid; i < nvec; i += stride) {
+    const u32x4 w = __builtin_nontemporal_load(v + i);
+    if (F32IN) {
+      m = max(m, max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu)));
+    } else {
+      const uint32_t a = max(max(w.x & 0x7FFFu, (w.x >> 16) & 0x7FFFu), max(w.y & 0x7FFFu, (w.y >> 16) & 0x7FFFu));
+      const uint32_t b = max(max(w.z & 0x7FFFu, (w.z >> 16) & 0x7FFFu), max(w.w & 0x7FFFu, (w.w >> 16) & 0x7FFFu));
+      m = max(m, max(a, b) << 16);
+    }
+  }
+  for (int64_t i = nvec * kPer + gid; i < n; i += stride) m = max(m, abs_bits<F32IN>(x, i));
+  absmax_publish(m, out);
 }
 
 hipError_t launch_absmax(const void* x, bool f32, int64_t n, float* out, hipStream_t s) {
   zero_float_kernel<<<1, 1, 0, s>>>(out);
   if (n > 0) {
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    if (f32) absmax_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
-    else absmax_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
+    const bool vec = (reinterpret_cast<uintptr_t>(x) & 15u) == 0;
+    const int64_t per = vec ? (f32 ? 4 : 8) : 1;
+    int64_t blocks = (n / per + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks < 1) blocks = 1;
+    if (vec) {
+      if (f32) absmax_vec_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
+      else absmax_vec_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
+    } else {
+      if (f32) absmax_kernel<true><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
+      else absmax_kernel<false><<<(unsigned)blocks, 256, 0, s>>>(x, n, out);
+    }
   }
   return hipGetLastError();
 }

@@ -71,6 +71,26 @@ __device__ __forceinline__ uint32_t block_scale_code(float amax, double six_st) 
   return (uint32_t)((e + 6) * 8 + (int)r);
 }
 
+// The same code, fast path first.  q = amax * inv6 (inv6 = 1/(6 s_t) rounded
+// to FP32) is within 2^-23 relative of the exact quotient, so q (1 - 2^-20)
+// and q (1 + 2^-20) bracket it; the hardware FP32 -> E4M3 conversion rounds
+// to nearest even and is monotone, so when the two brackets convert to the
+// same code that code is the exact answer.  Quotients of 448 and above clamp
+// to 0x7E; anything else (a bracket straddling a midpoint or 448, or a
+// quotient far below the E4M3 range where FP32 loses precision) takes the
+// exact double path.
+__device__ __forceinline__ uint32_t block_scale_code_fast(float amax, float inv6, double six_st) {
+  const float q = amax * inv6;
+  const float lo = q * (1.0f - 0x1p-20f), hi = q * (1.0f + 0x1p-20f);
+  if (lo >= 448.0f) return 0x7Eu;
+  if (hi < 448.0f && q >= 0x1p-100f) {
+    const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false);
+    if ((w & 0xFFu) == ((w >> 8) & 0xFFu)) return w & 0xFFu;
+  }
+  if (amax == 0.0f) return 0u;
+  return block_scale_code(amax, six_st);
+}
+
 // ------------------------------------------------------- element codes
 
 // Magnitude code (0..7) of |x| for exact step d = s_block * s_t (double):
@@ -93,20 +113,24 @@ __device__ __forceinline__ uint32_t e2m1_mag_exact(float x, double d) {
 // 4j..4j+3).  Fast path: the hardware FP32->E2M1 conversion rounds to nearest
 // even (and saturates at 6) for every FP32 input; x * y_lo and x * y_hi
 // bracket the exact quotient x / d, so when both conversions agree the exact
-// code is that value (the rounding is monotone).  Otherwise the lane redoes
-// its eight elements with exact double thresholds.
+// code is that value (the rounding is monotone); an element where they
+// disagree is decided exactly at its one candidate midpoint.  When d is
+// outside the range where the FP32 bracket holds, the lane redoes its eight
+// elements with exact double thresholds.
 __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t sb_code, float s_t) {
   uint32_t signs = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) signs |= (__float_as_uint(x[j]) >> 31) << (4 * j + 3);
   if (sb_code == 0u) return signs;                  // zero scale: magnitude 0
-  double d = (double)e4m3_to_float(sb_code) * (double)s_t;   // exact
-  double yd = 1.0 / d;
-  bool fast = yd < 1.0e37;
+  // d = s_block * s_t in FP32 (2^-24 relative) and its hardware reciprocal
+  // (1 ulp) give y within ~2^-22 of 1/d; the brackets are 2^-20 wide
+  const float df = e4m3_to_float(sb_code) * s_t;
+  const bool fast = df >= 0x1p-100f && df <= 0x1p100f;
   uint32_t lo = 0, hi = 0;
   if (fast) {
-    float y_lo = (float)(yd * (1.0 - 0x1p-20));
-    float y_hi = (float)(yd * (1.0 + 0x1p-20));
+    const float y = __builtin_amdgcn_rcpf(df);
+    const float y_lo = y * (1.0f - 0x1p-20f);
+    const float y_hi = y * (1.0f + 0x1p-20f);
     lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[0] * y_lo, x[1] * y_lo, 1.0f, 0);
     lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[2] * y_lo, x[3] * y_lo, 1.0f, 1);
     lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x[4] * y_lo, x[5] * y_lo, 1.0f, 2);
@@ -116,7 +140,31 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t sb_code, 
     hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[4] * y_hi, x[5] * y_hi, 1.0f, 2);
     hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x[6] * y_hi, x[7] * y_hi, 1.0f, 3);
   }
-  if (fast && lo == hi) return (lo & 0x77777777u) | signs;
+  if (fast) {
+    // an element whose brackets disagree sits within 2^-19 of the one
+    // midpoint t between its two candidate codes c and c+1; decide it
+    // exactly: t * s_block is exact in FP32 (at most 7 significant bits),
+    // p + e = t * s_block * s_t exactly (e from an FMA), and |x| - p is exact
+    // (Sterbenz: |x| and p are within 2^-18 of each other)
+    uint32_t diff = (lo ^ hi) & 0x77777777u;
+    if (diff) {
+      const float sbv = e4m3_to_float(sb_code);
+      do {
+        const int sh = (__builtin_ctz(diff) >> 2) << 2;
+        const uint32_t c = (lo >> sh) & 7u;                   // the lower candidate
+        const float t = c < 4u ? 0.25f + 0.5f * (float)c : (c == 4u ? 2.5f : (c == 5u ? 3.5f : 5.0f));
+        const float a = sbv * t;
+        const float pr = a * s_t;
+        const float e = __builtin_fmaf(a, s_t, -pr);
+        const float r = fabsf(x[sh >> 2]) - pr;
+        const bool up = r > e || (r == e && ((c + 1u) & 1u) == 0u);
+        lo = (lo & ~(7u << sh)) | ((c + (up ? 1u : 0u)) << sh);
+        diff &= ~(15u << sh);
+      } while (diff);
+    }
+    return (lo & 0x77777777u) | signs;
+  }
+  const double d = (double)e4m3_to_float(sb_code) * (double)s_t;   // exact
   uint32_t w = signs;
 #pragma unroll
   for (int j = 0; j < 8; ++j) w |= e2m1_mag_exact(x[j], d) << (4 * j);

@@ -19,6 +19,7 @@ struct AppendArgs {
   uint8_t* v_scales;
   float k_scale, v_scale;     // tensor scales s_t
   double k_six_st, v_six_st;  // 6 * s_t, exact in double
+  float k_inv6, v_inv6;       // 1 / (6 * s_t) rounded to FP32 (fast block-scale path)
   const void* k_new;
   const void* v_new;
   const int32_t* tok_seq;

@@ -27,6 +27,13 @@ def test_abs_max_exact(orc):
         assert api.tensor_scale_from_amax(got) == orc.tensor_scale(x)
     say("abs_max empty")
     assert api.abs_max(torch.empty(0, device="cuda")).item() == 0.0
+    # a start that is not 16-byte aligned and lengths that leave a tail
+    for dtype in ("bf16", "f32"):
+        x = W.random_rows(2, 300, "outlier", dtype=dtype).reshape(-1)
+        xd = to_dev(x, dtype)
+        for lo, hi in ((1, 1000), (0, 38397), (3, 38399)):
+            say(f"abs_max {dtype} [{lo}:{hi}]")
+            assert api.abs_max(xd[lo:hi]).item() == orc.abs_max(x[lo:hi])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -57,6 +64,45 @@ def test_append_bit_exact_and_sentinel(orc, dtype, dist):
     masks = P.touched_mask(pages, pos % 16)
     for arr, m, f in zip(P.arrays(), masks, P.untouched_fill(0xA5)):
         assert np.array_equal(arr[~m], f[~m])
+
+
+def test_append_block_scale_sweep(orc):
+    """Block amax values at every E4M3 midpoint of amax / (6 s_t) and up to 3
+    FP32 ulps either side, plus the saturation region and the subnormal
+    scales: the block scales (and the codes under them) match the oracle bit
+    for bit, so the device's fast conversion decides exactly as the exact
+    definition does."""
+    st = 2.0 ** -3                      # 6 s_t = 0.75: quotients are not exact in binary
+    six = 6.0 * st
+    vals = [orc.e4m3_value(c) for c in range(0x7F)]
+    targets = [0.5 * (a + b) for a, b in zip(vals, vals[1:])] + [448.0, 456.0, 464.0, 472.0, 1e4]
+    amaxes = []
+    for t in targets:
+        base = np.float32(t * six)
+        for k in range(-3, 4):
+            amaxes.append(np.float32(base + np.float32(k) * np.spacing(base)) if k else base)
+    amaxes = np.abs(np.array(amaxes, np.float32))
+    amaxes = amaxes[amaxes > 0]
+    pad = (-len(amaxes)) % 8
+    amaxes = np.concatenate([amaxes, np.full(pad, 1.0, np.float32)])
+    rows = len(amaxes) // 8
+    rng = np.random.default_rng(91)
+    x = (rng.uniform(-0.5, 0.5, (rows, 8, 16)) * amaxes.reshape(rows, 8, 1)).astype(np.float32)
+    x[:, :, 3] = amaxes.reshape(rows, 8) * np.where(rng.random((rows, 8)) < 0.5, -1.0, 1.0)
+    x = x.reshape(rows, 1, 128)
+    B, Hkv = 1, 1
+    pages = -(-rows // 16)
+    pt = np.arange(pages, dtype=np.int32).reshape(1, pages)
+    for dtype in ("f32",):
+        cache = api.KVCache(pages, Hkv, st, st, fill=0)
+        say(f"block scale sweep: {rows} rows")
+        api.append(cache, to_dev(x, dtype), to_dev(x, dtype), i32(np.zeros(rows)), i32(np.arange(rows)), i32(pt))
+        P = planes(cache)
+        got = P.gather(pt[0, np.arange(rows) // 16], np.arange(rows) % 16)
+        ec, es = orc.quantize_rows(x, st)
+        for g, e, nm in zip(got, (ec, es, ec, es), ("k codes", "k scales", "v codes", "v scales")):
+            bad = np.argwhere(g != e)
+            assert bad.size == 0, (nm, bad[:5].tolist())
 
 
 def test_append_token_pairs(orc):
