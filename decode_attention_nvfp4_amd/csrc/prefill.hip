@@ -39,13 +39,13 @@ template <> struct Prec<kPrefillFP8> {
   static constexpr int EB = 1;                       // bytes per operand element
   static constexpr float kExpand = 0.125f;           // K~, V~ carry 2^-3
   static constexpr int kQTop = 7;                    // |q| 2^shift in [2^7, 2^8)
-  static constexpr float kPScale = 256.0f;           // P carries 2^8
+  static constexpr float kPLog2 = 8.0f;              // P carries 2^8
 };
 template <> struct Prec<kPrefillF16> {
   static constexpr int EB = 2;
   static constexpr float kExpand = 1.0f;
   static constexpr int kQTop = 14;                   // |q| 2^shift in [2^14, 2^15)
-  static constexpr float kPScale = 1.0f;
+  static constexpr float kPLog2 = 0.0f;
 };
 
 // Position of key kk (0..63) of a tile inside a V~^T row.
@@ -263,7 +263,9 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.0f;
-  float m_ref = -INFINITY, l_run = 0.0f;
+  // the reference max starts finite and far below any score, so that keys
+  // masked to -inf give p = 0, never NaN
+  float m_ref = -1.0e30f, l_run = 0.0f;
 
   u32x4 pre[2 * CPT];
   if (ntiles > 0) {
@@ -302,47 +304,54 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
       }
       s[kb] = c;
     }
-    // ---- scale, mask, row max
+    // ---- mask and row max on the raw scores (the row scale is positive and
+    // is applied inside the exponent below)
     const int kbase = t * kTile;
     const bool need_mask = t >= mask_from || kbase + kTile > kv_len;
+    if (need_mask) {
+      // this lane's keys are kbase + 4h + off with off = kb*32 + 8*(r/4) + r%4
+      const int klim = min(lim, kv_len - 1) - kbase - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = off <= klim ? s[kb][r] : -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[kb][r] * rowscale;
-        if (need_mask) {
-          const int key = kbase + kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > lim || key >= kv_len) v = -INFINITY;
-        }
-        s[kb][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
-    mx = max_across_halves(mx);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_across_halves(mx) * rowscale;
     // lazy max: rescale only when the row max grows by more than 0.5 (log2),
-    // which keeps p <= 2^0.5 (p * 256 stays inside E4M3's range)
+    // which keeps p <= 2^0.5 (p * 2^8 stays inside E4M3's range)
     const bool grow = mx > m_ref + 0.5f;
     if (__any(grow)) {
       const float m_new = grow ? mx : m_ref;
-      const float alpha = grow ? exp2f(m_ref - m_new) : 1.0f;
+      const float alpha = fast_exp2(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc_o[i] *= alpha;
     }
-    // ---- P^T and the row sum
+    // ---- P^T = 2^(s * rowscale - m + kPLog2) and the row sum (the common
+    // factor 2^kPLog2 of P and of the sum cancels in O / l)
+    const float cexp = P::kPLog2 - m_ref;
     uint32_t pw[8 * EB];
     float lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int kb = w >> 2, r0 = (w & 3) * 4;
-      const float e0 = exp2f(s[kb][r0] - m_ref), e1 = exp2f(s[kb][r0 + 1] - m_ref);
-      const float e2 = exp2f(s[kb][r0 + 2] - m_ref), e3 = exp2f(s[kb][r0 + 3] - m_ref);
+      const float e0 = fast_exp2(fmaf(s[kb][r0], rowscale, cexp));
+      const float e1 = fast_exp2(fmaf(s[kb][r0 + 1], rowscale, cexp));
+      const float e2 = fast_exp2(fmaf(s[kb][r0 + 2], rowscale, cexp));
+      const float e3 = fast_exp2(fmaf(s[kb][r0 + 3], rowscale, cexp));
       lsum += (e0 + e1) + (e2 + e3);
       if (MODE == kPrefillFP8) {
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e0 * P::kPScale, e1 * P::kPScale, 0, false);
-        pw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e2 * P::kPScale, e3 * P::kPScale, lo, true);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        pw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, lo, true);
       } else {
         pw[2 * w] = encode<MODE>(e0) | (encode<MODE>(e1) << 16);
         pw[2 * w + 1] = encode<MODE>(e2) | (encode<MODE>(e3) << 16);
@@ -377,7 +386,7 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
   // ---- epilogue: O / l * s_tV, removing the operand scale factors
   const float l_tot = sum_across_halves(l_run);
   if (row_ok) {
-    const float f = l_tot > 0.0f ? p.v_scale / (P::kExpand * P::kPScale) / l_tot : 0.0f;
+    const float f = l_tot > 0.0f ? p.v_scale / P::kExpand / l_tot : 0.0f;
     float* o = p.out + ((size_t)qi * p.hq + head) * kD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
