@@ -5,8 +5,11 @@
 // on the dequantized operands with an FP32 accumulator.  Two operand
 // precisions share one kernel structure:
 //   FP8 (the pages' flow): K~, V~ = E4M3(e2m1 * s_block / 8) (<= 336, no
-//     overflow); Q = E4M3(q * 2^shift_row) with |q| 2^shift < 256; P =
-//     E4M3(p * 256) with p <= 2^0.5 (lazy max, below); 32x32x64 FP8 MFMAs.
+//     overflow); Q' = E4M3(q * c * 2^-e_row), row maximum in [64, 256), c
+//     the score scale into log2 units, with 2^e_row given back by the MFMA's
+//     per-row E8M0 operand scale; P = E4M3(p * 256) with p <= 2^0.5 (lazy
+//     max, below) and its row sums taken on the matrix core; 32x32x64 FP8
+//     MFMAs.
 //   F16: K~, V~ = e2m1 * s_block exactly (at most 6 significant bits,
 //     magnitudes 2^-10 .. 2688); Q = F16(q * 2^shift_row) (exact for bf16
 //     input in range); P = F16(p); 32x32x16 f16 MFMAs at half the FP8 rate.
@@ -33,19 +36,17 @@
 namespace nvfp4 {
 
 constexpr int kTile = kPrefillTile;      // 64 keys
+typedef short short2v __attribute__((vector_size(4)));
 
 template <int MODE> struct Prec;
 template <> struct Prec<kPrefillFP8> {
   static constexpr int EB = 1;                       // bytes per operand element
   static constexpr float kExpand = 0.125f;           // K~, V~ carry 2^-3
-  static constexpr int kQTop = 7;                    // |q| 2^shift in [2^7, 2^8)
-  static constexpr float kPLog2 = 8.0f;              // P carries 2^8
 };
 template <> struct Prec<kPrefillF16> {
   static constexpr int EB = 2;
   static constexpr float kExpand = 1.0f;
   static constexpr int kQTop = 14;                   // |q| 2^shift in [2^14, 2^15)
-  static constexpr float kPLog2 = 0.0f;
 };
 
 // Position of key kk (0..63) of a tile inside a V~^T row.
@@ -181,7 +182,8 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
   // ---- Q^T operand: lane (row n, half h) holds q[64h + e], e = 0..63, in
   // operand order (byte e for FP8, half e for F16)
   uint32_t qw[16 * EB];
-  float rowscale;
+  float rowscale = 1.0f;    // F16: scores * rowscale are in log2 units
+  int qscale = 127;         // FP8: E8M0 scale of the Q' operand
   {
     float qv[64];
     if (row_ok) {
@@ -212,16 +214,28 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(qv[i]));
     amax = max_across_halves(amax);
-    int shift = amax > 0.0f ? P::kQTop - ilogbf(amax) : 0;
-    shift = max(-120, min(120, shift));
-    rowscale = ldexpf(1.0f, -shift) / P::kExpand * p.k_scale * p.softmax_scale * 1.4426950408889634f;
+    // score scale: (q . K~) * c is the score in log2 units
+    const float c = p.k_scale * p.softmax_scale * 1.4426950408889634f / P::kExpand;
+    if constexpr (MODE == kPrefillFP8) {
+      // Q' = E4M3(q c 2^-(ea + ec - 6)) with the row maximum in [64, 256);
+      // the MFMA's per-row E8M0 scale on Q' gives back 2^(ea + ec - 6), so
+      // the scores come out of the MFMA in log2 units
+      const int ea = amax > 0.0f ? ilogbf(amax) : 0;
+      const int ec = c > 0.0f ? ilogbf(c) : 0;
+      const float cn = c > 0.0f ? ldexpf(c, 6 - ec) : 0.0f;
+      qscale = 127 + max(-127, min(127, ea + ec - 6));
 #pragma unroll
-    for (int w = 0; w < 16 * EB; ++w) {
-      if (MODE == kPrefillFP8) {
+      for (int w = 0; w < 16; ++w) {
         const float* v = qv + 4 * w;
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], shift), ldexpf(v[1], shift), 0, false);
-        qw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], shift), ldexpf(v[3], shift), lo, true);
-      } else {
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -ea) * cn, ldexpf(v[1], -ea) * cn, 0, false);
+        qw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -ea) * cn, ldexpf(v[3], -ea) * cn, lo, true);
+      }
+    } else {
+      int shift = amax > 0.0f ? P::kQTop - ilogbf(amax) : 0;
+      shift = max(-120, min(120, shift));
+      rowscale = ldexpf(c, -shift);
+#pragma unroll
+      for (int w = 0; w < 32; ++w) {
         const float* v = qv + 2 * w;
         qw[w] = encode<MODE>(ldexpf(v[0], shift)) | (encode<MODE>(ldexpf(v[1], shift)) << 16);
       }
@@ -240,50 +254,48 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
 
   // tile loads: K~ chunk c = key c/(8 EB), 16 bytes at (c % (8 EB)) * 16;
   // V~^T chunk c = d c/(4 EB), 16 bytes at (c % (4 EB)) * 16
-  auto gload = [&](int tile, u32x4 r[2 * CPT]) {
+  auto gload_k = [&](int tile, u32x4 r[CPT]) {
     const uint8_t* kt = kx + (size_t)tile * kTile * kD * EB;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(kt + (tid + 256 * i) * 16);
+  };
+  auto gload_v = [&](int tile, u32x4 r[CPT]) {
     const uint8_t* vt = vx + (size_t)tile * kD * kTile * EB;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      r[i] = *reinterpret_cast<const u32x4*>(kt + (tid + 256 * i) * 16);
-      r[CPT + i] = *reinterpret_cast<const u32x4*>(vt + (tid + 256 * i) * 16);
-    }
+    for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(vt + (tid + 256 * i) * 16);
   };
-  auto sstore = [&](int buf, const u32x4 r[2 * CPT]) {
+  auto sstore_k = [&](int buf, const u32x4 r[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
       *reinterpret_cast<u32x4*>(&ks[buf][(c / (8 * EB)) * KROW + (c % (8 * EB)) * 16]) = r[i];
-      *reinterpret_cast<u32x4*>(&vs[buf][(c / (4 * EB)) * VROW + (c % (4 * EB)) * 16]) = r[CPT + i];
+    }
+  };
+  auto sstore_v = [&](int buf, const u32x4 r[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(&vs[buf][(c / (4 * EB)) * VROW + (c % (4 * EB)) * 16]) = r[i];
     }
   };
 
-  floatx16 acc_o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.0f;
-  // the reference max starts finite and far below any score, so that keys
-  // masked to -inf give p = 0, never NaN
-  float m_ref = -1.0e30f, l_run = 0.0f;
+  // FP8: the score MFMAs start from -bias (an integer per row, 0 at first),
+  // so s and the reference max m are relative to it.  The rescale keeps
+  // |m| <= 100, moving the bias when needed; exponentials are then taken of
+  // s itself (2^s neither overflows nor loses a weight above 2^-26 of the
+  // row max) and the conversion to E4M3 divides by 2^(m - 8).
+  float bias = 0.0f;
+  floatx16 cbias = {};
+  float pscale = 0x1p-8f;
 
-  u32x4 pre[2 * CPT];
-  if (ntiles > 0) {
-    gload(0, pre);
-    sstore(0, pre);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1, pre);
-
-    // ---- S^T for the two 32-key blocks
-    floatx16 s[2];
+  // ---- S^T of the tile in ks[buf], two 32-key blocks
+  auto qk = [&](int buf, floatx16 s[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const uint8_t* kr = &ks[buf][(kb * 32 + n) * KROW + h * 64 * EB];
-      floatx16 c = {};
-      if (MODE == kPrefillFP8) {
+      floatx16 c;
+      if constexpr (MODE == kPrefillFP8) {
+        c = cbias;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           intx8 a, b;
@@ -291,9 +303,10 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
           for (int w = 0; w < 8; ++w) b[w] = (int)qw[8 * i + w];
           *reinterpret_cast<u32x4*>(&a) = *reinterpret_cast<const u32x4*>(kr + 32 * i);
           *(reinterpret_cast<u32x4*>(&a) + 1) = *reinterpret_cast<const u32x4*>(kr + 32 * i + 16);
-          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, qscale);
         }
       } else {
+        c = floatx16{};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const u32x4 av = *reinterpret_cast<const u32x4*>(kr + 16 * i);
@@ -304,65 +317,19 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
       }
       s[kb] = c;
     }
-    // ---- mask and row max on the raw scores (the row scale is positive and
-    // is applied inside the exponent below)
-    const int kbase = t * kTile;
-    const bool need_mask = t >= mask_from || kbase + kTile > kv_len;
-    if (need_mask) {
-      // this lane's keys are kbase + 4h + off with off = kb*32 + 8*(r/4) + r%4
-      const int klim = min(lim, kv_len - 1) - kbase - 4 * h;
+  };
+
+  floatx16 acc_o[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
-          s[kb][r] = off <= klim ? s[kb][r] : -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_across_halves(mx) * rowscale;
-    // lazy max: rescale only when the row max grows by more than 0.5 (log2),
-    // which keeps p <= 2^0.5 (p * 2^8 stays inside E4M3's range)
-    const bool grow = mx > m_ref + 0.5f;
-    if (__any(grow)) {
-      const float m_new = grow ? mx : m_ref;
-      const float alpha = fast_exp2(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc_o[i] *= alpha;
-    }
-    // ---- P^T = 2^(s * rowscale - m + kPLog2) and the row sum (the common
-    // factor 2^kPLog2 of P and of the sum cancels in O / l)
-    const float cexp = P::kPLog2 - m_ref;
-    uint32_t pw[8 * EB];
-    float lsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int kb = w >> 2, r0 = (w & 3) * 4;
-      const float e0 = fast_exp2(fmaf(s[kb][r0], rowscale, cexp));
-      const float e1 = fast_exp2(fmaf(s[kb][r0 + 1], rowscale, cexp));
-      const float e2 = fast_exp2(fmaf(s[kb][r0 + 2], rowscale, cexp));
-      const float e3 = fast_exp2(fmaf(s[kb][r0 + 3], rowscale, cexp));
-      lsum += (e0 + e1) + (e2 + e3);
-      if (MODE == kPrefillFP8) {
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-        pw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, lo, true);
-      } else {
-        pw[2 * w] = encode<MODE>(e0) | (encode<MODE>(e1) << 16);
-        pw[2 * w + 1] = encode<MODE>(e2) | (encode<MODE>(e3) << 16);
-      }
-    }
-    l_run += lsum;
-    // ---- O^T += V~^T P^T
+    for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.0f;
+  // ---- O^T += V~^T P^T with the tile in vs[buf]
+  auto pv = [&](int buf, const uint32_t pw[8 * EB]) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const uint8_t* vr = &vs[buf][(db * 32 + n) * VROW];
-      if (MODE == kPrefillFP8) {
+      if constexpr (MODE == kPrefillFP8) {
         intx8 a, b;
 #pragma unroll
         for (int w = 0; w < 8; ++w) b[w] = (int)pw[w];
@@ -379,12 +346,204 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
         }
       }
     }
-    if (t + 1 < ntiles) sstore(buf ^ 1, pre);
+  };
+
+  // the reference max starts finite and far below any score, so that keys
+  // masked to -inf give p = 0, never NaN
+  float m_ref = -1.0e30f, l_run = 0.0f;
+  // FP8: the row sum of P accumulates on the matrix core.  A 16x16x128 MFMA
+  // with P^T as its B operand and a 0/1 A operand: B column c gathers the
+  // lanes c, c+16, c+32, c+48 (rows c and c+16, both key halves); A rows 0
+  // and 8 select the key blocks of row c, rows 4 and 12 those of row c+16,
+  // so result element 0 of every lane is the sum of its own row.
+  floatx4 acc_l = {0.0f, 0.0f, 0.0f, 0.0f};
+  intx8 ones;
+  {
+    const int i = lane & 15, g = lane >> 4;
+    const bool one = ((i == 0 || i == 8) && !(g & 1)) || ((i == 4 || i == 12) && (g & 1));
+#pragma unroll
+    for (int w = 0; w < 8; ++w) ones[w] = one ? 0x38383838 : 0;   // E4M3 1.0
+  }
+
+  // ---- mask (diagonal and tail tiles), row max and the lazy rescale (FP8:
+  // on log2 scores; F16: on raw scores, the positive row scale being
+  // applied inside the exponent)
+  auto row_max = [&](int t, floatx16 s[2]) {
+    const int kbase = t * kTile;
+    if (t >= mask_from || kbase + kTile > kv_len) {
+      // this lane's keys are kbase + 4h + off with off = kb*32 + 8*(r/4) + r%4
+      const int klim = min(lim, kv_len - 1) - kbase - 4 * h;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = off <= klim ? s[kb][r] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    return max_across_halves(mx) * rowscale;
+  };
+  // lazy max: rescale only when the row max grows by more than 0.5 (log2),
+  // which keeps p <= 2^0.5 (p * 2^8 stays inside E4M3's range)
+  auto rescale = [&](float mx, floatx16 s[2]) {
+    const bool grow = mx > m_ref + 0.5f;
+    if (__any(grow)) {
+      // FP8 keeps the reference max an integer (the conversion scale is a
+      // power of two); m >= mx - 0.5 keeps p <= 2^0.5 on this tile too
+      const float m_new = grow ? (MODE == kPrefillFP8 ? ceilf(mx - 0.5f) : mx) : m_ref;
+      const float alpha = fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
+      acc_l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_o[i] *= alpha;
+      if constexpr (MODE == kPrefillFP8) {
+        // move the bias of rows whose max left [-100, 100] (a row still at
+        // the initial reference has seen no key yet and keeps it)
+        const float shift = (fabsf(m_ref) > 100.0f && m_ref > -1.0e29f) ? m_ref : 0.0f;
+        if (__any(shift != 0.0f)) {
+          bias += shift;
+          m_ref -= shift;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            cbias[r] = -bias;
+            s[0][r] -= shift;
+            s[1][r] -= shift;
+          }
+        }
+        pscale = ldexpf(1.0f, (int)fminf(fmaxf(m_ref, -100.0f), 100.0f) - 8);
+      }
+    }
+  };
+  // ---- P^T and the row sum
+  auto probs = [&](const floatx16 s[2], uint32_t pw[8 * EB]) {
+    if constexpr (MODE == kPrefillFP8) {
+      // P^T = E4M3(2^(s - m + 8)); the factor 2^8 cancels in O / l
+      auto conv = [&](float e0, float e1, float e2, float e3) {
+        const short2v lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(short2v{0, 0}, e0, e1, pscale, false);
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, e2, e3, pscale, true));
+      };
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2, r0 = (w & 3) * 4;
+        pw[w] = conv(fast_exp2(s[kb][r0]), fast_exp2(s[kb][r0 + 1]),
+                     fast_exp2(s[kb][r0 + 2]), fast_exp2(s[kb][r0 + 3]));
+      }
+      intx8 b;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) b[w] = (int)pw[w];
+      acc_l = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, b, acc_l, 0, 0, 0, 127, 0, 127);
+    } else {
+      // P^T = 2^(s * rowscale - m)
+      const float cexp = -m_ref;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2, r0 = (w & 3) * 4;
+        const float e0 = fast_exp2(fmaf(s[kb][r0], rowscale, cexp));
+        const float e1 = fast_exp2(fmaf(s[kb][r0 + 1], rowscale, cexp));
+        const float e2 = fast_exp2(fmaf(s[kb][r0 + 2], rowscale, cexp));
+        const float e3 = fast_exp2(fmaf(s[kb][r0 + 3], rowscale, cexp));
+        lsum += (e0 + e1) + (e2 + e3);
+        pw[2 * w] = encode<MODE>(e0) | (encode<MODE>(e1) << 16);
+        pw[2 * w + 1] = encode<MODE>(e2) | (encode<MODE>(e3) << 16);
+      }
+      l_run += lsum;
+    }
+  };
+
+  u32x4 rk[CPT], rv[CPT];
+  uint32_t pw[8 * EB];
+  if constexpr (MODE == kPrefillFP8) {
+    // Software pipeline, one step per tile t: the MFMAs of O += V~(t-1)
+    // P(t-1) run beside the row max of S(t), those of S(t+1) = K~(t+1) Q'^T
+    // beside the exponentials of S(t).  LDS holds K~(t+1) in ks[(t+1)&1] and
+    // V~(t-1) in vs[(t-1)&1] while step t stores K~(t+2) into ks[t&1] and
+    // V~(t) into vs[t&1]; one barrier per step.  Tile indices past the end
+    // are clamped, so the last step computes a score block it never uses.
+#pragma unroll
+    for (int w = 0; w < 8; ++w) pw[w] = 0u;                 // P(-1) = 0
+    floatx16 sa[2], sb[2];
+    auto step = [&](int t, floatx16 s_cur[2], floatx16 s_nxt[2]) {
+      const int b = t & 1;
+      gload_k(min(t + 2, ntiles - 1), rk);
+      gload_v(t, rv);
+      const float mx = row_max(t, s_cur);
+      pv(b ^ 1, pw);
+      rescale(mx, s_cur);
+      qk(b ^ 1, s_nxt);
+      probs(s_cur, pw);
+      // keep this step's products here (the compiler otherwise sinks them
+      // past the barrier, behind the exponentials) and interleave the MFMAs
+      // of S(t+1) with the exponent-side VALU work
+#pragma unroll
+      for (int w = 0; w < 8; ++w) asm volatile("" ::"v"(pw[w]));
+      asm volatile("" ::"v"(s_nxt[0]), "v"(s_nxt[1]), "v"(acc_l));
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      sstore_k(b, rk);
+      sstore_v(b, rv);
+      __syncthreads();
+    };
+    if (ntiles > 0) {
+      // prologue: S(0) from K~(0); K~(1) into ks[1]; vs[1] zeroed for the
+      // product with P(-1) = 0
+      gload_k(0, rk);
+      sstore_k(0, rk);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) rv[i] = u32x4{0u, 0u, 0u, 0u};
+      sstore_v(1, rv);
+      gload_k(min(1, ntiles - 1), rk);
+      __syncthreads();
+      qk(0, sa);
+      sstore_k(1, rk);
+      __syncthreads();
+      for (int t = 0; t < ntiles; t += 2) {
+        step(t, sa, sb);
+        if (t + 1 < ntiles) step(t + 1, sb, sa);
+      }
+      pv((ntiles - 1) & 1, pw);                            // O += V~(last) P(last)
+    }
+  } else {
+    // one tile per iteration, the next tile's loads in flight
+    if (ntiles > 0) {
+      gload_k(0, rk);
+      gload_v(0, rv);
+      sstore_k(0, rk);
+      sstore_v(0, rv);
+    }
     __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < ntiles) {
+        gload_k(t + 1, rk);
+        gload_v(t + 1, rv);
+      }
+      floatx16 s[2];
+      qk(buf, s);
+      rescale(row_max(t, s), s);
+      probs(s, pw);
+      pv(buf, pw);
+      if (t + 1 < ntiles) {
+        sstore_k(buf ^ 1, rk);
+        sstore_v(buf ^ 1, rv);
+      }
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O / l * s_tV, removing the operand scale factors
-  const float l_tot = sum_across_halves(l_run);
+  const float l_tot = MODE == kPrefillFP8 ? acc_l[0] : sum_across_halves(l_run);
   if (row_ok) {
     const float f = l_tot > 0.0f ? p.v_scale / P::kExpand / l_tot : 0.0f;
     float* o = p.out + ((size_t)qi * p.hq + head) * kD;

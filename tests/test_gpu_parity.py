@@ -304,8 +304,24 @@ def _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, causal):
     return ref, mag
 
 
+def _prefill_check(out, ref, mag, mode):
+    """FP8 operands: the local bound above and the L2 gate; exact 16-bit
+    operands (only P rounded, 2^-11 relative): the decode gate."""
+    err = np.abs(out.astype(np.float64) - ref)
+    if mode == api.PREFILL_FP8:
+        bound = TOL * np.maximum(1.0, np.abs(ref)) + FP8_LOCAL * mag
+    else:
+        bound = TOL * np.maximum(1.0, np.abs(ref))
+    ok, st = compare(out, ref)
+    say("   ", st, "worst err/bound", float((err / bound).max()))
+    assert np.all(np.isfinite(out)) and np.all(err <= bound), float((err / bound).max())
+    if mode == api.PREFILL_FP8:
+        assert st["rel_l2"] < FP8_REL_L2, st
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["fp8", "f16"])
 @pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"p{c[0]}-T{c[1]}-G{c[2] // c[3]}-c{int(c[4])}")
-def test_prefill_parity_small(orc, case):
+def test_prefill_parity_small(orc, case, mode):
     prefix, T, Hq, Hkv, causal = case
     pw = W.small_prefill(prefix, T, Hq, Hkv, seed_cfg=600 + prefix + T)
     kp, vp = pw.prefix_kv()
@@ -321,15 +337,41 @@ def test_prefill_parity_small(orc, case):
     api.append(cache, to_dev(k, "bf16"), to_dev(v, "bf16"), i32(np.zeros(total)), i32(np.arange(total)),
                i32(perm[None]))
     q = pw.q()
-    say(f"prefill {case}: attention")
-    out = api.prefill(cache, to_dev(q, "bf16"), i32(perm), prefix, causal=causal).cpu().numpy()
+    say(f"prefill {case} mode {mode}: attention")
+    out = api.prefill(cache, to_dev(q, "bf16"), i32(perm), prefix, causal=causal, mode=mode).cpu().numpy()
     ref, mag = _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, causal)
-    err = np.abs(out.astype(np.float64) - ref)
-    bound = TOL * np.maximum(1.0, np.abs(ref)) + FP8_LOCAL * mag
-    ok, st = compare(out, ref)
-    say("   ", st, "worst err/bound", float((err / bound).max()))
-    assert np.all(np.isfinite(out)) and np.all(err <= bound), float((err / bound).max())
-    assert st["rel_l2"] < FP8_REL_L2, st
+    _prefill_check(out, ref, mag, mode)
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["fp8", "f16"])
+@pytest.mark.parametrize("pattern", ["mixed", "low", "high"])
+def test_prefill_score_range(orc, mode, pattern):
+    """Scores of about +-300 in log2 units: every key is +u or -u (u all ones)
+    and q = a u, so a row's softmax is uniform over its visible keys of the
+    larger score whatever the operand rounding.  mixed: the first 64-key tile
+    holds only low-score keys, so the reference max first settles near -300
+    and then jumps by about 600 (the FP8 path moves its score bias twice);
+    low / high: every score near -300 / +300."""
+    prefix, T, Hq, Hkv = 200, 50, 8, 2
+    total = prefix + T
+    rng = np.random.default_rng(77)
+    t = np.arange(total)
+    hi = {"mixed": (t >= 64) & (t % 3 != 0), "low": t < 0, "high": t >= 0}[pattern]
+    s_key = np.where(hi, 1.0, -1.0)
+    k = np.repeat(s_key[:, None, None], Hkv, axis=1) * np.ones((1, 1, 128))
+    v = rng.standard_normal((total, Hkv, 128))
+    q = np.full((T, Hq, 128), 18.5)
+    k, v, q = (x.astype(np.float32) for x in (k, v, q))
+    stk, stv = orc.tensor_scale(k), orc.tensor_scale(v)
+    npages = -(-total // 16)
+    cache = api.KVCache(npages, Hkv, stk, stv, fill=0)
+    pt = np.arange(npages, dtype=np.int32)
+    api.append(cache, to_dev(k, "bf16"), to_dev(v, "bf16"), i32(np.zeros(total)), i32(np.arange(total)),
+               i32(pt[None]))
+    say(f"prefill score range {pattern} mode {mode}")
+    out = api.prefill(cache, to_dev(q, "bf16"), i32(pt), prefix, causal=True, mode=mode).cpu().numpy()
+    ref, mag = _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, True)
+    _prefill_check(out, ref, mag, mode)
 
 
 # ------------------------------------------------ full-size configurations
