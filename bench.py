@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "NVFP4-KV decode attention HBM GB/s (% of peak) + append quantize GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense FP16 MFMA
 BYTES_PER_TOKEN_HEAD = 2 * 128 * 0.5625   # K and V, codes + scales
 
 
@@ -102,8 +103,12 @@ def cpu_baseline(w, data, s_tk, s_tv, q, threads):
                       f"{nbytes / 1e6:.1f} MB of NVFP4 cache), without the append"}
 
 
-def bench_prefill(api, torch, stream, iters=3):
+def bench_prefill(api, torch, stream, iters=3, modes=None):
+    """Chunked prefill at its full size: the chunk's bulk append and the
+    attention, once per operand mode (FP8 as in the pages' flow, then exact
+    16-bit operands)."""
     from decode_attention_nvfp4_amd import workloads as W
+    modes = [api.PREFILL_FP8, api.PREFILL_F16] if modes is None else modes
     pw = W.PrefillWorkload()
     kp, vp = pw.prefix_kv()
     kc, vc = pw.chunk_kv()
@@ -118,27 +123,38 @@ def bench_prefill(api, torch, stream, iters=3):
     seq, pos = i32(np.zeros(pw.T)), i32(pw.prefix + np.arange(pw.T))
     q = dev(pw.q())
     out = torch.empty((pw.T, pw.Hq, 128), dtype=torch.float32, device="cuda")
-    ws = torch.empty(api.prefill_workspace_bytes(pw.T, pw.Hq, pw.Hkv, pw.prefix), dtype=torch.uint8,
-                     device="cuda")
 
     def chunk_append():
         api.append(cache, kcd, vcd, seq, pos, pt)
 
-    def attend():
-        api.prefill(cache, q, pt[0], pw.prefix, causal=True, workspace=ws, out=out)
-
-    chunk_append(); attend()
+    chunk_append()
     torch.cuda.synchronize()
     t_app = time_region(torch, chunk_append, iters, stream)
-    t_att = time_region(torch, attend, iters, stream)
-    flops = 4.0 * 128 * pw.Hq * sum(pw.prefix + i + 1 for i in range(pw.T))
     app_bytes = pw.T * pw.Hkv * 128 * 2 * (2 + 0.5625)
-    return {
+    flops = 4.0 * 128 * pw.Hq * sum(pw.prefix + i + 1 for i in range(pw.T))
+    res = {
         "workload": "chunked prefill: 2048 causal queries after a 32768-token NVFP4 prefix, 64 q / 8 kv heads",
-        "attention_ms": round(t_att, 4), "tflops": round(flops / t_att / 1e9, 2),
-        "frac_fp8_peak": round(flops / t_att / 1e9 / FP8_PEAK_TFLOPS, 4),
         "chunk_append_ms": round(t_app, 4), "chunk_append_gbs": round(app_bytes / t_app / 1e6, 1),
     }
+    for mode in modes:
+        ws = torch.empty(api.prefill_workspace_bytes(pw.T, pw.Hq, pw.Hkv, pw.prefix, mode), dtype=torch.uint8,
+                         device="cuda")
+
+        def attend():
+            api.prefill(cache, q, pt[0], pw.prefix, causal=True, workspace=ws, out=out, mode=mode)
+
+        attend()
+        torch.cuda.synchronize()
+        t_att = time_region(torch, attend, iters, stream)
+        tf = flops / t_att / 1e9
+        if mode == api.PREFILL_FP8:
+            res.update({"attention_ms": round(t_att, 4), "tflops": round(tf, 2),
+                        "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)})
+        else:
+            res["f16_operands"] = {"attention_ms": round(t_att, 4), "tflops": round(tf, 2),
+                                   "frac_f16_peak": round(tf / F16_PEAK_TFLOPS, 4)}
+        del ws
+    return res
 
 
 def stream_read_probe(api, torch, stream, gib=1, iters=10):
@@ -297,6 +313,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed steps, copy this many MiB device to device three times "
                          "(the calibration kernel of the HBM traffic counters)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the chunked prefill (both operand modes) and print its record; "
+                         "a profiling entry, not the benchmark line")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the decode traffic record from two rocprofv3 --pmc outputs "
                          "(FETCH_SIZE, then WRITE_SIZE) of a run with --copy-mib, then exit")
@@ -317,6 +336,10 @@ def main():
     torch.cuda.init()
     stream = torch.cuda.current_stream()
     threads = min(16, os.cpu_count() or 1)
+    if args.prefill_only:
+        print(json.dumps({"prefill_cfg5": bench_prefill(api, torch, stream, iters=max(1, args.steps))}),
+              flush=True)
+        return
 
     # ---- workload: paged large-batch decode
     t0 = time.time()
