@@ -32,8 +32,8 @@
 //     scale) to the A operand of eight 16x16x16 f16 MFMAs
 //     O^T[d][head] += V^T P^T with d = 8m + tile.  P^T comes straight from
 //     the S^T accumulator layout.
-// Pages stream through a 4-stage register pipeline (loads of page t+3 in
-// flight while page t is computed).
+// Pages stream through a kDepth-stage register pipeline (loads of pages
+// t+1 .. t+kDepth-1 in flight while page t is computed).
 #include <atomic>
 
 #include "common.h"
@@ -312,8 +312,13 @@ __device__ __forceinline__ uint32_t prepare_block(const DecodeArgs& p, SegPos& w
   return slab;
 }
 
+// Register stages of the page pipeline; the planner runs two waves per SIMD,
+// so the register budget is that of two waves.
+constexpr int kDepth = 8;
+static_assert(64 % kDepth == 0, "block switches must fall on a stage boundary");
+
 template <bool F32Q>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(F32Q ? 3 : 4, 8))) decode_kernel(DecodeArgs p) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) decode_kernel(DecodeArgs p) {
   const int lane = threadIdx.x;
   const int col = lane & 15, kg = lane >> 4;
   const int wave = blockIdx.x, W = gridDim.x;
@@ -419,11 +424,13 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(F32Q ? 
     }
   };
 
-  PageRegs r0, r1, r2, r3;
-  issue(r0, 0);
-  issue(r1, 1);
-  issue(r2, 2);
-  for (int t = 0; t < N; t += 4) {
+  // kDepth register stages: the loads of the next kDepth - 1 pages are in
+  // flight while a page is processed (kDepth divides 64, so block switches
+  // fall on stage 0)
+  PageRegs r[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) issue(r[i], i);
+  for (int t = 0; t < N; t += kDepth) {
     if (t == base + 64) {                  // the next block becomes current
       cur = nxt;
       base += 64;
@@ -432,25 +439,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(F32Q ? 
         prepared += min(64, N - prepared);
       }
     }
-    issue(r3, t + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    step(r0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (t + 1 >= N) break;
-    issue(r0, t + 4);
-    __builtin_amdgcn_sched_barrier(0);
-    step(r1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (t + 2 >= N) break;
-    issue(r1, t + 5);
-    __builtin_amdgcn_sched_barrier(0);
-    step(r2);
-    __builtin_amdgcn_sched_barrier(0);
-    if (t + 3 >= N) break;
-    issue(r2, t + 6);
-    __builtin_amdgcn_sched_barrier(0);
-    step(r3);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      if (j > 0 && t + j >= N) break;
+      issue(r[(j + kDepth - 1) % kDepth], t + j + kDepth - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      step(r[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -465,32 +461,54 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(F32Q ? 
 // elements 4e .. 4e + 3, so all partial loads are independent; the PL piece
 // lanes are combined in LDS.  PL = 8 when segments have many pieces (few
 // long sequences), else 2 (one wave per head).
+// Waves owning unit range ends: w0 owns unit a, w1 unit end - 1, and
+// start(w) = w U / W.  I is uint32_t when every product stays below 2^32 (the
+// usual case: 64-bit division is a long software sequence), else int64_t.
+template <typename I>
+struct RangeMath {
+  I U, W;
+  __device__ int owner(long long u) const { return (int)((I)((I)(u + 1) * W - 1) / U); }
+  __device__ long long start(int w) const { return (long long)((I)((I)w * U) / W); }
+};
+
+template <int PL, typename I>
+__device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMath<I> rm, long long a,
+                                              long long end, int g, float* out);
+
 template <int PL>
 __global__ void __launch_bounds__(32 * PL) merge_kernel(DecodeArgs p) {
   const int g = blockIdx.x % p.group;
   const int seg = blockIdx.x / p.group;
   const int b = seg / p.hkv, kvh = seg % p.hkv;
-  const int tid = threadIdx.x, pi = tid >> 5, e = tid & 31;
-  const int W = p.num_splits, G = p.group;
   const int pb = p.ws_prefix[b], np = p.ws_prefix[b + 1] - pb;
   const long long U = (long long)p.ws_prefix[p.batch] * p.hkv;
-  float* out = p.out + ((size_t)b * p.hq + (size_t)kvh * G + g) * kD;
+  float* out = p.out + ((size_t)b * p.hq + (size_t)kvh * p.group + g) * kD;
   if (np == 0) {
-    if (tid < 32) reinterpret_cast<float4*>(out)[tid] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (threadIdx.x < 32) reinterpret_cast<float4*>(out)[threadIdx.x] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     return;
   }
   const long long a = (long long)pb * p.hkv + (long long)kvh * np;
-  const long long end = a + np;
-  const int w0 = (int)(((a + 1) * W - 1) / U);
-  const int w1 = (int)((end * W - 1) / U);
+  if (U * (long long)p.num_splits < (1LL << 32))
+    merge_segment<PL>(p, RangeMath<uint32_t>{(uint32_t)U, (uint32_t)p.num_splits}, a, a + np, g, out);
+  else
+    merge_segment<PL>(p, RangeMath<long long>{U, (long long)p.num_splits}, a, a + np, g, out);
+}
+
+template <int PL, typename I>
+__device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMath<I> rm, long long a,
+                                              long long end, int g, float* out) {
+  const int tid = threadIdx.x, pi = tid >> 5, e = tid & 31;
+  const int G = p.group;
+  const int w0 = rm.owner(a);
+  const int w1 = rm.owner(end - 1);
   if (w0 == w1) return;                       // finished by one wave
   const int n = w1 - w0 + 1;
-  auto start = [&](int w) { return (long long)w * U / W; };
   // the piece of wave w0 + i: its workspace index, or -1 when w wrote none
   auto piece = [&](int i) -> int {
     const int w = w0 + i;
-    if (start(w) == start(w + 1)) return -1;
-    const int slot = start(w) >= a ? 0 : 1;
+    const long long sw = rm.start(w);
+    if (sw == rm.start(w + 1)) return -1;
+    const int slot = sw >= a ? 0 : 1;
     return (w * 2 + slot) * G + g;
   };
   // each thread merges its pieces online (running max m, rescaling as it
