@@ -20,9 +20,10 @@
 // once instead of once per query tile; the attention kernel (fa_kernel) then
 // streams 64-key tiles through LDS, double-buffered.
 //
-// fa_kernel: a 256-thread workgroup owns 128 consecutive (query, head) rows of
+// fa_kernel: a 512-thread workgroup owns 256 consecutive (query, head) rows of
 // one KV head (row r = query r / G, head r % G), 32 per wave (lane n = row,
-// lane half h).  Per 64-key tile and wave:
+// lane half h), in two groups of four waves that alternate between matrix
+// and softmax work (see the main loop).  Per 64-key tile and wave:
 //   S^T[key][row] = K~ Q^T over two 32-key blocks (the contraction over d is
 //     permuted identically in K~ and Q: lane half h holds d in [64h, 64h+64)).
 //   softmax over keys: each lane holds 32 keys of one row, the other 32 sit in
@@ -30,6 +31,8 @@
 //   O^T[d][row] += V~^T P^T: P^T is the S^T accumulator converted in place,
 //     so the key order inside a tile follows the accumulator layout
 //     (vt_pos below), which the V~ workspace matches.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -156,20 +159,22 @@ __global__ void __launch_bounds__(256) expand_kernel(PrefillArgs p) {
 }
 
 template <int MODE, bool F32Q>
-__global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
+__global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   using P = Prec<MODE>;
   constexpr int EB = P::EB;
   constexpr int KROW = kD * EB + 16;        // LDS bytes per K~ row (padded)
   constexpr int VROW = kTile * EB + 16;     // LDS bytes per V~^T row (padded)
+  constexpr int NT = 512;                   // threads: 8 waves of 32 rows
+  constexpr int ROWS = NT / 2;              // (query, head) rows per workgroup
   constexpr int NCH = 512 * EB;             // 16-byte chunks per operand tile
-  constexpr int CPT = NCH / 256;            // chunks per thread per operand
+  constexpr int CPT = NCH / NT;             // chunks per thread per operand
 
   const int nrows = p.T * p.group;
   const int kvh = blockIdx.x % p.hkv;       // one KV head's row tiles land on the same XCD
   const int rt = blockIdx.x / p.hkv;        // when Hkv divides the 8 XCDs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int n = lane & 31, h = lane >> 5;
-  const int row0 = rt * 128;
+  const int row0 = rt * ROWS;
   const int row = row0 + wave * 32 + n;
   const bool row_ok = row < nrows;
   const int qi = row_ok ? row / p.group : 0;
@@ -243,7 +248,7 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
   }
 
   // ---- key range of this workgroup
-  const int last_row = min(row0 + 127, nrows - 1);
+  const int last_row = min(row0 + ROWS - 1, nrows - 1);
   const int first_q = row0 / p.group, last_q = last_row / p.group;
   const int kv_len = p.causal ? min(p.total, p.prefix + last_q + 1) : p.total;
   const int ntiles = (kv_len + kTile - 1) / kTile;
@@ -257,24 +262,24 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
   auto gload_k = [&](int tile, u32x4 r[CPT]) {
     const uint8_t* kt = kx + (size_t)tile * kTile * kD * EB;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(kt + (tid + 256 * i) * 16);
+    for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(kt + (tid + NT * i) * 16);
   };
   auto gload_v = [&](int tile, u32x4 r[CPT]) {
     const uint8_t* vt = vx + (size_t)tile * kD * kTile * EB;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(vt + (tid + 256 * i) * 16);
+    for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(vt + (tid + NT * i) * 16);
   };
   auto sstore_k = [&](int buf, const u32x4 r[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       *reinterpret_cast<u32x4*>(&ks[buf][(c / (8 * EB)) * KROW + (c % (8 * EB)) * 16]) = r[i];
     }
   };
   auto sstore_v = [&](int buf, const u32x4 r[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NT * i;
       *reinterpret_cast<u32x4*>(&vs[buf][(c / (4 * EB)) * VROW + (c % (4 * EB)) * 16]) = r[i];
     }
   };
@@ -457,87 +462,82 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
     }
   };
 
-  u32x4 rk[CPT], rv[CPT];
+  u32x4 rk[CPT];
   uint32_t pw[8 * EB];
-  if constexpr (MODE == kPrefillFP8) {
-    // Software pipeline, one step per tile t: the MFMAs of O += V~(t-1)
-    // P(t-1) run beside the row max of S(t), those of S(t+1) = K~(t+1) Q'^T
-    // beside the exponentials of S(t).  LDS holds K~(t+1) in ks[(t+1)&1] and
-    // V~(t-1) in vs[(t-1)&1] while step t stores K~(t+2) into ks[t&1] and
-    // V~(t) into vs[t&1]; one barrier per step.  Tile indices past the end
-    // are clamped, so the last step computes a score block it never uses.
+  // Two wave groups in ping-pong: waves 0-3 (group A, rows 0-127) and 4-7
+  // (group B, rows 128-255) share each SIMD and the K~/V~ tiles.  Between
+  // workgroup barriers a group runs either its matrix interval for step t
+  // (S(t) = K~(t) Q'^T and O += V~(t-1) P(t-1)) or its softmax interval
+  // (P(t) from S(t)); B runs one interval behind A, so on every SIMD one
+  // wave feeds the matrix core while the other keeps the VALU busy.
+  // Interval k is step (k - g) / 2 of group g: a matrix interval when
+  // k - g is even.  K~(j) lives in ks[j&1] from interval 2j-1 on and is
+  // read in intervals 2j (A) and 2j+1 (B); V~(j) lives in vs[j&1] from
+  // interval 2j+1 on and is read in 2j+2 and 2j+3.  Each group stores its
+  // share of K~(t+1+g) and V~(t+g) in its softmax interval of step t, from
+  // registers loaded in its matrix interval of step t-1 (tile indices past
+  // the end are clamped for the loads and skipped for the stores).
+  const int grp = wave >> 2;
+  u32x4 stk[2][CPT], stv[2][CPT];
+  floatx16 sc[2];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) pw[w] = 0u;                 // P(-1) = 0
-    floatx16 sa[2], sb[2];
-    auto step = [&](int t, floatx16 s_cur[2], floatx16 s_nxt[2]) {
-      const int b = t & 1;
-      gload_k(min(t + 2, ntiles - 1), rk);
-      gload_v(t, rv);
-      const float mx = row_max(t, s_cur);
-      pv(b ^ 1, pw);
-      rescale(mx, s_cur);
-      qk(b ^ 1, s_nxt);
-      probs(s_cur, pw);
-      // keep this step's products here (the compiler otherwise sinks them
-      // past the barrier, behind the exponentials) and interleave the MFMAs
-      // of S(t+1) with the exponent-side VALU work
-#pragma unroll
-      for (int w = 0; w < 8; ++w) asm volatile("" ::"v"(pw[w]));
-      asm volatile("" ::"v"(s_nxt[0]), "v"(s_nxt[1]), "v"(acc_l));
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      sstore_k(b, rk);
-      sstore_v(b, rv);
+  for (int w = 0; w < 8 * EB; ++w) pw[w] = 0u;
+  auto tcl = [&](int t) { return min(max(t, 0), ntiles - 1); };
+  // matrix interval of step t (0 .. ntiles) and softmax interval of step t
+  // (-1 .. ntiles) of group G; the staging set is t & 1, a constant in the
+  // unrolled loop below (a run-time index would make the stores wait for
+  // the loads just issued)
+  auto matrix = [&](auto G, auto B, int t) {
+    gload_k(tcl(t + 2 + G()), stk[B()]);
+    gload_v(tcl(t + 1 + G()), stv[B()]);
+    if (t < ntiles) qk(B(), sc);
+    if (t > 0 && t <= ntiles) pv(B() ^ 1, pw);   // the last product is O += V~(ntiles-1) P
+  };
+  auto soft = [&](auto G, auto B, int t) {   // B = (t - 1) & 1, the set to store
+    if (t >= 0 && t < ntiles) {
+      rescale(row_max(t, sc), sc);
+      probs(sc, pw);
+    }
+    const int tk = t + 1 + G(), tv = t + G();
+    if (tk < ntiles) sstore_k(tk & 1, stk[B()]);
+    if (tv >= 0 && tv < ntiles) sstore_v(tv & 1, stv[B()]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  gload_k(0, rk);
+  sstore_k(0, rk);
+  if (grp == 1) {                        // for its interval 0 (step -1)
+    gload_k(tcl(1), stk[0]);
+    gload_v(0, stv[0]);
+  }
+  gload_k(tcl(1 + grp), stk[1]);
+  gload_v(tcl(grp), stv[1]);
+  __syncthreads();
+  // 2 ntiles + 2 intervals, four per iteration (the last ones may idle);
+  // every wave passes the same barriers
+  const int iters = (2 * ntiles + 2 + 3) / 4;
+  if (grp == 0) {
+    for (int i = 0; i < iters; ++i) {
+      const int t = 2 * i;
+      matrix(I0{}, I0{}, t);
       __syncthreads();
-    };
-    if (ntiles > 0) {
-      // prologue: S(0) from K~(0); K~(1) into ks[1]; vs[1] zeroed for the
-      // product with P(-1) = 0
-      gload_k(0, rk);
-      sstore_k(0, rk);
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) rv[i] = u32x4{0u, 0u, 0u, 0u};
-      sstore_v(1, rv);
-      gload_k(min(1, ntiles - 1), rk);
+      soft(I0{}, I1{}, t);
       __syncthreads();
-      qk(0, sa);
-      sstore_k(1, rk);
+      matrix(I0{}, I1{}, t + 1);
       __syncthreads();
-      for (int t = 0; t < ntiles; t += 2) {
-        step(t, sa, sb);
-        if (t + 1 < ntiles) step(t + 1, sb, sa);
-      }
-      pv((ntiles - 1) & 1, pw);                            // O += V~(last) P(last)
+      soft(I0{}, I0{}, t + 1);
+      __syncthreads();
     }
   } else {
-    // one tile per iteration, the next tile's loads in flight
-    if (ntiles > 0) {
-      gload_k(0, rk);
-      gload_v(0, rv);
-      sstore_k(0, rk);
-      sstore_v(0, rv);
-    }
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < ntiles) {
-        gload_k(t + 1, rk);
-        gload_v(t + 1, rv);
-      }
-      floatx16 s[2];
-      qk(buf, s);
-      rescale(row_max(t, s), s);
-      probs(s, pw);
-      pv(buf, pw);
-      if (t + 1 < ntiles) {
-        sstore_k(buf ^ 1, rk);
-        sstore_v(buf ^ 1, rv);
-      }
+    for (int i = 0; i < iters; ++i) {
+      const int t = 2 * i;
+      soft(I1{}, I0{}, t - 1);
+      __syncthreads();
+      matrix(I1{}, I0{}, t);
+      __syncthreads();
+      soft(I1{}, I1{}, t);
+      __syncthreads();
+      matrix(I1{}, I1{}, t + 1);
       __syncthreads();
     }
   }
@@ -562,10 +562,11 @@ __global__ void __launch_bounds__(256) fa_kernel(PrefillArgs p) {
 template <int MODE>
 static void launch_mode(const PrefillArgs& a, bool f32_q, hipStream_t s) {
   expand_kernel<MODE><<<dim3(a.num_tiles, a.hkv), 256, 0, s>>>(a);
+  constexpr int NT = 512, ROWS = NT / 2;
   const int nrows = a.T * a.group;
-  const unsigned blocks = (unsigned)((nrows + 127) / 128) * a.hkv;
-  if (f32_q) fa_kernel<MODE, true><<<blocks, 256, 0, s>>>(a);
-  else fa_kernel<MODE, false><<<blocks, 256, 0, s>>>(a);
+  const unsigned blocks = (unsigned)((nrows + ROWS - 1) / ROWS) * a.hkv;
+  if (f32_q) fa_kernel<MODE, true><<<blocks, NT, 0, s>>>(a);
+  else fa_kernel<MODE, false><<<blocks, NT, 0, s>>>(a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s) {
