@@ -40,6 +40,12 @@
  *  - Dequantization multiplies by s_t, which is dividing by the global
  *    encode scale g = 1/s_t ([GB10] §這個 80 行的 Triton 繞道: the global
  *    scale must divide, not multiply).
+ *  - The comparison formats.  FP8 KV cache ([EXPL] and [TRTL] set NVFP4
+ *    against an FP8 cache without defining it): every element is the E4M3
+ *    value nearest to x / s_t8 (FP32 quotient), ties to the even code,
+ *    clamped to 448, with one FP32 scale per tensor s_t8 = amax(|X|) / 448;
+ *    dequantization multiplies by s_t8.  BF16 KV cache: the bf16 values
+ *    themselves.
  */
 #include <math.h>
 #include <stddef.h>
@@ -217,6 +223,48 @@ void orc_f32_to_bf16_array(const float* x, size_t n, uint16_t* out) {
   for (size_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(x[i]);
 }
 
+/* ------------------------------------------ FP8 comparison format (E4M3) */
+
+/* Tensor scale of the FP8 cache: amax / 448 in FP32. */
+float orc_fp8_tensor_scale_from_amax(float amax) { return amax / 448.0f; }
+
+/* FP8 code of x: v = x / s_t in FP32 (IEEE division), then the finite E4M3
+ * magnitude nearest to |v|, ties to the even code, clamped to 448 (code
+ * 0x7E); bit 7 is the sign of v.  Walks the 126 midpoints between
+ * consecutive codes; |v| and each midpoint are exact in double. */
+unsigned orc_fp8_code(float x, float s_t) {
+  float v = x / s_t;
+  unsigned sign = signbit(v) ? 0x80u : 0u;
+  double a = fabs((double)v);
+  unsigned code = 0;
+  for (unsigned k = 0; k < 126u; ++k) {
+    double mid = 0.5 * (orc_e4m3_value(k) + orc_e4m3_value(k + 1u));
+    if (a > mid) {
+      code = k + 1u;
+    } else {
+      if (a == mid) code = (k % 2u == 0u) ? k : k + 1u;
+      break;
+    }
+  }
+  return sign | code;
+}
+
+void orc_fp8_codes(const float* x, size_t n, float s_t, uint8_t* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = (uint8_t)orc_fp8_code(x[i], s_t);
+}
+
+/* Dequantized FP8 element: fl32(e4m3(code) * s_t); the product of a 4-bit
+ * and a 24-bit significand is exact in double, so one rounding.  Code 0x80
+ * gives -0.0. */
+float orc_fp8_value(unsigned code, float s_t) {
+  double m = orc_e4m3_value(code & 0x7Fu) * (double)s_t;
+  return (float)((code & 0x80u) ? -m : m);
+}
+
+void orc_fp8_dequant(const uint8_t* codes, size_t n, float s_t, float* out) {
+  for (size_t i = 0; i < n; ++i) out[i] = orc_fp8_value(codes[i], s_t);
+}
+
 /* ----------------------------------------------------------- attention */
 
 /* Softmax attention of Hq query rows over L tokens of an already dequantized
@@ -253,6 +301,15 @@ static void attend_dequantized(const float* q, int Hq, int Hkv, const float* kh,
     }
     for (int d = 0; d < ORC_D; ++d) out[(size_t)h * ORC_D + d] = (float)(num[d] / den);
   }
+}
+
+/* Attention over an already dequantized cache ([L][Hkv][128] FP32 each), as
+ * for the comparison formats: FP8 values after orc_fp8_dequant, BF16 values
+ * widened.  Returns 0. */
+int orc_attend_dense(const float* q, int Hq, int Hkv, const float* kh, const float* vh,
+                     int L, double scale, double* work, float* out) {
+  attend_dequantized(q, Hq, Hkv, kh, vh, L, scale, work, out);
+  return 0;
 }
 
 /* Attention of Hq query rows of one sequence over its first L cached tokens:

@@ -77,6 +77,19 @@ def lib():
                                            _u8p, _u8p, ctypes.c_float,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_double, _f64p, _f32p]
+            L.orc_fp8_tensor_scale_from_amax.restype = ctypes.c_float
+            L.orc_fp8_tensor_scale_from_amax.argtypes = [ctypes.c_float]
+            L.orc_fp8_code.restype = ctypes.c_uint
+            L.orc_fp8_code.argtypes = [ctypes.c_float, ctypes.c_float]
+            L.orc_fp8_codes.restype = None
+            L.orc_fp8_codes.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_float, _u8p]
+            L.orc_fp8_value.restype = ctypes.c_float
+            L.orc_fp8_value.argtypes = [ctypes.c_uint, ctypes.c_float]
+            L.orc_fp8_dequant.restype = None
+            L.orc_fp8_dequant.argtypes = [_u8p, ctypes.c_size_t, ctypes.c_float, _f32p]
+            L.orc_attend_dense.restype = ctypes.c_int
+            L.orc_attend_dense.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, _f32p, _f32p,
+                                           ctypes.c_int, ctypes.c_double, _f64p, _f32p]
             _lib = L
     return _lib
 
@@ -271,4 +284,74 @@ def prefill_rows(q_rows, rows, Hkv, kcodes, kscales, s_tk, vcodes, vscales, s_tv
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(one, range(threads)))
+    return out
+
+
+# ------------------------------------------------ comparison formats (FP8, BF16)
+
+def fp8_tensor_scale(x) -> float:
+    """FP8 cache tensor scale: amax(|X|) / 448 in FP32."""
+    return float(lib().orc_fp8_tensor_scale_from_amax(ctypes.c_float(abs_max(x))))
+
+
+def fp8_code(x: float, s_t: float) -> int:
+    return int(lib().orc_fp8_code(float(x), float(s_t)))
+
+
+def fp8_codes(x, s_t: float) -> np.ndarray:
+    """E4M3 codes of x / s_t (nearest, ties to even, clamped to 448), any shape."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_fp8_codes(_p(x, _f32p), x.size, float(s_t), _p(out, _u8p))
+    return out
+
+
+def fp8_value(code: int, s_t: float) -> float:
+    return float(lib().orc_fp8_value(int(code), float(s_t)))
+
+
+def fp8_dequant(codes, s_t: float) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, np.float32)
+    lib().orc_fp8_dequant(_p(codes, _u8p), codes.size, float(s_t), _p(out, _f32p))
+    return out
+
+
+def attend_dense(q, Hkv, kh, vh, scale=None):
+    """Attention of q [Hq][128] over an already dequantized cache kh, vh
+    [L][Hkv][128] FP32 (the comparison formats).  Returns [Hq][128]."""
+    q = _c(q, np.float32)
+    Hq = q.shape[0]
+    L = kh.shape[0]
+    if L == 0:
+        kh = np.zeros((1, Hkv, D), np.float32)
+        vh = kh
+    kh = _c(kh, np.float32)
+    vh = _c(vh, np.float32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((Hq, D), np.float32)
+    work = np.empty(max(L, 1), np.float64)
+    lib().orc_attend_dense(_p(q, _f32p), Hq, Hkv, _p(kh, _f32p), _p(vh, _f32p), L, float(scale),
+                           _p(work, _f64p), _p(out, _f32p))
+    return out
+
+
+def decode_batch_dense(q, seqs, Hkv, scale=None, threads=None):
+    """Decode attention for a batch over dequantized caches: seqs is a list of
+    B pairs (kh [L][Hkv][128], vh [L][Hkv][128]) FP32.  Returns [B][Hq][128]."""
+    q = _c(q, np.float32)
+    B, Hq = q.shape[0], q.shape[1]
+    G = Hq // Hkv
+    out = np.empty(q.shape, np.float32)
+    threads = threads or os.cpu_count() or 1
+
+    def one(unit):
+        b, h = divmod(unit, Hkv)
+        kh, vh = seqs[b]
+        out[b, h * G:(h + 1) * G] = attend_dense(q[b, h * G:(h + 1) * G], 1, kh[:, h:h + 1],
+                                                 vh[:, h:h + 1], scale)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, range(B * Hkv)))
     return out
