@@ -18,6 +18,7 @@ from . import build as _build
 
 F32, BF16 = 0, 1
 PREFILL_FP8, PREFILL_F16 = 0, 1
+CMP_FP8, CMP_BF16 = 1, 2          # comparison KV formats (nvfp4_cmp_format)
 HEAD_DIM, PAGE_SIZE, BLOCK = 128, 16, 16
 
 _lib = None
@@ -40,8 +41,18 @@ class CacheStruct(ctypes.Structure):
     ]
 
 
+class CmpCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("format", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+    ]
+
+
 _VP, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _CP = ctypes.POINTER(CacheStruct)
+_XP = ctypes.POINTER(CmpCacheStruct)
 
 _SIGS = {
     "nvfp4_status_string": (ctypes.c_char_p, [_I32]),
@@ -59,6 +70,12 @@ _SIGS = {
     "nvfp4_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "nvfp4_prefill_attn": (_I32, [_CP, _VP, _I32, _I32, _I32, _VP, _I32, _I32, _I32, _F, _VP, _SZ,
                                   _VP, _VP]),
+    "nvfp4_cmp_plane_bytes": (_SZ, [_I32, _I32, _I32]),
+    "nvfp4_cmp_fp8_scale_from_amax": (_F, [_F]),
+    "nvfp4_cmp_append": (_I32, [_XP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
+    "nvfp4_cmp_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "nvfp4_cmp_decode_attn": (_I32, [_XP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _F, _I32,
+                                     _VP, _SZ, _VP, _VP]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -261,5 +278,92 @@ def prefill(cache: KVCache, q, page_table_row, prefix_len: int, causal: bool = T
     _check("nvfp4_prefill_attn", lib().nvfp4_prefill_attn(
         ctypes.byref(cs), _ptr(q), _dtype_code(q), T, Hq, _ptr(page_table_row), int(prefix_len),
         int(bool(causal)), int(mode), float(softmax_scale), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _ptr(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------ comparison KV formats
+
+def cmp_plane_bytes(num_pages: int, num_kv_heads: int, fmt: int) -> int:
+    return lib().nvfp4_cmp_plane_bytes(num_pages, num_kv_heads, fmt)
+
+
+def cmp_fp8_scale_from_amax(amax: float) -> float:
+    return float(lib().nvfp4_cmp_fp8_scale_from_amax(float(amax)))
+
+
+def cmp_decode_workspace_bytes(fmt, batch, num_q_heads, num_kv_heads, max_seq_len, num_splits=0) -> int:
+    return lib().nvfp4_cmp_decode_workspace_bytes(fmt, batch, num_q_heads, num_kv_heads, max_seq_len,
+                                                  num_splits)
+
+
+class CmpCache:
+    """The two device planes (k, v) of a paged FP8 or BF16 cache.  The scales
+    are the FP8 tensor scales (ignored for BF16)."""
+
+    def __init__(self, fmt: int, num_pages: int, num_kv_heads: int, k_scale: float = 1.0,
+                 v_scale: float = 1.0, device="cuda", fill: int | None = 0):
+        self.fmt = int(fmt)
+        self.num_pages = int(num_pages)
+        self.num_kv_heads = int(num_kv_heads)
+        self.k_scale = float(k_scale)
+        self.v_scale = float(v_scale)
+        n = cmp_plane_bytes(self.num_pages, self.num_kv_heads, self.fmt)
+        if n == 0:
+            raise ValueError(f"bad comparison cache ({fmt}, {num_pages}, {num_kv_heads})")
+        self.k = torch.empty(n, dtype=torch.uint8, device=device)
+        self.v = torch.empty(n, dtype=torch.uint8, device=device)
+        if fill is not None:
+            self.k.fill_(fill)
+            self.v.fill_(fill)
+
+    def struct(self) -> CmpCacheStruct:
+        return CmpCacheStruct(self.k.data_ptr(), self.v.data_ptr(), self.k_scale, self.v_scale, self.fmt,
+                              self.num_pages, self.num_kv_heads, PAGE_SIZE, HEAD_DIM)
+
+    def nbytes(self) -> int:
+        return self.k.numel() + self.v.numel()
+
+
+def cmp_append(cache: CmpCache, k_new, v_new, tok_seq, tok_pos, page_table, stream=None):
+    """Store rows k_new/v_new [n][Hkv][128] into the comparison cache."""
+    n = k_new.shape[0] if k_new.dim() else 0
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _dev(t, nm)
+        if tuple(t.shape[1:]) != (cache.num_kv_heads, HEAD_DIM):
+            raise ValueError(f"{nm} must be [n][{cache.num_kv_heads}][128], got {tuple(t.shape)}")
+    if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must match in shape and dtype")
+    _dev(tok_seq, "tok_seq", torch.int32)
+    _dev(tok_pos, "tok_pos", torch.int32)
+    _dev(page_table, "page_table", torch.int32)
+    if tok_seq.numel() < n or tok_pos.numel() < n:
+        raise ValueError("tok_seq / tok_pos shorter than the number of rows")
+    cs = cache.struct()
+    _check("nvfp4_cmp_append", lib().nvfp4_cmp_append(
+        ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), n, _ptr(tok_seq),
+        _ptr(tok_pos), _ptr(page_table), page_table.shape[-1], _stream(stream)))
+
+
+def cmp_decode(cache: CmpCache, q, page_table, seq_lens, max_seq_len: int, softmax_scale=None,
+               num_splits: int = 0, workspace=None, out=None, stream=None):
+    """Decode attention over a comparison cache: q [B][Hq][128] -> [B][Hq][128] FP32."""
+    _dev(q, "q")
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    B, Hq = q.shape[0], q.shape[1]
+    if q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [B][Hq][128]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = cmp_decode_workspace_bytes(cache.fmt, B, Hq, cache.num_kv_heads, max_seq_len, num_splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    cs = cache.struct()
+    _check("nvfp4_cmp_decode_attn", lib().nvfp4_cmp_decode_attn(
+        ctypes.byref(cs), _ptr(q), _dtype_code(q), B, Hq, _ptr(page_table), page_table.shape[-1],
+        _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(num_splits), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _ptr(out), _stream(stream)))
     return out

@@ -79,9 +79,10 @@ constexpr int64_t kMinPagesPerWave = 16;
 constexpr int64_t kWavesPerCu = 8;
 constexpr int64_t kMaxPiecesPerSegment = 128;
 
-int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, int32_t max_seq_len) {
+int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, int32_t max_seq_len,
+                   int fmt = kFmtNvfp4) {
   if (num_splits > 0) return num_splits;
-  const int64_t slots = (int64_t)cu_count() * std::min<int64_t>(kWavesPerCu, decode_occupancy(f32_q));
+  const int64_t slots = (int64_t)cu_count() * std::min<int64_t>(kWavesPerCu, decode_occupancy(f32_q, fmt));
   const int64_t units = (int64_t)batch * hkv * ((max_seq_len + NVFP4_PAGE_SIZE - 1) / NVFP4_PAGE_SIZE);
   const int64_t want = std::min((units + kMinPagesPerWave - 1) / kMinPagesPerWave,
                                  std::max<int64_t>(cu_count(), kMaxPiecesPerSegment * batch * hkv));
@@ -216,19 +217,19 @@ size_t nvfp4_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
   return decode_ws(batch, num_q_heads / num_kv_heads, w);
 }
 
-int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
-                          int32_t batch, int32_t num_q_heads, const int32_t* page_table,
-                          int32_t max_pages_per_seq, const int32_t* seq_lens,
-                          int32_t max_seq_len, float softmax_scale, int32_t num_splits,
-                          void* workspace, size_t workspace_bytes, float* out, void* stream) {
-  g_err[0] = 0;
-  int32_t st = check_cache(cache);
-  if (st) return st;
+// Validation and launch shared by the NVFP4 and comparison-format decodes
+// (the cache itself has been checked by the caller).
+static int32_t decode_call(int fmt, const uint8_t* kplane, const uint8_t* kscales, const uint8_t* vplane,
+                           const uint8_t* vscales, float k_scale, float v_scale, int32_t hkv,
+                           const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
+                           const int32_t* page_table, int32_t max_pages_per_seq,
+                           const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                           int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
+                           void* stream) {
   if (!dtype_ok(q_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
   if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0 || max_pages_per_seq <= 0)
     return fail(NVFP4_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d, max_seq_len %d, splits %d, "
                 "max_pages %d)", batch, num_q_heads, max_seq_len, num_splits, max_pages_per_seq);
-  const int32_t hkv = cache->num_kv_heads;
   if (num_q_heads % hkv != 0)
     return fail(NVFP4_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 num_q_heads, hkv);
@@ -243,7 +244,7 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
   if (!q || !page_table || !seq_lens || !out) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(NVFP4_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
   const bool f32q = q_dtype == NVFP4_DTYPE_F32;
-  const int32_t W = plan_waves(num_splits, f32q, batch, hkv, max_seq_len);
+  const int32_t W = plan_waves(num_splits, f32q, batch, hkv, max_seq_len, fmt);
   const size_t need = decode_ws(batch, G, W);
   if (!workspace || workspace_bytes < need)
     return fail(NVFP4_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
@@ -251,8 +252,8 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(NVFP4_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   DecodeArgs a;
-  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
-  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
+  a.k_codes = kplane; a.k_scales = kscales;
+  a.v_codes = vplane; a.v_scales = vscales;
   a.q = q; a.page_table = page_table; a.seq_lens = seq_lens; a.out = out;
   const size_t pieces = (size_t)W * 2 * G;
   char* ws = static_cast<char*>(workspace);
@@ -260,12 +261,115 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
   a.ws_lse = reinterpret_cast<float*>(ws + align256(pieces * NVFP4_HEAD_DIM * sizeof(float)));
   a.ws_prefix = reinterpret_cast<int32_t*>(ws + align256(pieces * NVFP4_HEAD_DIM * sizeof(float)) +
                                            align256(pieces * sizeof(float)));
-  a.qk_scale = (float)((double)cache->k_tensor_scale * (double)softmax_scale * 1.4426950408889634);
-  a.v_scale = cache->v_tensor_scale;
+  a.qk_scale = (float)((double)k_scale * (double)softmax_scale * 1.4426950408889634);
+  a.v_scale = v_scale;
   a.max_pages = max_pages_per_seq;
   a.batch = batch; a.hq = num_q_heads; a.hkv = hkv; a.group = G;
   a.num_splits = W;
-  return hip_status(launch_decode(a, f32q, (hipStream_t)stream), "decode launch");
+  return hip_status(launch_decode(a, f32q, fmt, (hipStream_t)stream), "decode launch");
+}
+
+int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
+                          int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                          int32_t max_pages_per_seq, const int32_t* seq_lens,
+                          int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  return decode_call(kFmtNvfp4, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales,
+                     cache->k_tensor_scale, cache->v_tensor_scale, cache->num_kv_heads, q, q_dtype,
+                     batch, num_q_heads, page_table, max_pages_per_seq, seq_lens, max_seq_len,
+                     softmax_scale, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+// ------------------------------------------------ comparison formats
+
+static int32_t cmp_elem_bytes(int32_t format) {
+  return format == NVFP4_CMP_FP8 ? 1 : format == NVFP4_CMP_BF16 ? 2 : 0;
+}
+
+static int32_t check_cmp_cache(const nvfp4_cmp_cache* c) {
+  if (!c) return fail(NVFP4_ERR_INVALID_ARG, "cache is NULL");
+  if (!cmp_elem_bytes(c->format)) return fail(NVFP4_ERR_UNSUPPORTED, "cache format %d", c->format);
+  if (c->head_dim != NVFP4_HEAD_DIM)
+    return fail(NVFP4_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", c->head_dim);
+  if (c->page_size != NVFP4_PAGE_SIZE)
+    return fail(NVFP4_ERR_UNSUPPORTED, "page_size %d is not supported (only 16)", c->page_size);
+  if (c->num_pages <= 0 || c->num_kv_heads <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "num_pages (%d) and num_kv_heads (%d) must be > 0",
+                c->num_pages, c->num_kv_heads);
+  if (!c->k || !c->v) return fail(NVFP4_ERR_INVALID_ARG, "a cache plane pointer is NULL");
+  if (!aligned16(c->k) || !aligned16(c->v))
+    return fail(NVFP4_ERR_INVALID_ARG, "cache planes must be 16-byte aligned");
+  if (c->format == NVFP4_CMP_FP8 && (!good_scale(c->k_scale) || !good_scale(c->v_scale)))
+    return fail(NVFP4_ERR_INVALID_ARG, "FP8 tensor scales must be finite and > 0 (k %g, v %g)",
+                (double)c->k_scale, (double)c->v_scale);
+  return NVFP4_OK;
+}
+
+size_t nvfp4_cmp_plane_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t format) {
+  if (num_pages <= 0 || num_kv_heads <= 0 || !cmp_elem_bytes(format)) return 0;
+  return (size_t)num_pages * num_kv_heads * NVFP4_PAGE_SIZE * NVFP4_HEAD_DIM * cmp_elem_bytes(format);
+}
+
+float nvfp4_cmp_fp8_scale_from_amax(float amax) {
+  if (!std::isfinite(amax) || !(amax > 0.0f)) return 0.0f;
+  return amax / 448.0f;
+}
+
+int32_t nvfp4_cmp_append(const nvfp4_cmp_cache* cache, const void* k_new, const void* v_new,
+                         int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                         const int32_t* tok_pos, const int32_t* page_table,
+                         int32_t max_pages_per_seq, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cmp_cache(cache);
+  if (st) return st;
+  if (!dtype_ok(dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (n_tok < 0) return fail(NVFP4_ERR_INVALID_ARG, "n_tok < 0");
+  if (max_pages_per_seq <= 0) return fail(NVFP4_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
+  if (n_tok == 0) return NVFP4_OK;
+  if (!k_new || !v_new || !tok_seq || !tok_pos || !page_table)
+    return fail(NVFP4_ERR_INVALID_ARG, "NULL input pointer");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(NVFP4_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
+  CmpAppendArgs a;
+  a.k = static_cast<uint8_t*>(cache->k);
+  a.v = static_cast<uint8_t*>(cache->v);
+  a.k_scale = cache->k_scale; a.v_scale = cache->v_scale;
+  a.k_new = k_new; a.v_new = v_new;
+  a.tok_seq = tok_seq; a.tok_pos = tok_pos; a.page_table = page_table;
+  a.max_pages = max_pages_per_seq; a.n_tok = n_tok; a.hkv = cache->num_kv_heads;
+  a.fmt = cache->format == NVFP4_CMP_FP8 ? kFmtFp8 : kFmtBf16;
+  return hip_status(launch_cmp_append(a, dtype == NVFP4_DTYPE_F32, (hipStream_t)stream), "append launch");
+}
+
+size_t nvfp4_cmp_decode_workspace_bytes(int32_t format, int32_t batch, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t max_seq_len,
+                                        int32_t num_splits) {
+  if (!cmp_elem_bytes(format) || batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      max_seq_len < 0 || num_splits < 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
+  const int fmt = format == NVFP4_CMP_FP8 ? kFmtFp8 : kFmtBf16;
+  const int32_t w = std::max(plan_waves(num_splits, false, batch, num_kv_heads, max_seq_len, fmt),
+                             plan_waves(num_splits, true, batch, num_kv_heads, max_seq_len, fmt));
+  return decode_ws(batch, num_q_heads / num_kv_heads, w);
+}
+
+int32_t nvfp4_cmp_decode_attn(const nvfp4_cmp_cache* cache, const void* q, int32_t q_dtype,
+                              int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                              int32_t max_pages_per_seq, const int32_t* seq_lens,
+                              int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                              void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cmp_cache(cache);
+  if (st) return st;
+  const bool fp8 = cache->format == NVFP4_CMP_FP8;
+  return decode_call(fp8 ? kFmtFp8 : kFmtBf16, static_cast<const uint8_t*>(cache->k), nullptr,
+                     static_cast<const uint8_t*>(cache->v), nullptr, fp8 ? cache->k_scale : 1.0f,
+                     fp8 ? cache->v_scale : 1.0f, cache->num_kv_heads, q, q_dtype, batch, num_q_heads,
+                     page_table, max_pages_per_seq, seq_lens, max_seq_len, softmax_scale, num_splits,
+                     workspace, workspace_bytes, out, stream);
 }
 
 static size_t prefill_ws(int32_t total, int32_t hkv, int32_t mode) {

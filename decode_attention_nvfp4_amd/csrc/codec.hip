@@ -144,6 +144,68 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
   }
 }
 
+// ------------------------------------------------ comparison formats
+
+// Append to an FP8 or BF16 cache.  16 lanes per (token, head) row, lane g
+// takes elements 8g .. 8g+7 of K and of V.  FP8: the E4M3 code of the FP32
+// quotient x / s_t (IEEE division), clamped to +-448 first so that the
+// hardware's nearest-even conversion saturates like the format's rule.
+// BF16: nearest even (input bf16 is copied).  K rows are contiguous; the V
+// element d of token t sits at ((t/4) * 128 + d) * 4 + t%4 (elements), so a
+// row's V goes out as single-element stores.
+template <bool F32IN>
+__global__ void __launch_bounds__(256) cmp_append_kernel(CmpAppendArgs a) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = gid >> 4;
+  const int g = (int)(gid & 15);
+  if (row >= (long long)a.n_tok * a.hkv) return;
+  const int tok = (int)(row / a.hkv), head = (int)(row % a.hkv);
+  const Raw8 rk = load_raw8<F32IN>(a.k_new, (size_t)row, g);
+  const Raw8 rv = load_raw8<F32IN>(a.v_new, (size_t)row, g);
+  const int seq = a.tok_seq[tok], pos = a.tok_pos[tok];
+  const int page = a.page_table[(size_t)seq * a.max_pages + pos / kPage];
+  const int t = pos % kPage;
+  const size_t slab = (size_t)page * a.hkv + head;
+  const size_t kelem = slab * kPage * kD + (size_t)t * kD + 8 * g;              // K element index
+  const size_t velem = slab * kPage * kD + ((size_t)(t >> 2) * kD + 8 * g) * 4 + (t & 3);
+  float k[8], v[8];
+  unpack8<F32IN>(rk, k);
+  unpack8<F32IN>(rv, v);
+  if (a.fmt == kFmtFp8) {
+    auto q = [](float x, float s) { return fminf(fmaxf(x / s, -448.0f), 448.0f); };
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q(k[4 * h], a.k_scale), q(k[4 * h + 1], a.k_scale), 0, false);
+      w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q(k[4 * h + 2], a.k_scale), q(k[4 * h + 3], a.k_scale), lo, true);
+    }
+    *reinterpret_cast<uint2*>(a.k + kelem) = uint2{w[0], w[1]};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t b = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q(v[e], a.v_scale), q(v[e + 1], a.v_scale), 0, false);
+      a.v[velem + 4 * e] = (uint8_t)(b & 0xFFu);
+      a.v[velem + 4 * (e + 1)] = (uint8_t)((b >> 8) & 0xFFu);
+    }
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = ((uint32_t)(uint16_t)bf16_bits(k[2 * j])) | ((uint32_t)(uint16_t)bf16_bits(k[2 * j + 1]) << 16);
+    *reinterpret_cast<uint4*>(a.k + 2 * kelem) = uint4{w[0], w[1], w[2], w[3]};
+    uint16_t* vp = reinterpret_cast<uint16_t*>(a.v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vp[velem + 4 * e] = (uint16_t)bf16_bits(v[e]);
+  }
+}
+
+hipError_t launch_cmp_append(const CmpAppendArgs& a, bool f32, hipStream_t s) {
+  const long long threads = (long long)a.n_tok * a.hkv * 16;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (f32) cmp_append_kernel<true><<<blocks, 256, 0, s>>>(a);
+  else cmp_append_kernel<false><<<blocks, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
   const dim3 grid((unsigned)((a.n_tok + 15) / 16), (unsigned)a.hkv);
   if (f32) append_kernel<true><<<grid, 256, 0, s>>>(a);

@@ -27,6 +27,8 @@ typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------ E4M3 decode
 
@@ -186,6 +188,9 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
 }
+
+// float -> bf16 bits, nearest even (the hardware conversion)
+__device__ __forceinline__ short bf16_bits(float f) { return __builtin_bit_cast(short, (__bf16)f); }
 
 // Cross-row reductions inside a wave64 (rows of 16 lanes).  permlane16_swap
 // with the same register on both sides yields, per lane, its own value and

@@ -41,17 +41,43 @@
 
 namespace nvfp4 {
 
-struct PageRegs {
+// Cache formats the kernel reads: NVFP4 (the product format) and the two
+// comparison formats (FP8 E4M3 with a tensor scale, BF16), whose planes hold
+// K as [token][element] and V as [token quad][element][token % 4].
+template <int FMT> struct PageRegs;
+template <> struct PageRegs<kFmtNvfp4> {
   u32x4 kq;       // K codes: 32 nibbles of token col
   u32x4 vq;       // V codes: 4 tokens x 8 nibbles
   uint16_t ksc;   // 2 K block scales
   uint32_t vsc;   // 4 V block scales
 };
+template <> struct PageRegs<kFmtFp8> {
+  u32x4 kq[2];    // K: 32 E4M3 bytes of token col
+  u32x4 vq[2];    // V: elements 8 col .. 8 col + 7 of tokens 4 kg .. 4 kg + 3
+};
+template <> struct PageRegs<kFmtBf16> {
+  u32x4 kq[4];    // K: 32 bf16 of token col
+  u32x4 vq[4];    // V: elements 8 col .. 8 col + 7 of tokens 4 kg .. 4 kg + 3
+};
 
-// Per-lane byte offsets of the four loads of a page (fixed per lane).
+// Bytes per element of a comparison format (FP8 1, BF16 2).
+template <int FMT> constexpr int kElemBytes = FMT == kFmtBf16 ? 2 : 1;
+
+// Per-lane byte offsets of the loads of a page (fixed per lane).
 struct LaneOffsets {
   int k, ks, v, vs;
 };
+
+template <int FMT>
+__device__ __forceinline__ LaneOffsets lane_offsets(int col, int kg) {
+  if constexpr (FMT == kFmtNvfp4) {
+    return {col * 64 + kg * 16, col * kNBlk + kg * 2, kg * 256 + col * 16, (col >> 1) * kPage + kg * 4};
+  } else {
+    constexpr int E = kElemBytes<FMT>;
+    // K: token col, elements 32 kg ..; V: quad kg, elements 8 col .. (x 4 tokens)
+    return {(col * kD + kg * 32) * E, 0, (kg * kD * 4 + col * 32) * E, 0};
+  }
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
@@ -59,12 +85,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* base)
 
 // Buffer loads: the slab base lives in scalar registers and the lane offsets
 // are fixed, so a page load needs no vector address temporaries.
+template <int FMT>
 __device__ __forceinline__ void load_page(const DecodeArgs& p, uint32_t slab, const LaneOffsets& o,
-                                          PageRegs& r) {
-  r.kq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.k_codes + (size_t)slab * kSlab), o.k, 0, 0);
-  r.ksc = __builtin_amdgcn_raw_buffer_load_b16(page_rsrc(p.k_scales + (size_t)slab * kScaleSlab), o.ks, 0, 0);
-  r.vq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.v_codes + (size_t)slab * kSlab), o.v, 0, 0);
-  r.vsc = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(p.v_scales + (size_t)slab * kScaleSlab), o.vs, 0, 0);
+                                          PageRegs<FMT>& r) {
+  if constexpr (FMT == kFmtNvfp4) {
+    r.kq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.k_codes + (size_t)slab * kSlab), o.k, 0, 0);
+    r.ksc = __builtin_amdgcn_raw_buffer_load_b16(page_rsrc(p.k_scales + (size_t)slab * kScaleSlab), o.ks, 0, 0);
+    r.vq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.v_codes + (size_t)slab * kSlab), o.v, 0, 0);
+    r.vsc = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(p.v_scales + (size_t)slab * kScaleSlab), o.vs, 0, 0);
+  } else {
+    constexpr int N = 2 * kElemBytes<FMT>;             // 16-byte loads per lane and operand
+    constexpr size_t S = (size_t)kPage * kD * kElemBytes<FMT>;
+    const auto kr = page_rsrc(p.k_codes + (size_t)slab * S);
+    const auto vr = page_rsrc(p.v_codes + (size_t)slab * S);
+#pragma unroll
+    for (int i = 0; i < N; ++i) r.kq[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k + 16 * i, 0, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) r.vq[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, o.v + 16 * i, 0, 0);
+  }
 }
 
 struct WaveState {
@@ -87,24 +125,45 @@ __device__ __forceinline__ void reset_state(WaveState& st) {
   st.l_run = 0.0f;
 }
 
-template <bool F32Q>
-__device__ __forceinline__ void process_page(const PageRegs& cur, int pg, int L, int kg, float qscale,
+template <bool F32Q, int FMT>
+__device__ __forceinline__ void process_page(const PageRegs<FMT>& cur, int pg, int L, int kg, float qscale,
                                              const halfx8 qh[4], const halfx8 ql[4], WaveState& st) {
   // ---- S^T = K~ Q^T
-  const halfx2 ks = e4m3x2_to_half((uint32_t)cur.ksc, false);
-  const halfx2 sa = {ks[0], ks[0]}, sb = {ks[1], ks[1]};
   floatx4 acc_s = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (FMT == kFmtNvfp4) {
+    const halfx2 ks = e4m3x2_to_half((uint32_t)cur.ksc, false);
+    const halfx2 sa = {ks[0], ks[0]}, sb = {ks[1], ks[1]};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = cur.kq[i];
-    const halfx2 sc = i < 2 ? sa : sb;
-    const halfx2 h0 = e2m1x2_to_half<0>(w) * sc;
-    const halfx2 h1 = e2m1x2_to_half<1>(w) * sc;
-    const halfx2 h2 = e2m1x2_to_half<2>(w) * sc;
-    const halfx2 h3 = e2m1x2_to_half<3>(w) * sc;
-    const halfx8 a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-    acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[i], acc_s, 0, 0, 0);
-    if (F32Q) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[i], acc_s, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = cur.kq[i];
+      const halfx2 sc = i < 2 ? sa : sb;
+      const halfx2 h0 = e2m1x2_to_half<0>(w) * sc;
+      const halfx2 h1 = e2m1x2_to_half<1>(w) * sc;
+      const halfx2 h2 = e2m1x2_to_half<2>(w) * sc;
+      const halfx2 h3 = e2m1x2_to_half<3>(w) * sc;
+      const halfx8 a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+      acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[i], acc_s, 0, 0, 0);
+      if (F32Q) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[i], acc_s, 0, 0, 0);
+    }
+  } else if constexpr (FMT == kFmtFp8) {
+    // E4M3 -> FP16 is exact; the tensor scale sits in qscale
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w0 = cur.kq[i >> 1][(2 * i) & 3], w1 = cur.kq[i >> 1][(2 * i + 1) & 3];
+      const halfx2 h0 = e4m3x2_to_half(w0, false), h1 = e4m3x2_to_half(w0, true);
+      const halfx2 h2 = e4m3x2_to_half(w1, false), h3 = e4m3x2_to_half(w1, true);
+      const halfx8 a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+      acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[i], acc_s, 0, 0, 0);
+      if (F32Q) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[i], acc_s, 0, 0, 0);
+    }
+  } else {
+    // BF16 operands as stored (qh / ql hold bf16 bit patterns)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 a = __builtin_bit_cast(bf16x8, cur.kq[i]);
+      acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, qh[i]), acc_s, 0, 0, 0);
+      if (F32Q) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, ql[i]), acc_s, 0, 0, 0);
+    }
   }
   // ---- softmax (log2 domain); lane holds tokens 4kg..4kg+3 of head col.
   // Only a sequence's last page is partial (uniform test).  qscale > 0, so
@@ -129,32 +188,63 @@ __device__ __forceinline__ void process_page(const PageRegs& cur, int pg, int L,
 #pragma unroll
   for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(acc_s[r], qscale, -st.m_run));
   st.l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  const halfx4 bp = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
-  // ---- O^T += V~^T P^T.  Byte e of word j / 2 (j = token pair) holds
-  // element d = 8 col + e of tokens (4kg + 2j, 4kg + 2j + 1): one conversion
-  // gives the two tokens of a pair, the A operand's k order.
-  const halfx2 v01 = e4m3x2_to_half(cur.vsc, false);
-  const halfx2 v23 = e4m3x2_to_half(cur.vsc, true);
-  auto tile = [&](halfx2 a0, halfx2 a1, floatx4& acc) {
-    a0 *= v01;
-    a1 *= v23;
-    const halfx4 a = {a0[0], a0[1], a1[0], a1[1]};
-    acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bp, acc, 0, 0, 0);
-  };
-  tile(e2m1x2_to_half<0>(cur.vq[0]), e2m1x2_to_half<0>(cur.vq[2]), st.acc_o[0]);
-  tile(e2m1x2_to_half<1>(cur.vq[0]), e2m1x2_to_half<1>(cur.vq[2]), st.acc_o[1]);
-  tile(e2m1x2_to_half<2>(cur.vq[0]), e2m1x2_to_half<2>(cur.vq[2]), st.acc_o[2]);
-  tile(e2m1x2_to_half<3>(cur.vq[0]), e2m1x2_to_half<3>(cur.vq[2]), st.acc_o[3]);
-  tile(e2m1x2_to_half<0>(cur.vq[1]), e2m1x2_to_half<0>(cur.vq[3]), st.acc_o[4]);
-  tile(e2m1x2_to_half<1>(cur.vq[1]), e2m1x2_to_half<1>(cur.vq[3]), st.acc_o[5]);
-  tile(e2m1x2_to_half<2>(cur.vq[1]), e2m1x2_to_half<2>(cur.vq[3]), st.acc_o[6]);
-  tile(e2m1x2_to_half<3>(cur.vq[1]), e2m1x2_to_half<3>(cur.vq[3]), st.acc_o[7]);
+  if constexpr (FMT == kFmtNvfp4) {
+    const halfx4 bp = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+    // ---- O^T += V~^T P^T.  Byte e of word j / 2 (j = token pair) holds
+    // element d = 8 col + e of tokens (4kg + 2j, 4kg + 2j + 1): one conversion
+    // gives the two tokens of a pair, the A operand's k order.
+    const halfx2 v01 = e4m3x2_to_half(cur.vsc, false);
+    const halfx2 v23 = e4m3x2_to_half(cur.vsc, true);
+    auto tile = [&](halfx2 a0, halfx2 a1, floatx4& acc) {
+      a0 *= v01;
+      a1 *= v23;
+      const halfx4 a = {a0[0], a0[1], a1[0], a1[1]};
+      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bp, acc, 0, 0, 0);
+    };
+    tile(e2m1x2_to_half<0>(cur.vq[0]), e2m1x2_to_half<0>(cur.vq[2]), st.acc_o[0]);
+    tile(e2m1x2_to_half<1>(cur.vq[0]), e2m1x2_to_half<1>(cur.vq[2]), st.acc_o[1]);
+    tile(e2m1x2_to_half<2>(cur.vq[0]), e2m1x2_to_half<2>(cur.vq[2]), st.acc_o[2]);
+    tile(e2m1x2_to_half<3>(cur.vq[0]), e2m1x2_to_half<3>(cur.vq[2]), st.acc_o[3]);
+    tile(e2m1x2_to_half<0>(cur.vq[1]), e2m1x2_to_half<0>(cur.vq[3]), st.acc_o[4]);
+    tile(e2m1x2_to_half<1>(cur.vq[1]), e2m1x2_to_half<1>(cur.vq[3]), st.acc_o[5]);
+    tile(e2m1x2_to_half<2>(cur.vq[1]), e2m1x2_to_half<2>(cur.vq[3]), st.acc_o[6]);
+    tile(e2m1x2_to_half<3>(cur.vq[1]), e2m1x2_to_half<3>(cur.vq[3]), st.acc_o[7]);
+  } else if constexpr (FMT == kFmtFp8) {
+    // ---- O^T += V~^T P^T: word i holds element d = 8 col + i of the four
+    // tokens of quad kg (the A operand's k order)
+    const halfx4 bp = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = cur.vq[i >> 2][i & 3];
+      const halfx2 lo = e4m3x2_to_half(w, false), hi = e4m3x2_to_half(w, true);
+      const halfx4 a = {lo[0], lo[1], hi[0], hi[1]};
+      st.acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bp, st.acc_o[i], 0, 0, 0);
+    }
+  } else {
+    // ---- BF16: P = hi + lo in two bf16 parts (16 significant bits, as
+    // close as FP16's P; one bf16 part alone moves outputs by up to 2^-9 of
+    // the weighted |v|); element d = 8 col + i of the four tokens of quad kg
+    // sits in 8 bytes
+    shortx4 bh, bl;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bh[r] = bf16_bits(pr[r]);
+      bl[r] = bf16_bits(pr[r] - __builtin_bit_cast(float, (uint32_t)(uint16_t)bh[r] << 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w0 = cur.vq[i >> 1][(2 * i) & 3], w1 = cur.vq[i >> 1][(2 * i + 1) & 3];
+      const shortx4 a = {(short)(w0 & 0xFFFFu), (short)(w0 >> 16), (short)(w1 & 0xFFFFu), (short)(w1 >> 16)};
+      st.acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bh, st.acc_o[i], 0, 0, 0);
+      st.acc_o[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bl, st.acc_o[i], 0, 0, 0);
+    }
+  }
 }
 
 // Q of (sequence b, KV head kvh) as the B operand of S^T = K~ Q^T: lane
 // (head col, group kg) holds q[32kg + 8i + j] in element j of qh[i], scaled by
 // 2^shift into FP16 (the max |q| of the head lands in [2^14, 2^15)).
-template <bool F32Q>
+template <bool F32Q, int FMT>
 __device__ __forceinline__ void load_q(const DecodeArgs& p, int b, int kvh, int col, int kg,
                                        halfx8 qh[4], halfx8 ql[4], float& qscale) {
   float qv[32];
@@ -181,6 +271,22 @@ __device__ __forceinline__ void load_q(const DecodeArgs& p, int b, int kvh, int 
   } else {
 #pragma unroll
     for (int i = 0; i < 32; ++i) qv[i] = 0.0f;
+  }
+  if constexpr (FMT == kFmtBf16) {
+    // bf16 operands (bit patterns in the half registers): q = hi + lo, with
+    // lo = 0 for bf16 queries; no range scaling (bf16 spans FP32's range)
+    qscale = p.qk_scale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = qv[8 * i + j];
+        const uint16_t hb = (uint16_t)bf16_bits(v);
+        qh[i][j] = __builtin_bit_cast(_Float16, hb);
+        const float hv = __builtin_bit_cast(float, (uint32_t)hb << 16);
+        ql[i][j] = F32Q ? __builtin_bit_cast(_Float16, (uint16_t)bf16_bits(v - hv)) : (_Float16)0.0f;
+      }
+    return;
   }
   float amax = 0.0f;
 #pragma unroll
@@ -313,12 +419,15 @@ __device__ __forceinline__ uint32_t prepare_block(const DecodeArgs& p, SegPos& w
 }
 
 // Register stages of the page pipeline; the planner runs two waves per SIMD,
-// so the register budget is that of two waves.
-constexpr int kDepth = 8;
-static_assert(64 % kDepth == 0, "block switches must fall on a stage boundary");
+// so the register budget is that of two waves (a BF16 page takes three times
+// the registers of an NVFP4 one).
+template <int FMT> constexpr int kDepth = FMT == kFmtBf16 ? 4 : 8;
+static_assert(64 % kDepth<kFmtNvfp4> == 0 && 64 % kDepth<kFmtBf16> == 0,
+              "block switches must fall on a stage boundary");
 
-template <bool F32Q>
+template <bool F32Q, int FMT>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) decode_kernel(DecodeArgs p) {
+  constexpr int kD8 = kDepth<FMT>;
   const int lane = threadIdx.x;
   const int col = lane & 15, kg = lane >> 4;
   const int wave = blockIdx.x, W = gridDim.x;
@@ -388,13 +497,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
     nxt = prepare_block(p, walker, wwin, N - prepared, lane);
     prepared += min(64, N - prepared);
   }
-  const LaneOffsets lo = {col * 64 + kg * 16, col * kNBlk + kg * 2, kg * 256 + col * 16,
-                           (col >> 1) * kPage + kg * 4};
+  const LaneOffsets lo = lane_offsets<FMT>(col, kg);
   // units past the end reload the last one (never consumed)
-  auto issue = [&](PageRegs& r, int x) {
+  auto issue = [&](PageRegs<FMT>& r, int x) {
     const int o = min(x, N - 1) - base;
     const uint32_t slab = o < 64 ? __builtin_amdgcn_readlane(cur, o) : __builtin_amdgcn_readlane(nxt, o - 64);
-    load_page(p, slab, lo, r);
+    load_page<FMT>(p, slab, lo, r);
   };
 
   // ---- process side: one piece (the wave's part of one segment) at a time
@@ -406,16 +514,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   halfx8 qh[4], ql[4];
   float qscale = 0.0f;
   WaveState st;
-  auto step = [&](const PageRegs& r) {
+  auto step = [&](const PageRegs<FMT>& r) {
     if (piece_left == 0) {                 // a new piece starts with this page
       if (started) next_segment(p, seg, pwin, lane);
       started = true;
       piece_left = min(seg.np - seg.pg, N - done);
       whole = seg.pg == 0 && piece_left == seg.np;
-      load_q<F32Q>(p, seg.b, seg.kvh, col, kg, qh, ql, qscale);
+      load_q<F32Q, FMT>(p, seg.b, seg.kvh, col, kg, qh, ql, qscale);
       reset_state(st);
     }
-    process_page<F32Q>(r, seg.pg, seg.L, kg, qscale, qh, ql, st);
+    process_page<F32Q, FMT>(r, seg.pg, seg.L, kg, qscale, qh, ql, st);
     ++seg.pg;
     ++done;
     if (--piece_left == 0) {
@@ -424,13 +532,13 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
     }
   };
 
-  // kDepth register stages: the loads of the next kDepth - 1 pages are in
-  // flight while a page is processed (kDepth divides 64, so block switches
+  // kD8 register stages: the loads of the next kD8 - 1 pages are in
+  // flight while a page is processed (kD8 divides 64, so block switches
   // fall on stage 0)
-  PageRegs r[kDepth];
+  PageRegs<FMT> r[kD8];
 #pragma unroll
-  for (int i = 0; i < kDepth - 1; ++i) issue(r[i], i);
-  for (int t = 0; t < N; t += kDepth) {
+  for (int i = 0; i < kD8 - 1; ++i) issue(r[i], i);
+  for (int t = 0; t < N; t += kD8) {
     if (t == base + 64) {                  // the next block becomes current
       cur = nxt;
       base += 64;
@@ -440,9 +548,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
       }
     }
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
+    for (int j = 0; j < kD8; ++j) {
       if (j > 0 && t + j >= N) break;
-      issue(r[(j + kDepth - 1) % kDepth], t + j + kDepth - 1);
+      issue(r[(j + kD8 - 1) % kD8], t + j + kD8 - 1);
       __builtin_amdgcn_sched_barrier(0);
       step(r[j]);
       __builtin_amdgcn_sched_barrier(0);
@@ -569,20 +677,35 @@ __device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMa
 
 // Resident decode waves per CU, queried once per process (every device here
 // is gfx950, so the answer does not depend on the device).
-int decode_occupancy(bool f32_q) {
-  static std::atomic<int> cached[2] = {0, 0};
-  int n = cached[f32_q].load(std::memory_order_relaxed);
+template <int FMT>
+static int occupancy_of(bool f32_q) {
+  int n = 0;
+  hipError_t e = f32_q ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<true, FMT>, 64, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<false, FMT>, 64, 0);
+  return e == hipSuccess ? n : 0;
+}
+
+int decode_occupancy(bool f32_q, int fmt) {
+  static std::atomic<int> cached[2][3] = {};
+  const int f = fmt == kFmtFp8 ? 1 : fmt == kFmtBf16 ? 2 : 0;
+  int n = cached[f32_q][f].load(std::memory_order_relaxed);
   if (n > 0) return n;
-  hipError_t e = f32_q ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<true>, 64, 0)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<false>, 64, 0);
-  if (e != hipSuccess || n <= 0) return 8;
-  cached[f32_q].store(n, std::memory_order_relaxed);
+  n = f == 1 ? occupancy_of<kFmtFp8>(f32_q) : f == 2 ? occupancy_of<kFmtBf16>(f32_q) : occupancy_of<kFmtNvfp4>(f32_q);
+  if (n <= 0) return 8;
+  cached[f32_q][f].store(n, std::memory_order_relaxed);
   return n;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, bool f32_q, hipStream_t s) {
-  if (f32_q) decode_kernel<true><<<a.num_splits, 64, 0, s>>>(a);
-  else decode_kernel<false><<<a.num_splits, 64, 0, s>>>(a);
+template <int FMT>
+static void launch_fmt(const DecodeArgs& a, bool f32_q, hipStream_t s) {
+  if (f32_q) decode_kernel<true, FMT><<<a.num_splits, 64, 0, s>>>(a);
+  else decode_kernel<false, FMT><<<a.num_splits, 64, 0, s>>>(a);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, bool f32_q, int fmt, hipStream_t s) {
+  if (fmt == kFmtFp8) launch_fmt<kFmtFp8>(a, f32_q, s);
+  else if (fmt == kFmtBf16) launch_fmt<kFmtBf16>(a, f32_q, s);
+  else launch_fmt<kFmtNvfp4>(a, f32_q, s);
   const unsigned heads = (unsigned)(a.batch * a.hkv * a.group);
   if ((long long)a.num_splits > 8LL * a.batch * a.hkv) merge_kernel<8><<<heads, 256, 0, s>>>(a);
   else merge_kernel<2><<<heads, 64, 0, s>>>(a);

@@ -9,6 +9,9 @@
 namespace nvfp4 {
 
 constexpr int kPrefillTile = 64;   // keys per prefill tile
+constexpr int kFmtNvfp4 = 0;       // cache formats of the decode kernel: NVFP4,
+constexpr int kFmtFp8 = 1;         // and the comparison formats (values of
+constexpr int kFmtBf16 = 2;        // nvfp4_cmp_format)
 constexpr int kPrefillFP8 = 0;     // operand precisions of the prefill path
 constexpr int kPrefillF16 = 1;
 
@@ -30,6 +33,23 @@ struct AppendArgs {
   int32_t hkv;
 };
 
+// Append to a comparison-format cache: k / v planes of E4M3 codes of
+// x / s_t, or of bf16 values.
+struct CmpAppendArgs {
+  uint8_t* k;
+  uint8_t* v;
+  float k_scale, v_scale;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* tok_seq;
+  const int32_t* tok_pos;
+  const int32_t* page_table;
+  int32_t max_pages;
+  int32_t n_tok;
+  int32_t hkv;
+  int32_t fmt;
+};
+
 struct DequantArgs {
   const uint8_t* k_codes;
   const uint8_t* k_scales;
@@ -43,9 +63,9 @@ struct DequantArgs {
 };
 
 struct DecodeArgs {
-  const uint8_t* k_codes;
-  const uint8_t* k_scales;
-  const uint8_t* v_codes;
+  const uint8_t* k_codes;     // comparison formats: the k plane
+  const uint8_t* k_scales;    // (unused by the comparison formats)
+  const uint8_t* v_codes;     // comparison formats: the v plane
   const uint8_t* v_scales;
   const void* q;              // [B][Hq][128]
   const int32_t* page_table;  // [B][max_pages]
@@ -83,8 +103,9 @@ struct PrefillArgs {
 hipError_t launch_append(const AppendArgs& a, bool f32_in, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, bool f32_out, hipStream_t s);
 hipError_t launch_absmax(const void* x, bool f32_in, int64_t n, float* out, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, bool f32_q, hipStream_t s);
-int decode_occupancy(bool f32_q);   // resident decode waves per CU
+hipError_t launch_cmp_append(const CmpAppendArgs& a, bool f32_in, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, bool f32_q, int fmt, hipStream_t s);
+int decode_occupancy(bool f32_q, int fmt);   // resident decode waves per CU
 hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s);
 
 }  // namespace nvfp4

@@ -225,6 +225,79 @@ int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q
                            int32_t mode, float softmax_scale, void* workspace,
                            size_t workspace_bytes, float* out, void* stream);
 
+/* ------------------------------------------------ comparison KV formats
+ * The formats NVFP4 is measured against ([EXPL] §なぜ4ビット量子化が必要か and
+ * §メモリ削減効果: FP8 caches are in wide use and NVFP4 halves their bytes;
+ * FP16/BF16 is the unquantized baseline; [TRTL] §Pourquoi FP8 est toujours le
+ * sol pour KV cache), stored in the same paging and decoded by the same
+ * decode kernel, so that the speed ratio of the formats can be measured.
+ *
+ *   NVFP4_CMP_FP8 : each element is an OCP E4M3FN byte, the value nearest to
+ *                   x / s_t (FP32 quotient), ties to the even code, clamped
+ *                   to 448; one FP32 tensor scale s_t per K and per V, e.g.
+ *                   amax(|X|) / 448 (nvfp4_cmp_fp8_scale_from_amax); a
+ *                   value is e4m3 * s_t.  1 byte per element.
+ *   NVFP4_CMP_BF16: each element is the bf16 value (F32 input rounded to
+ *                   nearest even, BF16 input copied); the scales are unused.
+ *                   2 bytes per element.
+ * Layout: two planes k and v, each [num_pages][num_kv_heads][slab] with E
+ * bytes per element (1 or 2):
+ *   k slab 16 * 128 * E: [token 16][element 128];
+ *   v slab 16 * 128 * E: [token quad 4][element 128][token 4], i.e. element
+ *                        d of token t at ((t/4) * 128 + d) * 4 + t%4 (in
+ *                        elements), so that the four tokens of a quad at one
+ *                        element are adjacent (the operand order of PV).
+ */
+typedef enum nvfp4_cmp_format {
+  NVFP4_CMP_FP8 = 1,
+  NVFP4_CMP_BF16 = 2
+} nvfp4_cmp_format;
+
+/* Host description of a paged comparison-format cache (one layer).  k and v
+ * are 16-byte aligned device planes; for FP8 the scales must be finite and
+ * > 0. */
+typedef struct nvfp4_cmp_cache {
+  void* k;
+  void* v;
+  float k_scale;
+  float v_scale;
+  int32_t format;      /* an nvfp4_cmp_format */
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t page_size;   /* must be 16 */
+  int32_t head_dim;    /* must be 128 */
+} nvfp4_cmp_cache;
+
+/* Bytes of one plane (k or v): num_pages * num_kv_heads * 16 * 128 * E.
+ * 0 for invalid arguments. */
+size_t nvfp4_cmp_plane_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t format);
+
+/* FP8 tensor scale: amax / 448 in FP32; 0 when amax is not finite or not > 0. */
+float nvfp4_cmp_fp8_scale_from_amax(float amax);
+
+/* Append rows to a comparison-format cache; the arguments and index rules
+ * are those of nvfp4_kv_append.  Writes each (token, head) row of K and V;
+ * nothing else changes.  n_tok == 0 is a no-op. */
+int32_t nvfp4_cmp_append(const nvfp4_cmp_cache* cache, const void* k_new, const void* v_new,
+                         int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                         const int32_t* tok_pos, const int32_t* page_table,
+                         int32_t max_pages_per_seq, void* stream);
+
+/* Workspace bytes of nvfp4_cmp_decode_attn (0 for invalid arguments). */
+size_t nvfp4_cmp_decode_workspace_bytes(int32_t format, int32_t batch, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t max_seq_len,
+                                        int32_t num_splits);
+
+/* Decode attention over a comparison-format cache: the operation, arguments
+ * and work split of nvfp4_decode_attn, with the cached values of the format
+ * (FP8: e4m3 * s_t, exact in FP16 and expanded to it; BF16: the bf16 values,
+ * multiplied in bf16 with P carried as two bf16 parts). */
+int32_t nvfp4_cmp_decode_attn(const nvfp4_cmp_cache* cache, const void* q, int32_t q_dtype,
+                              int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                              int32_t max_pages_per_seq, const int32_t* seq_lens,
+                              int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                              void* workspace, size_t workspace_bytes, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -155,3 +155,89 @@ class BuiltDecode:
                 if not np.array_equal(g, e):
                     bad = np.argwhere(g != e)[:5]
                     raise AssertionError(f"seq {b}: {nm} differ at {bad.tolist()}")
+
+
+# ------------------------------------------------ comparison formats
+
+class BuiltCmp:
+    """A decode workload appended into an FP8 or BF16 comparison cache, plus
+    the oracle's stored values for every sequence.  FP8 tensor scales come
+    from the oracle's calibration over the whole tensor (steps included)."""
+
+    def __init__(self, w: W.DecodeWorkload, oracle, fmt: int, fill=0xA5, chunk=16):
+        from layout import CmpPlanes  # noqa: F401  (used by check_codes)
+        self.w, self.fmt = w, fmt
+        data = [w.kv(b) for b in range(w.B)]
+        if fmt == api.CMP_FP8:
+            ka = max([oracle.abs_max(k) for k, _ in data] + [oracle.abs_max(w.append_kv(s)[0]) for s in range(w.steps)])
+            va = max([oracle.abs_max(v) for _, v in data] + [oracle.abs_max(w.append_kv(s)[1]) for s in range(w.steps)])
+            self.s_k = oracle.fp8_tensor_scale(np.array([ka], np.float32))
+            self.s_v = oracle.fp8_tensor_scale(np.array([va], np.float32))
+        else:
+            self.s_k = self.s_v = 1.0
+        self.cache = api.CmpCache(fmt, w.num_pages, w.Hkv, self.s_k, self.s_v, fill=fill)
+        self.pt = i32(w.page_table)
+        self.vals = {}
+        for b0 in range(0, w.B, chunk):
+            ks, vs, seqs, poss = [], [], [], []
+            for b in range(b0, min(w.B, b0 + chunk)):
+                k, v = data[b]
+                ks.append(k)
+                vs.append(v)
+                seqs.append(np.full(len(k), b, np.int32))
+                poss.append(np.arange(len(k), dtype=np.int32))
+                self.vals[b] = (self.encode(oracle, k, self.s_k), self.encode(oracle, v, self.s_v))
+            k = np.concatenate(ks)
+            if len(k) == 0:
+                continue
+            api.cmp_append(self.cache, to_dev(k, w.dtype), to_dev(np.concatenate(vs), w.dtype),
+                           i32(np.concatenate(seqs)), i32(np.concatenate(poss)), self.pt)
+        self.lens = w.lens.copy()
+        torch.cuda.synchronize()
+
+    def encode(self, oracle, x, s):
+        """The stored elements: FP8 codes, or bf16 bit patterns."""
+        return oracle.fp8_codes(x, s) if self.fmt == api.CMP_FP8 else oracle.f32_to_bf16_bits(x)
+
+    def values(self, oracle, enc, s):
+        if self.fmt == api.CMP_FP8:
+            return oracle.fp8_dequant(enc, s)
+        return (enc.astype(np.uint32) << 16).view(np.float32)
+
+    def append_step(self, step, oracle):
+        w = self.w
+        k, v = w.append_kv(step)
+        api.cmp_append(self.cache, to_dev(k, w.dtype), to_dev(v, w.dtype), i32(np.arange(w.B)),
+                       i32(self.lens.copy()), self.pt)
+        for b in range(w.B):
+            ek, ev = self.vals[b]
+            self.vals[b] = (np.concatenate([ek, self.encode(oracle, k[b:b + 1], self.s_k)]),
+                            np.concatenate([ev, self.encode(oracle, v[b:b + 1], self.s_v)]))
+        self.lens += 1
+
+    def check_codes(self, seqs):
+        from layout import CmpPlanes
+        torch.cuda.synchronize()
+        R = CmpPlanes(self.cache.k.cpu().numpy(), self.cache.v.cpu().numpy(), self.w.num_pages, self.w.Hkv,
+                      self.fmt)
+        for b in seqs:
+            pages, slots = sequence_tokens(self.w.page_table[b], int(self.lens[b]))
+            gk, gv = R.gather(pages, slots)
+            for g, e, nm in ((gk, self.vals[b][0], "k"), (gv, self.vals[b][1], "v")):
+                if not np.array_equal(g, e):
+                    bad = np.argwhere(g != e)[:5]
+                    raise AssertionError(f"seq {b}: {nm} differ at {bad.tolist()}")
+
+    def decode(self, q: np.ndarray, num_splits=0, dtype=None):
+        qd = to_dev(q, dtype or self.w.dtype)
+        return api.cmp_decode(self.cache, qd, self.pt, i32(self.lens), int(self.lens.max()),
+                              num_splits=num_splits)
+
+    def oracle_decode(self, oracle, q: np.ndarray, seqs, scale=None):
+        """(reference, magnitude) as in BuiltDecode, over the stored values."""
+        seqs = list(seqs)
+        kv = [(self.values(oracle, self.vals[b][0], self.s_k), self.values(oracle, self.vals[b][1], self.s_v))
+              for b in seqs]
+        ref = oracle.decode_batch_dense(q[seqs], kv, self.w.Hkv, scale=scale)
+        mag = oracle.decode_batch_dense(q[seqs], [(k, np.abs(v)) for k, v in kv], self.w.Hkv, scale=scale)
+        return ref, mag

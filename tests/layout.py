@@ -80,3 +80,23 @@ def sequence_tokens(page_table_row, L):
     """(pages, slots) of positions 0..L-1 of one sequence."""
     pos = np.arange(L)
     return np.asarray(page_table_row)[pos // PAGE], pos % PAGE
+
+
+class CmpPlanes:
+    """Reader of a comparison-format cache (FP8 or BF16), from the header's
+    description: k slab [token 16][element 128]; v slab [token quad 4]
+    [element 128][token 4].  Elements are uint8 codes (FP8) or uint16 bf16
+    bit patterns (BF16).  self.k, self.v: [page][head][token 16][element 128]."""
+
+    def __init__(self, k_bytes, v_bytes, num_pages, hkv, fmt):
+        dt = np.uint8 if fmt == 1 else np.uint16
+        k = np.asarray(k_bytes).view(dt).reshape(num_pages, hkv, PAGE, D)
+        v = np.asarray(v_bytes).view(dt).reshape(num_pages, hkv, 4, D, 4)     # [..][quad][d][t%4]
+        self.k = k
+        self.v = np.ascontiguousarray(v.transpose(0, 1, 2, 4, 3)).reshape(num_pages, hkv, PAGE, D)
+
+    def gather(self, pages, slots):
+        """(k, v) of token lists, each [n][Hkv][128]."""
+        pages = np.asarray(pages)
+        slots = np.asarray(slots)
+        return self.k[pages, :, slots], self.v[pages, :, slots]

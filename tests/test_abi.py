@@ -203,3 +203,62 @@ def test_binding_refuses_host_tensors(api):
     with pytest.raises(ValueError):
         api.append(cache, torch.zeros(2, 8, 128), torch.zeros(2, 8, 128), torch.zeros(2, dtype=torch.int32),
                    torch.zeros(2, dtype=torch.int32), torch.zeros(1, 4, dtype=torch.int32))
+
+
+# --------------------------------------------------- comparison KV formats
+
+def _fake_cmp(api, **kw):
+    c = api.CmpCacheStruct(0x10000, 0x20000, 0.01, 0.02, api.CMP_FP8, 64, 8, 16, 128)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_cmp_sizes_and_fp8_scale(api):
+    L = api.lib()
+    # 1 byte (FP8) or 2 bytes (BF16) per element, 16 tokens x 128 per (page, head)
+    assert L.nvfp4_cmp_plane_bytes(10, 8, api.CMP_FP8) == 10 * 8 * 16 * 128
+    assert L.nvfp4_cmp_plane_bytes(10, 8, api.CMP_BF16) == 2 * 10 * 8 * 16 * 128
+    assert L.nvfp4_cmp_plane_bytes(10, 8, 0) == 0 and L.nvfp4_cmp_plane_bytes(0, 8, 1) == 0
+    # NVFP4 against the comparison formats: 0.5625 vs 1 vs 2 bytes per element
+    nv = L.nvfp4_kv_cache_bytes(10, 8)
+    assert 2 * L.nvfp4_cmp_plane_bytes(10, 8, api.CMP_FP8) / nv == pytest.approx(1 / 0.5625)
+    assert 2 * L.nvfp4_cmp_plane_bytes(10, 8, api.CMP_BF16) / nv == pytest.approx(2 / 0.5625)
+    assert L.nvfp4_cmp_fp8_scale_from_amax(448.0) == 1.0
+    assert L.nvfp4_cmp_fp8_scale_from_amax(3.0) == np.float32(3.0) / np.float32(448.0)
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert L.nvfp4_cmp_fp8_scale_from_amax(bad) == 0.0
+
+
+def test_cmp_append_and_decode_reject_bad_arguments(api):
+    L = api.lib()
+
+    def app(c, dtype=1, n_tok=4, ptrs=True):
+        p = FAKE if ptrs else None
+        return L.nvfp4_cmp_append(ctypes.byref(c), p, p, dtype, n_tok, p, p, p, 8, None)
+
+    def dec(c, q_dtype=1, Hq=32, ws=FAKE, ws_bytes=1 << 30, splits=4, B=2):
+        return L.nvfp4_cmp_decode_attn(ctypes.byref(c), FAKE, q_dtype, B, Hq, FAKE, 64, FAKE, 1000, 0.088,
+                                       splits, ws, ws_bytes, FAKE, None)
+
+    assert L.nvfp4_cmp_append(None, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == 1
+    assert app(_fake_cmp(api, format=0)) == 2
+    assert app(_fake_cmp(api, format=3)) == 2
+    assert app(_fake_cmp(api, head_dim=64)) == 2
+    assert app(_fake_cmp(api, k=0x10008)) == 1                  # misaligned plane
+    assert app(_fake_cmp(api, v=None)) == 1
+    assert app(_fake_cmp(api, k_scale=0.0)) == 1                 # FP8 needs scales
+    assert app(_fake_cmp(api, format=api.CMP_BF16, k_scale=0.0, v_scale=0.0), n_tok=0) == 0
+    assert app(_fake_cmp(api), dtype=9) == 2
+    assert app(_fake_cmp(api), ptrs=False) == 1
+    assert app(_fake_cmp(api), n_tok=0, ptrs=False) == 0
+    c = _fake_cmp(api)
+    assert dec(_fake_cmp(api, format=5)) == 2
+    assert dec(c, q_dtype=4) == 2
+    assert dec(c, Hq=12) == 1
+    assert dec(c, ws=None, ws_bytes=0) == 3
+    assert dec(c, ws=ctypes.c_void_p(0x50010)) == 1
+    assert dec(c, B=0) == 0
+    assert L.nvfp4_cmp_decode_workspace_bytes(0, 2, 32, 8, 1000, 0) == 0
+    assert L.nvfp4_cmp_decode_workspace_bytes(api.CMP_FP8, 2, 32, 8, 1000, 4) == \
+        L.nvfp4_decode_workspace_bytes(2, 32, 8, 1000, 4)

@@ -8,7 +8,7 @@ import torch
 
 from decode_attention_nvfp4_amd import api
 from decode_attention_nvfp4_amd import workloads as W
-from gpu_common import TOL, BuiltDecode, check_decode, compare, i32, planes, say, to_dev
+from gpu_common import TOL, BuiltCmp, BuiltDecode, check_decode, compare, i32, planes, say, to_dev
 from layout import sequence_tokens
 
 pytestmark = pytest.mark.gpu
@@ -466,3 +466,101 @@ def test_config5_prefill_sampled(orc):
     ok, st = compare(out[rows], ref)
     say("   ", st)
     assert ok, st
+
+
+# ------------------------------------------------ comparison KV formats
+
+CMP_FMTS = [(1, "fp8"), (2, "bf16")]
+# FP8 values are exact in FP16 and P is FP16, as in the NVFP4 decode; BF16
+# carries P as two bf16 parts (16 significant bits): the same derived bound
+CMP_FACTOR = {1: 1.0, 2: 1.0}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", [f for f, _ in CMP_FMTS], ids=[n for _, n in CMP_FMTS])
+def test_cmp_append_exact_with_ties_and_saturation(orc, fmt, dtype):
+    """Unit scales, inputs at every E4M3 value, midpoint and neighbour, and
+    beyond 448: the stored elements equal the oracle's, bit for bit; nothing
+    outside the appended rows changes."""
+    e4 = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    mids = ((e4[:-1].astype(np.float64) + e4[1:]) / 2).astype(np.float32)
+    pts = np.concatenate([e4, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                          np.float32([449, 463.9, 464, 465, 1e4, 0.0])])
+    pts = np.concatenate([pts, -pts]).astype(np.float32)
+    Hkv, npages = 2, 12
+    n = -(-pts.size // (Hkv * 128))
+    x = np.resize(pts, n * Hkv * 128).reshape(n, Hkv, 128).astype(np.float32)
+    if dtype == "bf16":
+        x = (orc.f32_to_bf16_bits(x).astype(np.uint32) << 16).view(np.float32)
+    y = np.ascontiguousarray(x[::-1])
+    cache = api.CmpCache(fmt, npages, Hkv, 1.0, 1.0, fill=0x5A)
+    perm = np.random.default_rng(fmt).permutation(npages).astype(np.int32)
+    say(f"cmp append fmt {fmt} dtype {dtype}: {n} rows")
+    api.cmp_append(cache, to_dev(x, dtype), to_dev(y, dtype), i32(np.zeros(n)), i32(np.arange(n)), i32(perm[None]))
+    torch.cuda.synchronize()
+    from layout import CmpPlanes
+    R = CmpPlanes(cache.k.cpu().numpy(), cache.v.cpu().numpy(), npages, Hkv, fmt)
+    pages, slots = sequence_tokens(perm, n)
+    gk, gv = R.gather(pages, slots)
+    enc = (lambda a: orc.fp8_codes(a, 1.0)) if fmt == 1 else orc.f32_to_bf16_bits
+    np.testing.assert_array_equal(gk, enc(x))
+    np.testing.assert_array_equal(gv, enc(y))
+    # untouched rows keep the fill
+    mask = np.ones((npages, Hkv, 16), bool)
+    mask[pages, :, slots] = False
+    fillv = 0x5A if fmt == 1 else 0x5A5A
+    assert np.all(R.k[mask] == fillv) and np.all(R.v[mask] == fillv)
+
+
+CMP_DECODE_CASES = [
+    # seed, B, Hq, Hkv, lens, dtype
+    (3, 3, 4, 1, [15, 16, 17], "f32"),
+    (4, 4, 32, 8, [1, 100, 257, 1000], "bf16"),
+    (6, 5, 16, 2, [0, 31, 64, 65, 700], "bf16"),
+    (7, 2, 12, 4, [129, 2049], "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CMP_DECODE_CASES, ids=lambda c: f"s{c[0]}-B{c[1]}-G{c[2] // c[3]}")
+@pytest.mark.parametrize("fmt", [f for f, _ in CMP_FMTS], ids=[n for _, n in CMP_FMTS])
+def test_cmp_decode_parity_small(orc, fmt, case):
+    seed, B, Hq, Hkv, lens, dtype = case
+    w = W.custom_decode(seed, B, Hq, Hkv, lens, dtype=dtype, outliers=(seed % 2 == 0))
+    built = BuiltCmp(w, orc, fmt)
+    built.check_codes(range(B))
+    q = w.q(0)
+    say(f"cmp decode fmt {fmt} {case}")
+    out = built.decode(q).cpu().numpy()
+    ref, mag = built.oracle_decode(orc, q, range(B))
+    say("   ", check_decode(out, ref, mag, factor=CMP_FACTOR[fmt]))
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[b] == 0)
+
+
+@pytest.mark.parametrize("fmt", [f for f, _ in CMP_FMTS], ids=[n for _, n in CMP_FMTS])
+def test_cmp_decode_splits_f32_query_and_steps(orc, fmt):
+    """Wave counts 1 .. 5000 and automatic, an FP32 query, and appended
+    decode steps (one token per sequence) on a GQA 32/8 batch."""
+    w = W.custom_decode(12, 3, 32, 8, [1500, 77, 4000], dtype="bf16", outliers=True, steps=3)
+    built = BuiltCmp(w, orc, fmt)
+    q = w.q(0)
+    ref, mag = built.oracle_decode(orc, q, range(3))
+    outs = {}
+    for S in (1, 7, 64, 5000, 0):
+        say(f"cmp fmt {fmt} split S={S}")
+        outs[S] = built.decode(q, num_splits=S).cpu().numpy()
+        check_decode(outs[S], ref, mag, factor=CMP_FACTOR[fmt])
+    again = built.decode(q, num_splits=0).cpu().numpy()
+    assert np.array_equal(again, outs[0])                # run-to-run bitwise identical
+    qf = np.random.default_rng(7).standard_normal((3, 32, 128)).astype(np.float32)
+    say(f"cmp fmt {fmt} f32 query")
+    outf = built.decode(qf, dtype="f32").cpu().numpy()
+    check_decode(outf, *built.oracle_decode(orc, qf, range(3)), factor=CMP_FACTOR[fmt])
+    for step in range(w.steps):
+        built.append_step(step, orc)
+    built.check_codes(range(3))
+    q2 = w.q(1)
+    say(f"cmp fmt {fmt} after {w.steps} steps")
+    out2 = built.decode(q2).cpu().numpy()
+    check_decode(out2, *built.oracle_decode(orc, q2, range(3)), factor=CMP_FACTOR[fmt])

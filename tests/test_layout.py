@@ -41,3 +41,24 @@ def test_reader_matches_header_formulas():
     f = R2.untouched_fill(0xA5)
     assert np.array_equal(R2.vc, f[2])
     assert np.all(R2.vc[:, :, 0::2] == 5) and np.all(R2.vc[:, :, 1::2] == 0xA)
+
+
+def test_cmp_reader_matches_header_formulas():
+    from layout import CmpPlanes
+    rng = np.random.default_rng(1)
+    P_, H = 2, 3
+    for fmt, dt in ((1, np.uint8), (2, np.uint16)):
+        k = rng.integers(0, np.iinfo(dt).max, (P_, H, 16, 128), dtype=dt)
+        v = rng.integers(0, np.iinfo(dt).max, (P_, H, 16, 128), dtype=dt)
+        kb = np.zeros((P_, H, 16 * 128), dt)
+        vb = np.zeros((P_, H, 16 * 128), dt)
+        for p in range(P_):
+            for h in range(H):
+                for t in range(16):
+                    for d in range(128):
+                        kb[p, h, t * 128 + d] = k[p, h, t, d]                      # [token][element]
+                        vb[p, h, ((t // 4) * 128 + d) * 4 + t % 4] = v[p, h, t, d]  # [quad][element][t%4]
+        R = CmpPlanes(kb.ravel().view(np.uint8), vb.ravel().view(np.uint8), P_, H, fmt)
+        assert np.array_equal(R.k, k) and np.array_equal(R.v, v)
+        gk, gv = R.gather([1, 0], [5, 14])
+        assert np.array_equal(gk, k[[1, 0], :, [5, 14]]) and np.array_equal(gv, v[[1, 0], :, [5, 14]])
