@@ -47,9 +47,16 @@ def gen_decode(w, threads=16):
         return list(ex.map(w.kv, range(w.B)))
 
 
-def build_cache(api, torch, w, data, s_tk, s_tv, chunk=16):
-    from decode_attention_nvfp4_amd.workloads import round_bf16  # noqa: F401  (inputs already bf16)
-    cache = api.KVCache(w.num_pages, w.Hkv, s_tk, s_tv, fill=0)
+def build_cache(api, torch, w, data, s_tk, s_tv, chunk=16, fmt=None):
+    """The workload's cache in NVFP4 (fmt None; s_t the NVFP4 tensor scales)
+    or in a comparison format (api.CMP_FP8 with FP8 tensor scales s_t, or
+    api.CMP_BF16), built through the library's append."""
+    if fmt is None:
+        cache = api.KVCache(w.num_pages, w.Hkv, s_tk, s_tv, fill=0)
+        put = api.append
+    else:
+        cache = api.CmpCache(fmt, w.num_pages, w.Hkv, s_tk, s_tv, fill=0)
+        put = api.cmp_append
     pt = torch.from_numpy(w.page_table).cuda()
     for b0 in range(0, w.B, chunk):
         idx = range(b0, min(w.B, b0 + chunk))
@@ -57,11 +64,30 @@ def build_cache(api, torch, w, data, s_tk, s_tv, chunk=16):
         v = np.concatenate([data[b][1] for b in idx])
         seq = np.concatenate([np.full(len(data[b][0]), b, np.int32) for b in idx])
         pos = np.concatenate([np.arange(len(data[b][0]), dtype=np.int32) for b in idx])
-        api.append(cache, torch.from_numpy(k).to(torch.bfloat16).cuda(),
-                   torch.from_numpy(v).to(torch.bfloat16).cuda(),
-                   torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), pt)
+        put(cache, torch.from_numpy(k).to(torch.bfloat16).cuda(), torch.from_numpy(v).to(torch.bfloat16).cuda(),
+            torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), pt)
     torch.cuda.synchronize()
     return cache, pt
+
+
+# bytes per (token, KV head) of K and V in each cache format
+FORMAT_BYTES = {"nvfp4": 144, "fp8": 256, "bf16": 512}
+
+
+def format_caches(api, torch, w, data, nv_scales, amax):
+    """(name, cache, page table, decode fn) for NVFP4, FP8 and BF16 caches of
+    the same data; amax = (K amax, V amax) for the FP8 tensor scales."""
+    out = []
+    for name, fmt in (("nvfp4", None), ("fp8", api.CMP_FP8), ("bf16", api.CMP_BF16)):
+        if fmt is None:
+            s_k, s_v = nv_scales
+        elif fmt == api.CMP_FP8:
+            s_k, s_v = api.cmp_fp8_scale_from_amax(amax[0]), api.cmp_fp8_scale_from_amax(amax[1])
+        else:
+            s_k = s_v = 1.0
+        c, pt = build_cache(api, torch, w, data, s_k, s_v, fmt=fmt)
+        out.append((name, c, pt, api.decode if fmt is None else api.cmp_decode))
+    return out
 
 
 def device_scale(api, torch, arrays):
@@ -171,49 +197,87 @@ def stream_read_probe(api, torch, stream, gib=1, iters=10):
 
 
 def bench_small_decode(api, torch, stream, cfg, iters=20):
-    """Decode of configurations 2 (GQA batch 8, L 4096) and 3 (L 65536).  The
-    caches fit in the 256 MB last-level cache; to read from HBM the timing
-    rotates over 4 replicas (> 1 GB together with the flush buffer)."""
+    """Decode of configurations 2 (GQA batch 8, L 4096) and 3 (L 65536), in
+    NVFP4 and in the FP8 and BF16 comparison formats built from the same
+    data.  The caches fit in the 256 MB last-level cache; to read from HBM
+    the cold timing rotates over 4 replicas and fills a 512 MB buffer
+    between launches."""
     from decode_attention_nvfp4_amd import workloads as W
     w = W.decode_workload(cfg)
     data = gen_decode(w)
-    s_tk, _ = device_scale(api, torch, [d[0] for d in data])
-    s_tv, _ = device_scale(api, torch, [d[1] for d in data])
-    reps = [build_cache(api, torch, w, data, s_tk, s_tv) for _ in range(4)]
+    s_tk, amax_k = device_scale(api, torch, [d[0] for d in data])
+    s_tv, amax_v = device_scale(api, torch, [d[1] for d in data])
     q = torch.from_numpy(w.q(0)).to(torch.bfloat16).cuda()
     lens = torch.from_numpy(w.lens).cuda()
     L = int(w.lens.max())
     out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, api.decode_workspace_bytes(w.B, w.Hq, w.Hkv, L)), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(1, 2 * api.decode_workspace_bytes(w.B, w.Hq, w.Hkv, L)), dtype=torch.uint8,
+                     device="cuda")
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    state = {"i": 0}
+    res = {"workload": f"decode config {cfg}: batch {w.B}, {w.Hq}/{w.Hkv} heads, L {L}",
+           "splits": api.decode_num_splits(w.B, w.Hkv, L)}
+    reps = [format_caches(api, torch, w, data, (s_tk, s_tv), (amax_k, amax_v)) for _ in range(4)]
+    for f, name in enumerate(FORMAT_BYTES):
+        state = {"i": 0}
 
-    def one():
-        c, pt = reps[state["i"] % 4]
-        state["i"] += 1
-        api.decode(c, q, pt, lens, L, workspace=ws, out=out)
+        def one():
+            _, c, pt, fn = reps[state["i"] % 4][f]
+            state["i"] += 1
+            fn(c, q, pt, lens, L, workspace=ws, out=out)
 
-    one(); torch.cuda.synchronize()
-    # cold: flush the caches between launches; time only the decode launches
-    times = []
-    for _ in range(iters):
-        flush.fill_(1)
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        one()
-        e.record(stream)
-        e.synchronize()
-        times.append(s.elapsed_time(e))
-    t_cold = float(np.median(times))
-    t_warm = time_region(torch, lambda: api.decode(reps[0][0], q, reps[0][1], lens, L, workspace=ws, out=out),
-                         iters, stream)
-    nbytes = int(w.lens.sum()) * w.Hkv * BYTES_PER_TOKEN_HEAD
-    return {"workload": f"decode config {cfg}: batch {w.B}, {w.Hq}/{w.Hkv} heads, L {L}",
-            "cache_mb": round(nbytes / 1e6, 2), "cold_us": round(t_cold * 1e3, 2),
-            "cold_gbs": round(nbytes / t_cold / 1e6, 1), "warm_us": round(t_warm * 1e3, 2),
-            "warm_gbs": round(nbytes / t_warm / 1e6, 1),
-            "splits": api.decode_num_splits(w.B, w.Hkv, L)}
+        one(); torch.cuda.synchronize()
+        times = []
+        for _ in range(iters):
+            flush.fill_(1)
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            one()
+            e.record(stream)
+            e.synchronize()
+            times.append(s.elapsed_time(e))
+        t_cold = float(np.median(times))
+        _, c0, pt0, fn0 = reps[0][f]
+        t_warm = time_region(torch, lambda: fn0(c0, q, pt0, lens, L, workspace=ws, out=out), iters, stream)
+        nbytes = int(w.lens.sum()) * w.Hkv * FORMAT_BYTES[name]
+        entry = {"cache_mb": round(nbytes / 1e6, 2), "cold_us": round(t_cold * 1e3, 2),
+                 "cold_gbs": round(nbytes / t_cold / 1e6, 1), "warm_us": round(t_warm * 1e3, 2),
+                 "warm_gbs": round(nbytes / t_warm / 1e6, 1)}
+        if name == "nvfp4":
+            res.update(entry)
+        else:
+            res[name] = entry
+    for name in ("fp8", "bf16"):
+        res[f"nvfp4_speedup_vs_{name}_cold"] = round(res[name]["cold_us"] / res["cold_us"], 3)
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_formats_cfg4(api, torch, stream, w, data, nv_scales, amax, q_np, iters=10):
+    """Configuration 4's decode (batch 128, L_b ~ U[1024, 8192], permuted
+    pages) over NVFP4, FP8 and BF16 caches of the same data: the speed ratio
+    of the formats on one GPU.  Every cache exceeds the 256 MB last-level
+    cache, so each call streams it from HBM."""
+    q = torch.from_numpy(q_np).to(torch.bfloat16).cuda()
+    lens = torch.from_numpy(w.lens.astype(np.int32)).cuda()
+    L = int(w.lens.max())
+    out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, 2 * api.decode_workspace_bytes(w.B, w.Hq, w.Hkv, L)), dtype=torch.uint8,
+                     device="cuda")
+    res = {"workload": "decode config 4: batch 128, 32/8 heads, context U[1024,8192], same data per format"}
+    for name, c, pt, fn in format_caches(api, torch, w, data, nv_scales, amax):
+        fn(c, q, pt, lens, L, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        t = time_region(torch, lambda: fn(c, q, pt, lens, L, workspace=ws, out=out), iters, stream)
+        nbytes = int(w.lens.sum()) * w.Hkv * FORMAT_BYTES[name]
+        res[name] = {"cache_mb": round(nbytes / 1e6, 1), "us": round(t * 1e3, 2),
+                     "gbs": round(nbytes / t / 1e6, 1), "frac_hbm_peak": round(nbytes / t / 1e6 / HBM_PEAK_GBS, 4)}
+        del c
+        torch.cuda.empty_cache()
+    for name in ("fp8", "bf16"):
+        res[f"nvfp4_speedup_vs_{name}"] = round(res[name]["us"] / res["nvfp4"]["us"], 3)
+    return res
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_paged_b128_traffic.json")
@@ -470,6 +534,12 @@ def main():
             except Exception as e:  # noqa: BLE001
                 res["extra"][f"decode_cfg{cfg}"] = {"error": repr(e)}
             log(f"decode config {cfg}: {res['extra'][f'decode_cfg{cfg}']}")
+        try:
+            res["extra"]["kv_formats_cfg4"] = bench_formats_cfg4(api, torch, stream, w, data, (s_tk, s_tv),
+                                                                 (amax_k, amax_v), q_np)
+        except Exception as e:  # noqa: BLE001
+            res["extra"]["kv_formats_cfg4"] = {"error": repr(e)}
+        log(f"kv formats: {res['extra']['kv_formats_cfg4']}")
         try:
             res["extra"]["prefill_cfg5"] = bench_prefill(api, torch, stream)
         except Exception as e:  # noqa: BLE001
