@@ -40,6 +40,15 @@
  *  - Dequantization multiplies by s_t, which is dividing by the global
  *    encode scale g = 1/s_t ([GB10] §這個 80 行的 Triton 繞道: the global
  *    scale must divide, not multiply).
+ *  - MSE-searched block scale ([EXPL] §E2M1 + 2レベルスケーリング describes
+ *    the E4M3 block scale as chosen for least squared error, with no
+ *    procedure): among the E4M3 codes within 8 of the amax/6 code (code 0
+ *    excluded), the one whose element codes give the smallest squared error
+ *    of the block against the
+ *    exact products e2m1 * s_block * s_t; the error is summed in double over
+ *    elements 0..15 in order, each operation rounded once (no fused
+ *    multiply-add); ties go to the candidate nearest the amax/6 code, then
+ *    to the smaller code.  A block whose amax/6 code is 0 keeps 0.
  *  - The comparison formats.  FP8 KV cache ([EXPL] and [TRTL] set NVFP4
  *    against an FP8 cache without defining it): every element is the E4M3
  *    value nearest to x / s_t8 (FP32 quotient), ties to the even code,
@@ -185,6 +194,65 @@ void orc_quantize_rows(const float* x, size_t nrows, float s_t,
         unsigned e = j * ORC_BLOCK + i;
         codes[r * ORC_D + e] = (uint8_t)orc_element_code(row[e], sb, s_t);
       }
+    }
+  }
+}
+
+/* ------------------------------------------ MSE-searched block scale */
+
+#define ORC_MSE_RADIUS 8
+
+/* Squared error of a 16-element block under block-scale code sb: the sum
+ * over e = 0..15, in order, of (x_e - e2m1(code_e) * sb * s_t)^2, with the
+ * element codes of orc_element_code.  The product is exact in double; the
+ * difference, the square and each partial sum are rounded once. */
+double orc_block_sq_error(const float* x, unsigned sb, float s_t) {
+  double sum = 0.0;
+  for (unsigned e = 0; e < ORC_BLOCK; ++e) {
+    unsigned c = orc_element_code(x[e], sb, s_t);
+    double p = orc_e2m1_value(c) * orc_e4m3_value(sb) * (double)s_t;
+    double d = (double)x[e] - p;
+    double sq = d * d;
+    sum = sum + sq;
+  }
+  return sum;
+}
+
+/* The MSE-searched block-scale code of x[0..15] (rule in the header). */
+unsigned orc_block_scale_code_mse(const float* x, float s_t) {
+  float amax = 0.0f;
+  for (unsigned e = 0; e < ORC_BLOCK; ++e) {
+    float a = fabsf(x[e]);
+    if (a > amax) amax = a;
+  }
+  unsigned c0 = orc_block_scale_code(amax, s_t);
+  if (c0 == 0u) return 0u;
+  unsigned best = c0;
+  double best_err = orc_block_sq_error(x, c0, s_t);
+  for (int dist = 1; dist <= ORC_MSE_RADIUS; ++dist) {
+    for (int sgn = -1; sgn <= 1; sgn += 2) {      /* the smaller code first */
+      int c = (int)c0 + sgn * dist;
+      if (c < 1 || c > 126) continue;
+      double err = orc_block_sq_error(x, (unsigned)c, s_t);
+      if (err < best_err) {
+        best = (unsigned)c;
+        best_err = err;
+      }
+    }
+  }
+  return best;
+}
+
+/* quantize_rows with the MSE-searched block scale. */
+void orc_quantize_rows_mse(const float* x, size_t nrows, float s_t,
+                           uint8_t* codes, uint8_t* scales) {
+  for (size_t r = 0; r < nrows; ++r) {
+    const float* row = x + r * ORC_D;
+    for (unsigned blk = 0; blk < ORC_NBLK; ++blk) {
+      unsigned sb = orc_block_scale_code_mse(row + blk * ORC_BLOCK, s_t);
+      scales[r * ORC_NBLK + blk] = (uint8_t)sb;
+      for (unsigned e = blk * ORC_BLOCK; e < (blk + 1) * ORC_BLOCK; ++e)
+        codes[r * ORC_D + e] = (uint8_t)orc_element_code(row[e], sb, s_t);
     }
   }
 }

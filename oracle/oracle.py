@@ -77,6 +77,12 @@ def lib():
                                            _u8p, _u8p, ctypes.c_float,
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_double, _f64p, _f32p]
+            L.orc_block_sq_error.restype = ctypes.c_double
+            L.orc_block_sq_error.argtypes = [_f32p, ctypes.c_uint, ctypes.c_float]
+            L.orc_block_scale_code_mse.restype = ctypes.c_uint
+            L.orc_block_scale_code_mse.argtypes = [_f32p, ctypes.c_float]
+            L.orc_quantize_rows_mse.restype = None
+            L.orc_quantize_rows_mse.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_float, _u8p, _u8p]
             L.orc_fp8_tensor_scale_from_amax.restype = ctypes.c_float
             L.orc_fp8_tensor_scale_from_amax.argtypes = [ctypes.c_float]
             L.orc_fp8_code.restype = ctypes.c_uint
@@ -166,6 +172,34 @@ def quantize_rows(x, s_t: float):
     scales = np.empty((n, NBLK), np.uint8)
     if n:
         lib().orc_quantize_rows(_p(flat, _f32p), n, float(s_t), _p(codes, _u8p), _p(scales, _u8p))
+    return codes.reshape(shape), scales.reshape(shape[:-1] + (NBLK,))
+
+
+def block_sq_error(x16, sb_code: int, s_t: float) -> float:
+    """Squared error of one 16-element block under block-scale code sb_code
+    (the MSE search's criterion, summed in element order)."""
+    x16 = _c(x16, np.float32)
+    assert x16.size == BLOCK
+    return float(lib().orc_block_sq_error(_p(x16, _f32p), int(sb_code), float(s_t)))
+
+
+def block_scale_code_mse(x16, s_t: float) -> int:
+    x16 = _c(x16, np.float32)
+    assert x16.size == BLOCK
+    return int(lib().orc_block_scale_code_mse(_p(x16, _f32p), float(s_t)))
+
+
+def quantize_rows_mse(x, s_t: float):
+    """quantize_rows with the MSE-searched block scale."""
+    x = _c(x, np.float32)
+    shape = x.shape
+    assert shape[-1] == D
+    flat = x.reshape(-1, D)
+    n = flat.shape[0]
+    codes = np.empty((n, D), np.uint8)
+    scales = np.empty((n, NBLK), np.uint8)
+    if n:
+        lib().orc_quantize_rows_mse(_p(flat, _f32p), n, float(s_t), _p(codes, _u8p), _p(scales, _u8p))
     return codes.reshape(shape), scales.reshape(shape[:-1] + (NBLK,))
 
 
