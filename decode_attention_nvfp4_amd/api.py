@@ -62,6 +62,7 @@ _SIGS = {
     "nvfp4_tensor_scale_from_amax": (_F, [_F]),
     "nvfp4_abs_max": (_I32, [_VP, _I32, _I64, _VP, _VP]),
     "nvfp4_kv_append": (_I32, [_CP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
+    "nvfp4_kv_append_mse": (_I32, [_CP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
     "nvfp4_kv_dequant": (_I32, [_CP, _VP, _I32, _I32, _VP, _VP, _I32, _VP]),
     "nvfp4_decode_num_splits": (_I32, [_I32, _I32, _I32, _I32]),
     "nvfp4_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
@@ -204,6 +205,15 @@ def abs_max(x: torch.Tensor, stream=None) -> torch.Tensor:
 
 def append(cache: KVCache, k_new, v_new, tok_seq, tok_pos, page_table, stream=None):
     """Quantize rows k_new/v_new [n][Hkv][128] into the cache at (tok_seq, tok_pos)."""
+    _append("nvfp4_kv_append", cache, k_new, v_new, tok_seq, tok_pos, page_table, stream)
+
+
+def append_mse(cache: KVCache, k_new, v_new, tok_seq, tok_pos, page_table, stream=None):
+    """append() with the MSE-searched block scale."""
+    _append("nvfp4_kv_append_mse", cache, k_new, v_new, tok_seq, tok_pos, page_table, stream)
+
+
+def _append(name, cache, k_new, v_new, tok_seq, tok_pos, page_table, stream):
     n = k_new.shape[0] if k_new.dim() else 0
     for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
         _dev(t, nm)
@@ -217,7 +227,7 @@ def append(cache: KVCache, k_new, v_new, tok_seq, tok_pos, page_table, stream=No
     if tok_seq.numel() < n or tok_pos.numel() < n:
         raise ValueError("tok_seq / tok_pos shorter than the number of rows")
     cs = cache.struct()
-    _check("nvfp4_kv_append", lib().nvfp4_kv_append(
+    _check(name, getattr(lib(), name)(
         ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), n, _ptr(tok_seq),
         _ptr(tok_pos), _ptr(page_table), page_table.shape[-1], _stream(stream)))
 

@@ -29,9 +29,10 @@ def hipcc() -> str:
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
-    # FP32 packed math stays off; IEEE-correct FP32 division and square root
+    # FP32 packed math stays off; IEEE-correct FP32 division and square root;
+    # multiply-adds are fused except where a source turns contraction off
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math", "-ffp-contract=fast",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math", "-ffp-contract=fast-honor-pragmas",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]

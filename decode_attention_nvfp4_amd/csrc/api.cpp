@@ -139,10 +139,10 @@ int32_t nvfp4_abs_max(const void* x, int32_t dtype, int64_t n, float* amax_out, 
                     "abs_max launch");
 }
 
-int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
-                        int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
-                        const int32_t* tok_pos, const int32_t* page_table,
-                        int32_t max_pages_per_seq, void* stream) {
+static int32_t append_call(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
+                           int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                           const int32_t* tok_pos, const int32_t* page_table,
+                           int32_t max_pages_per_seq, bool mse, void* stream) {
   g_err[0] = 0;
   int32_t st = check_cache(cache);
   if (st) return st;
@@ -168,7 +168,23 @@ int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const vo
   a.k_new = k_new; a.v_new = v_new;
   a.tok_seq = tok_seq; a.tok_pos = tok_pos; a.page_table = page_table;
   a.max_pages = max_pages_per_seq; a.n_tok = n_tok; a.hkv = cache->num_kv_heads;
-  return hip_status(launch_append(a, dtype == NVFP4_DTYPE_F32, (hipStream_t)stream), "append launch");
+  return hip_status(launch_append(a, dtype == NVFP4_DTYPE_F32, mse, (hipStream_t)stream), "append launch");
+}
+
+int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
+                        int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                        const int32_t* tok_pos, const int32_t* page_table,
+                        int32_t max_pages_per_seq, void* stream) {
+  return append_call(cache, k_new, v_new, dtype, n_tok, tok_seq, tok_pos, page_table, max_pages_per_seq,
+                     false, stream);
+}
+
+int32_t nvfp4_kv_append_mse(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
+                            int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                            const int32_t* tok_pos, const int32_t* page_table,
+                            int32_t max_pages_per_seq, void* stream) {
+  return append_call(cache, k_new, v_new, dtype, n_tok, tok_seq, tok_pos, page_table, max_pages_per_seq,
+                     true, stream);
 }
 
 int32_t nvfp4_kv_dequant(const nvfp4_kv_cache* cache, const int32_t* page_table_row,

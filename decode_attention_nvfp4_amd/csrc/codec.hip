@@ -60,6 +60,84 @@ __device__ __forceinline__ uint32_t quantize_half_block(const float x[8], float 
   return encode8(x, code, s_t);
 }
 
+// ------------------------------------------------ MSE-searched block scale
+//
+// The block scale may instead be searched ("NVIDIA解説: NVFP4 KV Cacheで長コン
+// テキストLLM推論を最適化", section E2M1 + 2レベルスケーリング, describes the
+// NVFP4 block scale as chosen for least squared error): the E4M3 codes within
+// kMseRadius of the amax/6 code (code 0 excluded) are tried and the one whose
+// element codes give the smallest squared error of the block is kept.  The
+// error of a candidate is summed in double over the block's elements in
+// order, every operation rounded once (no fused multiply-add); ties go to
+// the candidate nearest the amax/6 code, then to the smaller code.  A zero
+// amax/6 code stays zero.
+constexpr int kMseRadius = 8;
+
+// Squared error of the 16-element block xb under block-scale code c.  The
+// product e2m1 * s_block * s_t is exact in double (3 + 4 + 24 significant
+// bits); |x| - |p| has the magnitude of x - p because an element's code
+// carries the sign of x.
+__device__ __forceinline__ double block_sq_error(const float xb[16], uint32_t c, float s_t) {
+#pragma clang fp contract(off)
+  const uint32_t w0 = encode8(xb, c, s_t), w1 = encode8(xb + 8, c, s_t);
+  const double step = (double)e4m3_to_float(c) * (double)s_t;
+  double sum = 0.0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t m = ((e < 8 ? w0 >> (4 * e) : w1 >> (4 * (e - 8)))) & 7u;
+    const double g = m < 4u ? 0.5 * (double)m : (m == 7u ? 6.0 : (double)m - 2.0);
+    const double d = (double)fabsf(xb[e]) - g * step;
+    sum = sum + d * d;
+  }
+  return sum;
+}
+
+// quantize_half_block with the searched scale.  The lane pair swaps halves
+// so both hold the block's 16 elements in order; search position k = 0 is
+// the amax/6 code, k = 2j - 1 and 2j its neighbours at distance j below and
+// above.  The even lane tries the even positions, the odd lane the odd ones,
+// and the pair keeps the smallest (error, position); an unusable position
+// (code outside 1..126) is skipped.  Non-finite errors (non-finite inputs)
+// compare as ties, so the amax/6 code is kept, as in a plain ordered scan.
+__device__ __forceinline__ uint32_t quantize_half_block_mse(const float x[8], float s_t, float inv6,
+                                                            double six_st, uint32_t* sb) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
+  a = fmaxf(a, __shfl_xor(a, 1));
+  const int c0 = (int)block_scale_code_fast(a, inv6, six_st);
+  const int odd = (int)(threadIdx.x & 1);
+  float xb[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float o = __shfl_xor(x[j], 1);
+    xb[j] = odd ? o : x[j];
+    xb[8 + j] = odd ? x[j] : o;
+  }
+  uint32_t code = 0u;
+  if (c0 != 0) {
+    // a lane may have no usable position (the odd lane when c0 is 1): its
+    // (inf, past-the-end) then loses to any of its partner's
+    double best = __builtin_huge_val();
+    int best_k = 2 * kMseRadius + 1;
+    for (int k = odd; k <= 2 * kMseRadius; k += 2) {
+      const int c = k == 0 ? c0 : ((k & 1) ? c0 - (k + 1) / 2 : c0 + k / 2);
+      if (c < 1 || c > 126) continue;
+      const double err = block_sq_error(xb, (uint32_t)c, s_t);
+      if (best_k > 2 * kMseRadius || err < best) {
+        best = err;
+        best_k = k;
+      }
+    }
+    const double o_best = __shfl_xor(best, 1);
+    const int o_k = __shfl_xor(best_k, 1);
+    if (o_best < best || (!(best < o_best) && o_k < best_k)) best_k = o_k;
+    code = (uint32_t)(best_k == 0 ? c0 : ((best_k & 1) ? c0 - (best_k + 1) / 2 : c0 + best_k / 2));
+  }
+  *sb = code;
+  return encode8(x, code, s_t);
+}
+
 // Eight nibbles (element e in bits 4e..4e+3) spread to the low nibbles of
 // eight bytes: elements 0..3 in *w0, 4..7 in *w1.
 __device__ __forceinline__ void spread_nibbles(uint32_t w, uint32_t* w0, uint32_t* w1) {
@@ -76,7 +154,7 @@ __device__ __forceinline__ void spread_nibbles(uint32_t w, uint32_t* w0, uint32_
 // and 2i+1) the even row writes the whole bytes; a token whose partner is
 // elsewhere updates its nibbles with atomic AND / OR, which commute with the
 // partner's own update of the other nibbles.
-template <bool F32IN>
+template <bool F32IN, bool MSE>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
   const int lane16 = threadIdx.x & 15, r = threadIdx.x >> 4;
   const int tok = blockIdx.x * 16 + r;
@@ -109,9 +187,11 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
     uint32_t ksb;
     float x[8];
     unpack8<F32IN>(rk, x);
-    const uint32_t kw = quantize_half_block(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
+    const uint32_t kw = MSE ? quantize_half_block_mse(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb)
+                            : quantize_half_block(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
     unpack8<F32IN>(rv, x);
-    vw = quantize_half_block(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
+    vw = MSE ? quantize_half_block_mse(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb)
+             : quantize_half_block(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
     slab = (size_t)page * p.hkv + h;
     // K: token-major codes [16][64 B], token-major scales [16][8]
     *reinterpret_cast<uint32_t*>(p.k_codes + slab * kSlab + slot * 64 + lane16 * 4) = kw;
@@ -206,10 +286,15 @@ hipError_t launch_cmp_append(const CmpAppendArgs& a, bool f32, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendArgs& a, bool f32, hipStream_t s) {
+hipError_t launch_append(const AppendArgs& a, bool f32, bool mse, hipStream_t s) {
   const dim3 grid((unsigned)((a.n_tok + 15) / 16), (unsigned)a.hkv);
-  if (f32) append_kernel<true><<<grid, 256, 0, s>>>(a);
-  else append_kernel<false><<<grid, 256, 0, s>>>(a);
+  if (mse) {
+    if (f32) append_kernel<true, true><<<grid, 256, 0, s>>>(a);
+    else append_kernel<false, true><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (f32) append_kernel<true, false><<<grid, 256, 0, s>>>(a);
+    else append_kernel<false, false><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 

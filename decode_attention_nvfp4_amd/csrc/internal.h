@@ -100,7 +100,7 @@ struct PrefillArgs {
   int32_t mode;               // kPrefillFP8 or kPrefillF16
 };
 
-hipError_t launch_append(const AppendArgs& a, bool f32_in, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, bool f32_in, bool mse, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, bool f32_out, hipStream_t s);
 hipError_t launch_absmax(const void* x, bool f32_in, int64_t n, float* out, hipStream_t s);
 hipError_t launch_cmp_append(const CmpAppendArgs& a, bool f32_in, hipStream_t s);

@@ -143,6 +143,22 @@ int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const vo
                         const int32_t* tok_pos, const int32_t* page_table,
                         int32_t max_pages_per_seq, void* stream);
 
+/* Quantize-on-append with a searched block scale ([EXPL] §E2M1 + 2レベル
+ * スケーリング describes the NVFP4 block scale as chosen for least squared
+ * error, without a procedure).  Arguments, layout, ownership and errors are
+ * those of nvfp4_kv_append; only the block scale differs: among the E4M3
+ * codes within 8 of the amax/6 code (code 0 excluded), the one whose element
+ * codes (the usual nearest-even rounding) give the smallest squared error
+ * sum_e (x_e - e2m1_e * s_block * s_t)^2 over the block, summed in double in
+ * element order with every operation rounded once; ties go to the candidate
+ * nearest the amax/6 code, then to the smaller code.  A block whose amax/6
+ * code is 0 keeps scale 0.  The cache is read by the same decode and prefill
+ * calls. */
+int32_t nvfp4_kv_append_mse(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
+                            int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                            const int32_t* tok_pos, const int32_t* page_table,
+                            int32_t max_pages_per_seq, void* stream);
+
 /* Dequantization (step A10, for checks and fallbacks): positions
  * pos0 .. pos0+n-1 of the sequence whose page-table row is page_table_row
  * (device int32, at least ceil((pos0+n)/16) entries) into k_out and v_out,

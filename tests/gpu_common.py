@@ -87,8 +87,11 @@ class BuiltDecode:
     """A decode workload appended into a device cache, plus the oracle's
     logical codes for the sequences it may check."""
 
-    def __init__(self, w: W.DecodeWorkload, oracle, keep=None, fill=0xA5, chunk=16):
+    def __init__(self, w: W.DecodeWorkload, oracle, keep=None, fill=0xA5, chunk=16, mse=False):
         self.w = w
+        # mse: the cache is written with the MSE-searched block scale
+        self._append = api.append_mse if mse else api.append
+        self._quant = oracle.quantize_rows_mse if mse else oracle.quantize_rows
         self.keep = set(range(w.B)) if keep is None else set(keep)
         data = [w.kv(b) for b in range(w.B)]
         # tensor scales: static calibration over the whole tensor (all
@@ -106,11 +109,11 @@ class BuiltDecode:
                 seqs.append(np.full(len(k), b, np.int32))
                 poss.append(np.arange(len(k), dtype=np.int32))
                 if b in self.keep:
-                    self.codes[b] = (*oracle.quantize_rows(k, self.s_tk), *oracle.quantize_rows(v, self.s_tv))
+                    self.codes[b] = (*self._quant(k, self.s_tk), *self._quant(v, self.s_tv))
             k = np.concatenate(ks)
             if len(k) == 0:
                 continue
-            api.append(self.cache, to_dev(k, w.dtype), to_dev(np.concatenate(vs), w.dtype),
+            self._append(self.cache, to_dev(k, w.dtype), to_dev(np.concatenate(vs), w.dtype),
                        i32(np.concatenate(seqs)), i32(np.concatenate(poss)), self.pt)
         del data
         self.lens = w.lens.copy()
@@ -120,11 +123,11 @@ class BuiltDecode:
         w = self.w
         k, v = w.append_kv(step)
         pos = self.lens.copy()
-        api.append(self.cache, to_dev(k, w.dtype), to_dev(v, w.dtype), i32(np.arange(w.B)), i32(pos), self.pt)
+        self._append(self.cache, to_dev(k, w.dtype), to_dev(v, w.dtype), i32(np.arange(w.B)), i32(pos), self.pt)
         if oracle is not None:
             for b in self.keep:
-                kc, ksc = oracle.quantize_rows(k[b:b + 1], self.s_tk)
-                vc, vsc = oracle.quantize_rows(v[b:b + 1], self.s_tv)
+                kc, ksc = self._quant(k[b:b + 1], self.s_tk)
+                vc, vsc = self._quant(v[b:b + 1], self.s_tv)
                 c = self.codes[b]
                 self.codes[b] = (np.concatenate([c[0], kc]), np.concatenate([c[1], ksc]),
                                  np.concatenate([c[2], vc]), np.concatenate([c[3], vsc]))

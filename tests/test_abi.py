@@ -63,28 +63,32 @@ def _fake_cache(api, **kw):
 FAKE = ctypes.c_void_p(0x50000)
 
 
-def _append(api, cache, dtype=1, n_tok=4, max_pages=8, ptrs=True):
+def _append(api, cache, dtype=1, n_tok=4, max_pages=8, ptrs=True, name="nvfp4_kv_append"):
     p = FAKE if ptrs else None
-    return api.lib().nvfp4_kv_append(ctypes.byref(cache), p, p, dtype, n_tok, p, p, p, max_pages, None)
+    return getattr(api.lib(), name)(ctypes.byref(cache), p, p, dtype, n_tok, p, p, p, max_pages, None)
 
 
-def test_append_rejects_bad_arguments(api):
+@pytest.mark.parametrize("name", ["nvfp4_kv_append", "nvfp4_kv_append_mse"])
+def test_append_rejects_bad_arguments(api, name):
     L = api.lib()
-    assert L.nvfp4_kv_append(None, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == 1
-    assert _append(api, _fake_cache(api, head_dim=64)) == 2
-    assert _append(api, _fake_cache(api, page_size=32)) == 2
-    assert _append(api, _fake_cache(api, k_tensor_scale=0.0)) == 1
-    assert _append(api, _fake_cache(api, v_tensor_scale=-1.0)) == 1
-    assert _append(api, _fake_cache(api, k_tensor_scale=float("nan"))) == 1
-    assert _append(api, _fake_cache(api, k_tensor_scale=float("inf"))) == 1
-    assert _append(api, _fake_cache(api, k_codes=0x10008)) == 1        # misaligned plane
-    assert _append(api, _fake_cache(api, v_scales=None)) == 1
-    assert _append(api, _fake_cache(api, num_pages=0)) == 1
-    assert _append(api, _fake_cache(api), dtype=7) == 2
-    assert _append(api, _fake_cache(api), n_tok=-1) == 1
-    assert _append(api, _fake_cache(api), max_pages=0) == 1
-    assert _append(api, _fake_cache(api), ptrs=False) == 1
-    assert _append(api, _fake_cache(api), n_tok=0, ptrs=False) == 0     # empty append: no-op
+    assert getattr(L, name)(None, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 8, None) == 1
+
+    def ap(cache, **kw):
+        return _append(api, cache, name=name, **kw)
+    assert ap(_fake_cache(api, head_dim=64)) == 2
+    assert ap(_fake_cache(api, page_size=32)) == 2
+    assert ap(_fake_cache(api, k_tensor_scale=0.0)) == 1
+    assert ap(_fake_cache(api, v_tensor_scale=-1.0)) == 1
+    assert ap(_fake_cache(api, k_tensor_scale=float("nan"))) == 1
+    assert ap(_fake_cache(api, k_tensor_scale=float("inf"))) == 1
+    assert ap(_fake_cache(api, k_codes=0x10008)) == 1        # misaligned plane
+    assert ap(_fake_cache(api, v_scales=None)) == 1
+    assert ap(_fake_cache(api, num_pages=0)) == 1
+    assert ap(_fake_cache(api), dtype=7) == 2
+    assert ap(_fake_cache(api), n_tok=-1) == 1
+    assert ap(_fake_cache(api), max_pages=0) == 1
+    assert ap(_fake_cache(api), ptrs=False) == 1
+    assert ap(_fake_cache(api), n_tok=0, ptrs=False) == 0     # empty append: no-op
 
 
 def test_dequant_rejects_bad_arguments(api):

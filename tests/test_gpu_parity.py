@@ -176,6 +176,94 @@ def test_append_edge_values(orc):
             assert np.array_equal(g, e), (dtype, nm, np.argwhere(g != e)[:5].tolist())
 
 
+# ------------------------------------------- MSE-searched block scale
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dist", ["normal", "outlier", "mixed", "tiny"])
+def test_append_mse_bit_exact_and_sentinel(orc, dtype, dist):
+    """The searched block scale: random scatter into a sentinel-filled cache;
+    codes and scales equal the oracle's search, other bytes keep 0xA5."""
+    rng = np.random.default_rng(100 + ["normal", "outlier", "mixed", "tiny"].index(dist) * 2 + (dtype == "f32"))
+    B, Hkv, max_pages, num_pages = 3, 4, 6, 24
+    pt = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    n = 150
+    slots = rng.choice(B * max_pages * 16, n, replace=False)
+    seq = (slots // (max_pages * 16)).astype(np.int32)
+    pos = (slots % (max_pages * 16)).astype(np.int32)
+    k = W.random_rows(20, n * Hkv, dist, dtype).reshape(n, Hkv, 128)
+    v = W.random_rows(21, n * Hkv, dist, dtype).reshape(n, Hkv, 128)
+    stk, stv = orc.tensor_scale(k) * 0.8, orc.tensor_scale(v)
+    cache = api.KVCache(num_pages, Hkv, stk, stv, fill=0xA5)
+    say(f"append_mse {dtype} {dist} n={n}")
+    api.append_mse(cache, to_dev(k, dtype), to_dev(v, dtype), i32(seq), i32(pos), i32(pt))
+    P = planes(cache)
+    pages = pt[seq, pos // 16]
+    got = P.gather(pages, pos % 16)
+    exp = (*orc.quantize_rows_mse(k, stk), *orc.quantize_rows_mse(v, stv))
+    for g, e, nm in zip(got, exp, ("k codes", "k scales", "v codes", "v scales")):
+        bad = np.argwhere(g != e)
+        assert bad.size == 0, (nm, bad[:5].tolist())
+    masks = P.touched_mask(pages, pos % 16)
+    for arr, m, f in zip(P.arrays(), masks, P.untouched_fill(0xA5)):
+        assert np.array_equal(arr[~m], f[~m])
+    if dist == "normal":
+        # the search never loses to amax/6 and changes many blocks
+        base = orc.quantize_rows(k, stk)
+        assert np.mean(got[1] != base[1]) > 0.3
+
+
+def test_append_mse_closed_forms_and_edges(orc):
+    """Blocks whose search result is fixed by hand (ties to the amax/6 code,
+    equal-distance ties to the smaller code, a clipping scale that wins),
+    scale-range ends, zeros, underflow and saturation."""
+    rows = []
+    r = np.zeros(128, np.float32)
+    r[0] = 6.0                                   # exact at 1.0, 1.5 and 2.0: keeps 1.0
+    r[16] = 6.0625
+    r[17:23] = 3.5                               # 0.9375 and 1.125 tie: keeps 0.9375
+    r[32] = 6.0
+    r[33:48] = 4.9                               # a smaller, clipping scale wins
+    r[48:64] = np.linspace(-1, 1, 16) * 6 * 2.0 ** -9   # amax/6 code 1: searches upwards only
+    r[64:80] = 1e-30                             # amax/6 code 0
+    r[80:96] = -0.0
+    r[96] = 3e4                                  # the amax/6 code saturates at 448
+    r[97:112] = np.linspace(-5e3, 5e3, 15)
+    r[112:128] = np.linspace(-1, 1, 16)
+    rows.append(r)
+    rows.append(-r)
+    rows.append(r * np.float32(0.75))
+    x = np.stack(rows).reshape(len(rows), 1, 128)
+    st = 1.0
+    say("append_mse closed forms")
+    sc = orc.quantize_rows_mse(x, st)[1]
+    assert sc[0, 0, 0] == 0x38 and sc[0, 0, 1] == 0x37 and sc[0, 0, 2] not in (0, 0x38)
+    assert sc[0, 0, 4] == 0 and sc[0, 0, 5] == 0 and orc.block_scale_code(6 * 2.0 ** -9, st) == 1
+    for dtype in ("f32", "bf16"):
+        xx = x if dtype == "f32" else W.round_bf16(x)
+        n = xx.shape[0]
+        cache = api.KVCache(4, 1, st, st, fill=0xA5)
+        pt = np.arange(4, dtype=np.int32)[None]
+        say(f"append_mse edges {dtype}")
+        api.append_mse(cache, to_dev(xx, dtype), to_dev(-xx, dtype), i32(np.zeros(n)), i32(np.arange(n)), i32(pt))
+        P = planes(cache)
+        got = P.gather(np.zeros(n, int), np.arange(n))
+        exp = (*orc.quantize_rows_mse(xx, st), *orc.quantize_rows_mse(-xx, st))
+        for g, e, nm in zip(got, exp, ("k codes", "k scales", "v codes", "v scales")):
+            assert np.array_equal(g, e), (dtype, nm, np.argwhere(g != e)[:5].tolist())
+
+
+def test_decode_over_mse_cache(orc):
+    """The decode path reads a cache written with the searched scale
+    unchanged: parity with the oracle's attention over the oracle's codes."""
+    w = W.custom_decode(12, 3, 32, 8, [200, 1100, 17], dtype="bf16", outliers=True)
+    built = BuiltDecode(w, orc, mse=True)
+    built.check_codes(range(3))
+    q = w.q(0)
+    say("decode over MSE cache")
+    out = built.decode(q).cpu().numpy()
+    check_decode(out, *built.oracle_decode(orc, q, range(3)))
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_dequant_bit_exact(orc, out_dtype):
     w = W.custom_decode(1, 2, 8, 4, [37, 70], dtype="bf16")
