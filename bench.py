@@ -280,6 +280,74 @@ def bench_formats_cfg4(api, torch, stream, w, data, nv_scales, amax, q_np, iters
     return res
 
 
+def bench_mse_scale(api, torch, stream, w, data, scales, q_np, sample=8, iters=3):
+    """The MSE-searched block scale against amax/6 on configuration 4's data:
+    bulk-append time of the whole cache under each rule, the quantization
+    error of K and V, and the decode output's error against attention over
+    the unquantized bf16 K/V (FP32, on the device), on a sample of sequences."""
+    s_tk, s_tv = scales
+    pt = torch.from_numpy(w.page_table).cuda()
+    kd = torch.from_numpy(np.concatenate([d[0] for d in data])).to(torch.bfloat16).cuda()
+    vd = torch.from_numpy(np.concatenate([d[1] for d in data])).to(torch.bfloat16).cuda()
+    seq = torch.from_numpy(np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(w.lens)])).cuda()
+    pos = torch.from_numpy(np.concatenate([np.arange(int(L), dtype=np.int32) for L in w.lens])).cuda()
+    ntok = kd.shape[0]
+    bulk_bytes = ntok * w.Hkv * 128 * 2 * (2 + 0.5625) + ntok * 8
+    res = {"workload": f"decode config 4 data ({ntok} tokens x {w.Hkv} heads); errors over sequences "
+                       f"0..{sample - 1}"}
+    caches = {}
+    for name, put in (("amax6", api.append), ("mse", api.append_mse)):
+        c = api.KVCache(w.num_pages, w.Hkv, s_tk, s_tv, fill=0)
+        put(c, kd, vd, seq, pos, pt)
+        torch.cuda.synchronize()
+        t = time_region(torch, lambda: put(c, kd, vd, seq, pos, pt), iters, stream)
+        caches[name] = c
+        res[name] = {"bulk_append_ms": round(t, 3), "bulk_append_gbs": round(bulk_bytes / t / 1e6, 1)}
+    del kd, vd, seq, pos
+    torch.cuda.empty_cache()
+    G = w.Hq // w.Hkv
+    scale = 1.0 / np.sqrt(128.0)
+    q = torch.from_numpy(q_np).to(torch.bfloat16).cuda()
+    qf = q.float()
+    refs = []
+    for b in range(sample):
+        k = torch.from_numpy(data[b][0]).cuda()
+        v = torch.from_numpy(data[b][1]).cuda()
+        o = torch.empty((w.Hq, 128), dtype=torch.float32, device="cuda")
+        for h in range(w.Hkv):
+            kh = k[:, h, :].contiguous()
+            sc = torch.matmul(qf[b, h * G:(h + 1) * G], kh.t().contiguous()) * scale
+            o[h * G:(h + 1) * G] = torch.matmul(torch.softmax(sc, dim=-1), v[:, h, :].contiguous())
+        refs.append(o)
+    ref = torch.stack(refs)
+    lens = torch.from_numpy(w.lens.astype(np.int32)).cuda()
+    L = int(w.lens.max())
+    out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, api.decode_workspace_bytes(w.B, w.Hq, w.Hkv, L)), dtype=torch.uint8, device="cuda")
+    for name, c in caches.items():
+        se = {"k": 0.0, "v": 0.0}
+        sq = {"k": 0.0, "v": 0.0}
+        for b in range(sample):
+            kh, vh = api.dequant(c, pt[b], 0, int(w.lens[b]))
+            for nm, xh, x in (("k", kh, data[b][0]), ("v", vh, data[b][1])):
+                xd = torch.from_numpy(x).cuda().double()
+                se[nm] += float(((xh.double() - xd) ** 2).sum())
+                sq[nm] += float((xd ** 2).sum())
+        api.decode(c, q, pt, lens, L, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        d = out[:sample].double() - ref.double()
+        res[name].update({
+            "rel_mse_k": se["k"] / sq["k"], "rel_mse_v": se["v"] / sq["v"],
+            "decode_rel_l2_err": float(d.norm() / ref.double().norm()),
+        })
+    for key in ("rel_mse_k", "rel_mse_v", "decode_rel_l2_err"):
+        res[f"mse_over_amax6_{key}"] = round(res["mse"][key] / res["amax6"][key], 4)
+    res["mse_append_slowdown"] = round(res["mse"]["bulk_append_ms"] / res["amax6"]["bulk_append_ms"], 3)
+    del caches
+    torch.cuda.empty_cache()
+    return res
+
+
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_paged_b128_traffic.json")
 DECODE_SOURCES = [os.path.join(ROOT, "decode_attention_nvfp4_amd", "csrc", f)
                   for f in ("decode.hip", "common.h", "internal.h", "api.cpp")]
@@ -540,6 +608,11 @@ def main():
         except Exception as e:  # noqa: BLE001
             res["extra"]["kv_formats_cfg4"] = {"error": repr(e)}
         log(f"kv formats: {res['extra']['kv_formats_cfg4']}")
+        try:
+            res["extra"]["mse_scale_cfg4"] = bench_mse_scale(api, torch, stream, w, data, (s_tk, s_tv), q_np)
+        except Exception as e:  # noqa: BLE001
+            res["extra"]["mse_scale_cfg4"] = {"error": repr(e)}
+        log(f"mse block scale: {res['extra']['mse_scale_cfg4']}")
         try:
             res["extra"]["prefill_cfg5"] = bench_prefill(api, torch, stream)
         except Exception as e:  # noqa: BLE001
