@@ -333,6 +333,32 @@ void orc_fp8_dequant(const uint8_t* codes, size_t n, float s_t, float* out) {
   for (size_t i = 0; i < n; ++i) out[i] = orc_fp8_value(codes[i], s_t);
 }
 
+/* ------------------------------------------------- NVFP4 -> FP8 conversion */
+
+/* Conversion of a row-major NVFP4 tensor to FP8 for an FP8 GEMM ([GB10]
+ * §這個 80 行的 Triton 繞道: NVFP4 weights are turned into FP8 when the model
+ * loads, and the dequantization divides by the global scale).  Element e of
+ * the flat tensor: code = nibble e%2 (low nibble first) of byte e/2, block
+ * scale byte e/16; its value e2m1 * s_block (exact in FP32) is divided by
+ * the global encode scale g in FP32 (IEEE division), and the result is
+ * written as the FP8 code of that value over the output scale s8 (the rule
+ * of orc_fp8_code: FP32 quotient, nearest E4M3, ties to even, clamped to
+ * 448).  Dequantizing the output multiplies by s8. */
+unsigned orc_nvfp4_to_fp8_code(unsigned code, unsigned sb, float g, float s8) {
+  float v = (float)(orc_e2m1_value(code) * orc_e4m3_value(sb));
+  float xh = v / g;
+  return orc_fp8_code(xh, s8);
+}
+
+void orc_nvfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, size_t n,
+                      float g, float s8, uint8_t* out) {
+  for (size_t e = 0; e < n; ++e) {
+    unsigned byte = codes[e / 2];
+    unsigned c = (e % 2 == 0) ? (byte & 15u) : (byte >> 4);
+    out[e] = (uint8_t)orc_nvfp4_to_fp8_code(c, scales[e / 16], g, s8);
+  }
+}
+
 /* ----------------------------------------------------------- attention */
 
 /* Softmax attention of Hq query rows over L tokens of an already dequantized

@@ -83,6 +83,10 @@ def lib():
             L.orc_block_scale_code_mse.argtypes = [_f32p, ctypes.c_float]
             L.orc_quantize_rows_mse.restype = None
             L.orc_quantize_rows_mse.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_float, _u8p, _u8p]
+            L.orc_nvfp4_to_fp8_code.restype = ctypes.c_uint
+            L.orc_nvfp4_to_fp8_code.argtypes = [ctypes.c_uint, ctypes.c_uint, ctypes.c_float, ctypes.c_float]
+            L.orc_nvfp4_to_fp8.restype = None
+            L.orc_nvfp4_to_fp8.argtypes = [_u8p, _u8p, ctypes.c_size_t, ctypes.c_float, ctypes.c_float, _u8p]
             L.orc_fp8_tensor_scale_from_amax.restype = ctypes.c_float
             L.orc_fp8_tensor_scale_from_amax.argtypes = [ctypes.c_float]
             L.orc_fp8_code.restype = ctypes.c_uint
@@ -348,6 +352,33 @@ def fp8_dequant(codes, s_t: float) -> np.ndarray:
     codes = _c(codes, np.uint8)
     out = np.empty(codes.shape, np.float32)
     lib().orc_fp8_dequant(_p(codes, _u8p), codes.size, float(s_t), _p(out, _f32p))
+    return out
+
+
+def nvfp4_to_fp8_code(code: int, sb_code: int, g: float, s8: float) -> int:
+    return int(lib().orc_nvfp4_to_fp8_code(int(code), int(sb_code), float(g), float(s8)))
+
+
+def nvfp4_to_fp8(codes, scales, g: float, s8: float) -> np.ndarray:
+    """FP8 codes [rows][cols] of a row-major NVFP4 tensor: codes as one
+    nibble per element [rows][cols] (low nibble of the packed byte first),
+    block scales [rows][cols/16]; dequantize dividing by the global scale g,
+    then encode over the output scale s8."""
+    codes = _c(codes, np.uint8)
+    packed = (codes[:, 0::2] & 15) | ((codes[:, 1::2] & 15) << 4)
+    return nvfp4_to_fp8_packed(packed.astype(np.uint8), scales, g, s8)
+
+
+def nvfp4_to_fp8_packed(packed, scales, g: float, s8: float) -> np.ndarray:
+    """nvfp4_to_fp8 from packed bytes [rows][cols/2] (element 2j in the low
+    nibble of byte j)."""
+    packed = _c(packed, np.uint8)
+    scales = _c(scales, np.uint8)
+    rows, cols = packed.shape[0], packed.shape[1] * 2
+    assert cols % 16 == 0 and scales.shape == (rows, cols // 16)
+    out = np.empty((rows, cols), np.uint8)
+    if out.size:
+        lib().orc_nvfp4_to_fp8(_p(packed, _u8p), _p(scales, _u8p), out.size, float(g), float(s8), _p(out, _u8p))
     return out
 
 
