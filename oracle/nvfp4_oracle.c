@@ -355,7 +355,8 @@ void orc_nvfp4_to_fp8(const uint8_t* codes, const uint8_t* scales, size_t n,
   for (size_t e = 0; e < n; ++e) {
     unsigned byte = codes[e / 2];
     unsigned c = (e % 2 == 0) ? (byte & 15u) : (byte >> 4);
-    out[e] = (uint8_t)orc_nvfp4_to_fp8_code(c, scales[e / 16], g, s8);
+    /* block scales are non-negative; a set sign bit is ignored */
+    out[e] = (uint8_t)orc_nvfp4_to_fp8_code(c, scales[e / 16] & 0x7Fu, g, s8);
   }
 }
 

@@ -52,6 +52,9 @@ def test_nibble_order_and_block_index(orc):
     assert val[16] == 3.0 and val[17] == -2.0
     assert np.all(val[2:16] == 0) and np.all(val[18:] == 0)
     assert out[0, 2] == 0x00                       # +0 stays +0
+    # a block scale byte with its sign bit set converts as the plain scale
+    neg = orc.nvfp4_to_fp8_packed(packed, scales | 0x80, 1.0, 1.0)
+    assert np.array_equal(neg, out)
 
 
 def test_divides_by_the_global_scale(orc):
