@@ -348,6 +348,28 @@ def bench_mse_scale(api, torch, stream, w, data, scales, q_np, sample=8, iters=3
     return res
 
 
+def bench_to_fp8(api, torch, stream, rows=16384, cols=16384, iters=10):
+    """NVFP4 -> FP8 conversion of a weight-sized [rows][cols] tensor of random
+    NVFP4 bytes (block scales 0..126): HBM bytes 0.5 + 1/16 in and 1 out per
+    element."""
+    n = rows * cols
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    codes = torch.randint(0, 256, (n // 2,), dtype=torch.uint8, device="cuda", generator=gen)
+    scales = torch.randint(0, 127, (n // 16,), dtype=torch.uint8, device="cuda", generator=gen)
+    out = torch.empty(n, dtype=torch.uint8, device="cuda")
+    g = 2688.0 / 3.0
+    s8 = 6.0 / g
+    api.to_fp8(codes, scales, g, s8, out=out)
+    torch.cuda.synchronize()
+    t = time_region(torch, lambda: api.to_fp8(codes, scales, g, s8, out=out), iters, stream)
+    nbytes = n * (0.5 + 1.0 / 16 + 1.0)
+    res = {"workload": f"NVFP4 -> FP8 of a [{rows}][{cols}] tensor", "us": round(t * 1e3, 2),
+           "gbs": round(nbytes / t / 1e6, 1), "frac_hbm_peak": round(nbytes / t / 1e6 / HBM_PEAK_GBS, 4)}
+    del codes, scales, out
+    torch.cuda.empty_cache()
+    return res
+
+
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_paged_b128_traffic.json")
 DECODE_SOURCES = [os.path.join(ROOT, "decode_attention_nvfp4_amd", "csrc", f)
                   for f in ("decode.hip", "common.h", "internal.h", "api.cpp")]
@@ -613,6 +635,11 @@ def main():
         except Exception as e:  # noqa: BLE001
             res["extra"]["mse_scale_cfg4"] = {"error": repr(e)}
         log(f"mse block scale: {res['extra']['mse_scale_cfg4']}")
+        try:
+            res["extra"]["nvfp4_to_fp8"] = bench_to_fp8(api, torch, stream)
+        except Exception as e:  # noqa: BLE001
+            res["extra"]["nvfp4_to_fp8"] = {"error": repr(e)}
+        log(f"nvfp4 -> fp8: {res['extra']['nvfp4_to_fp8']}")
         try:
             res["extra"]["prefill_cfg5"] = bench_prefill(api, torch, stream)
         except Exception as e:  # noqa: BLE001

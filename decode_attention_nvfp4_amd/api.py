@@ -63,6 +63,7 @@ _SIGS = {
     "nvfp4_abs_max": (_I32, [_VP, _I32, _I64, _VP, _VP]),
     "nvfp4_kv_append": (_I32, [_CP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
     "nvfp4_kv_append_mse": (_I32, [_CP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
+    "nvfp4_to_fp8": (_I32, [_VP, _VP, _I64, _F, _F, _VP, _VP]),
     "nvfp4_kv_dequant": (_I32, [_CP, _VP, _I32, _I32, _VP, _VP, _I32, _VP]),
     "nvfp4_decode_num_splits": (_I32, [_I32, _I32, _I32, _I32]),
     "nvfp4_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
@@ -230,6 +231,24 @@ def _append(name, cache, k_new, v_new, tok_seq, tok_pos, page_table, stream):
     _check(name, getattr(lib(), name)(
         ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), n, _ptr(tok_seq),
         _ptr(tok_pos), _ptr(page_table), page_table.shape[-1], _stream(stream)))
+
+
+def to_fp8(codes, scales, global_scale: float, out_scale: float, out=None, stream=None):
+    """FP8 codes (uint8, one per element) of a row-major NVFP4 tensor: packed
+    codes (uint8, n/2 bytes) and block scales (uint8, n/16 bytes); the
+    values divide by the global encode scale and encode over out_scale."""
+    _dev(codes, "codes", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    n = codes.numel() * 2
+    if scales.numel() * 16 != n:
+        raise ValueError("scales must hold one byte per 16 elements")
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=codes.device)
+    elif out.numel() != n or out.dtype != torch.uint8:
+        raise ValueError("out must be uint8 with one byte per element")
+    _check("nvfp4_to_fp8", lib().nvfp4_to_fp8(_ptr(codes), _ptr(scales), n, float(global_scale),
+                                              float(out_scale), _ptr(out), _stream(stream)))
+    return out
 
 
 def dequant(cache: KVCache, page_table_row, pos0: int, n: int, out_dtype=torch.float32,

@@ -139,6 +139,28 @@ int32_t nvfp4_abs_max(const void* x, int32_t dtype, int64_t n, float* amax_out, 
                     "abs_max launch");
 }
 
+int32_t nvfp4_to_fp8(const void* codes, const void* scales, int64_t n, float global_scale,
+                     float out_scale, void* fp8_out, void* stream) {
+  g_err[0] = 0;
+  if (n < 0 || n % 16 != 0) return fail(NVFP4_ERR_INVALID_ARG, "n must be a non-negative multiple of 16");
+  if (!good_scale(global_scale))
+    return fail(NVFP4_ERR_INVALID_ARG, "global_scale must be finite and > 0");
+  if (!good_scale(out_scale))
+    return fail(NVFP4_ERR_INVALID_ARG, "out_scale must be finite and > 0");
+  if (n == 0) return NVFP4_OK;
+  if (!codes || !scales || !fp8_out) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(codes) || !aligned16(fp8_out))
+    return fail(NVFP4_ERR_INVALID_ARG, "codes / fp8_out must be 16-byte aligned");
+  ToFp8Args a;
+  a.codes = static_cast<const uint8_t*>(codes);
+  a.scales = static_cast<const uint8_t*>(scales);
+  a.out = static_cast<uint8_t*>(fp8_out);
+  a.n_blocks = n / 16;
+  a.g = global_scale;
+  a.s8 = out_scale;
+  return hip_status(launch_to_fp8(a, (hipStream_t)stream), "to_fp8 launch");
+}
+
 static int32_t append_call(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
                            int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
                            const int32_t* tok_pos, const int32_t* page_table,

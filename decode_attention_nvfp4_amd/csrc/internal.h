@@ -50,6 +50,16 @@ struct CmpAppendArgs {
   int32_t fmt;
 };
 
+// NVFP4 -> FP8 conversion of a flat run of 16-element blocks.
+struct ToFp8Args {
+  const uint8_t* codes;     // 8 bytes per block, 16-byte aligned
+  const uint8_t* scales;    // 1 byte per block
+  uint8_t* out;             // 16 bytes per block, 16-byte aligned
+  long long n_blocks;
+  float g;                  // global encode scale (divides)
+  float s8;                 // output scale (divides)
+};
+
 struct DequantArgs {
   const uint8_t* k_codes;
   const uint8_t* k_scales;
@@ -102,6 +112,7 @@ struct PrefillArgs {
 
 hipError_t launch_append(const AppendArgs& a, bool f32_in, bool mse, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, bool f32_out, hipStream_t s);
+hipError_t launch_to_fp8(const ToFp8Args& a, hipStream_t s);
 hipError_t launch_absmax(const void* x, bool f32_in, int64_t n, float* out, hipStream_t s);
 hipError_t launch_cmp_append(const CmpAppendArgs& a, bool f32_in, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, bool f32_q, int fmt, hipStream_t s);

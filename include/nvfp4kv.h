@@ -159,6 +159,29 @@ int32_t nvfp4_kv_append_mse(const nvfp4_kv_cache* cache, const void* k_new, cons
                             const int32_t* tok_pos, const int32_t* page_table,
                             int32_t max_pages_per_seq, void* stream);
 
+/* NVFP4 -> FP8 conversion for an FP8 GEMM ([GB10] §這個 80 行的 Triton 繞道:
+ * NVFP4 weights are converted to FP8 when a model loads, and dequantization
+ * divides by the global scale).  Converts n elements of a row-major NVFP4
+ * tensor [rows][cols] (cols a multiple of 16, so the tensor is a flat run
+ * of n/16 blocks), e.g. a weight matrix or a cache's K codes and K scales
+ * planes (whose slabs are row-major [token][128]; the V planes are not).
+ *   codes       : device, n/2 bytes, element 2j in the low nibble of byte j,
+ *                 16-byte aligned
+ *   scales      : device, n/16 bytes, E4M3 block scales 0x00..0x7E (the
+ *                 sign bit is ignored; 0x7F gives unspecified output)
+ *   global_scale: the global encode scale g (finite, > 0); NVFP4 values are
+ *                 e2m1 * s_block / g, so g = 1 / s_t of this library's caches
+ *   out_scale   : s8 (finite, > 0); the output dequantizes as e4m3 * s8.
+ *                 6 / g maps the largest NVFP4 magnitude (2688 / g) onto 448;
+ *                 a power of two such as 8 / g keeps more values exact
+ *   fp8_out     : device, n bytes of OCP E4M3FN codes, 16-byte aligned
+ * Element: x = FP32(e2m1 * s_block) / g, then the E4M3 code nearest to
+ * FP32(x / s8), ties to the even code, clamped to 448, sign of x (both
+ * divisions IEEE FP32).  Reads codes and scales, writes fp8_out only.
+ * n == 0 is a no-op; n < 0 or not a multiple of 16 is invalid. */
+int32_t nvfp4_to_fp8(const void* codes, const void* scales, int64_t n, float global_scale,
+                     float out_scale, void* fp8_out, void* stream);
+
 /* Dequantization (step A10, for checks and fallbacks): positions
  * pos0 .. pos0+n-1 of the sequence whose page-table row is page_table_row
  * (device int32, at least ceil((pos0+n)/16) entries) into k_out and v_out,

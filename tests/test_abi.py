@@ -91,6 +91,25 @@ def test_append_rejects_bad_arguments(api, name):
     assert ap(_fake_cache(api), n_tok=0, ptrs=False) == 0     # empty append: no-op
 
 
+def test_to_fp8_rejects_bad_arguments(api):
+    L = api.lib()
+
+    def tf(n=64, g=100.0, s8=0.06, codes=FAKE, scales=FAKE, out=FAKE):
+        return L.nvfp4_to_fp8(codes, scales, n, g, s8, out, None)
+    assert tf(n=-16) == 1
+    assert tf(n=40) == 1
+    assert tf(g=0.0) == 1
+    assert tf(g=float("nan")) == 1
+    assert tf(s8=float("inf")) == 1
+    assert tf(s8=-1.0) == 1
+    assert tf(codes=None) == 1
+    assert tf(scales=None) == 1
+    assert tf(codes=ctypes.c_void_p(0x50008)) == 1        # misaligned
+    assert tf(out=ctypes.c_void_p(0x50004)) == 1
+    assert tf(n=0, codes=None, scales=None, out=None) == 0
+    assert tf(n=40) == 1 and b"multiple of 16" in L.nvfp4_last_error()
+
+
 def test_dequant_rejects_bad_arguments(api):
     L = api.lib()
     c = _fake_cache(api)

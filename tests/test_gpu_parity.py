@@ -264,6 +264,76 @@ def test_decode_over_mse_cache(orc):
     check_decode(out, *built.oracle_decode(orc, q, range(3)))
 
 
+# ------------------------------------------------ NVFP4 -> FP8 conversion
+
+def _u8(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.uint8)).to("cuda")
+
+
+@pytest.mark.parametrize("amax,s8_mul", [(1.0, 6.0), (3.7, 8.0), (1e-3, 0.37), (250.0, 6.0)])
+def test_to_fp8_every_code_and_scale(orc, amax, s8_mul):
+    """All 16 codes under all 127 block scales (127 blocks: an odd count, so
+    the last block takes the tail path), bit-exact vs the oracle."""
+    g = float(np.float32(2688.0) / np.float32(amax))
+    s8 = float(np.float32(s8_mul) / np.float32(g))
+    codes = np.tile(np.arange(16, dtype=np.uint8), 127)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    scales = np.arange(127, dtype=np.uint8)
+    say(f"to_fp8 all pairs amax {amax} s8 {s8_mul}/g")
+    got = api.to_fp8(_u8(packed), _u8(scales), g, s8).cpu().numpy()
+    exp = orc.nvfp4_to_fp8_packed(packed[None], scales[None], g, s8)[0]
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5].tolist()
+
+
+def _fp8_by_table(orc, packed, scales, g, s8):
+    """The oracle's output for every element, through the fact that it
+    depends only on (code, block scale): a 127 x 16 table of oracle calls."""
+    T = np.array([[orc.nvfp4_to_fp8_code(c, sb, g, s8) for c in range(16)] for sb in range(128)],
+                 np.uint8)
+    codes = np.stack([packed & 15, packed >> 4], axis=-1).reshape(packed.shape[0], -1)
+    sb = np.repeat(scales & 0x7F, 16, axis=1)
+    return T[sb, codes]
+
+
+def test_to_fp8_large_grid_stride(orc):
+    """A weight-sized tensor [4112][4096] of random NVFP4 bytes: more pairs
+    of blocks than the grid has lanes, so workgroups loop.  Every element is
+    checked through the oracle's (code, scale) table, and whole sampled
+    blocks through the oracle's conversion itself."""
+    rows, cols = 4112, 4096
+    rng = np.random.default_rng(41)
+    packed = rng.integers(0, 256, (rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 127, (rows, cols // 16), dtype=np.uint8)
+    g = float(np.float32(2688.0) / np.float32(3.0))
+    s8 = float(np.float32(6.0) / np.float32(g))
+    say(f"to_fp8 [{rows}][{cols}]")
+    got = api.to_fp8(_u8(packed), _u8(scales), g, s8).cpu().numpy().reshape(rows, cols)
+    exp = _fp8_by_table(orc, packed, scales, g, s8)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5].tolist()
+    blocks = rng.choice(rows * cols // 16, 4096, replace=False)
+    blocks[-1] = rows * cols // 16 - 1
+    pb = packed.reshape(-1, 8)[blocks]
+    sb = scales.reshape(-1, 1)[blocks]
+    exp_b = orc.nvfp4_to_fp8_packed(pb, sb, g, s8)          # one 16-element row per block
+    assert np.array_equal(got.reshape(-1, 16)[blocks], exp_b)
+
+
+def test_to_fp8_of_a_cache_k_plane(orc):
+    """The K codes and scales planes of a cache written by append convert as
+    a row-major [pages * heads * 16][128] tensor."""
+    w = W.custom_decode(13, 2, 8, 2, [70, 33], dtype="bf16")
+    built = BuiltDecode(w, orc)
+    c = built.cache
+    g = float(np.float32(1.0) / np.float32(built.s_tk))
+    s8 = float(np.float32(8.0) / np.float32(g))
+    say("to_fp8 K plane")
+    got = api.to_fp8(c.k_codes, c.k_scales, g, s8).cpu().numpy()
+    rows = c.num_pages * c.num_kv_heads * 16
+    exp = orc.nvfp4_to_fp8_packed(c.k_codes.cpu().numpy().reshape(rows, 64),
+                                  c.k_scales.cpu().numpy().reshape(rows, 8), g, s8)
+    assert np.array_equal(got.reshape(rows, 128), exp)
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_dequant_bit_exact(orc, out_dtype):
     w = W.custom_decode(1, 2, 8, 4, [37, 70], dtype="bf16")
