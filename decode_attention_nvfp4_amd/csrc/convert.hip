@@ -20,6 +20,7 @@
 namespace nvfp4 {
 
 constexpr int kConvThreads = 256;
+constexpr int kPer = 4;           // blocks per lane per step
 
 // Four nibbles (bits 0..15 of x, element j in bits 4j..4j+3) spread to the
 // low nibbles of four bytes.
@@ -49,38 +50,40 @@ __global__ void __launch_bounds__(kConvThreads) to_fp8_kernel(ToFp8Args a) {
     tb[i] = (uint8_t)((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xFFu);
   }
   __syncthreads();
-  // wave w takes blocks [128w, 128w + 128) of each stride: lane l converts
-  // blocks 128w + l and 128w + 64 + l, so every load and store instruction
-  // of the wave covers one contiguous run (512 B of codes, 1 KiB of output)
+  // wave w takes blocks [kPer*64*w, kPer*64*(w+1)) of each stride: lane l
+  // converts blocks base + 64j + l, so every load and store instruction of
+  // the wave covers one contiguous run (512 B of codes, 1 KiB of output);
+  // the kPer loads of a lane are issued before any conversion
   const int lane = threadIdx.x & 63;
   const long long wave = ((long long)blockIdx.x * kConvThreads + threadIdx.x) >> 6;
-  const long long stride = ((long long)gridDim.x * kConvThreads >> 6) * 128;
-  for (long long base = wave * 128; base < a.n_blocks; base += stride) {
-    const long long b0 = base + lane, b1 = base + 64 + lane;
-    const bool v0 = b0 < a.n_blocks, v1 = b1 < a.n_blocks;
-    uint2 w0 = make_uint2(0u, 0u), w1 = make_uint2(0u, 0u);
-    uint32_t s0 = 0u, s1 = 0u;
-    if (v0) {
-      w0 = *reinterpret_cast<const uint2*>(a.codes + 8 * b0);
-      s0 = a.scales[b0] & 0x7Fu;
+  const long long stride = ((long long)gridDim.x * kConvThreads >> 6) * (kPer * 64);
+  for (long long base = wave * (kPer * 64); base < a.n_blocks; base += stride) {
+    uint2 w[kPer];
+    uint32_t sc[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const long long b = base + 64 * j + lane;
+      w[j] = make_uint2(0u, 0u);
+      sc[j] = 0u;
+      if (b < a.n_blocks) {
+        w[j] = *reinterpret_cast<const uint2*>(a.codes + 8 * b);
+        sc[j] = a.scales[b] & 0x7Fu;
+      }
     }
-    if (v1) {
-      w1 = *reinterpret_cast<const uint2*>(a.codes + 8 * b1);
-      s1 = a.scales[b1] & 0x7Fu;
-    }
-    if (v0) {
-      const uint2 r0 = convert8(w0.x, table[s0][0], table[s0][1]), r1 = convert8(w0.y, table[s0][0], table[s0][1]);
-      *reinterpret_cast<uint4*>(a.out + 16 * b0) = make_uint4(r0.x, r0.y, r1.x, r1.y);
-    }
-    if (v1) {
-      const uint2 r0 = convert8(w1.x, table[s1][0], table[s1][1]), r1 = convert8(w1.y, table[s1][0], table[s1][1]);
-      *reinterpret_cast<uint4*>(a.out + 16 * b1) = make_uint4(r0.x, r0.y, r1.x, r1.y);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const long long b = base + 64 * j + lane;
+      if (b < a.n_blocks) {
+        const uint32_t lo = table[sc[j]][0], hi = table[sc[j]][1];
+        const uint2 r0 = convert8(w[j].x, lo, hi), r1 = convert8(w[j].y, lo, hi);
+        *reinterpret_cast<uint4*>(a.out + 16 * b) = make_uint4(r0.x, r0.y, r1.x, r1.y);
+      }
     }
   }
 }
 
 hipError_t launch_to_fp8(const ToFp8Args& a, hipStream_t s) {
-  const long long waves = (a.n_blocks + 127) / 128;
+  const long long waves = (a.n_blocks + kPer * 64 - 1) / (kPer * 64);
   long long blocks = (waves + kConvThreads / 64 - 1) / (kConvThreads / 64);
   // a grid-stride loop over at most 8 workgroups per CU; each fills its
   // table once
