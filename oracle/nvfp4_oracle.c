@@ -333,6 +333,77 @@ void orc_fp8_dequant(const uint8_t* codes, size_t n, float s_t, float* out) {
   for (size_t i = 0; i < n; ++i) out[i] = orc_fp8_value(codes[i], s_t);
 }
 
+/* ---------------------------------------------------------------- MXFP4 */
+
+/* MXFP4, the OCP format set against NVFP4 in [EXPL] §MXFP4との比較 (table):
+ * E2M1 elements in blocks of 32, one E8M0 (power-of-two) scale per block,
+ * no tensor scale.  Readings (the page gives only block size and scale
+ * type; the rest follows the OCP MX definition): block exponent
+ * e = floor(log2(amax)) - 2, 2 being the exponent of E2M1's largest value
+ * 6 = 1.5 * 2^2, clamped to [-127, 127]; a zero block takes -127; the
+ * scale byte is e + 127.  Element: the E2M1 magnitude nearest to |x| / 2^e,
+ * ties to the even code, clamped to 6; sign bit from x. */
+#define ORC_MX_BLOCK 32
+#define ORC_MX_NBLK (ORC_D / ORC_MX_BLOCK)
+
+int orc_mx_block_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e = ilogbf(amax) - 2;          /* floor(log2(amax)), subnormals included */
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+/* 2^(byte - 127); the byte 0xFF (NaN in E8M0) is not produced here. */
+double orc_e8m0_value(unsigned byte) { return ldexp(1.0, (int)byte - 127); }
+
+unsigned orc_mx_element_code(float x, int e) {
+  unsigned sign = signbit(x) ? 8u : 0u;
+  double r = fabs((double)x) / ldexp(1.0, e);   /* exact: a power-of-two scaling */
+  unsigned mag = 0;
+  for (unsigned k = 0; k < 7u; ++k) {
+    double mid = 0.5 * (kE2M1[k] + kE2M1[k + 1u]);
+    if (r > mid) {
+      mag = k + 1u;
+    } else {
+      if (r == mid) mag = (k % 2u == 0u) ? k : k + 1u;
+      break;
+    }
+  }
+  return sign | mag;
+}
+
+/* Quantize nrows rows of 128 values: codes [nrows][128] (one 4-bit code per
+ * byte), scales [nrows][4] E8M0 bytes, block j covering elements
+ * 32j..32j+31. */
+void orc_mx_quantize_rows(const float* x, size_t nrows, uint8_t* codes, uint8_t* scales) {
+  for (size_t r = 0; r < nrows; ++r) {
+    const float* row = x + r * ORC_D;
+    for (unsigned j = 0; j < ORC_MX_NBLK; ++j) {
+      float amax = 0.0f;
+      for (unsigned i = 0; i < ORC_MX_BLOCK; ++i) {
+        float a = fabsf(row[j * ORC_MX_BLOCK + i]);
+        if (a > amax) amax = a;
+      }
+      int e = orc_mx_block_exp(amax);
+      scales[r * ORC_MX_NBLK + j] = (uint8_t)(e + 127);
+      for (unsigned i = 0; i < ORC_MX_BLOCK; ++i) {
+        unsigned k = j * ORC_MX_BLOCK + i;
+        codes[r * ORC_D + k] = (uint8_t)orc_mx_element_code(row[k], e);
+      }
+    }
+  }
+}
+
+/* x_hat = e2m1(code) * 2^(scale - 127), exact in FP32 for every value the
+ * quantizer produces from FP32 input (at least 0.5 * 2^-127). */
+void orc_mx_dequant_rows(const uint8_t* codes, const uint8_t* scales, size_t nrows, float* out) {
+  for (size_t r = 0; r < nrows; ++r)
+    for (unsigned k = 0; k < ORC_D; ++k)
+      out[r * ORC_D + k] = (float)(orc_e2m1_value(codes[r * ORC_D + k]) *
+                                   orc_e8m0_value(scales[r * ORC_MX_NBLK + k / ORC_MX_BLOCK]));
+}
+
 /* ------------------------------------------------- NVFP4 -> FP8 conversion */
 
 /* Conversion of a row-major NVFP4 tensor to FP8 for an FP8 GEMM ([GB10]

@@ -83,6 +83,16 @@ def lib():
             L.orc_block_scale_code_mse.argtypes = [_f32p, ctypes.c_float]
             L.orc_quantize_rows_mse.restype = None
             L.orc_quantize_rows_mse.argtypes = [_f32p, ctypes.c_size_t, ctypes.c_float, _u8p, _u8p]
+            L.orc_mx_block_exp.restype = ctypes.c_int
+            L.orc_mx_block_exp.argtypes = [ctypes.c_float]
+            L.orc_e8m0_value.restype = ctypes.c_double
+            L.orc_e8m0_value.argtypes = [ctypes.c_uint]
+            L.orc_mx_element_code.restype = ctypes.c_uint
+            L.orc_mx_element_code.argtypes = [ctypes.c_float, ctypes.c_int]
+            L.orc_mx_quantize_rows.restype = None
+            L.orc_mx_quantize_rows.argtypes = [_f32p, ctypes.c_size_t, _u8p, _u8p]
+            L.orc_mx_dequant_rows.restype = None
+            L.orc_mx_dequant_rows.argtypes = [_u8p, _u8p, ctypes.c_size_t, _f32p]
             L.orc_nvfp4_to_fp8_code.restype = ctypes.c_uint
             L.orc_nvfp4_to_fp8_code.argtypes = [ctypes.c_uint, ctypes.c_uint, ctypes.c_float, ctypes.c_float]
             L.orc_nvfp4_to_fp8.restype = None
@@ -353,6 +363,48 @@ def fp8_dequant(codes, s_t: float) -> np.ndarray:
     out = np.empty(codes.shape, np.float32)
     lib().orc_fp8_dequant(_p(codes, _u8p), codes.size, float(s_t), _p(out, _f32p))
     return out
+
+
+# ------------------------------------------------------------------ MXFP4
+
+MX_BLOCK = 32
+
+
+def mx_block_exp(amax: float) -> int:
+    return int(lib().orc_mx_block_exp(float(amax)))
+
+
+def e8m0_value(byte: int) -> float:
+    return float(lib().orc_e8m0_value(int(byte)))
+
+
+def mx_element_code(x: float, e: int) -> int:
+    return int(lib().orc_mx_element_code(float(x), int(e)))
+
+
+def mx_quantize_rows(x):
+    """MXFP4 of rows [...][128]: (codes [...][128], E8M0 scales [...][4])."""
+    x = _c(x, np.float32)
+    shape = x.shape
+    assert shape[-1] == D
+    n = x.size // D
+    codes = np.empty((n, D), np.uint8)
+    scales = np.empty((n, D // MX_BLOCK), np.uint8)
+    if n:
+        lib().orc_mx_quantize_rows(_p(x.reshape(-1, D), _f32p), n, _p(codes, _u8p), _p(scales, _u8p))
+    return codes.reshape(shape), scales.reshape(shape[:-1] + (D // MX_BLOCK,))
+
+
+def mx_dequant_rows(codes, scales) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    shape = codes.shape
+    n = codes.size // D
+    out = np.empty((n, D), np.float32)
+    if n:
+        lib().orc_mx_dequant_rows(_p(codes.reshape(-1, D), _u8p), _p(scales.reshape(-1, D // MX_BLOCK), _u8p),
+                                  n, _p(out, _f32p))
+    return out.reshape(shape)
 
 
 def nvfp4_to_fp8_code(code: int, sb_code: int, g: float, s8: float) -> int:
