@@ -50,9 +50,20 @@ class CmpCacheStruct(ctypes.Structure):
     ]
 
 
+class MxCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("k_exp_offset", ctypes.c_int32), ("v_exp_offset", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+    ]
+
+
 _VP, _I32, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _CP = ctypes.POINTER(CacheStruct)
 _XP = ctypes.POINTER(CmpCacheStruct)
+_MP = ctypes.POINTER(MxCacheStruct)
 
 _SIGS = {
     "nvfp4_status_string": (ctypes.c_char_p, [_I32]),
@@ -78,6 +89,12 @@ _SIGS = {
     "nvfp4_cmp_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "nvfp4_cmp_decode_attn": (_I32, [_XP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _F, _I32,
                                      _VP, _SZ, _VP, _VP]),
+    "nvfp4_mx_plane_bytes": (_SZ, [_I32, _I32, _I32]),
+    "nvfp4_mx_exp_offset_from_amax": (_I32, [_F]),
+    "nvfp4_mx_append": (_I32, [_MP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
+    "nvfp4_mx_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "nvfp4_mx_decode_attn": (_I32, [_MP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _F, _I32,
+                                    _VP, _SZ, _VP, _VP]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -392,6 +409,80 @@ def cmp_decode(cache: CmpCache, q, page_table, seq_lens, max_seq_len: int, softm
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     cs = cache.struct()
     _check("nvfp4_cmp_decode_attn", lib().nvfp4_cmp_decode_attn(
+        ctypes.byref(cs), _ptr(q), _dtype_code(q), B, Hq, _ptr(page_table), page_table.shape[-1],
+        _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(num_splits), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _ptr(out), _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------- MXFP4
+
+def mx_plane_bytes(num_pages: int, num_kv_heads: int, plane: int) -> int:
+    return lib().nvfp4_mx_plane_bytes(num_pages, num_kv_heads, plane)
+
+
+def mx_exp_offset_from_amax(amax: float) -> int:
+    return lib().nvfp4_mx_exp_offset_from_amax(float(amax))
+
+
+class MxCache:
+    """The four device planes of a paged MXFP4 cache plus the power-of-two
+    offsets its decode takes the K and V values relative to."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, k_exp_offset: int = 0, v_exp_offset: int = 0,
+                 device="cuda", fill: int | None = 0):
+        self.num_pages = int(num_pages)
+        self.num_kv_heads = int(num_kv_heads)
+        self.k_exp_offset = int(k_exp_offset)
+        self.v_exp_offset = int(v_exp_offset)
+        planes = []
+        for p in range(4):
+            n = mx_plane_bytes(self.num_pages, self.num_kv_heads, p)
+            if n == 0:
+                raise ValueError(f"bad MXFP4 cache ({num_pages}, {num_kv_heads})")
+            t = torch.empty(n, dtype=torch.uint8, device=device)
+            if fill is not None:
+                t.fill_(fill)
+            planes.append(t)
+        self.k_codes, self.k_scales, self.v_codes, self.v_scales = planes
+
+    def struct(self) -> MxCacheStruct:
+        return MxCacheStruct(self.k_codes.data_ptr(), self.k_scales.data_ptr(),
+                             self.v_codes.data_ptr(), self.v_scales.data_ptr(),
+                             self.k_exp_offset, self.v_exp_offset,
+                             self.num_pages, self.num_kv_heads, PAGE_SIZE, HEAD_DIM)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
+
+
+def mx_append(cache: MxCache, k_new, v_new, tok_seq, tok_pos, page_table, stream=None):
+    """Quantize rows k_new/v_new [n][Hkv][128] to MXFP4 at (tok_seq, tok_pos)."""
+    _append("nvfp4_mx_append", cache, k_new, v_new, tok_seq, tok_pos, page_table, stream)
+
+
+def mx_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len, num_splits=0) -> int:
+    return lib().nvfp4_mx_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len, num_splits)
+
+
+def mx_decode(cache: MxCache, q, page_table, seq_lens, max_seq_len: int, softmax_scale=None,
+              num_splits: int = 0, workspace=None, out=None, stream=None):
+    """Decode attention over an MXFP4 cache: q [B][Hq][128] -> [B][Hq][128] FP32."""
+    _dev(q, "q")
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    B, Hq = q.shape[0], q.shape[1]
+    if q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [B][Hq][128]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = mx_decode_workspace_bytes(B, Hq, cache.num_kv_heads, max_seq_len, num_splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    cs = cache.struct()
+    _check("nvfp4_mx_decode_attn", lib().nvfp4_mx_decode_attn(
         ctypes.byref(cs), _ptr(q), _dtype_code(q), B, Hq, _ptr(page_table), page_table.shape[-1],
         _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(num_splits), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _ptr(out), _stream(stream)))

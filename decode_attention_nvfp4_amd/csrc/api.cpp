@@ -161,13 +161,12 @@ int32_t nvfp4_to_fp8(const void* codes, const void* scales, int64_t n, float glo
   return hip_status(launch_to_fp8(a, (hipStream_t)stream), "to_fp8 launch");
 }
 
-static int32_t append_call(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
+// Validation of the row arguments and launch shared by the NVFP4 and MXFP4
+// appends; a holds the cache planes and scales, hkv the cache's heads.
+static int32_t append_rows(AppendArgs a, int mode, const void* k_new, const void* v_new,
                            int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
                            const int32_t* tok_pos, const int32_t* page_table,
-                           int32_t max_pages_per_seq, bool mse, void* stream) {
-  g_err[0] = 0;
-  int32_t st = check_cache(cache);
-  if (st) return st;
+                           int32_t max_pages_per_seq, void* stream) {
   if (!dtype_ok(dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "dtype %d", dtype);
   if (n_tok < 0) return fail(NVFP4_ERR_INVALID_ARG, "n_tok < 0");
   if (max_pages_per_seq <= 0) return fail(NVFP4_ERR_INVALID_ARG, "max_pages_per_seq must be > 0");
@@ -176,6 +175,19 @@ static int32_t append_call(const nvfp4_kv_cache* cache, const void* k_new, const
     return fail(NVFP4_ERR_INVALID_ARG, "NULL input pointer");
   if (!aligned16(k_new) || !aligned16(v_new))
     return fail(NVFP4_ERR_INVALID_ARG, "k_new / v_new must be 16-byte aligned");
+  a.k_new = k_new; a.v_new = v_new;
+  a.tok_seq = tok_seq; a.tok_pos = tok_pos; a.page_table = page_table;
+  a.max_pages = max_pages_per_seq; a.n_tok = n_tok;
+  return hip_status(launch_append(a, dtype == NVFP4_DTYPE_F32, mode, (hipStream_t)stream), "append launch");
+}
+
+static int32_t append_call(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
+                           int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                           const int32_t* tok_pos, const int32_t* page_table,
+                           int32_t max_pages_per_seq, int mode, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cache(cache);
+  if (st) return st;
   AppendArgs a;
   a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
   a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
@@ -187,10 +199,9 @@ static int32_t append_call(const nvfp4_kv_cache* cache, const void* k_new, const
   auto inv6 = [](double six) { return (six > 0x1p-100 && six < 0x1p100) ? (float)(1.0 / six) : 0.0f; };
   a.k_inv6 = inv6(a.k_six_st);
   a.v_inv6 = inv6(a.v_six_st);
-  a.k_new = k_new; a.v_new = v_new;
-  a.tok_seq = tok_seq; a.tok_pos = tok_pos; a.page_table = page_table;
-  a.max_pages = max_pages_per_seq; a.n_tok = n_tok; a.hkv = cache->num_kv_heads;
-  return hip_status(launch_append(a, dtype == NVFP4_DTYPE_F32, mse, (hipStream_t)stream), "append launch");
+  a.hkv = cache->num_kv_heads;
+  return append_rows(a, mode, k_new, v_new, dtype, n_tok, tok_seq, tok_pos, page_table, max_pages_per_seq,
+                     stream);
 }
 
 int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
@@ -198,7 +209,7 @@ int32_t nvfp4_kv_append(const nvfp4_kv_cache* cache, const void* k_new, const vo
                         const int32_t* tok_pos, const int32_t* page_table,
                         int32_t max_pages_per_seq, void* stream) {
   return append_call(cache, k_new, v_new, dtype, n_tok, tok_seq, tok_pos, page_table, max_pages_per_seq,
-                     false, stream);
+                     kAppendAmax6, stream);
 }
 
 int32_t nvfp4_kv_append_mse(const nvfp4_kv_cache* cache, const void* k_new, const void* v_new,
@@ -206,7 +217,7 @@ int32_t nvfp4_kv_append_mse(const nvfp4_kv_cache* cache, const void* k_new, cons
                             const int32_t* tok_pos, const int32_t* page_table,
                             int32_t max_pages_per_seq, void* stream) {
   return append_call(cache, k_new, v_new, dtype, n_tok, tok_seq, tok_pos, page_table, max_pages_per_seq,
-                     true, stream);
+                     kAppendMse, stream);
 }
 
 int32_t nvfp4_kv_dequant(const nvfp4_kv_cache* cache, const int32_t* page_table_row,
@@ -263,7 +274,7 @@ static int32_t decode_call(int fmt, const uint8_t* kplane, const uint8_t* kscale
                            const int32_t* page_table, int32_t max_pages_per_seq,
                            const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
                            int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
-                           void* stream) {
+                           void* stream, int32_t k_exp = 0, int32_t v_exp = 0) {
   if (!dtype_ok(q_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
   if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0 || max_pages_per_seq <= 0)
     return fail(NVFP4_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d, max_seq_len %d, splits %d, "
@@ -301,6 +312,8 @@ static int32_t decode_call(int fmt, const uint8_t* kplane, const uint8_t* kscale
                                            align256(pieces * sizeof(float)));
   a.qk_scale = (float)((double)k_scale * (double)softmax_scale * 1.4426950408889634);
   a.v_scale = v_scale;
+  a.k_exp = k_exp;
+  a.v_exp = v_exp;
   a.max_pages = max_pages_per_seq;
   a.batch = batch; a.hq = num_q_heads; a.hkv = hkv; a.group = G;
   a.num_splits = W;
@@ -408,6 +421,84 @@ int32_t nvfp4_cmp_decode_attn(const nvfp4_cmp_cache* cache, const void* q, int32
                      fp8 ? cache->v_scale : 1.0f, cache->num_kv_heads, q, q_dtype, batch, num_q_heads,
                      page_table, max_pages_per_seq, seq_lens, max_seq_len, softmax_scale, num_splits,
                      workspace, workspace_bytes, out, stream);
+}
+
+// ------------------------------------------------------------------ MXFP4
+
+static int32_t check_mx_cache(const nvfp4_mx_cache* c) {
+  if (!c) return fail(NVFP4_ERR_INVALID_ARG, "cache is NULL");
+  if (c->head_dim != NVFP4_HEAD_DIM)
+    return fail(NVFP4_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", c->head_dim);
+  if (c->page_size != NVFP4_PAGE_SIZE)
+    return fail(NVFP4_ERR_UNSUPPORTED, "page_size %d is not supported (only 16)", c->page_size);
+  if (c->num_pages <= 0 || c->num_kv_heads <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "num_pages (%d) and num_kv_heads (%d) must be > 0",
+                c->num_pages, c->num_kv_heads);
+  if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales)
+    return fail(NVFP4_ERR_INVALID_ARG, "a cache plane pointer is NULL");
+  if (!aligned16(c->k_codes) || !aligned16(c->k_scales) || !aligned16(c->v_codes) ||
+      !aligned16(c->v_scales))
+    return fail(NVFP4_ERR_INVALID_ARG, "cache planes must be 16-byte aligned");
+  if (c->k_exp_offset < -126 || c->k_exp_offset > 127 || c->v_exp_offset < -126 || c->v_exp_offset > 127)
+    return fail(NVFP4_ERR_INVALID_ARG, "exp offsets must lie in [-126, 127] (k %d, v %d)", c->k_exp_offset,
+                c->v_exp_offset);
+  return NVFP4_OK;
+}
+
+size_t nvfp4_mx_plane_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t plane) {
+  if (num_pages <= 0 || num_kv_heads <= 0) return 0;
+  const size_t slabs = (size_t)num_pages * num_kv_heads;
+  switch (plane) {
+    case 0: case 2: return slabs * (NVFP4_PAGE_SIZE * NVFP4_HEAD_DIM / 2);
+    case 1: case 3: return slabs * (NVFP4_PAGE_SIZE * NVFP4_HEAD_DIM / 32);   // one E8M0 byte per 32
+    default: return 0;
+  }
+}
+
+int32_t nvfp4_mx_exp_offset_from_amax(float amax) {
+  if (!std::isfinite(amax) || !(amax > 0.0f)) return 0;
+  return std::ilogb(amax) - 10;
+}
+
+int32_t nvfp4_mx_append(const nvfp4_mx_cache* cache, const void* k_new, const void* v_new,
+                        int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                        const int32_t* tok_pos, const int32_t* page_table,
+                        int32_t max_pages_per_seq, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_mx_cache(cache);
+  if (st) return st;
+  AppendArgs a = {};
+  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
+  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
+  a.k_scale = a.v_scale = 1.0f;
+  a.hkv = cache->num_kv_heads;
+  return append_rows(a, kAppendMx, k_new, v_new, dtype, n_tok, tok_seq, tok_pos, page_table,
+                     max_pages_per_seq, stream);
+}
+
+size_t nvfp4_mx_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t max_seq_len, int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 || num_splits < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  const int32_t w = std::max(plan_waves(num_splits, false, batch, num_kv_heads, max_seq_len, kFmtMxfp4),
+                             plan_waves(num_splits, true, batch, num_kv_heads, max_seq_len, kFmtMxfp4));
+  return decode_ws(batch, num_q_heads / num_kv_heads, w);
+}
+
+int32_t nvfp4_mx_decode_attn(const nvfp4_mx_cache* cache, const void* q, int32_t q_dtype,
+                             int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens,
+                             int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_mx_cache(cache);
+  if (st) return st;
+  return decode_call(kFmtMxfp4, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales,
+                     std::ldexp(1.0f, cache->k_exp_offset), std::ldexp(1.0f, cache->v_exp_offset),
+                     cache->num_kv_heads, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
+                     seq_lens, max_seq_len, softmax_scale, num_splits, workspace, workspace_bytes, out,
+                     stream, cache->k_exp_offset, cache->v_exp_offset);
 }
 
 static size_t prefill_ws(int32_t total, int32_t hkv, int32_t mode) {

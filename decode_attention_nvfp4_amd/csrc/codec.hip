@@ -138,6 +138,52 @@ __device__ __forceinline__ uint32_t quantize_half_block_mse(const float x[8], fl
   return encode8(x, code, s_t);
 }
 
+// ------------------------------------------------------------ MXFP4 blocks
+//
+// MXFP4 (the OCP format set against NVFP4 in "NVIDIA解説: NVFP4 KV Cacheで
+// 長コンテキストLLM推論を最適化", section MXFP4との比較): 32-element blocks
+// (four lanes of a row), E8M0 scale 2^e with e = floor(log2(amax)) - 2
+// clamped to [-127, 127] (-127 for a zero block), elements the E2M1 value
+// nearest to |x| / 2^e, ties to the even code, clamped to 6.
+
+// floor(log2(a)) of a finite a > 0 from its bits, subnormals included.
+__device__ __forceinline__ int floor_log2(float a) {
+  const uint32_t b = __float_as_uint(a);
+  const int field = (int)(b >> 23);
+  if (field > 0) return field - 127;
+  return (31 - (int)__builtin_clz(b & 0x7FFFFFu)) - 149;
+}
+
+// The lane's 8 packed codes; *sb gets the block's E8M0 byte.  |x| * 2^-e is
+// exact (a power-of-two scaling; a product below the FP32 normal range is
+// far below the first threshold), so the thresholds decide exactly.
+__device__ __forceinline__ uint32_t quantize_half_block_mx(const float x[8], uint32_t* sb) {
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
+  a = fmaxf(a, __shfl_xor(a, 1));
+  a = fmaxf(a, __shfl_xor(a, 2));
+  int e = a > 0.0f ? floor_log2(a) - 2 : -127;
+  e = max(-127, min(127, e));                 // a finite amax gives e <= 125
+  *sb = (uint32_t)(e + 127);
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, a normal FP32
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float r = fabsf(x[j]) * inv;
+    uint32_t m = 0;
+    m += r > 0.25f;
+    m += r >= 0.75f;
+    m += r > 1.25f;
+    m += r >= 1.75f;
+    m += r > 2.5f;
+    m += r >= 3.5f;
+    m += r > 5.0f;
+    w |= (m | ((__float_as_uint(x[j]) >> 31) << 3)) << (4 * j);
+  }
+  return w;
+}
+
 // Eight nibbles (element e in bits 4e..4e+3) spread to the low nibbles of
 // eight bytes: elements 0..3 in *w0, 4..7 in *w1.
 __device__ __forceinline__ void spread_nibbles(uint32_t w, uint32_t* w0, uint32_t* w1) {
@@ -154,7 +200,7 @@ __device__ __forceinline__ void spread_nibbles(uint32_t w, uint32_t* w0, uint32_
 // and 2i+1) the even row writes the whole bytes; a token whose partner is
 // elsewhere updates its nibbles with atomic AND / OR, which commute with the
 // partner's own update of the other nibbles.
-template <bool F32IN, bool MSE>
+template <bool F32IN, int MODE>
 __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
   const int lane16 = threadIdx.x & 15, r = threadIdx.x >> 4;
   const int tok = blockIdx.x * 16 + r;
@@ -187,17 +233,36 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
     uint32_t ksb;
     float x[8];
     unpack8<F32IN>(rk, x);
-    const uint32_t kw = MSE ? quantize_half_block_mse(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb)
-                            : quantize_half_block(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
-    unpack8<F32IN>(rv, x);
-    vw = MSE ? quantize_half_block_mse(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb)
-             : quantize_half_block(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
+    uint32_t kw;
+    if constexpr (MODE == kAppendMse) {
+      kw = quantize_half_block_mse(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
+      unpack8<F32IN>(rv, x);
+      vw = quantize_half_block_mse(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
+    } else if constexpr (MODE == kAppendMx) {
+      kw = quantize_half_block_mx(x, &ksb);
+      unpack8<F32IN>(rv, x);
+      vw = quantize_half_block_mx(x, &vsb);
+    } else {
+      kw = quantize_half_block(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
+      unpack8<F32IN>(rv, x);
+      vw = quantize_half_block(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
+    }
     slab = (size_t)page * p.hkv + h;
-    // K: token-major codes [16][64 B], token-major scales [16][8]
+    // K: token-major codes [16][64 B]; the V codes follow below
     *reinterpret_cast<uint32_t*>(p.k_codes + slab * kSlab + slot * 64 + lane16 * 4) = kw;
-    if ((lane16 & 1) == 0) p.k_scales[slab * kScaleSlab + slot * kNBlk + (lane16 >> 1)] = (uint8_t)ksb;
-    // V scales [block 8][token 16]; the V codes follow below
-    if ((lane16 & 1) == 0) p.v_scales[slab * kScaleSlab + (lane16 >> 1) * kPage + slot] = (uint8_t)vsb;
+    if constexpr (MODE == kAppendMx) {
+      // K scales [token 16][block 4], V scales [block 4][token 16]
+      if ((lane16 & 3) == 0) {
+        p.k_scales[slab * kMxScaleSlab + slot * kMxNBlk + (lane16 >> 2)] = (uint8_t)ksb;
+        p.v_scales[slab * kMxScaleSlab + (lane16 >> 2) * kPage + slot] = (uint8_t)vsb;
+      }
+    } else {
+      // K scales [token 16][block 8], V scales [block 8][token 16]
+      if ((lane16 & 1) == 0) {
+        p.k_scales[slab * kScaleSlab + slot * kNBlk + (lane16 >> 1)] = (uint8_t)ksb;
+        p.v_scales[slab * kScaleSlab + (lane16 >> 1) * kPage + slot] = (uint8_t)vsb;
+      }
+    }
   }
   s_vw[r][lane16] = vw;
   __syncthreads();
@@ -286,15 +351,17 @@ hipError_t launch_cmp_append(const CmpAppendArgs& a, bool f32, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendArgs& a, bool f32, bool mse, hipStream_t s) {
+template <int MODE>
+static void launch_append_mode(const AppendArgs& a, bool f32, dim3 grid, hipStream_t s) {
+  if (f32) append_kernel<true, MODE><<<grid, 256, 0, s>>>(a);
+  else append_kernel<false, MODE><<<grid, 256, 0, s>>>(a);
+}
+
+hipError_t launch_append(const AppendArgs& a, bool f32, int mode, hipStream_t s) {
   const dim3 grid((unsigned)((a.n_tok + 15) / 16), (unsigned)a.hkv);
-  if (mse) {
-    if (f32) append_kernel<true, true><<<grid, 256, 0, s>>>(a);
-    else append_kernel<false, true><<<grid, 256, 0, s>>>(a);
-  } else {
-    if (f32) append_kernel<true, false><<<grid, 256, 0, s>>>(a);
-    else append_kernel<false, false><<<grid, 256, 0, s>>>(a);
-  }
+  if (mode == kAppendMse) launch_append_mode<kAppendMse>(a, f32, grid, s);
+  else if (mode == kAppendMx) launch_append_mode<kAppendMx>(a, f32, grid, s);
+  else launch_append_mode<kAppendAmax6>(a, f32, grid, s);
   return hipGetLastError();
 }
 

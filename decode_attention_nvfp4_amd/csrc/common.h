@@ -17,6 +17,9 @@ constexpr int kBlock = 16;     // elements per micro-block
 constexpr int kNBlk = kD / kBlock;
 constexpr int kSlab = kPage * kD / 2;        // code bytes per (page, head): 1024
 constexpr int kScaleSlab = kPage * kNBlk;    // scale bytes per (page, head): 128
+constexpr int kMxBlock = 32;                  // MXFP4 elements per block
+constexpr int kMxNBlk = kD / kMxBlock;
+constexpr int kMxScaleSlab = kPage * kMxNBlk; // MXFP4 scale bytes per (page, head): 64
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -53,6 +56,14 @@ __device__ __forceinline__ halfx2 e4m3x2_to_half(uint32_t w, bool hi) {
 template <int SEL>
 __device__ __forceinline__ halfx2 e2m1x2_to_half(uint32_t w) {
   fp16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+  return __builtin_bit_cast(halfx2, h);
+}
+
+// Two E2M1 codes of byte SEL of `w` times the power of two `scale` (an FP32
+// 2^k, or 0), as two halves; exact while the products lie in FP16's range.
+template <int SEL>
+__device__ __forceinline__ halfx2 e2m1x2_to_half_scaled(uint32_t w, float scale) {
+  fp16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, SEL);
   return __builtin_bit_cast(halfx2, h);
 }
 

@@ -41,15 +41,22 @@
 
 namespace nvfp4 {
 
-// Cache formats the kernel reads: NVFP4 (the product format) and the two
-// comparison formats (FP8 E4M3 with a tensor scale, BF16), whose planes hold
-// K as [token][element] and V as [token quad][element][token % 4].
+// Cache formats the kernel reads: NVFP4 (the product format), MXFP4 (the
+// same code planes with E8M0 scales per 32 elements) and the two comparison
+// formats (FP8 E4M3 with a tensor scale, BF16), whose planes hold K as
+// [token][element] and V as [token quad][element][token % 4].
 template <int FMT> struct PageRegs;
 template <> struct PageRegs<kFmtNvfp4> {
   u32x4 kq;       // K codes: 32 nibbles of token col
   u32x4 vq;       // V codes: 4 tokens x 8 nibbles
   uint16_t ksc;   // 2 K block scales
   uint32_t vsc;   // 4 V block scales
+};
+template <> struct PageRegs<kFmtMxfp4> {
+  u32x4 kq;       // K codes: 32 nibbles of token col (MX block kg)
+  u32x4 vq;       // V codes: 4 tokens x 8 nibbles
+  uint32_t ksc;   // the K block's E8M0 byte
+  uint32_t vsc;   // 4 V E8M0 bytes (tokens 4kg .. 4kg + 3)
 };
 template <> struct PageRegs<kFmtFp8> {
   u32x4 kq[2];    // K: 32 E4M3 bytes of token col
@@ -72,6 +79,9 @@ template <int FMT>
 __device__ __forceinline__ LaneOffsets lane_offsets(int col, int kg) {
   if constexpr (FMT == kFmtNvfp4) {
     return {col * 64 + kg * 16, col * kNBlk + kg * 2, kg * 256 + col * 16, (col >> 1) * kPage + kg * 4};
+  } else if constexpr (FMT == kFmtMxfp4) {
+    // K scales [token][block 4]: token col, block kg; V scales [block 4][token]
+    return {col * 64 + kg * 16, col * kMxNBlk + kg, kg * 256 + col * 16, (col >> 2) * kPage + kg * 4};
   } else {
     constexpr int E = kElemBytes<FMT>;
     // K: token col, elements 32 kg ..; V: quad kg, elements 8 col .. (x 4 tokens)
@@ -93,6 +103,11 @@ __device__ __forceinline__ void load_page(const DecodeArgs& p, uint32_t slab, co
     r.ksc = __builtin_amdgcn_raw_buffer_load_b16(page_rsrc(p.k_scales + (size_t)slab * kScaleSlab), o.ks, 0, 0);
     r.vq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.v_codes + (size_t)slab * kSlab), o.v, 0, 0);
     r.vsc = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(p.v_scales + (size_t)slab * kScaleSlab), o.vs, 0, 0);
+  } else if constexpr (FMT == kFmtMxfp4) {
+    r.kq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.k_codes + (size_t)slab * kSlab), o.k, 0, 0);
+    r.ksc = __builtin_amdgcn_raw_buffer_load_b8(page_rsrc(p.k_scales + (size_t)slab * kMxScaleSlab), o.ks, 0, 0);
+    r.vq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.v_codes + (size_t)slab * kSlab), o.v, 0, 0);
+    r.vsc = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(p.v_scales + (size_t)slab * kMxScaleSlab), o.vs, 0, 0);
   } else {
     constexpr int N = 2 * kElemBytes<FMT>;             // 16-byte loads per lane and operand
     constexpr size_t S = (size_t)kPage * kD * kElemBytes<FMT>;
@@ -125,9 +140,19 @@ __device__ __forceinline__ void reset_state(WaveState& st) {
   st.l_run = 0.0f;
 }
 
+// 2^(byte - 127 - ex) as an FP32, for an E8M0 byte taken relative to 2^ex:
+// 0 below the FP32 normal range, and at most 2^13 so that 6 * 2^13 stays
+// finite in FP16 (bytes of slots no token owns yet may hold anything, and
+// their zero weights must not meet an infinity).
+__device__ __forceinline__ float e8m0_rel(uint32_t byte, int ex) {
+  const int f = min(127 + 13, max(0, (int)byte - ex));
+  return __uint_as_float((uint32_t)f << 23);
+}
+
 template <bool F32Q, int FMT>
 __device__ __forceinline__ void process_page(const PageRegs<FMT>& cur, int pg, int L, int kg, float qscale,
-                                             const halfx8 qh[4], const halfx8 ql[4], WaveState& st) {
+                                             const halfx8 qh[4], const halfx8 ql[4], WaveState& st,
+                                             int kex, int vex) {
   // ---- S^T = K~ Q^T
   floatx4 acc_s = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (FMT == kFmtNvfp4) {
@@ -141,6 +166,20 @@ __device__ __forceinline__ void process_page(const PageRegs<FMT>& cur, int pg, i
       const halfx2 h1 = e2m1x2_to_half<1>(w) * sc;
       const halfx2 h2 = e2m1x2_to_half<2>(w) * sc;
       const halfx2 h3 = e2m1x2_to_half<3>(w) * sc;
+      const halfx8 a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+      acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[i], acc_s, 0, 0, 0);
+      if (F32Q) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[i], acc_s, 0, 0, 0);
+    }
+  } else if constexpr (FMT == kFmtMxfp4) {
+    // the conversion applies the block's power of two itself: e2m1 * 2^(e - kex)
+    const float sk = e8m0_rel(cur.ksc & 0xFFu, kex);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = cur.kq[i];
+      const halfx2 h0 = e2m1x2_to_half_scaled<0>(w, sk);
+      const halfx2 h1 = e2m1x2_to_half_scaled<1>(w, sk);
+      const halfx2 h2 = e2m1x2_to_half_scaled<2>(w, sk);
+      const halfx2 h3 = e2m1x2_to_half_scaled<3>(w, sk);
       const halfx8 a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
       acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[i], acc_s, 0, 0, 0);
       if (F32Q) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[i], acc_s, 0, 0, 0);
@@ -188,13 +227,21 @@ __device__ __forceinline__ void process_page(const PageRegs<FMT>& cur, int pg, i
 #pragma unroll
   for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(acc_s[r], qscale, -st.m_run));
   st.l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-  if constexpr (FMT == kFmtNvfp4) {
+  if constexpr (FMT == kFmtNvfp4 || FMT == kFmtMxfp4) {
     const halfx4 bp = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
     // ---- O^T += V~^T P^T.  Byte e of word j / 2 (j = token pair) holds
     // element d = 8 col + e of tokens (4kg + 2j, 4kg + 2j + 1): one conversion
-    // gives the two tokens of a pair, the A operand's k order.
-    const halfx2 v01 = e4m3x2_to_half(cur.vsc, false);
-    const halfx2 v23 = e4m3x2_to_half(cur.vsc, true);
+    // gives the two tokens of a pair, the A operand's k order.  The block
+    // scales of the four tokens: E4M3 (exact in FP16) or E8M0 relative to
+    // 2^vex.
+    halfx2 v01, v23;
+    if constexpr (FMT == kFmtNvfp4) {
+      v01 = e4m3x2_to_half(cur.vsc, false);
+      v23 = e4m3x2_to_half(cur.vsc, true);
+    } else {
+      v01 = halfx2{(_Float16)e8m0_rel(cur.vsc & 0xFFu, vex), (_Float16)e8m0_rel((cur.vsc >> 8) & 0xFFu, vex)};
+      v23 = halfx2{(_Float16)e8m0_rel((cur.vsc >> 16) & 0xFFu, vex), (_Float16)e8m0_rel(cur.vsc >> 24, vex)};
+    }
     auto tile = [&](halfx2 a0, halfx2 a1, floatx4& acc) {
       a0 *= v01;
       a1 *= v23;
@@ -422,7 +469,7 @@ __device__ __forceinline__ uint32_t prepare_block(const DecodeArgs& p, SegPos& w
 // so the register budget is that of two waves (a BF16 page takes three times
 // the registers of an NVFP4 one).
 template <int FMT> constexpr int kDepth = FMT == kFmtBf16 ? 4 : 8;
-static_assert(64 % kDepth<kFmtNvfp4> == 0 && 64 % kDepth<kFmtBf16> == 0,
+static_assert(64 % kDepth<kFmtNvfp4> == 0 && 64 % kDepth<kFmtBf16> == 0 && 64 % kDepth<kFmtMxfp4> == 0,
               "block switches must fall on a stage boundary");
 
 template <bool F32Q, int FMT>
@@ -523,7 +570,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
       load_q<F32Q, FMT>(p, seg.b, seg.kvh, col, kg, qh, ql, qscale);
       reset_state(st);
     }
-    process_page<F32Q, FMT>(r, seg.pg, seg.L, kg, qscale, qh, ql, st);
+    process_page<F32Q, FMT>(r, seg.pg, seg.L, kg, qscale, qh, ql, st, p.k_exp, p.v_exp);
     ++seg.pg;
     ++done;
     if (--piece_left == 0) {
@@ -686,11 +733,13 @@ static int occupancy_of(bool f32_q) {
 }
 
 int decode_occupancy(bool f32_q, int fmt) {
-  static std::atomic<int> cached[2][3] = {};
-  const int f = fmt == kFmtFp8 ? 1 : fmt == kFmtBf16 ? 2 : 0;
+  static std::atomic<int> cached[2][4] = {};
+  const int f = fmt == kFmtFp8 ? 1 : fmt == kFmtBf16 ? 2 : fmt == kFmtMxfp4 ? 3 : 0;
   int n = cached[f32_q][f].load(std::memory_order_relaxed);
   if (n > 0) return n;
-  n = f == 1 ? occupancy_of<kFmtFp8>(f32_q) : f == 2 ? occupancy_of<kFmtBf16>(f32_q) : occupancy_of<kFmtNvfp4>(f32_q);
+  n = f == 1 ? occupancy_of<kFmtFp8>(f32_q)
+      : f == 2 ? occupancy_of<kFmtBf16>(f32_q)
+      : f == 3 ? occupancy_of<kFmtMxfp4>(f32_q) : occupancy_of<kFmtNvfp4>(f32_q);
   if (n <= 0) return 8;
   cached[f32_q][f].store(n, std::memory_order_relaxed);
   return n;
@@ -705,6 +754,7 @@ static void launch_fmt(const DecodeArgs& a, bool f32_q, hipStream_t s) {
 hipError_t launch_decode(const DecodeArgs& a, bool f32_q, int fmt, hipStream_t s) {
   if (fmt == kFmtFp8) launch_fmt<kFmtFp8>(a, f32_q, s);
   else if (fmt == kFmtBf16) launch_fmt<kFmtBf16>(a, f32_q, s);
+  else if (fmt == kFmtMxfp4) launch_fmt<kFmtMxfp4>(a, f32_q, s);
   else launch_fmt<kFmtNvfp4>(a, f32_q, s);
   const unsigned heads = (unsigned)(a.batch * a.hkv * a.group);
   if ((long long)a.num_splits > 8LL * a.batch * a.hkv) merge_kernel<8><<<heads, 256, 0, s>>>(a);

@@ -12,6 +12,11 @@ constexpr int kPrefillTile = 64;   // keys per prefill tile
 constexpr int kFmtNvfp4 = 0;       // cache formats of the decode kernel: NVFP4,
 constexpr int kFmtFp8 = 1;         // and the comparison formats (values of
 constexpr int kFmtBf16 = 2;        // nvfp4_cmp_format)
+constexpr int kFmtMxfp4 = 3;       // the MXFP4 cache
+// block-scale rules of the append kernel
+constexpr int kAppendAmax6 = 0;    // NVFP4, E4M3 nearest to amax / (6 s_t)
+constexpr int kAppendMse = 1;      // NVFP4, MSE-searched E4M3 scale
+constexpr int kAppendMx = 2;       // MXFP4, E8M0 floor(log2 amax) - 2
 constexpr int kPrefillFP8 = 0;     // operand precisions of the prefill path
 constexpr int kPrefillF16 = 1;
 
@@ -89,6 +94,7 @@ struct DecodeArgs {
   int32_t max_pages;
   int32_t batch, hq, hkv, group;
   int32_t num_splits;         // W: number of waves (work ranges)
+  int32_t k_exp, v_exp;       // MXFP4: values are taken relative to 2^k_exp, 2^v_exp
 };
 
 struct PrefillArgs {
@@ -110,7 +116,7 @@ struct PrefillArgs {
   int32_t mode;               // kPrefillFP8 or kPrefillF16
 };
 
-hipError_t launch_append(const AppendArgs& a, bool f32_in, bool mse, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, bool f32_in, int mode, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, bool f32_out, hipStream_t s);
 hipError_t launch_to_fp8(const ToFp8Args& a, hipStream_t s);
 hipError_t launch_absmax(const void* x, bool f32_in, int64_t n, float* out, hipStream_t s);

@@ -337,6 +337,73 @@ int32_t nvfp4_cmp_decode_attn(const nvfp4_cmp_cache* cache, const void* q, int32
                               int32_t max_seq_len, float softmax_scale, int32_t num_splits,
                               void* workspace, size_t workspace_bytes, float* out, void* stream);
 
+/* ---------------------------------------------------------------- MXFP4
+ *
+ * An MXFP4 KV cache, the OCP format set against NVFP4 in [EXPL]
+ * §MXFP4との比較 (table: 32-element blocks, E8M0 power-of-two scales, no
+ * tensor scale), with the same paging and decode as NVFP4.
+ * Codec (per (token, head) row of 128 elements, 4 blocks of 32): block
+ * exponent e = floor(log2(block amax)) - 2, clamped to [-127, 127], -127 for
+ * a zero block; scale byte e + 127 (E8M0); element code = the E2M1
+ * magnitude nearest to |x| / 2^e, ties to the even code, clamped to 6, sign
+ * bit from x.  Value = e2m1 * 2^(scale - 127).
+ * Layout: the code planes are those of the NVFP4 cache (K [token][64 B],
+ * V token pairs sharing bytes); the scale planes hold 64 bytes per
+ * (page, head) slab:
+ *   k_scales slab 64 B: [token 16][block 4];
+ *   v_scales slab 64 B: [block 4][token 16].
+ * 0.53125 bytes per element; K and V of one (page, head) are 2176 bytes.
+ *
+ * Decode multiplies exact FP16 operands: K and V values are taken relative
+ * to 2^exp_offset (the cache's k_exp_offset, v_exp_offset) and the power of
+ * two is applied to the scores and the output.  Values are exact when the
+ * block exponents lie within [exp_offset - 23, exp_offset + 13];
+ * nvfp4_mx_exp_offset_from_amax gives the offset that puts a tensor's
+ * largest block at exp_offset + 8, so a block loses exactness only when its
+ * amax is below about 2^-31 of the tensor's (a negligible contribution).
+ */
+typedef struct nvfp4_mx_cache {
+  uint8_t* k_codes;
+  uint8_t* k_scales;
+  uint8_t* v_codes;
+  uint8_t* v_scales;
+  int32_t k_exp_offset;  /* in [-126, 127] */
+  int32_t v_exp_offset;
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t page_size;     /* must be 16 */
+  int32_t head_dim;      /* must be 128 */
+} nvfp4_mx_cache;
+
+/* Bytes of one plane: plane 0 k_codes, 1 k_scales, 2 v_codes, 3 v_scales
+ * (codes num_pages * num_kv_heads * 1024, scales num_pages * num_kv_heads *
+ * 64).  0 for invalid arguments. */
+size_t nvfp4_mx_plane_bytes(int32_t num_pages, int32_t num_kv_heads, int32_t plane);
+
+/* floor(log2(amax)) - 10 for a tensor's amax (finite, > 0), else 0. */
+int32_t nvfp4_mx_exp_offset_from_amax(float amax);
+
+/* Quantize rows to MXFP4 and append them; arguments, index rules and
+ * ownership are those of nvfp4_kv_append (the exp offsets are not used).
+ * Writes the 128 codes and 4 block scales of each (token, head) row of K and
+ * of V; nothing else changes. */
+int32_t nvfp4_mx_append(const nvfp4_mx_cache* cache, const void* k_new, const void* v_new,
+                        int32_t dtype, int32_t n_tok, const int32_t* tok_seq,
+                        const int32_t* tok_pos, const int32_t* page_table,
+                        int32_t max_pages_per_seq, void* stream);
+
+/* Workspace bytes of nvfp4_mx_decode_attn (0 for invalid arguments). */
+size_t nvfp4_mx_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t max_seq_len, int32_t num_splits);
+
+/* Decode attention over an MXFP4 cache: the operation, arguments and work
+ * split of nvfp4_decode_attn, with the MXFP4 values of the cache. */
+int32_t nvfp4_mx_decode_attn(const nvfp4_mx_cache* cache, const void* q, int32_t q_dtype,
+                             int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens,
+                             int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,6 +2,7 @@
 compute the oracle's answer on the same seeded inputs, compare."""
 from __future__ import annotations
 
+import math
 import sys
 
 import numpy as np
@@ -33,11 +34,13 @@ def i32(x):
     return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(dev())
 
 
-def planes(cache: api.KVCache) -> Planes:
+def planes(cache) -> Planes:
+    """The layout reader over a copy of an NVFP4 or MXFP4 cache's planes."""
     torch.cuda.synchronize()
+    nblk = 4 if isinstance(cache, api.MxCache) else 8
     return Planes(cache.k_codes.cpu().numpy(), cache.k_scales.cpu().numpy(),
                   cache.v_codes.cpu().numpy(), cache.v_scales.cpu().numpy(),
-                  cache.num_pages, cache.num_kv_heads)
+                  cache.num_pages, cache.num_kv_heads, nblk=nblk)
 
 
 def compare(got: np.ndarray, ref: np.ndarray, tol: float = TOL):
@@ -241,6 +244,81 @@ class BuiltCmp:
         seqs = list(seqs)
         kv = [(self.values(oracle, self.vals[b][0], self.s_k), self.values(oracle, self.vals[b][1], self.s_v))
               for b in seqs]
+        ref = oracle.decode_batch_dense(q[seqs], kv, self.w.Hkv, scale=scale)
+        mag = oracle.decode_batch_dense(q[seqs], [(k, np.abs(v)) for k, v in kv], self.w.Hkv, scale=scale)
+        return ref, mag
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def mx_exp_offset(amax: float) -> int:
+    """floor(log2(amax)) - 10 (the offset the header states)."""
+    return math.frexp(amax)[1] - 1 - 10 if amax > 0 else 0
+
+
+class BuiltMx:
+    """A decode workload appended into an MXFP4 cache, plus the oracle's
+    codes and scales for every sequence.  The exp offsets come from the
+    whole tensor's amax (steps included)."""
+
+    def __init__(self, w: W.DecodeWorkload, oracle, fill=0xA5, chunk=16):
+        self.w = w
+        data = [w.kv(b) for b in range(w.B)]
+        ka = max([oracle.abs_max(k) for k, _ in data] + [oracle.abs_max(w.append_kv(s)[0]) for s in range(w.steps)])
+        va = max([oracle.abs_max(v) for _, v in data] + [oracle.abs_max(w.append_kv(s)[1]) for s in range(w.steps)])
+        self.k_exp, self.v_exp = mx_exp_offset(ka), mx_exp_offset(va)
+        self.cache = api.MxCache(w.num_pages, w.Hkv, self.k_exp, self.v_exp, fill=fill)
+        self.pt = i32(w.page_table)
+        self.codes = {}
+        for b0 in range(0, w.B, chunk):
+            ks, vs, seqs, poss = [], [], [], []
+            for b in range(b0, min(w.B, b0 + chunk)):
+                k, v = data[b]
+                ks.append(k)
+                vs.append(v)
+                seqs.append(np.full(len(k), b, np.int32))
+                poss.append(np.arange(len(k), dtype=np.int32))
+                self.codes[b] = (*oracle.mx_quantize_rows(k), *oracle.mx_quantize_rows(v))
+            k = np.concatenate(ks)
+            if len(k) == 0:
+                continue
+            api.mx_append(self.cache, to_dev(k, w.dtype), to_dev(np.concatenate(vs), w.dtype),
+                          i32(np.concatenate(seqs)), i32(np.concatenate(poss)), self.pt)
+        self.lens = w.lens.copy()
+        torch.cuda.synchronize()
+
+    def append_step(self, step, oracle):
+        w = self.w
+        k, v = w.append_kv(step)
+        api.mx_append(self.cache, to_dev(k, w.dtype), to_dev(v, w.dtype), i32(np.arange(w.B)),
+                      i32(self.lens.copy()), self.pt)
+        for b in range(w.B):
+            c = self.codes[b]
+            kc, ksc = oracle.mx_quantize_rows(k[b:b + 1])
+            vc, vsc = oracle.mx_quantize_rows(v[b:b + 1])
+            self.codes[b] = (np.concatenate([c[0], kc]), np.concatenate([c[1], ksc]),
+                             np.concatenate([c[2], vc]), np.concatenate([c[3], vsc]))
+        self.lens += 1
+
+    def check_codes(self, seqs):
+        P = planes(self.cache)
+        for b in seqs:
+            pages, slots = sequence_tokens(self.w.page_table[b], int(self.lens[b]))
+            got = P.gather(pages, slots)
+            for g, e, nm in zip(got, self.codes[b], ("k codes", "k scales", "v codes", "v scales")):
+                if not np.array_equal(g, e):
+                    bad = np.argwhere(g != e)[:5]
+                    raise AssertionError(f"seq {b}: {nm} differ at {bad.tolist()}")
+
+    def decode(self, q: np.ndarray, num_splits=0, dtype=None):
+        qd = to_dev(q, dtype or self.w.dtype)
+        return api.mx_decode(self.cache, qd, self.pt, i32(self.lens), int(self.lens.max()), num_splits=num_splits)
+
+    def oracle_decode(self, oracle, q: np.ndarray, seqs, scale=None):
+        """(reference, magnitude) as in BuiltDecode, over the MXFP4 values."""
+        seqs = list(seqs)
+        kv = [(oracle.mx_dequant_rows(self.codes[b][0], self.codes[b][1]),
+               oracle.mx_dequant_rows(self.codes[b][2], self.codes[b][3])) for b in seqs]
         ref = oracle.decode_batch_dense(q[seqs], kv, self.w.Hkv, scale=scale)
         mag = oracle.decode_batch_dense(q[seqs], [(k, np.abs(v)) for k, v in kv], self.w.Hkv, scale=scale)
         return ref, mag

@@ -18,9 +18,12 @@ def unpack_nibbles(b: np.ndarray) -> np.ndarray:
 
 
 class Planes:
-    def __init__(self, k_codes, k_scales, v_codes, v_scales, num_pages, hkv):
+    """nblk: scale blocks per row, 8 for NVFP4 (16 elements each), 4 for
+    MXFP4 (32 each); the code planes are the same."""
+
+    def __init__(self, k_codes, k_scales, v_codes, v_scales, num_pages, hkv, nblk=NBLK):
         self.kc = np.asarray(k_codes).reshape(num_pages, hkv, PAGE, 64)
-        self.ks = np.asarray(k_scales).reshape(num_pages, hkv, PAGE, NBLK)
+        self.ks = np.asarray(k_scales).reshape(num_pages, hkv, PAGE, nblk)
         # v codes: [page][head][token quad 4][element group 16][token pair 2]
         # [element 8]; each byte holds the even token of its pair in the low
         # nibble and the odd token in the high nibble.  self.vc is the
@@ -29,8 +32,8 @@ class Planes:
         nib = np.stack([vb & 0xF, vb >> 4], axis=-1)        # [..][quad][group][pair][e][nibble]
         nib = nib.transpose(0, 1, 2, 4, 6, 3, 5)             # [..][quad][pair][nibble][group][e]
         self.vc = np.ascontiguousarray(nib).reshape(num_pages, hkv, PAGE, D)
-        # v scales: [page][head][block 8][token 16]
-        self.vs = np.asarray(v_scales).reshape(num_pages, hkv, NBLK, PAGE)
+        # v scales: [page][head][block][token 16]
+        self.vs = np.asarray(v_scales).reshape(num_pages, hkv, nblk, PAGE)
 
     def k_row(self, page, slot):
         """codes [Hkv][128], scales [Hkv][8] of the K row at (page, slot)."""

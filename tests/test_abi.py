@@ -110,6 +110,37 @@ def test_to_fp8_rejects_bad_arguments(api):
     assert tf(n=40) == 1 and b"multiple of 16" in L.nvfp4_last_error()
 
 
+def test_mx_sizes_offsets_and_bad_arguments(api):
+    L = api.lib()
+    assert api.mx_plane_bytes(10, 8, 0) == 10 * 8 * 1024
+    assert api.mx_plane_bytes(10, 8, 1) == 10 * 8 * 64
+    assert api.mx_plane_bytes(10, 8, 4) == 0 and api.mx_plane_bytes(0, 8, 0) == 0
+    # K + V per (token, head): 2 * (64 + 4) bytes, 0.53125 per element
+    per = sum(api.mx_plane_bytes(1, 1, p) for p in range(4)) / 16
+    assert per == 136 and per / 256 == 0.53125
+    assert api.mx_exp_offset_from_amax(1.0) == -10
+    assert api.mx_exp_offset_from_amax(1000.0) == 9 - 10
+    assert api.mx_exp_offset_from_amax(0.0) == 0 and api.mx_exp_offset_from_amax(float("nan")) == 0
+
+    def mx(**kw):
+        c = api.MxCacheStruct(0x10000, 0x20000, 0x30000, 0x40000, -3, 2, 64, 8, 16, 128)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return c
+    p = FAKE
+    assert L.nvfp4_mx_append(ctypes.byref(mx(head_dim=64)), p, p, 1, 4, p, p, p, 8, None) == 2
+    assert L.nvfp4_mx_append(ctypes.byref(mx(k_exp_offset=-127)), p, p, 1, 4, p, p, p, 8, None) == 1
+    assert L.nvfp4_mx_append(ctypes.byref(mx(v_scales=0x40008)), p, p, 1, 4, p, p, p, 8, None) == 1
+    assert L.nvfp4_mx_append(ctypes.byref(mx()), p, p, 5, 4, p, p, p, 8, None) == 2
+    assert L.nvfp4_mx_append(ctypes.byref(mx()), None, None, 1, 0, None, None, None, 8, None) == 0
+    c = mx()
+    assert L.nvfp4_mx_decode_attn(ctypes.byref(c), FAKE, 1, 2, 12, FAKE, 64, FAKE, 1000, 0.088, 0,
+                                  FAKE, 1 << 30, FAKE, None) == 1          # 12 heads over 8 KV heads
+    assert L.nvfp4_mx_decode_attn(ctypes.byref(c), FAKE, 1, 2, 32, FAKE, 64, FAKE, 1000, 0.088, 4,
+                                  None, 0, FAKE, None) == 3
+    assert api.mx_decode_workspace_bytes(2, 32, 8, 1000, 4) == api.decode_workspace_bytes(2, 32, 8, 1000, 4)
+
+
 def test_dequant_rejects_bad_arguments(api):
     L = api.lib()
     c = _fake_cache(api)

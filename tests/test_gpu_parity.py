@@ -8,7 +8,7 @@ import torch
 
 from decode_attention_nvfp4_amd import api
 from decode_attention_nvfp4_amd import workloads as W
-from gpu_common import TOL, BuiltCmp, BuiltDecode, check_decode, compare, i32, planes, say, to_dev
+from gpu_common import TOL, BuiltCmp, BuiltDecode, BuiltMx, check_decode, compare, i32, planes, say, to_dev
 from layout import sequence_tokens
 
 pytestmark = pytest.mark.gpu
@@ -722,3 +722,122 @@ def test_cmp_decode_splits_f32_query_and_steps(orc, fmt):
     say(f"cmp fmt {fmt} after {w.steps} steps")
     out2 = built.decode(q2).cpu().numpy()
     check_decode(out2, *built.oracle_decode(orc, q2, range(3)), factor=CMP_FACTOR[fmt])
+
+
+# ------------------------------------------------------------------ MXFP4
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dist", ["normal", "outlier", "mixed", "tiny"])
+def test_mx_append_bit_exact_and_sentinel(orc, dtype, dist):
+    """MXFP4 rows scattered into a sentinel-filled cache: codes and E8M0
+    scales equal the oracle's, every other byte keeps 0xA5."""
+    rng = np.random.default_rng(200 + ["normal", "outlier", "mixed", "tiny"].index(dist) * 2 + (dtype == "f32"))
+    B, Hkv, max_pages, num_pages = 3, 4, 6, 24
+    pt = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    n = 150
+    slots = rng.choice(B * max_pages * 16, n, replace=False)
+    seq = (slots // (max_pages * 16)).astype(np.int32)
+    pos = (slots % (max_pages * 16)).astype(np.int32)
+    k = W.random_rows(30, n * Hkv, dist, dtype).reshape(n, Hkv, 128)
+    v = W.random_rows(31, n * Hkv, dist, dtype).reshape(n, Hkv, 128)
+    cache = api.MxCache(num_pages, Hkv, fill=0xA5)
+    say(f"mx append {dtype} {dist} n={n}")
+    api.mx_append(cache, to_dev(k, dtype), to_dev(v, dtype), i32(seq), i32(pos), i32(pt))
+    P = planes(cache)
+    pages = pt[seq, pos // 16]
+    got = P.gather(pages, pos % 16)
+    exp = (*orc.mx_quantize_rows(k), *orc.mx_quantize_rows(v))
+    for g, e, nm in zip(got, exp, ("k codes", "k scales", "v codes", "v scales")):
+        bad = np.argwhere(g != e)
+        assert bad.size == 0, (nm, bad[:5].tolist())
+    masks = P.touched_mask(pages, pos % 16)
+    for arr, m, f in zip(P.arrays(), masks, P.untouched_fill(0xA5)):
+        assert np.array_equal(arr[~m], f[~m])
+
+
+def test_mx_append_edges(orc):
+    """Exact grid points and midpoints at several block exponents, zeros of
+    both signs, a zero block, subnormal and huge blocks."""
+    rows = []
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    mids = np.array([.25, .75, 1.25, 1.75, 2.5, 3.5, 5], np.float32)
+    for e in (-126, -20, 0, 5, 100):
+        X = np.float32(2.0 ** e)
+        r = np.zeros(128, np.float32)
+        r[0] = np.float32(6) * X                         # pins the block exponent to e
+        r[1:8] = mids * X
+        r[8:15] = np.nextafter(mids * X, np.float32(np.inf))
+        r[15] = -0.0
+        r[16:24] = -grid * X
+        r[32] = np.float32(7.99) * X                     # clipped to 6
+        r[33:40] = -np.nextafter(mids * X, np.float32(0))
+        r[64:96] = -0.0                                  # a zero block
+        r[96:128] = np.float32(1e-44)                    # a subnormal block
+        rows.append(r)
+    big = np.zeros(128, np.float32)
+    big[:] = np.float32(3e38)
+    rows.append(big)
+    x = np.stack(rows).reshape(len(rows), 1, 128)
+    for dtype in ("f32", "bf16"):
+        xx = x if dtype == "f32" else W.round_bf16(x)
+        n = xx.shape[0]
+        cache = api.MxCache(4, 1, fill=0xA5)
+        pt = np.arange(4, dtype=np.int32)[None]
+        say(f"mx append edges {dtype}")
+        api.mx_append(cache, to_dev(xx, dtype), to_dev(-xx, dtype), i32(np.zeros(n)), i32(np.arange(n)), i32(pt))
+        P = planes(cache)
+        got = P.gather(np.zeros(n, int), np.arange(n))
+        exp = (*orc.mx_quantize_rows(xx), *orc.mx_quantize_rows(-xx))
+        for g, e, nm in zip(got, exp, ("k codes", "k scales", "v codes", "v scales")):
+            assert np.array_equal(g, e), (dtype, nm, np.argwhere(g != e)[:5].tolist())
+
+
+MX_CASES = [
+    (2, 1, 1, 1, [1], "f32"),
+    (3, 3, 4, 1, [15, 16, 17], "f32"),
+    (4, 4, 32, 8, [1, 100, 257, 1000], "bf16"),
+    (6, 5, 16, 2, [0, 31, 64, 65, 700], "bf16"),
+    (8, 2, 16, 1, [400, 33], "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", MX_CASES, ids=lambda c: f"s{c[0]}-B{c[1]}-G{c[2] // c[3]}")
+def test_mx_decode_parity_small(orc, case):
+    seed, B, Hq, Hkv, lens, dtype = case
+    w = W.custom_decode(seed, B, Hq, Hkv, lens, dtype=dtype, outliers=(seed % 2 == 0))
+    built = BuiltMx(w, orc)
+    assert api.mx_exp_offset_from_amax(2.0 ** (built.k_exp + 10)) == built.k_exp
+    built.check_codes(range(B))
+    q = w.q(0)
+    say(f"mx decode {case}")
+    out = built.decode(q).cpu().numpy()
+    ref, mag = built.oracle_decode(orc, q, range(B))
+    say("   ", check_decode(out, ref, mag))
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[b] == 0)
+
+
+def test_mx_decode_splits_f32_query_and_steps(orc):
+    """Wave counts 1 .. 5000 and automatic, an FP32 query, and appended
+    decode steps on a GQA 32/8 batch with outlier channels."""
+    w = W.custom_decode(12, 3, 32, 8, [1500, 77, 4000], dtype="bf16", outliers=True, steps=3)
+    built = BuiltMx(w, orc)
+    q = w.q(0)
+    ref, mag = built.oracle_decode(orc, q, range(3))
+    outs = {}
+    for S in (1, 7, 64, 5000, 0):
+        say(f"mx split S={S}")
+        outs[S] = built.decode(q, num_splits=S).cpu().numpy()
+        check_decode(outs[S], ref, mag)
+    again = built.decode(q, num_splits=0).cpu().numpy()
+    assert np.array_equal(again, outs[0])
+    qf = np.random.default_rng(8).standard_normal((3, 32, 128)).astype(np.float32)
+    say("mx f32 query")
+    check_decode(built.decode(qf, dtype="f32").cpu().numpy(), *built.oracle_decode(orc, qf, range(3)))
+    for step in range(w.steps):
+        built.append_step(step, orc)
+    built.check_codes(range(3))
+    q2 = w.q(1)
+    say(f"mx after {w.steps} steps")
+    check_decode(built.decode(q2).cpu().numpy(), *built.oracle_decode(orc, q2, range(3)))
