@@ -280,11 +280,34 @@ def bench_formats_cfg4(api, torch, stream, w, data, nv_scales, amax, q_np, iters
     return res
 
 
-def bench_mse_scale(api, torch, stream, w, data, scales, q_np, sample=8, iters=3):
-    """The MSE-searched block scale against amax/6 on configuration 4's data:
-    bulk-append time of the whole cache under each rule, the quantization
-    error of K and V, and the decode output's error against attention over
-    the unquantized bf16 K/V (FP32, on the device), on a sample of sequences."""
+def _mx_dequant_seq(torch, c, pt_row, L, plane):
+    """MXFP4 values [L][Hkv][128] of one sequence's K (plane 0) or V (plane 1),
+    read from the device planes by the layout the header states."""
+    H = c.num_kv_heads
+    pos = torch.arange(L, device="cuda")
+    pages = pt_row.long()[pos // 16]
+    slots = pos % 16
+    if plane == 0:
+        b = c.k_codes.view(c.num_pages, H, 16, 64)[pages, :, slots]              # [L][H][64]
+        codes = torch.stack([b & 15, b >> 4], dim=-1).reshape(L, H, 128)
+        sc = c.k_scales.view(c.num_pages, H, 16, 4)[pages, :, slots]             # [L][H][4]
+    else:
+        vb = c.v_codes.view(c.num_pages, H, 4, 16, 2, 8)
+        nib = torch.stack([vb & 15, vb >> 4], dim=-1).permute(0, 1, 2, 4, 6, 3, 5)
+        codes = nib.reshape(c.num_pages, H, 16, 128)[pages, :, slots]
+        sc = c.v_scales.view(c.num_pages, H, 4, 16).permute(0, 1, 3, 2)[pages, :, slots]
+    grid = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6], dtype=torch.float64, device="cuda")
+    mag = grid[(codes & 7).long()]
+    val = torch.where((codes & 8) != 0, -mag, mag)
+    return val * torch.exp2(sc.double() - 127).repeat_interleave(32, dim=-1)
+
+
+def bench_block_scales(api, torch, stream, w, data, scales, amax, q_np, sample=8, iters=3, dec_iters=10):
+    """Configuration 4's data under three block-scale rules: NVFP4 with the
+    amax/6 scale, NVFP4 with the MSE-searched scale, and MXFP4 (E8M0 per 32):
+    bulk-append time of the whole cache, decode time, the quantization error
+    of K and V, and the decode output's error against attention over the
+    unquantized bf16 K/V (FP32, on the device), on a sample of sequences."""
     s_tk, s_tv = scales
     pt = torch.from_numpy(w.page_table).cuda()
     kd = torch.from_numpy(np.concatenate([d[0] for d in data])).to(torch.bfloat16).cuda()
@@ -292,17 +315,23 @@ def bench_mse_scale(api, torch, stream, w, data, scales, q_np, sample=8, iters=3
     seq = torch.from_numpy(np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(w.lens)])).cuda()
     pos = torch.from_numpy(np.concatenate([np.arange(int(L), dtype=np.int32) for L in w.lens])).cuda()
     ntok = kd.shape[0]
-    bulk_bytes = ntok * w.Hkv * 128 * 2 * (2 + 0.5625) + ntok * 8
     res = {"workload": f"decode config 4 data ({ntok} tokens x {w.Hkv} heads); errors over sequences "
                        f"0..{sample - 1}"}
     caches = {}
-    for name, put in (("amax6", api.append), ("mse", api.append_mse)):
-        c = api.KVCache(w.num_pages, w.Hkv, s_tk, s_tv, fill=0)
+    for name, put in (("amax6", api.append), ("mse", api.append_mse), ("mxfp4", api.mx_append)):
+        if name == "mxfp4":
+            c = api.MxCache(w.num_pages, w.Hkv, api.mx_exp_offset_from_amax(amax[0]),
+                            api.mx_exp_offset_from_amax(amax[1]), fill=0)
+            per_elem = 0.53125
+        else:
+            c = api.KVCache(w.num_pages, w.Hkv, s_tk, s_tv, fill=0)
+            per_elem = 0.5625
         put(c, kd, vd, seq, pos, pt)
         torch.cuda.synchronize()
         t = time_region(torch, lambda: put(c, kd, vd, seq, pos, pt), iters, stream)
         caches[name] = c
-        res[name] = {"bulk_append_ms": round(t, 3), "bulk_append_gbs": round(bulk_bytes / t / 1e6, 1)}
+        nbytes = ntok * w.Hkv * 128 * 2 * (2 + per_elem)
+        res[name] = {"bulk_append_ms": round(t, 3), "bulk_append_gbs": round(nbytes / t / 1e6, 1)}
     del kd, vd, seq, pos
     torch.cuda.empty_cache()
     G = w.Hq // w.Hkv
@@ -328,20 +357,29 @@ def bench_mse_scale(api, torch, stream, w, data, scales, q_np, sample=8, iters=3
         se = {"k": 0.0, "v": 0.0}
         sq = {"k": 0.0, "v": 0.0}
         for b in range(sample):
-            kh, vh = api.dequant(c, pt[b], 0, int(w.lens[b]))
+            Lb = int(w.lens[b])
+            if name == "mxfp4":
+                kh, vh = _mx_dequant_seq(torch, c, pt[b], Lb, 0), _mx_dequant_seq(torch, c, pt[b], Lb, 1)
+            else:
+                kh, vh = api.dequant(c, pt[b], 0, Lb)
             for nm, xh, x in (("k", kh, data[b][0]), ("v", vh, data[b][1])):
                 xd = torch.from_numpy(x).cuda().double()
                 se[nm] += float(((xh.double() - xd) ** 2).sum())
                 sq[nm] += float((xd ** 2).sum())
-        api.decode(c, q, pt, lens, L, workspace=ws, out=out)
+        dec = api.mx_decode if name == "mxfp4" else api.decode
+        dec(c, q, pt, lens, L, workspace=ws, out=out)
         torch.cuda.synchronize()
         d = out[:sample].double() - ref.double()
+        t = time_region(torch, lambda: dec(c, q, pt, lens, L, workspace=ws, out=out), dec_iters, stream)
+        nbytes = int(w.lens.sum()) * w.Hkv * 256 * (0.53125 if name == "mxfp4" else 0.5625)
         res[name].update({
             "rel_mse_k": se["k"] / sq["k"], "rel_mse_v": se["v"] / sq["v"],
             "decode_rel_l2_err": float(d.norm() / ref.double().norm()),
+            "decode_us": round(t * 1e3, 2), "decode_gbs": round(nbytes / t / 1e6, 1),
         })
-    for key in ("rel_mse_k", "rel_mse_v", "decode_rel_l2_err"):
-        res[f"mse_over_amax6_{key}"] = round(res["mse"][key] / res["amax6"][key], 4)
+    for other in ("mse", "mxfp4"):
+        for key in ("rel_mse_k", "rel_mse_v", "decode_rel_l2_err", "decode_us"):
+            res[f"{other}_over_amax6_{key}"] = round(res[other][key] / res["amax6"][key], 4)
     res["mse_append_slowdown"] = round(res["mse"]["bulk_append_ms"] / res["amax6"]["bulk_append_ms"], 3)
     del caches
     torch.cuda.empty_cache()
@@ -631,10 +669,11 @@ def main():
             res["extra"]["kv_formats_cfg4"] = {"error": repr(e)}
         log(f"kv formats: {res['extra']['kv_formats_cfg4']}")
         try:
-            res["extra"]["mse_scale_cfg4"] = bench_mse_scale(api, torch, stream, w, data, (s_tk, s_tv), q_np)
+            res["extra"]["block_scales_cfg4"] = bench_block_scales(api, torch, stream, w, data, (s_tk, s_tv),
+                                                                   (amax_k, amax_v), q_np)
         except Exception as e:  # noqa: BLE001
-            res["extra"]["mse_scale_cfg4"] = {"error": repr(e)}
-        log(f"mse block scale: {res['extra']['mse_scale_cfg4']}")
+            res["extra"]["block_scales_cfg4"] = {"error": repr(e)}
+        log(f"block scales: {res['extra']['block_scales_cfg4']}")
         try:
             res["extra"]["nvfp4_to_fp8"] = bench_to_fp8(api, torch, stream)
         except Exception as e:  # noqa: BLE001
