@@ -605,17 +605,19 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   }
 }
 
-// One workgroup per (sequence, KV head, query head).  A segment cut by wave
-// ranges is combined from its pieces:
+// A segment cut by wave ranges is combined from its pieces:
 //   o = sum_w 2^(lse_w - M) o_w / sum_w 2^(lse_w - M), times s_tV.
 // Wave w's range starts at start(w) = w U / W; unit u belongs to wave
 // floor(((u + 1) W - 1) / U); the piece of wave w sits in slot 0 when w's range
 // starts inside the segment, else in slot 1.  Waves between the first and the
 // last owner with an empty range (W > U) wrote nothing and are skipped.
-// Thread (i, e) = (tid / 32, tid % 32) takes pieces i, i + PL, ... and output
-// elements 4e .. 4e + 3, so all partial loads are independent; the PL piece
-// lanes are combined in LDS.  PL = 8 when segments have many pieces (few
-// long sequences), else 2 (one wave per head).
+// A query head's thread (i, e) = (tid / 32, tid % 32) takes pieces i,
+// i + PL, ... and output elements 4e .. 4e + 3, so all partial loads are
+// independent; the PL piece lanes are combined in LDS.  PL = 8 when segments
+// have many pieces (few long sequences): one workgroup per query head.  Else
+// PL = 2 and one workgroup holds the G query heads of a segment, 64 threads
+// each (a quarter of the workgroups of one per head: their launch, not the
+// merging, dominated the kernel's time).
 // Waves owning unit range ends: w0 owns unit a, w1 unit end - 1, and
 // start(w) = w U / W.  I is uint32_t when every product stays below 2^32 (the
 // usual case: 64-bit division is a long software sequence), else int64_t.
@@ -626,33 +628,40 @@ struct RangeMath {
   __device__ long long start(int w) const { return (long long)((I)((I)w * U) / W); }
 };
 
-template <int PL, typename I>
-__device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMath<I> rm, long long a,
-                                              long long end, int g, float* out);
+constexpr int kMaxGroup = 16;   // query heads per KV head the decode accepts
 
-template <int PL>
-__global__ void __launch_bounds__(32 * PL) merge_kernel(DecodeArgs p) {
-  const int g = blockIdx.x % p.group;
-  const int seg = blockIdx.x / p.group;
+template <int PL, bool PER_SEG, typename I>
+__device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMath<I> rm, long long a,
+                                              long long end, int g, int tid, float* out);
+
+template <int PL, bool PER_SEG>
+__global__ void __launch_bounds__(PER_SEG ? 64 * kMaxGroup : 32 * PL) merge_kernel(DecodeArgs p) {
+  const int g = PER_SEG ? (int)(threadIdx.x / (32 * PL)) : (int)(blockIdx.x % p.group);
+  const int seg = PER_SEG ? (int)blockIdx.x : (int)(blockIdx.x / p.group);
+  const int tid = (int)(threadIdx.x % (32 * PL));
   const int b = seg / p.hkv, kvh = seg % p.hkv;
   const int pb = p.ws_prefix[b], np = p.ws_prefix[b + 1] - pb;
   const long long U = (long long)p.ws_prefix[p.batch] * p.hkv;
   float* out = p.out + ((size_t)b * p.hq + (size_t)kvh * p.group + g) * kD;
   if (np == 0) {
-    if (threadIdx.x < 32) reinterpret_cast<float4*>(out)[threadIdx.x] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (tid < 32) reinterpret_cast<float4*>(out)[tid] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     return;
   }
   const long long a = (long long)pb * p.hkv + (long long)kvh * np;
   if (U * (long long)p.num_splits < (1LL << 32))
-    merge_segment<PL>(p, RangeMath<uint32_t>{(uint32_t)U, (uint32_t)p.num_splits}, a, a + np, g, out);
+    merge_segment<PL, PER_SEG>(p, RangeMath<uint32_t>{(uint32_t)U, (uint32_t)p.num_splits}, a, a + np, g, tid,
+                               out);
   else
-    merge_segment<PL>(p, RangeMath<long long>{U, (long long)p.num_splits}, a, a + np, g, out);
+    merge_segment<PL, PER_SEG>(p, RangeMath<long long>{U, (long long)p.num_splits}, a, a + np, g, tid, out);
 }
 
-template <int PL, typename I>
+// The exits before the workgroup barrier (empty sequence, a segment finished
+// by one wave) depend only on the segment, so every head of a workgroup
+// takes them together.
+template <int PL, bool PER_SEG, typename I>
 __device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMath<I> rm, long long a,
-                                              long long end, int g, float* out) {
-  const int tid = threadIdx.x, pi = tid >> 5, e = tid & 31;
+                                              long long end, int g, int tid, float* out) {
+  const int pi = tid >> 5, e = tid & 31;
   const int G = p.group;
   const int w0 = rm.owner(a);
   const int w1 = rm.owner(end - 1);
@@ -668,8 +677,11 @@ __device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMa
   };
   // each thread merges its pieces online (running max m, rescaling as it
   // grows); the 8 piece lanes are then combined once
-  __shared__ float4 s_acc[PL][32];
-  __shared__ float s_m[PL], s_den[PL];
+  __shared__ float4 s_acc_h[PER_SEG ? kMaxGroup : 1][PL][32];
+  __shared__ float s_m_h[PER_SEG ? kMaxGroup : 1][PL], s_den_h[PER_SEG ? kMaxGroup : 1][PL];
+  float4 (&s_acc)[PL][32] = s_acc_h[PER_SEG ? g : 0];
+  float (&s_m)[PL] = s_m_h[PER_SEG ? g : 0];
+  float (&s_den)[PL] = s_den_h[PER_SEG ? g : 0];
   float m = -INFINITY, den = 0.0f;
   float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
@@ -757,8 +769,8 @@ hipError_t launch_decode(const DecodeArgs& a, bool f32_q, int fmt, hipStream_t s
   else if (fmt == kFmtMxfp4) launch_fmt<kFmtMxfp4>(a, f32_q, s);
   else launch_fmt<kFmtNvfp4>(a, f32_q, s);
   const unsigned heads = (unsigned)(a.batch * a.hkv * a.group);
-  if ((long long)a.num_splits > 8LL * a.batch * a.hkv) merge_kernel<8><<<heads, 256, 0, s>>>(a);
-  else merge_kernel<2><<<heads, 64, 0, s>>>(a);
+  if ((long long)a.num_splits > 8LL * a.batch * a.hkv) merge_kernel<8, false><<<heads, 256, 0, s>>>(a);
+  else merge_kernel<2, true><<<(unsigned)(a.batch * a.hkv), 64 * a.group, 0, s>>>(a);
   return hipGetLastError();
 }
 
