@@ -13,7 +13,8 @@ step does identical work.
 Prints one JSON line.  `value` is the step's algorithmic bytes (cache bytes
 read by decode at 0.5625 B/element, plus the append's bf16 input and NVFP4
 output, plus queries and outputs) per second.  `roofline` is for the decode
-kernels, timed with HIP events on their stream.  `cpu_baseline` times the CPU
+kernels, timed with HIP events on their stream around each decode call of a
+second pass of K steps (the same work as the timed steps).  `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload.  `extra` holds the other
 measured paths (bulk append, prefill, the other decode workloads).
 """
@@ -593,9 +594,24 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
-    # per-kernel timing with HIP events on the launch stream
-    t_dec = time_region(torch, decode_step, args.steps, stream)
-    t_app = time_region(torch, append_step, args.steps, stream)
+    # per-call timing with HIP events on the launch stream: a second pass of
+    # K steps, events around each append and each decode call, so every call
+    # runs in the same context as in the timed steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        append_step()
+        e[1].record(stream)
+        e[2].record(stream)
+        decode_step()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t_app = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    t_dec = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    # decode calls back to back (no append between them) run slower on the
+    # boxes measured; reported for reference
+    t_dec_b2b = None if args.no_extra else time_region(torch, decode_step, args.steps, stream)
 
     if args.copy_mib:
         src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
@@ -640,6 +656,7 @@ def main():
         },
         "extra": {
             "decode_ms": round(t_dec, 5), "append_step_us": round(t_app * 1e3, 2),
+            "decode_back_to_back_ms": None if t_dec_b2b is None else round(t_dec_b2b, 5),
             "bulk_append": {"tokens": ntok, "ms": round(t_bulk, 3),
                             "gbs": round(bulk_bytes / (t_bulk * 1e-3) / 1e9, 1),
                             "frac_hbm_peak": round(bulk_bytes / (t_bulk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
