@@ -613,8 +613,10 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 // last owner with an empty range (W > U) wrote nothing and are skipped.
 // A query head's thread (i, e) = (tid / 32, tid % 32) takes pieces i,
 // i + PL, ... and output elements 4e .. 4e + 3, so all partial loads are
-// independent; the PL piece lanes are combined in LDS.  PL = 8 when segments
-// have many pieces (few long sequences): one workgroup per query head.  Else
+// independent; the PL piece lanes are combined in LDS.  PL = 32 or 8 when
+// segments have many pieces (few long sequences; more than 64 or 8 on
+// average): one workgroup per query head, so that its loop over the pieces
+// stays a few steps long.  Else
 // PL = 2 and one workgroup holds the G query heads of a segment, 64 threads
 // each (a quarter of the workgroups of one per head: their launch, not the
 // merging, dominated the kernel's time).
@@ -769,8 +771,10 @@ hipError_t launch_decode(const DecodeArgs& a, bool f32_q, int fmt, hipStream_t s
   else if (fmt == kFmtMxfp4) launch_fmt<kFmtMxfp4>(a, f32_q, s);
   else launch_fmt<kFmtNvfp4>(a, f32_q, s);
   const unsigned heads = (unsigned)(a.batch * a.hkv * a.group);
-  if ((long long)a.num_splits > 8LL * a.batch * a.hkv) merge_kernel<8, false><<<heads, 256, 0, s>>>(a);
-  else merge_kernel<2, true><<<(unsigned)(a.batch * a.hkv), 64 * a.group, 0, s>>>(a);
+  const long long segs = (long long)a.batch * a.hkv;
+  if (a.num_splits > 64 * segs) merge_kernel<32, false><<<heads, 1024, 0, s>>>(a);
+  else if (a.num_splits > 8 * segs) merge_kernel<8, false><<<heads, 256, 0, s>>>(a);
+  else merge_kernel<2, true><<<(unsigned)segs, 64 * a.group, 0, s>>>(a);
   return hipGetLastError();
 }
 
