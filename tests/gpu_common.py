@@ -261,8 +261,9 @@ class BuiltMx:
     codes and scales for every sequence.  The exp offsets come from the
     whole tensor's amax (steps included)."""
 
-    def __init__(self, w: W.DecodeWorkload, oracle, fill=0xA5, chunk=16):
+    def __init__(self, w: W.DecodeWorkload, oracle, fill=0xA5, chunk=16, keep=None):
         self.w = w
+        self.keep = set(range(w.B)) if keep is None else set(keep)
         data = [w.kv(b) for b in range(w.B)]
         ka = max([oracle.abs_max(k) for k, _ in data] + [oracle.abs_max(w.append_kv(s)[0]) for s in range(w.steps)])
         va = max([oracle.abs_max(v) for _, v in data] + [oracle.abs_max(w.append_kv(s)[1]) for s in range(w.steps)])
@@ -278,7 +279,8 @@ class BuiltMx:
                 vs.append(v)
                 seqs.append(np.full(len(k), b, np.int32))
                 poss.append(np.arange(len(k), dtype=np.int32))
-                self.codes[b] = (*oracle.mx_quantize_rows(k), *oracle.mx_quantize_rows(v))
+                if b in self.keep:
+                    self.codes[b] = (*oracle.mx_quantize_rows(k), *oracle.mx_quantize_rows(v))
             k = np.concatenate(ks)
             if len(k) == 0:
                 continue
@@ -292,7 +294,7 @@ class BuiltMx:
         k, v = w.append_kv(step)
         api.mx_append(self.cache, to_dev(k, w.dtype), to_dev(v, w.dtype), i32(np.arange(w.B)),
                       i32(self.lens.copy()), self.pt)
-        for b in range(w.B):
+        for b in self.keep:
             c = self.codes[b]
             kc, ksc = oracle.mx_quantize_rows(k[b:b + 1])
             vc, vsc = oracle.mx_quantize_rows(v[b:b + 1])

@@ -841,3 +841,37 @@ def test_mx_decode_splits_f32_query_and_steps(orc):
     q2 = w.q(1)
     say(f"mx after {w.steps} steps")
     check_decode(built.decode(q2).cpu().numpy(), *built.oracle_decode(orc, q2, range(3)))
+
+
+def test_mx_config4_paged_sampled(orc):
+    """Configuration 4 in MXFP4, built in full on the device; the oracle
+    checks the codes and the attention of 6 sequences."""
+    w = W.decode_workload(4)
+    rng = np.random.default_rng(45)
+    sample = sorted(set([int(np.argmin(w.lens)), int(np.argmax(w.lens))] +
+                        rng.choice(w.B, 4, replace=False).tolist()))
+    built = BuiltMx(w, orc, keep=sample, fill=0)
+    built.check_codes(sample)
+    q = w.q(0)
+    say(f"mx config 4 decode, checking {sample}")
+    out = built.decode(q).cpu().numpy()
+    ref, mag = built.oracle_decode(orc, q, sample)
+    say("   ", check_decode(out[sample], ref, mag))
+    assert np.all(np.isfinite(out))
+
+
+def test_mse_config2_steps(orc):
+    """Configuration 2 (outlier channels) written with the MSE-searched scale,
+    then 3 appended steps: the oracle checks sequence 3's codes and decode
+    (its search over the whole batch takes a minute on the CPU)."""
+    w = W.decode_workload(2)
+    built = BuiltDecode(w, orc, keep=[3], mse=True)
+    built.check_codes([3])
+    for step in range(3):
+        built.append_step(step, orc)
+    built.check_codes([3])
+    q = w.q(2)
+    say("mse config 2 decode")
+    out = built.decode(q).cpu().numpy()
+    check_decode(out[[3]], *built.oracle_decode(orc, q, [3]))
+    assert np.all(np.isfinite(out))
