@@ -288,10 +288,10 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   // so s and the reference max m are relative to it.  The rescale keeps
   // |m| <= 100, moving the bias when needed; exponentials are then taken of
   // s itself (2^s neither overflows nor loses a weight above 2^-26 of the
-  // row max) and the conversion to E4M3 divides by 2^(m - 8).
+  // row max) and the conversion to E4M3 divides by 2^(m - 4).
   float bias = 0.0f;
   floatx16 cbias = {};
-  float pscale = 0x1p-8f;
+  float pscale = 0x1p-4f;
 
   // ---- S^T of the tile in ks[buf], two 32-key blocks
   auto qk = [&](int buf, floatx16 s[2]) {
@@ -393,14 +393,17 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     return max_across_halves(mx) * rowscale;
   };
-  // lazy max: rescale only when the row max grows by more than 0.5 (log2),
-  // which keeps p <= 2^0.5 (p * 2^8 stays inside E4M3's range)
+  // lazy max: rescale only when a row max grows by more than kLazy (log2)
+  // over the reference, so p <= 2^kLazy (FP8: p * 2^4 <= 256 stays inside
+  // E4M3's range; F16: p <= 256).  A rescale of any row costs the whole
+  // wave a pass over its accumulators, so the threshold is kept large
+  constexpr float kLazy = MODE == kPrefillFP8 ? 4.0f : 8.0f;
   auto rescale = [&](float mx, floatx16 s[2]) {
-    const bool grow = mx > m_ref + 0.5f;
+    const bool grow = mx > m_ref + kLazy;
     if (__any(grow)) {
       // FP8 keeps the reference max an integer (the conversion scale is a
-      // power of two); m >= mx - 0.5 keeps p <= 2^0.5 on this tile too
-      const float m_new = grow ? (MODE == kPrefillFP8 ? ceilf(mx - 0.5f) : mx) : m_ref;
+      // power of two); m >= mx keeps p <= 1 on this tile
+      const float m_new = grow ? (MODE == kPrefillFP8 ? ceilf(mx) : mx) : m_ref;
       const float alpha = fast_exp2(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
@@ -421,14 +424,15 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
             s[1][r] -= shift;
           }
         }
-        pscale = ldexpf(1.0f, (int)fminf(fmaxf(m_ref, -100.0f), 100.0f) - 8);
+        pscale = ldexpf(1.0f, (int)fminf(fmaxf(m_ref, -100.0f), 100.0f) - 4);
       }
     }
   };
   // ---- P^T and the row sum
   auto probs = [&](const floatx16 s[2], uint32_t pw[8 * EB]) {
     if constexpr (MODE == kPrefillFP8) {
-      // P^T = E4M3(2^(s - m + 8)); the factor 2^8 cancels in O / l
+      // P^T = E4M3(2^(s - m + 4)); the factor 2^4 cancels in O / l (weights
+      // below 2^-13 of 2^m fall under E4M3's smallest value)
       auto conv = [&](float e0, float e1, float e2, float e3) {
         const short2v lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(short2v{0, 0}, e0, e1, pscale, false);
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, e2, e3, pscale, true));
