@@ -92,6 +92,48 @@ __device__ __forceinline__ double block_sq_error(const float xb[16], uint32_t c,
   return sum;
 }
 
+// An FP32 estimate of block_sq_error(xb, c, s_t) with a bound on its
+// distance from it: [*lo, *hi] holds the double criterion.  Element codes
+// come from the hardware conversion of |x| * rcp(d) (d = s_block * s_t in
+// FP32), so a code may differ from the exact one only when |x| / d lies
+// within 2^-21 of an E2M1 midpoint, which moves that element's squared
+// error by at most 24 * 2^-21 * d^2; the FP32 arithmetic adds at most
+// 2^-17 d^2 + 2^-18.6 * (the sum) over the 16 elements.  The bound used,
+// 2^-11 d^2 + 2^-17 * sum, covers both with a margin.  Returns false where
+// the estimate does not apply (d outside [2^-40, 2^40], or a non-finite
+// sum), and the candidate is then evaluated exactly.
+__device__ __forceinline__ bool block_sq_error_est(const float xb[16], uint32_t c, float s_t, float* lo,
+                                                   float* hi) {
+  const float d = e4m3_to_float(c) * s_t;
+  if (!(d >= 0x1p-40f && d <= 0x1p40f)) return false;
+  const float y = __builtin_amdgcn_rcpf(d);
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float* v = xb + 8 * q;
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fabsf(v[0]) * y, fabsf(v[1]) * y, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fabsf(v[2]) * y, fabsf(v[3]) * y, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fabsf(v[4]) * y, fabsf(v[5]) * y, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, fabsf(v[6]) * y, fabsf(v[7]) * y, 1.0f, 3);
+    floatx2 g[4];
+    g[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    g[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    g[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    g[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float r = __builtin_fmaf(-g[e >> 1][e & 1], d, fabsf(v[e]));
+      acc = __builtin_fmaf(r, r, acc);
+    }
+  }
+  if (!__builtin_isfinite(acc)) return false;
+  const float tol = 0x1p-11f * d * d + 0x1p-17f * acc;
+  *lo = acc - tol;
+  *hi = acc + tol;
+  return true;
+}
+
 // quantize_half_block with the searched scale.  The lane pair swaps halves
 // so both hold the block's 16 elements in order; search position k = 0 is
 // the amax/6 code, k = 2j - 1 and 2j its neighbours at distance j below and
@@ -99,6 +141,10 @@ __device__ __forceinline__ double block_sq_error(const float xb[16], uint32_t c,
 // and the pair keeps the smallest (error, position); an unusable position
 // (code outside 1..126) is skipped.  Non-finite errors (non-finite inputs)
 // compare as ties, so the amax/6 code is kept, as in a plain ordered scan.
+// The exact error is computed only for candidates whose FP32 interval
+// (block_sq_error_est) reaches below the smallest upper end of the pair's
+// intervals: any other candidate is strictly worse than the candidate with
+// that upper end, which is always evaluated, so the choice is unchanged.
 __device__ __forceinline__ uint32_t quantize_half_block_mse(const float x[8], float s_t, float inv6,
                                                             double six_st, uint32_t* sb) {
   float a = 0.0f;
@@ -118,15 +164,47 @@ __device__ __forceinline__ uint32_t quantize_half_block_mse(const float x[8], fl
   if (c0 != 0) {
     // a lane may have no usable position (the odd lane when c0 is 1): its
     // (inf, past-the-end) then loses to any of its partner's
+    constexpr int kMine = kMseRadius + 1;       // positions of one lane
+    float lo[kMine];
+    bool est[kMine];
+    float min_hi = __builtin_huge_valf();
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int k = odd + 2 * i;
+      const int c = k == 0 ? c0 : ((k & 1) ? c0 - (k + 1) / 2 : c0 + k / 2);
+      est[i] = false;
+      lo[i] = 0.0f;
+      if (k > 2 * kMseRadius || c < 1 || c > 126) continue;
+      float hi;
+      est[i] = block_sq_error_est(xb, (uint32_t)c, s_t, &lo[i], &hi);
+      if (est[i]) min_hi = fminf(min_hi, hi);
+    }
+    min_hi = fminf(min_hi, __shfl_xor(min_hi, 1));
+    // the lane's candidates still in the running, as a bit mask; each
+    // pass evaluates one per lane, so the wave makes as many passes as its
+    // lanes have survivors at most (usually one), not one per position
+    uint32_t mask = 0u;
+#pragma unroll
+    for (int i = 0; i < kMine; ++i) {
+      const int k = odd + 2 * i;
+      const int c = k == 0 ? c0 : ((k & 1) ? c0 - (k + 1) / 2 : c0 + k / 2);
+      if (k > 2 * kMseRadius || c < 1 || c > 126) continue;
+      if (est[i] && lo[i] > min_hi) continue;   // strictly worse than another candidate
+      mask |= 1u << i;
+    }
     double best = __builtin_huge_val();
     int best_k = 2 * kMseRadius + 1;
-    for (int k = odd; k <= 2 * kMseRadius; k += 2) {
-      const int c = k == 0 ? c0 : ((k & 1) ? c0 - (k + 1) / 2 : c0 + k / 2);
-      if (c < 1 || c > 126) continue;
-      const double err = block_sq_error(xb, (uint32_t)c, s_t);
-      if (best_k > 2 * kMseRadius || err < best) {
-        best = err;
-        best_k = k;
+    while (__any(mask != 0u)) {
+      if (mask != 0u) {
+        const int i = __builtin_ctz(mask);      // increasing position order
+        mask &= mask - 1u;
+        const int k = odd + 2 * i;
+        const int c = k == 0 ? c0 : ((k & 1) ? c0 - (k + 1) / 2 : c0 + k / 2);
+        const double err = block_sq_error(xb, (uint32_t)c, s_t);
+        if (best_k > 2 * kMseRadius || err < best) {
+          best = err;
+          best_k = k;
+        }
       }
     }
     const double o_best = __shfl_xor(best, 1);
