@@ -131,6 +131,9 @@ __device__ __forceinline__ uint32_t e2m1_mag_exact(float x, double d) {
 // outside the range where the FP32 bracket holds, the lane redoes its eight
 // elements with exact double thresholds.
 __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t sb_code, float s_t) {
+  // the midpoint decision below needs |x| - p rounded on its own: a fused
+  // |x| - a * s_t would compare a different residual with e
+#pragma clang fp contract(off)
   uint32_t signs = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) signs |= (__float_as_uint(x[j]) >> 31) << (4 * j + 3);

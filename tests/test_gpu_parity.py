@@ -252,6 +252,48 @@ def test_append_mse_closed_forms_and_edges(orc):
             assert np.array_equal(g, e), (dtype, nm, np.argwhere(g != e)[:5].tolist())
 
 
+@pytest.mark.parametrize("mse", [False, True], ids=["amax6", "mse"])
+def test_append_near_midpoints(orc, mse):
+    """Blocks whose elements sit on, or one ulp beside, the E2M1 midpoints of
+    the grids of several candidate scales, with a tensor scale that is not a
+    power of two (so s_block * s_t is inexact): the element encoder's
+    midpoint decision and the search's FP32 screen must still give the
+    oracle's codes and scales.  (A fused |x| - a * s_t in the midpoint
+    decision once rounded such elements the wrong way.)"""
+    rng = np.random.default_rng(61)
+    mids = np.array([.25, .75, 1.25, 1.75, 2.5, 3.5, 5], np.float32)
+    st = float(np.float32(0.37))
+    rows = []
+    for _ in range(48):
+        r = np.empty(128, np.float32)
+        for blk in range(8):
+            c0 = int(rng.integers(20, 110))
+            amax = np.float32(6 * orc.e4m3_value(c0) * st)
+            b = np.empty(16, np.float32)
+            b[0] = amax
+            for e in range(1, 16):
+                c = c0 + int(rng.integers(-3, 4))
+                d = np.float32(orc.e4m3_value(c) * st)
+                v = np.float32(rng.choice(mids) * d)
+                v = [v, np.nextafter(v, np.float32(0)), np.nextafter(v, np.float32(np.inf))][int(rng.integers(0, 3))]
+                b[e] = min(v, amax) * (1 if rng.random() < 0.5 else -1)
+            r[16 * blk:16 * blk + 16] = b
+        rows.append(r)
+    x = np.stack(rows).reshape(-1, 1, 128)
+    n = x.shape[0]
+    cache = api.KVCache(4, 1, st, st, fill=0xA5)
+    pt = np.arange(4, dtype=np.int32)[None]
+    say(f"append near midpoints (mse {mse})")
+    put, quant = (api.append_mse, orc.quantize_rows_mse) if mse else (api.append, orc.quantize_rows)
+    put(cache, to_dev(x, "f32"), to_dev(-x, "f32"), i32(np.zeros(n)), i32(np.arange(n)), i32(pt))
+    P = planes(cache)
+    pos = np.arange(n)
+    got = P.gather(pt[0][pos // 16], pos % 16)
+    exp = (*quant(x, st), *quant(-x, st))
+    for g, e, nm in zip(got, exp, ("k codes", "k scales", "v codes", "v scales")):
+        assert np.array_equal(g, e), (nm, np.argwhere(g != e)[:5].tolist())
+
+
 def test_decode_over_mse_cache(orc):
     """The decode path reads a cache written with the searched scale
     unchanged: parity with the oracle's attention over the oracle's codes."""
