@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -87,6 +88,37 @@ int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, i
   const int64_t want = std::min((units + kMinPagesPerWave - 1) / kMinPagesPerWave,
                                  std::max<int64_t>(cu_count(), kMaxPiecesPerSegment * batch * hkv));
   return (int32_t)std::max<int64_t>(1, std::min(slots, want));
+}
+
+// Work weights of the decode waves.  A launch of exactly two waves per SIMD
+// is placed one wave per SIMD for the first 4 x CUs workgroups and a second
+// wave per SIMD for the rest (measured on MI355X).  The SIMD's issue
+// arbitration favours the older wave, which then runs about 1.6 times as
+// fast as its partner on NVFP4 and MXFP4 pages (their expansion makes the
+// SIMD, not HBM, the limit; FP8 and BF16 pages are bound by HBM and gain
+// nothing), so equal ranges leave each SIMD's second wave finishing alone,
+// some 40 us after its partner on a 700 MB cache.  The first round's ranges
+// are weighted 8 : 5 instead (12 : 7 and 3 : 2 were measured too), and the
+// two waves of a SIMD finish within a few us of each other.  Every other
+// wave count keeps equal ranges.  The results do not depend on the
+// placement: the decode and the merge kernels derive the same ranges from
+// these weights.
+constexpr int64_t kSimdsPerCu = 4;
+constexpr int32_t kWeightFirst = 8, kWeightRest = 5;
+
+void set_wave_weights(DecodeArgs& a, int fmt, int64_t max_units) {
+  const int64_t simds = kSimdsPerCu * cu_count();
+  a.first_waves = a.num_splits;
+  a.weight_first = 1;
+  a.weight_rest = 1;
+  if ((fmt == kFmtNvfp4 || fmt == kFmtMxfp4) && a.num_splits == 2 * simds) {
+    const int64_t T = (kWeightFirst + kWeightRest) * simds;   // sum of the weights
+    if (max_units <= (INT64_MAX / 4) / T) {
+      a.first_waves = (int32_t)simds;
+      a.weight_first = kWeightFirst;
+      a.weight_rest = kWeightRest;
+    }
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -317,6 +349,7 @@ static int32_t decode_call(int fmt, const uint8_t* kplane, const uint8_t* kscale
   a.max_pages = max_pages_per_seq;
   a.batch = batch; a.hq = num_q_heads; a.hkv = hkv; a.group = G;
   a.num_splits = W;
+  set_wave_weights(a, fmt, (int64_t)batch * hkv * max_pages_per_seq);
   return hip_status(launch_decode(a, f32q, fmt, (hipStream_t)stream), "decode launch");
 }
 

@@ -6,11 +6,12 @@
 //
 // Work decomposition (balanced stream): the work units are (sequence, KV
 // head, page) triples, ordered sequence-major, then KV head, then page.  The
-// grid is one wave64 per resident wave slot of the device; wave w takes the
-// contiguous unit range [w U / W, (w+1) U / W), so every wave streams the same
-// number of pages whatever the mix of sequence lengths (work counts that do
-// not divide the machine evenly waste it: "【CUDA 16GB向け】RTX 5090の長文推論
-// 遅延修正と…", section 利用者の報告).  A (sequence, KV head) segment that lies
+// grid is one wave64 per resident wave slot of the device; wave w takes a
+// contiguous unit range, of equal length for every wave (or weighted by the
+// issue share a wave gets on its SIMD: RangeMath), whatever the mix of
+// sequence lengths (work counts that do not divide the machine evenly waste
+// it: "【CUDA 16GB向け】RTX 5090の長文推論遅延修正と…", section 利用者の報告).
+// A (sequence, KV head) segment that lies
 // inside one wave's range is finished by that wave; a segment cut by range
 // boundaries leaves one normalized partial per wave (at most two per wave: its
 // first and its last segment) and merge_kernel combines them with a
@@ -396,22 +397,6 @@ __device__ __forceinline__ int wave_scan(int v, int lane) {
   return v;
 }
 
-// Sequence lengths of 64 consecutive sequences base .. base + 63, one per
-// lane (0 past the batch), so that walking to the next sequence is a
-// readlane rather than a memory round trip.
-struct LenWindow {
-  int base;
-  int len;
-};
-
-__device__ __forceinline__ int window_len(const DecodeArgs& p, LenWindow& w, int b, int lane) {
-  if (b - w.base >= 64) {                  // rare: move the window forward
-    w.base = b;
-    w.len = b + lane < p.batch ? seq_len(p, b + lane) : 0;
-  }
-  return __builtin_amdgcn_readlane(w.len, b - w.base);
-}
-
 // Position in the (sequence, KV head, page) order: the segment (b, kvh) of a
 // sequence of length L with np pages, and page pg inside it.  All fields are
 // wave-uniform.
@@ -419,58 +404,79 @@ struct SegPos {
   int b, kvh, L, np, pg;
 };
 
+// Wave-uniform reads of the page table and the sequence lengths go through
+// the scalar data cache: scalar loads are counted apart from vector memory,
+// so waiting for one never waits for the page loads in flight (vector loads
+// complete in order under one counter, and a vector load read soon after its
+// issue would hold up every page behind it).  Both arrays are read-only here.
+typedef __attribute__((address_space(4))) const int32_t ConstI32;
+
+__device__ __forceinline__ int32_t scalar_load(const int32_t* base, size_t i) {
+  return ((const ConstI32*)base)[i];
+}
+
+__device__ __forceinline__ int seq_len_uniform(const DecodeArgs& p, int b) {
+  return min(max(scalar_load(p.seq_lens, (size_t)b), 0), p.max_pages * kPage);
+}
+
+__device__ __forceinline__ uint32_t page_id_uniform(const DecodeArgs& p, const SegPos& s) {
+  return (uint32_t)scalar_load(p.page_table, (size_t)s.b * p.max_pages + s.pg);
+}
+
 // Move to the first page of the next non-empty segment.  The caller knows
 // that one exists (a unit of the wave's range lies beyond).
-__device__ __forceinline__ void next_segment(const DecodeArgs& p, SegPos& s, LenWindow& w, int lane) {
+__device__ __forceinline__ void next_segment(const DecodeArgs& p, SegPos& s) {
   s.pg = 0;
   if (++s.kvh == p.hkv) {
     s.kvh = 0;
     do {
       ++s.b;
-      s.L = window_len(p, w, s.b, lane);
+      s.L = seq_len_uniform(p, s.b);
       s.np = pages_of(s.L);
     } while (s.np == 0);
   }
 }
 
-// Slab ids (page * Hkv + head) of the next n = min(64, left) units of the
-// stream, lane j holding unit j; `w` advances past them.  Lanes j >= n are
-// left at 0 and never read.  The page-table loads are not waited for here:
-// their results are read a whole block later.
-__device__ __forceinline__ uint32_t prepare_block(const DecodeArgs& p, SegPos& w, LenWindow& win, int left,
-                                                  int lane) {
-  const int n = min(64, left);
-  int off = w.pg + lane;
-  SegPos s = w;
-  LenWindow sw = win;
-  uint32_t slab = 0;
-  bool need = lane < n;
-  while (true) {
-    const bool here = need && off < s.np;
-    if (here) slab = (uint32_t)p.page_table[(size_t)s.b * p.max_pages + off] * (uint32_t)p.hkv + (uint32_t)s.kvh;
-    need = need && !here;
-    if (!__any(need)) break;
-    off -= s.np;
-    next_segment(p, s, sw, lane);
+// Wave ranges: wave w takes the units [start(w), start(w + 1)) with
+//   start(w) = floor(U S(w) / S(W)),  S(w) = A min(w, R) + B max(0, w - R),
+// so the first R waves weigh A and the others B (A = B: equal ranges).  The
+// wave owning unit u is the largest w with start(w) <= u, which is the
+// largest w with S(w) <= floor(((u + 1) S(W) - 1) / U) (S grows strictly).
+// I is uint32_t when every product stays below 2^32 (the usual case: 64-bit
+// division is a long software sequence), else int64_t.
+template <typename I>
+struct RangeMath {
+  I U, T;                                  // units; T = S(W)
+  int R, A, B;
+  __device__ I S(int w) const { return (I)A * (I)min(w, R) + (I)B * (I)max(0, w - R); }
+  __device__ long long start(int w) const { return (long long)((I)((I)U * S(w)) / T); }
+  __device__ int owner(long long u) const {
+    const I smax = (I)((I)(u + 1) * T - 1) / U;
+    const I ar = (I)A * (I)R;
+    return smax < ar ? (int)(smax / (I)A) : R + (int)((smax - ar) / (I)B);
   }
-  // the walker moves to unit n (only needed while units remain)
-  w.pg += n;
-  if (left > n) {
-    while (w.pg >= w.np) {
-      const int rest = w.pg - w.np;
-      next_segment(p, w, win, lane);
-      w.pg = rest;
-    }
-  }
-  return slab;
+};
+
+template <typename I>
+__device__ __forceinline__ RangeMath<I> range_math(const DecodeArgs& p, long long U) {
+  RangeMath<I> rm;
+  rm.U = (I)U;
+  rm.R = p.first_waves;
+  rm.A = p.weight_first;
+  rm.B = p.weight_rest;
+  rm.T = rm.S(p.num_splits);
+  return rm;
+}
+
+__device__ __forceinline__ bool range_fits_u32(const DecodeArgs& p, long long U) {
+  const long long T = (long long)max(p.weight_first, p.weight_rest) * p.num_splits;
+  return U * T < (1LL << 32);
 }
 
 // Register stages of the page pipeline; the planner runs two waves per SIMD,
 // so the register budget is that of two waves (a BF16 page takes three times
 // the registers of an NVFP4 one).
 template <int FMT> constexpr int kDepth = FMT == kFmtBf16 ? 4 : 8;
-static_assert(64 % kDepth<kFmtNvfp4> == 0 && 64 % kDepth<kFmtBf16> == 0 && 64 % kDepth<kFmtMxfp4> == 0,
-              "block switches must fall on a stage boundary");
 
 template <bool F32Q, int FMT>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) decode_kernel(DecodeArgs p) {
@@ -492,7 +498,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   }
   if (wave == 0 && lane == 0) p.ws_prefix[B] = total_pages;
   const long long U = (long long)total_pages * Hkv;
-  const long long u0 = (long long)wave * U / W, u1 = (long long)(wave + 1) * U / W;
+  long long u0, u1;
+  if (range_fits_u32(p, U)) {
+    const RangeMath<uint32_t> rm = range_math<uint32_t>(p, U);
+    u0 = rm.start(wave);
+    u1 = rm.start(wave + 1);
+  } else {
+    const RangeMath<long long> rm = range_math<long long>(p, U);
+    u0 = rm.start(wave);
+    u1 = rm.start(wave + 1);
+  }
   if (u0 >= u1) return;
   const int N = (int)(u1 - u0);            // units of this wave
 
@@ -500,7 +515,6 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   // passes u0), KV head and page inside it
   int b0 = 0;
   long long a_b0 = 0;
-  LenWindow win0 = {0, 0};
   {
     int carry = 0;
     for (int c = 0; c < B; c += 64) {
@@ -513,17 +527,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
         const int idx = __ffsll((long long)hit) - 1;
         b0 = c + idx;
         a_b0 = (long long)(carry + __builtin_amdgcn_readlane(incl - np, idx)) * Hkv;
-        win0.base = c;
-        win0.len = len;
         break;
       }
       carry += __builtin_amdgcn_readlane(incl, 63);
     }
   }
-  win0.base = __builtin_amdgcn_readfirstlane(win0.base);
   SegPos start;
   start.b = __builtin_amdgcn_readfirstlane(b0);
-  start.L = __builtin_amdgcn_readlane(win0.len, start.b - win0.base);
+  start.L = seq_len_uniform(p, start.b);
   start.np = pages_of(start.L);
   {
     const long long off0 = u0 - a_b0;
@@ -531,30 +542,24 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
     start.pg = (int)(off0 % start.np);
   }
 
-  // ---- issue side: the wave's units form one stream of pages; the slab ids
-  // of the current 64-unit block (cur, units base..) and of the next one
-  // (nxt) sit one per lane
-  SegPos walker = start;
-  LenWindow wwin = win0;
-  int prepared = 0, base = 0;
-  uint32_t cur = prepare_block(p, walker, wwin, N, lane);
-  prepared = min(64, N);
-  uint32_t nxt = cur;
-  if (prepared < N) {
-    nxt = prepare_block(p, walker, wwin, N - prepared, lane);
-    prepared += min(64, N - prepared);
-  }
+  // ---- issue side: the wave's units form one stream of pages; `iw` is
+  // the unit issued next and `ipage` its page id, read one issue ahead
+  SegPos iw = start;
+  uint32_t ipage = page_id_uniform(p, iw);
+  int issued = 0;
   const LaneOffsets lo = lane_offsets<FMT>(col, kg);
   // units past the end reload the last one (never consumed)
-  auto issue = [&](PageRegs<FMT>& r, int x) {
-    const int o = min(x, N - 1) - base;
-    const uint32_t slab = o < 64 ? __builtin_amdgcn_readlane(cur, o) : __builtin_amdgcn_readlane(nxt, o - 64);
-    load_page<FMT>(p, slab, lo, r);
+  auto issue = [&](PageRegs<FMT>& r) {
+    load_page<FMT>(p, ipage * (uint32_t)Hkv + (uint32_t)iw.kvh, lo, r);
+    if (issued + 1 < N) {
+      ++issued;
+      if (++iw.pg == iw.np) next_segment(p, iw);
+      ipage = page_id_uniform(p, iw);
+    }
   };
 
   // ---- process side: one piece (the wave's part of one segment) at a time
   SegPos seg = start;
-  LenWindow pwin = win0;
   int piece_left = 0;                      // pages of the current piece still to process
   bool whole = false, first_piece = true, started = false;
   int done = 0;                            // units processed
@@ -563,7 +568,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   WaveState st;
   auto step = [&](const PageRegs<FMT>& r) {
     if (piece_left == 0) {                 // a new piece starts with this page
-      if (started) next_segment(p, seg, pwin, lane);
+      if (started) next_segment(p, seg);
       started = true;
       piece_left = min(seg.np - seg.pg, N - done);
       whole = seg.pg == 0 && piece_left == seg.np;
@@ -580,26 +585,26 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   };
 
   // kD8 register stages: the loads of the next kD8 - 1 pages are in
-  // flight while a page is processed (kD8 divides 64, so block switches
-  // fall on stage 0)
+  // flight while a page is processed.  The barriers keep the first loads in
+  // stream order: the compiler derives the loop's waits from that order too,
+  // and a reordered start makes every iteration wait for all but the newest
+  // page.
   PageRegs<FMT> r[kD8];
 #pragma unroll
-  for (int i = 0; i < kD8 - 1; ++i) issue(r[i], i);
+  for (int i = 0; i < kD8 - 1; ++i) {
+    issue(r[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Every stage issues, also past the end of the range (reloads of the last
+  // unit), and only the loop's latch exits: every path around the back edge
+  // then carries a whole iteration of page loads, which the compiler's waits
+  // rely on (an exit in the middle, however rare, gives it a short path).
   for (int t = 0; t < N; t += kD8) {
-    if (t == base + 64) {                  // the next block becomes current
-      cur = nxt;
-      base += 64;
-      if (prepared < N) {
-        nxt = prepare_block(p, walker, wwin, N - prepared, lane);
-        prepared += min(64, N - prepared);
-      }
-    }
 #pragma unroll
     for (int j = 0; j < kD8; ++j) {
-      if (j > 0 && t + j >= N) break;
-      issue(r[(j + kD8 - 1) % kD8], t + j + kD8 - 1);
+      issue(r[(j + kD8 - 1) % kD8]);
       __builtin_amdgcn_sched_barrier(0);
-      step(r[j]);
+      if (t + j < N) step(r[j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -607,10 +612,11 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 
 // A segment cut by wave ranges is combined from its pieces:
 //   o = sum_w 2^(lse_w - M) o_w / sum_w 2^(lse_w - M), times s_tV.
-// Wave w's range starts at start(w) = w U / W; unit u belongs to wave
-// floor(((u + 1) W - 1) / U); the piece of wave w sits in slot 0 when w's range
-// starts inside the segment, else in slot 1.  Waves between the first and the
-// last owner with an empty range (W > U) wrote nothing and are skipped.
+// The waves holding the segment's first and last units come from the same
+// range arithmetic as the decode kernel (RangeMath); the piece of wave w sits
+// in slot 0 when w's range starts inside the segment, else in slot 1.  Waves
+// between the first and the last owner with an empty range (W > U) wrote
+// nothing and are skipped.
 // A query head's thread (i, e) = (tid / 32, tid % 32) takes pieces i,
 // i + PL, ... and output elements 4e .. 4e + 3, so all partial loads are
 // independent; the PL piece lanes are combined in LDS.  PL = 32 or 8 when
@@ -620,16 +626,6 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
 // PL = 2 and one workgroup holds the G query heads of a segment, 64 threads
 // each (a quarter of the workgroups of one per head: their launch, not the
 // merging, dominated the kernel's time).
-// Waves owning unit range ends: w0 owns unit a, w1 unit end - 1, and
-// start(w) = w U / W.  I is uint32_t when every product stays below 2^32 (the
-// usual case: 64-bit division is a long software sequence), else int64_t.
-template <typename I>
-struct RangeMath {
-  I U, W;
-  __device__ int owner(long long u) const { return (int)((I)((I)(u + 1) * W - 1) / U); }
-  __device__ long long start(int w) const { return (long long)((I)((I)w * U) / W); }
-};
-
 constexpr int kMaxGroup = 16;   // query heads per KV head the decode accepts
 
 template <int PL, bool PER_SEG, typename I>
@@ -650,11 +646,10 @@ __global__ void __launch_bounds__(PER_SEG ? 64 * kMaxGroup : 32 * PL) merge_kern
     return;
   }
   const long long a = (long long)pb * p.hkv + (long long)kvh * np;
-  if (U * (long long)p.num_splits < (1LL << 32))
-    merge_segment<PL, PER_SEG>(p, RangeMath<uint32_t>{(uint32_t)U, (uint32_t)p.num_splits}, a, a + np, g, tid,
-                               out);
+  if (range_fits_u32(p, U))
+    merge_segment<PL, PER_SEG>(p, range_math<uint32_t>(p, U), a, a + np, g, tid, out);
   else
-    merge_segment<PL, PER_SEG>(p, RangeMath<long long>{U, (long long)p.num_splits}, a, a + np, g, tid, out);
+    merge_segment<PL, PER_SEG>(p, range_math<long long>(p, U), a, a + np, g, tid, out);
 }
 
 // The exits before the workgroup barrier (empty sequence, a segment finished

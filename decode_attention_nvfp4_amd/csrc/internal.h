@@ -95,6 +95,9 @@ struct DecodeArgs {
   int32_t batch, hq, hkv, group;
   int32_t num_splits;         // W: number of waves (work ranges)
   int32_t k_exp, v_exp;       // MXFP4: values are taken relative to 2^k_exp, 2^v_exp
+  // work weights of the waves: the first first_waves weigh weight_first,
+  // the rest weight_rest (equal weights: equal ranges)
+  int32_t first_waves, weight_first, weight_rest;
 };
 
 struct PrefillArgs {

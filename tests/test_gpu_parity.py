@@ -426,6 +426,12 @@ def test_decode_parity_small(orc, case):
             assert np.all(out[b] == 0)
 
 
+def two_waves_per_simd() -> int:
+    """The wave count at which the decode weights the first dispatch round's
+    ranges (two waves on each of the device's 4 x CU SIMDs)."""
+    return 2 * 4 * torch.cuda.get_device_properties(0).multi_processor_count
+
+
 def test_decode_split_sweep_and_determinism(orc):
     w = W.custom_decode(9, 3, 32, 8, [1500, 77, 4000], dtype="bf16", outliers=True)
     built = BuiltDecode(w, orc)
@@ -433,15 +439,17 @@ def test_decode_split_sweep_and_determinism(orc):
     ref, mag = built.oracle_decode(orc, q, range(3))
     outs = {}
     # 5000 waves exceed the 2800 (sequence, KV head, page) units: waves with
-    # empty ranges sit between the owners of a segment
-    for S in (1, 2, 7, 64, 5000, 0):
+    # empty ranges sit between the owners of a segment; two waves per SIMD
+    # take weighted ranges (empty ones among them)
+    sw = two_waves_per_simd()
+    for S in (1, 2, 7, 64, 5000, sw, 0):
         say(f"decode split sweep S={S}")
         outs[S] = built.decode(q, num_splits=S).cpu().numpy()
         check_decode(outs[S], ref, mag)
     # splits change the reference max each probability is taken against, so
     # the FP16 rounding of P differs; each result is within the bound of the
     # oracle, so two are within twice the bound of each other
-    for S in (2, 7, 64, 5000, 0):
+    for S in (2, 7, 64, 5000, sw, 0):
         check_decode(outs[S], outs[1], mag, factor=2.0)
     say("decode determinism")
     again = built.decode(q, num_splits=0).cpu().numpy()
@@ -868,7 +876,7 @@ def test_mx_decode_splits_f32_query_and_steps(orc):
     q = w.q(0)
     ref, mag = built.oracle_decode(orc, q, range(3))
     outs = {}
-    for S in (1, 7, 64, 5000, 0):
+    for S in (1, 7, 64, 5000, two_waves_per_simd(), 0):
         say(f"mx split S={S}")
         outs[S] = built.decode(q, num_splits=S).cpu().numpy()
         check_decode(outs[S], ref, mag)
