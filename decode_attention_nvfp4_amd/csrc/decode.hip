@@ -150,11 +150,11 @@ __device__ __forceinline__ float e8m0_rel(uint32_t byte, int ex) {
   return __uint_as_float((uint32_t)f << 23);
 }
 
+// S^T = K~ Q^T of one page (before the softmax scale): lane (col, kg) gets
+// the products of tokens 4kg .. 4kg + 3 with query head col.
 template <bool F32Q, int FMT>
-__device__ __forceinline__ void process_page(const PageRegs<FMT>& cur, int pg, int L, int kg, float qscale,
-                                             const halfx8 qh[4], const halfx8 ql[4], WaveState& st,
-                                             int kex, int vex) {
-  // ---- S^T = K~ Q^T
+__device__ __forceinline__ floatx4 qk_page(const PageRegs<FMT>& cur, const halfx8 qh[4], const halfx8 ql[4],
+                                           int kex) {
   floatx4 acc_s = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (FMT == kFmtNvfp4) {
     const halfx2 ks = e4m3x2_to_half((uint32_t)cur.ksc, false);
@@ -205,6 +205,62 @@ __device__ __forceinline__ void process_page(const PageRegs<FMT>& cur, int pg, i
       if (F32Q) acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, ql[i]), acc_s, 0, 0, 0);
     }
   }
+  return acc_s;
+}
+
+// V block scales of a page's four tokens 4kg .. 4kg + 3 as FP16 pairs:
+// E4M3 (exact in FP16) or E8M0 relative to 2^vex.
+template <int FMT>
+__device__ __forceinline__ void v_scales(const PageRegs<FMT>& cur, int vex, halfx2& v01, halfx2& v23) {
+  if constexpr (FMT == kFmtNvfp4) {
+    v01 = e4m3x2_to_half(cur.vsc, false);
+    v23 = e4m3x2_to_half(cur.vsc, true);
+  } else {
+    v01 = halfx2{(_Float16)e8m0_rel(cur.vsc & 0xFFu, vex), (_Float16)e8m0_rel((cur.vsc >> 8) & 0xFFu, vex)};
+    v23 = halfx2{(_Float16)e8m0_rel((cur.vsc >> 16) & 0xFFu, vex), (_Float16)e8m0_rel(cur.vsc >> 24, vex)};
+  }
+}
+
+// Element SEL of the lane's d run (d = 8 col + 4 HI + SEL) of tokens
+// 4kg .. 4kg + 3, times the tokens' block scales: byte SEL of word
+// 2 j + HI holds it for the token pair j (4kg + 2j, 4kg + 2j + 1).
+template <int SEL, int HI, int FMT>
+__device__ __forceinline__ halfx4 v_column(const PageRegs<FMT>& cur, halfx2 v01, halfx2 v23) {
+  const halfx2 a0 = e2m1x2_to_half<SEL>(cur.vq[HI]) * v01;
+  const halfx2 a1 = e2m1x2_to_half<SEL>(cur.vq[2 + HI]) * v23;
+  return halfx4{a0[0], a0[1], a1[0], a1[1]};
+}
+
+// Clear the V bytes of the lane's tokens 4kg + r, r >= live: slots that no
+// token owns may hold any bytes (NaN patterns among them), and a zero weight
+// times a NaN would still be NaN.  Cleared bytes expand to exact zeros in
+// every format (an E4M3 scale 0; an E8M0 scale 0 goes to 2^-127 relative to
+// the offset, times a finite element).  Each word holds the four tokens in
+// order: bytes for the scale words and FP8, 16-bit halves for BF16 pairs.
+__device__ __forceinline__ uint32_t live_bytes(int live) {
+  return live >= 4 ? 0xFFFFFFFFu : (1u << (8 * max(live, 0))) - 1u;
+}
+
+template <int FMT>
+__device__ __forceinline__ void drop_v(PageRegs<FMT>& c, int live) {
+  if constexpr (FMT == kFmtNvfp4 || FMT == kFmtMxfp4) {
+    c.vsc &= live_bytes(live);
+  } else if constexpr (FMT == kFmtFp8) {
+    const uint32_t m = live_bytes(live);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) c.vq[i] &= u32x4{m, m, m, m};
+  } else {
+    const uint32_t m01 = live_bytes(2 * live), m23 = live_bytes(2 * live - 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c.vq[i] &= u32x4{m01, m23, m01, m23};
+  }
+}
+
+template <bool F32Q, int FMT>
+__device__ __forceinline__ void process_page(PageRegs<FMT> cur, int pg, int L, int kg, float qscale,
+                                             const halfx8 qh[4], const halfx8 ql[4], WaveState& st,
+                                             int kex, int vex) {
+  floatx4 acc_s = qk_page<F32Q, FMT>(cur, qh, ql, kex);
   // ---- softmax (log2 domain); lane holds tokens 4kg..4kg+3 of head col.
   // Only a sequence's last page is partial (uniform test).  qscale > 0, so
   // the max is taken on the raw products and scaled once.
@@ -212,6 +268,7 @@ __device__ __forceinline__ void process_page(const PageRegs<FMT>& cur, int pg, i
     const int tbase = pg * kPage + kg * 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc_s[r] = (tbase + r < L) ? acc_s[r] : -INFINITY;
+    drop_v<FMT>(cur, L - tbase);
   }
   float mx = fmaxf(fmaxf(acc_s[0], acc_s[1]), fmaxf(acc_s[2], acc_s[3]));
   mx = max_across_rows(mx) * qscale;
@@ -230,33 +287,19 @@ __device__ __forceinline__ void process_page(const PageRegs<FMT>& cur, int pg, i
   st.l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   if constexpr (FMT == kFmtNvfp4 || FMT == kFmtMxfp4) {
     const halfx4 bp = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
-    // ---- O^T += V~^T P^T.  Byte e of word j / 2 (j = token pair) holds
-    // element d = 8 col + e of tokens (4kg + 2j, 4kg + 2j + 1): one conversion
-    // gives the two tokens of a pair, the A operand's k order.  The block
-    // scales of the four tokens: E4M3 (exact in FP16) or E8M0 relative to
-    // 2^vex.
+    // ---- O^T += V~^T P^T: one 16-token MFMA per element of the lane's
+    // d run; P^T comes straight from the S^T accumulator layout
     halfx2 v01, v23;
-    if constexpr (FMT == kFmtNvfp4) {
-      v01 = e4m3x2_to_half(cur.vsc, false);
-      v23 = e4m3x2_to_half(cur.vsc, true);
-    } else {
-      v01 = halfx2{(_Float16)e8m0_rel(cur.vsc & 0xFFu, vex), (_Float16)e8m0_rel((cur.vsc >> 8) & 0xFFu, vex)};
-      v23 = halfx2{(_Float16)e8m0_rel((cur.vsc >> 16) & 0xFFu, vex), (_Float16)e8m0_rel(cur.vsc >> 24, vex)};
-    }
-    auto tile = [&](halfx2 a0, halfx2 a1, floatx4& acc) {
-      a0 *= v01;
-      a1 *= v23;
-      const halfx4 a = {a0[0], a0[1], a1[0], a1[1]};
-      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bp, acc, 0, 0, 0);
-    };
-    tile(e2m1x2_to_half<0>(cur.vq[0]), e2m1x2_to_half<0>(cur.vq[2]), st.acc_o[0]);
-    tile(e2m1x2_to_half<1>(cur.vq[0]), e2m1x2_to_half<1>(cur.vq[2]), st.acc_o[1]);
-    tile(e2m1x2_to_half<2>(cur.vq[0]), e2m1x2_to_half<2>(cur.vq[2]), st.acc_o[2]);
-    tile(e2m1x2_to_half<3>(cur.vq[0]), e2m1x2_to_half<3>(cur.vq[2]), st.acc_o[3]);
-    tile(e2m1x2_to_half<0>(cur.vq[1]), e2m1x2_to_half<0>(cur.vq[3]), st.acc_o[4]);
-    tile(e2m1x2_to_half<1>(cur.vq[1]), e2m1x2_to_half<1>(cur.vq[3]), st.acc_o[5]);
-    tile(e2m1x2_to_half<2>(cur.vq[1]), e2m1x2_to_half<2>(cur.vq[3]), st.acc_o[6]);
-    tile(e2m1x2_to_half<3>(cur.vq[1]), e2m1x2_to_half<3>(cur.vq[3]), st.acc_o[7]);
+    v_scales<FMT>(cur, vex, v01, v23);
+    auto tile = [&](halfx4 a, floatx4& acc) { acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bp, acc, 0, 0, 0); };
+    tile(v_column<0, 0>(cur, v01, v23), st.acc_o[0]);
+    tile(v_column<1, 0>(cur, v01, v23), st.acc_o[1]);
+    tile(v_column<2, 0>(cur, v01, v23), st.acc_o[2]);
+    tile(v_column<3, 0>(cur, v01, v23), st.acc_o[3]);
+    tile(v_column<0, 1>(cur, v01, v23), st.acc_o[4]);
+    tile(v_column<1, 1>(cur, v01, v23), st.acc_o[5]);
+    tile(v_column<2, 1>(cur, v01, v23), st.acc_o[6]);
+    tile(v_column<3, 1>(cur, v01, v23), st.acc_o[7]);
   } else if constexpr (FMT == kFmtFp8) {
     // ---- O^T += V~^T P^T: word i holds element d = 8 col + i of the four
     // tokens of quad kg (the A operand's k order)
@@ -590,15 +633,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   // and a reordered start makes every iteration wait for all but the newest
   // page.
   PageRegs<FMT> r[kD8];
+  // Every stage issues, also past the end of the range (reloads of the last
+  // unit), and only the loop's latch exits: every path around the back edge
+  // then carries a whole iteration of page loads, which the compiler's waits
+  // rely on (an exit in the middle, however rare, gives it a short path).
 #pragma unroll
   for (int i = 0; i < kD8 - 1; ++i) {
     issue(r[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Every stage issues, also past the end of the range (reloads of the last
-  // unit), and only the loop's latch exits: every path around the back edge
-  // then carries a whole iteration of page loads, which the compiler's waits
-  // rely on (an exit in the middle, however rare, gives it a short path).
   for (int t = 0; t < N; t += kD8) {
 #pragma unroll
     for (int j = 0; j < kD8; ++j) {
@@ -631,6 +674,7 @@ constexpr int kMaxGroup = 16;   // query heads per KV head the decode accepts
 template <int PL, bool PER_SEG, typename I>
 __device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMath<I> rm, long long a,
                                               long long end, int g, int tid, float* out);
+
 
 template <int PL, bool PER_SEG>
 __global__ void __launch_bounds__(PER_SEG ? 64 * kMaxGroup : 32 * PL) merge_kernel(DecodeArgs p) {

@@ -925,3 +925,26 @@ def test_mse_config2_steps(orc):
     out = built.decode(q).cpu().numpy()
     check_decode(out[[3]], *built.oracle_decode(orc, q, [3]))
     assert np.all(np.isfinite(out))
+
+
+@pytest.mark.parametrize("kind", ["nvfp4", "mxfp4", "fp8", "bf16"])
+def test_decode_unowned_slots_hold_nan_patterns(orc, kind):
+    """Slots past a sequence's length keep whatever bytes the cache memory
+    held.  With every byte 0xFF (NaN as an E4M3 scale, an FP8 value or a BF16
+    half, the largest E8M0 scale), partial last pages, one-token sequences
+    and wave counts that cut segments between the two pages a 4-bit decode
+    takes together still give finite outputs within the bound."""
+    w = W.custom_decode(21, 5, 32, 8, [17, 1, 33, 250, 16], dtype="bf16")
+    if kind == "nvfp4":
+        built = BuiltDecode(w, orc, fill=0xFF)
+    elif kind == "mxfp4":
+        built = BuiltMx(w, orc, fill=0xFF)
+    else:
+        built = BuiltCmp(w, orc, 1 if kind == "fp8" else 2, fill=0xFF)
+    q = w.q(0)
+    ref, mag = built.oracle_decode(orc, q, range(5))
+    for S in (1, 3, 5, 64, 0):
+        say(f"{kind} 0xFF-filled cache, S={S}")
+        out = built.decode(q, num_splits=S).cpu().numpy()
+        assert np.isfinite(out).all()
+        check_decode(out, ref, mag)
