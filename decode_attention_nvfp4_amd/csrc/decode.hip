@@ -511,8 +511,10 @@ __device__ __forceinline__ RangeMath<I> range_math(const DecodeArgs& p, long lon
   return rm;
 }
 
+// Every product of the range arithmetic is at most U S(W).
 __device__ __forceinline__ bool range_fits_u32(const DecodeArgs& p, long long U) {
-  const long long T = (long long)max(p.weight_first, p.weight_rest) * p.num_splits;
+  const long long T = (long long)p.weight_first * p.first_waves +
+                      (long long)p.weight_rest * (p.num_splits - p.first_waves);
   return U * T < (1LL << 32);
 }
 
