@@ -948,3 +948,24 @@ def test_decode_unowned_slots_hold_nan_patterns(orc, kind):
         out = built.decode(q, num_splits=S).cpu().numpy()
         assert np.isfinite(out).all()
         check_decode(out, ref, mag)
+
+
+def test_weighted_ranges_in_64_bits(orc):
+    """Two waves per SIMD over more units than 32-bit weighted range
+    arithmetic holds (units x (8 R + 5 R) >= 2^32, R the SIMD count), so the
+    decode and the merge split the work with 64-bit arithmetic: a batch of
+    160 sequences of 3500 .. 5500 tokens, sampled against the oracle."""
+    rng = np.random.default_rng(45)
+    lens = rng.integers(3500, 5501, 160).tolist()
+    w = W.custom_decode(31, 160, 32, 8, lens, dtype="bf16")
+    sw = two_waves_per_simd()
+    units = sum((L + 15) // 16 for L in lens) * 8
+    assert units * 13 * (sw // 2) >= 2 ** 32
+    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 77, 159})
+    built = BuiltDecode(w, orc, keep=sample)
+    q = w.q(0)
+    say(f"{units} units at {sw} waves, checking {sample}")
+    out = built.decode(q, num_splits=sw).cpu().numpy()
+    ref, mag = built.oracle_decode(orc, q, sample)
+    say("   ", check_decode(out[sample], ref, mag))
+    assert np.all(np.isfinite(out))
