@@ -532,9 +532,29 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   const int Hkv = p.hkv, B = p.batch;
 
   // ---- total work U = Hkv * sum_b pages(b), and (wave 0) the page prefix
-  // sums for merge_kernel
+  // sums for merge_kernel.  The page counts of the first kHeld * 64
+  // sequences and their in-chunk prefix sums stay in registers: their
+  // lengths are loaded together, so both passes below cost one memory round
+  // trip for batches up to that size (the rest is read a chunk at a time).
+  // (Lanes past the batch read the last length, B >= 1 here, and drop it.)
+  constexpr int kHeld = 4;
+  int np_h[kHeld], incl_h[kHeld];
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i) np_h[i] = p.seq_lens[min(64 * i + lane, B - 1)];
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i) {
+    const int b = 64 * i + lane;
+    np_h[i] = b < B ? pages_of(min(max(np_h[i], 0), p.max_pages * kPage)) : 0;
+  }
   int total_pages = 0;
-  for (int c = 0; c < B; c += 64) {
+#pragma unroll
+  for (int i = 0; i < kHeld; ++i) {
+    const int b = 64 * i + lane;
+    incl_h[i] = wave_scan(np_h[i], lane);
+    if (wave == 0 && b < B) p.ws_prefix[b] = total_pages + incl_h[i] - np_h[i];
+    total_pages += __builtin_amdgcn_readlane(incl_h[i], 63);
+  }
+  for (int c = 64 * kHeld; c < B; c += 64) {
     const int b = c + lane;
     const int np = b < B ? pages_of(seq_len(p, b)) : 0;
     const int incl = wave_scan(np, lane);
@@ -562,19 +582,35 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   long long a_b0 = 0;
   {
     int carry = 0;
-    for (int c = 0; c < B; c += 64) {
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+      if (!found) {
+        const int b = 64 * i + lane;
+        const unsigned long long hit = __ballot(b < B && (long long)(carry + incl_h[i]) * Hkv > u0);
+        if (hit) {
+          const int idx = __ffsll((long long)hit) - 1;
+          b0 = 64 * i + idx;
+          a_b0 = (long long)(carry + __builtin_amdgcn_readlane(incl_h[i] - np_h[i], idx)) * Hkv;
+          found = true;
+        } else {
+          carry += __builtin_amdgcn_readlane(incl_h[i], 63);
+        }
+      }
+    }
+    for (int c = 64 * kHeld; !found && c < B; c += 64) {
       const int b = c + lane;
-      const int len = b < B ? seq_len(p, b) : 0;
-      const int np = pages_of(len);
+      const int np = b < B ? pages_of(seq_len(p, b)) : 0;
       const int incl = wave_scan(np, lane);
       const unsigned long long hit = __ballot(b < B && (long long)(carry + incl) * Hkv > u0);
       if (hit) {
         const int idx = __ffsll((long long)hit) - 1;
         b0 = c + idx;
         a_b0 = (long long)(carry + __builtin_amdgcn_readlane(incl - np, idx)) * Hkv;
-        break;
+        found = true;
+      } else {
+        carry += __builtin_amdgcn_readlane(incl, 63);
       }
-      carry += __builtin_amdgcn_readlane(incl, 63);
     }
   }
   SegPos start;

@@ -407,6 +407,9 @@ DECODE_CASES = [
     (6, 5, 16, 2, [0, 31, 64, 65, 700], "bf16"),
     (7, 2, 12, 4, [129, 2049], "bf16"),
     (8, 2, 16, 1, [400, 33], "bf16"),
+    # more sequences than the decode holds lengths for in registers (256):
+    # the rest are walked a chunk at a time; empty sequences on both sides
+    (9, 300, 8, 2, [int(x) for x in np.random.default_rng(9).integers(0, 41, 300)], "bf16"),
 ]
 
 
@@ -848,6 +851,9 @@ MX_CASES = [
     (4, 4, 32, 8, [1, 100, 257, 1000], "bf16"),
     (6, 5, 16, 2, [0, 31, 64, 65, 700], "bf16"),
     (8, 2, 16, 1, [400, 33], "bf16"),
+    # more sequences than the decode holds lengths for in registers (256):
+    # the rest are walked a chunk at a time; empty sequences on both sides
+    (9, 300, 8, 2, [int(x) for x in np.random.default_rng(9).integers(0, 41, 300)], "bf16"),
 ]
 
 
