@@ -218,8 +218,12 @@ size_t nvfp4_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
  *   max_seq_len: host bound on seq_lens, used by the split planner
  *   softmax_scale: > 0 and finite (1/sqrt(128) is the usual value)
  *   num_splits : 0 = automatic, else the number of work ranges: the
- *                (sequence, KV head, page) work is cut into that many equal
- *                contiguous ranges, one per wave
+ *                (sequence, KV head, page) work is cut into that many
+ *                contiguous ranges, one per wave; equal ranges, except that
+ *                exactly two waves per SIMD (2 x 4 x CUs) give the first
+ *                4 x CUs waves 8/5 of the others' share (the SIMD favours
+ *                its older wave).  The split changes rounding only within
+ *                the stated tolerance, and a given split is deterministic.
  *   workspace  : device, >= nvfp4_decode_workspace_bytes(...) bytes,
  *                256-byte aligned
  *   out        : device FP32 [batch][num_q_heads][128]
@@ -328,9 +332,11 @@ size_t nvfp4_cmp_decode_workspace_bytes(int32_t format, int32_t batch, int32_t n
                                         int32_t num_splits);
 
 /* Decode attention over a comparison-format cache: the operation, arguments
- * and work split of nvfp4_decode_attn, with the cached values of the format
- * (FP8: e4m3 * s_t, exact in FP16 and expanded to it; BF16: the bf16 values,
- * multiplied in bf16 with P carried as two bf16 parts). */
+ * and work split of nvfp4_decode_attn (with equal ranges at every wave
+ * count: these pages are bound by HBM, not by the SIMD), with the cached
+ * values of the format (FP8: e4m3 * s_t, exact in FP16 and expanded to it;
+ * BF16: the bf16 values, multiplied in bf16 with P carried as two bf16
+ * parts). */
 int32_t nvfp4_cmp_decode_attn(const nvfp4_cmp_cache* cache, const void* q, int32_t q_dtype,
                               int32_t batch, int32_t num_q_heads, const int32_t* page_table,
                               int32_t max_pages_per_seq, const int32_t* seq_lens,
