@@ -409,6 +409,49 @@ def bench_to_fp8(api, torch, stream, rows=16384, cols=16384, iters=10):
     return res
 
 
+def decode_only(api, torch, stream, steps, warmup):
+    """Configuration 4's decode call alone, on a cache of random bytes (block
+    scales drawn from the finite E4M3 codes 0..126) filled on the device: the
+    shape, page table and lengths of the workload without its data generation
+    and appends, so that profilers see the decode kernels after a few seconds.
+    Per-call HIP events on the launch stream; median, p10, p90 and mean."""
+    from decode_attention_nvfp4_amd import workloads as W
+    w = W.decode_workload(4)
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    cache = api.KVCache(w.num_pages, w.Hkv, 1.0 / 2688, 1.0 / 2688, fill=None)
+    for t in (cache.k_codes, cache.v_codes):
+        t.copy_(torch.randint(0, 256, t.shape, dtype=torch.uint8, device="cuda", generator=gen))
+    for t in (cache.k_scales, cache.v_scales):
+        t.copy_(torch.randint(0, 127, t.shape, dtype=torch.uint8, device="cuda", generator=gen))
+    pt = torch.from_numpy(w.page_table).cuda()
+    lens = torch.from_numpy(w.lens.astype(np.int32)).cuda()
+    L = int(w.lens.max())
+    q = torch.randn((w.B, w.Hq, 128), device="cuda", generator=gen).to(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, api.decode_workspace_bytes(w.B, w.Hq, w.Hkv, L)), dtype=torch.uint8, device="cuda")
+
+    def call():
+        api.decode(cache, q, pt, lens, L, workspace=ws, out=out, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s, e in ev:
+        s.record(stream)
+        call()
+        e.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([s.elapsed_time(e) for s, e in ev]) * 1e3
+    nbytes = int(w.lens.sum()) * w.Hkv * BYTES_PER_TOKEN_HEAD
+    return {"workload": "decode config 4 shape (batch 128, 32/8 heads, U[1024,8192], permuted pages), "
+                        "random cache bytes", "calls": steps, "cache_mb": round(nbytes / 1e6, 1),
+            "us_mean": round(float(t.mean()), 2), "us_median": round(float(np.median(t)), 2),
+            "us_p10": round(float(np.percentile(t, 10)), 2), "us_p90": round(float(np.percentile(t, 90)), 2),
+            "tbs_median": round(nbytes / float(np.median(t)) / 1e6, 3),
+            "splits": api.decode_num_splits(w.B, w.Hkv, L)}
+
+
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_paged_b128_traffic.json")
 DECODE_SOURCES = [os.path.join(ROOT, "decode_attention_nvfp4_amd", "csrc", f)
                   for f in ("decode.hip", "common.h", "internal.h", "api.cpp")]
@@ -509,6 +552,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (both operand modes) and print its record; "
                          "a profiling entry, not the benchmark line")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only configuration 4's decode call on a random-byte cache and print its "
+                         "record; a profiling entry, not the benchmark line")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the decode traffic record from two rocprofv3 --pmc outputs "
                          "(FETCH_SIZE, then WRITE_SIZE) of a run with --copy-mib, then exit")
@@ -531,6 +577,10 @@ def main():
     threads = min(16, os.cpu_count() or 1)
     if args.prefill_only:
         print(json.dumps({"prefill_cfg5": bench_prefill(api, torch, stream, iters=max(1, args.steps))}),
+              flush=True)
+        return
+    if args.decode_only:
+        print(json.dumps({"decode_cfg4": decode_only(api, torch, stream, max(1, args.steps), args.warmup)}),
               flush=True)
         return
 
