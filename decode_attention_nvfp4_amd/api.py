@@ -80,6 +80,8 @@ _SIGS = {
     "nvfp4_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "nvfp4_decode_attn": (_I32, [_CP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _F, _I32,
                                  _VP, _SZ, _VP, _VP]),
+    "nvfp4_decode_attn_noalloc": (_I32, [_CP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _F, _I32,
+                                         _VP, _VP]),
     "nvfp4_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "nvfp4_prefill_attn": (_I32, [_CP, _VP, _I32, _I32, _I32, _VP, _I32, _I32, _I32, _F, _VP, _SZ,
                                   _VP, _VP]),
@@ -303,6 +305,30 @@ def decode(cache: KVCache, q, page_table, seq_lens, max_seq_len: int, softmax_sc
         ctypes.byref(cs), _ptr(q), _dtype_code(q), B, Hq, _ptr(page_table), page_table.shape[-1],
         _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(num_splits), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _ptr(out), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 40 << 20   # NVFP4_DECODE_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(cache: KVCache, q, page_table, seq_lens, max_seq_len: int, softmax_scale=None,
+                   num_splits: int = 0, out=None, stream=None):
+    """decode() through nvfp4_decode_attn_noalloc: no workspace, the
+    library's fixed per-device scratch holds the partial results."""
+    _dev(q, "q")
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    B, Hq = q.shape[0], q.shape[1]
+    if q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [B][Hq][128]")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    cs = cache.struct()
+    _check("nvfp4_decode_attn_noalloc", lib().nvfp4_decode_attn_noalloc(
+        ctypes.byref(cs), _ptr(q), _dtype_code(q), B, Hq, _ptr(page_table), page_table.shape[-1],
+        _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(num_splits), _ptr(out), _stream(stream)))
     return out
 
 

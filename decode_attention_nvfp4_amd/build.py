@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnvfp4kv.so")
-SOURCES = ["api.cpp", "codec.hip", "convert.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "codec.hip", "convert.hip", "decode.hip", "prefill.hip", "scratch.hip"]
 ARCH = os.environ.get("NVFP4KV_ARCH", "gfx950")
 
 

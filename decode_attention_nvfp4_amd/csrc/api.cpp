@@ -306,7 +306,8 @@ static int32_t decode_call(int fmt, const uint8_t* kplane, const uint8_t* kscale
                            const int32_t* page_table, int32_t max_pages_per_seq,
                            const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
                            int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
-                           void* stream, int32_t k_exp = 0, int32_t v_exp = 0) {
+                           void* stream, int32_t k_exp = 0, int32_t v_exp = 0,
+                           bool fixed_scratch = false) {
   if (!dtype_ok(q_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
   if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0 || max_pages_per_seq <= 0)
     return fail(NVFP4_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d, max_seq_len %d, splits %d, "
@@ -327,6 +328,14 @@ static int32_t decode_call(int fmt, const uint8_t* kplane, const uint8_t* kscale
   const bool f32q = q_dtype == NVFP4_DTYPE_F32;
   const int32_t W = plan_waves(num_splits, f32q, batch, hkv, max_seq_len, fmt);
   const size_t need = decode_ws(batch, G, W);
+  if (fixed_scratch) {
+    if (need > kScratchBytes)
+      return fail(NVFP4_ERR_WORKSPACE, "decode needs %zu workspace bytes, more than the fixed scratch of %zu "
+                  "(use nvfp4_decode_attn with a workspace)", need, kScratchBytes);
+    hipError_t e = scratch_address(&workspace);
+    if (e != hipSuccess) return hip_status(e, "scratch address");
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < need)
     return fail(NVFP4_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -365,6 +374,20 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
                      cache->k_tensor_scale, cache->v_tensor_scale, cache->num_kv_heads, q, q_dtype,
                      batch, num_q_heads, page_table, max_pages_per_seq, seq_lens, max_seq_len,
                      softmax_scale, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+int32_t nvfp4_decode_attn_noalloc(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
+                                  int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                                  int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                  int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                  float* out, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  return decode_call(kFmtNvfp4, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales,
+                     cache->k_tensor_scale, cache->v_tensor_scale, cache->num_kv_heads, q, q_dtype,
+                     batch, num_q_heads, page_table, max_pages_per_seq, seq_lens, max_seq_len,
+                     softmax_scale, num_splits, nullptr, 0, out, stream, 0, 0, true);
 }
 
 // ------------------------------------------------ comparison formats

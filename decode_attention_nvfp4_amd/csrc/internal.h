@@ -128,4 +128,10 @@ hipError_t launch_decode(const DecodeArgs& a, bool f32_q, int fmt, hipStream_t s
 int decode_occupancy(bool f32_q, int fmt);   // resident decode waves per CU
 hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s);
 
+// Bytes of the fixed device scratch that nvfp4_decode_attn_noalloc uses as
+// its decode workspace (NVFP4_DECODE_NOALLOC_SCRATCH_BYTES in the header).
+constexpr size_t kScratchBytes = size_t(40) << 20;
+// Device address of the current device's scratch (taken once per device).
+hipError_t scratch_address(void** out);
+
 }  // namespace nvfp4

@@ -49,7 +49,8 @@
  * ---------------------------------------------------------- conventions
  *  - Every buffer is caller-owned device memory unless marked host.  The
  *    library allocates nothing, keeps no pointer after a call returns and
- *    holds no global state except a thread-local error string.
+ *    holds no global state except a thread-local error string and the fixed
+ *    per-device scratch of nvfp4_decode_attn_noalloc.
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  All
  *    work is enqueued on it; no call synchronizes.
  *  - Arguments are validated on the host before anything is enqueued; a
@@ -234,6 +235,30 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
                           int32_t max_pages_per_seq, const int32_t* seq_lens,
                           int32_t max_seq_len, float softmax_scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/* Bytes of the fixed device scratch of nvfp4_decode_attn_noalloc (40 MiB:
+ * every automatic split of up to 8 waves per CU on 256 CUs with up to 16
+ * query heads per KV head fits). */
+#define NVFP4_DECODE_NOALLOC_SCRATCH_BYTES 41943040
+
+/* Decode attention that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation).  The operation, arguments, work split, results and
+ * errors are those of nvfp4_decode_attn without the workspace: the partial
+ * results live in a fixed scratch of NVFP4_DECODE_NOALLOC_SCRATCH_BYTES bytes
+ * that the library keeps in each device's memory from the first call on that
+ * device until the process ends.  A call whose partial results need more
+ * than that (the size nvfp4_decode_workspace_bytes reports for the same
+ * arguments) fails with NVFP4_ERR_WORKSPACE before enqueueing anything.
+ * Every call on one device uses that device's one scratch, which keeps the
+ * last call's contents: calls that may overlap on one device (other streams,
+ * other threads) race, and the caller must serialize them.  The call makes
+ * no hipMalloc or hipFree and no allocating library call. */
+int32_t nvfp4_decode_attn_noalloc(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
+                                  int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                                  int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                  int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                  float* out, void* stream);
 
 /* Operand precision of the prefill path. */
 typedef enum nvfp4_prefill_mode {

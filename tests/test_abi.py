@@ -174,6 +174,26 @@ def test_decode_rejects_bad_arguments(api):
     assert _decode(api, c, B=0) == 0                    # empty batch: no-op
 
 
+def test_decode_noalloc_rejects_bad_arguments_and_oversized_requests(api):
+    """The no-allocation decode validates like nvfp4_decode_attn and refuses,
+    before touching the device, a split whose partials exceed its fixed
+    scratch (9000 waves x 2 pieces x 16 heads x 516 B > 40 MiB)."""
+    L = api.lib()
+    c = _fake_cache(api)
+
+    def call(cache, B=2, Hq=32, max_pages=64, max_len=1000, scale=0.088, splits=0):
+        return L.nvfp4_decode_attn_noalloc(ctypes.byref(cache), FAKE, 1, B, Hq, FAKE, max_pages, FAKE,
+                                           max_len, scale, splits, FAKE, None)
+
+    assert call(_fake_cache(api, head_dim=256)) == 2
+    assert call(c, Hq=12) == 1
+    assert call(c, scale=0.0) == 1
+    assert call(c, B=0) == 0
+    assert api.decode_workspace_bytes(2, 8 * 16, 8, 1000, 9000) > api.NOALLOC_SCRATCH_BYTES
+    assert call(c, Hq=8 * 16, splits=9000) == 3
+    assert b"fixed scratch" in L.nvfp4_last_error()
+
+
 def test_prefill_rejects_bad_arguments(api):
     L = api.lib()
     c = _fake_cache(api)
