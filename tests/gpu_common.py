@@ -3,7 +3,9 @@ compute the oracle's answer on the same seeded inputs, compare."""
 from __future__ import annotations
 
 import math
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -13,6 +15,16 @@ from decode_attention_nvfp4_amd import workloads as W
 from layout import Planes, sequence_tokens
 
 TOL = 2e-2   # pass iff |o - r| <= TOL * max(1, |r|) for every output element
+
+# Host threads for input generation and the oracle (its C calls release the
+# GIL); a GPU machine's share is 16 cores.
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def pmap(fn, items):
+    """list(map(fn, items)) on THREADS threads."""
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
+        return list(ex.map(fn, items))
 
 
 def say(*a):
@@ -41,6 +53,22 @@ def planes(cache) -> Planes:
     return Planes(cache.k_codes.cpu().numpy(), cache.k_scales.cpu().numpy(),
                   cache.v_codes.cpu().numpy(), cache.v_scales.cpu().numpy(),
                   cache.num_pages, cache.num_kv_heads, nblk=nblk)
+
+
+def check_planes(P: Planes, page_table, lens, codes, seqs):
+    """The device planes (layout reader P) hold, for every listed sequence,
+    exactly the oracle's codes and scales (codes[b] = (k codes, k scales,
+    v codes, v scales))."""
+    def one(b):
+        pages, slots = sequence_tokens(page_table[b], int(lens[b]))
+        got = P.gather(pages, slots)
+        for g, e, nm in zip(got, codes[b], ("k codes", "k scales", "v codes", "v scales")):
+            if not np.array_equal(g, e):
+                bad = np.argwhere(g != e)[:5]
+                return f"seq {b}: {nm} differ at {bad.tolist()}"
+        return None
+    errs = [e for e in pmap(one, list(seqs)) if e]
+    assert not errs, errs[:4]
 
 
 def compare(got: np.ndarray, ref: np.ndarray, tol: float = TOL):
@@ -96,13 +124,15 @@ class BuiltDecode:
         self._append = api.append_mse if mse else api.append
         self._quant = oracle.quantize_rows_mse if mse else oracle.quantize_rows
         self.keep = set(range(w.B)) if keep is None else set(keep)
-        data = [w.kv(b) for b in range(w.B)]
+        data = pmap(w.kv, range(w.B))
         # tensor scales: static calibration over the whole tensor (all
         # sequences plus the appended steps), with the oracle's definition
         self.s_tk, self.s_tv = calibrate(w, oracle, data)
         self.cache = api.KVCache(w.num_pages, w.Hkv, self.s_tk, self.s_tv, fill=fill)
         self.pt = i32(w.page_table)
-        self.codes = {}
+        kept = sorted(self.keep)
+        self.codes = dict(zip(kept, pmap(lambda b: (*self._quant(data[b][0], self.s_tk),
+                                                    *self._quant(data[b][1], self.s_tv)), kept)))
         for b0 in range(0, w.B, chunk):
             ks, vs, seqs, poss = [], [], [], []
             for b in range(b0, min(w.B, b0 + chunk)):
@@ -111,8 +141,6 @@ class BuiltDecode:
                 vs.append(v)
                 seqs.append(np.full(len(k), b, np.int32))
                 poss.append(np.arange(len(k), dtype=np.int32))
-                if b in self.keep:
-                    self.codes[b] = (*self._quant(k, self.s_tk), *self._quant(v, self.s_tv))
             k = np.concatenate(ks)
             if len(k) == 0:
                 continue
@@ -153,14 +181,7 @@ class BuiltDecode:
 
     def check_codes(self, seqs):
         """Bit-exact comparison of the device planes with the oracle's codes."""
-        P = planes(self.cache)
-        for b in seqs:
-            pages, slots = sequence_tokens(self.w.page_table[b], int(self.lens[b]))
-            got = P.gather(pages, slots)
-            for g, e, nm in zip(got, self.codes[b], ("k codes", "k scales", "v codes", "v scales")):
-                if not np.array_equal(g, e):
-                    bad = np.argwhere(g != e)[:5]
-                    raise AssertionError(f"seq {b}: {nm} differ at {bad.tolist()}")
+        check_planes(planes(self.cache), self.w.page_table, self.lens, self.codes, seqs)
 
 
 # ------------------------------------------------ comparison formats
@@ -173,7 +194,7 @@ class BuiltCmp:
     def __init__(self, w: W.DecodeWorkload, oracle, fmt: int, fill=0xA5, chunk=16):
         from layout import CmpPlanes  # noqa: F401  (used by check_codes)
         self.w, self.fmt = w, fmt
-        data = [w.kv(b) for b in range(w.B)]
+        data = pmap(w.kv, range(w.B))
         if fmt == api.CMP_FP8:
             ka = max([oracle.abs_max(k) for k, _ in data] + [oracle.abs_max(w.append_kv(s)[0]) for s in range(w.steps)])
             va = max([oracle.abs_max(v) for _, v in data] + [oracle.abs_max(w.append_kv(s)[1]) for s in range(w.steps)])
@@ -264,13 +285,15 @@ class BuiltMx:
     def __init__(self, w: W.DecodeWorkload, oracle, fill=0xA5, chunk=16, keep=None):
         self.w = w
         self.keep = set(range(w.B)) if keep is None else set(keep)
-        data = [w.kv(b) for b in range(w.B)]
+        data = pmap(w.kv, range(w.B))
         ka = max([oracle.abs_max(k) for k, _ in data] + [oracle.abs_max(w.append_kv(s)[0]) for s in range(w.steps)])
         va = max([oracle.abs_max(v) for _, v in data] + [oracle.abs_max(w.append_kv(s)[1]) for s in range(w.steps)])
         self.k_exp, self.v_exp = mx_exp_offset(ka), mx_exp_offset(va)
         self.cache = api.MxCache(w.num_pages, w.Hkv, self.k_exp, self.v_exp, fill=fill)
         self.pt = i32(w.page_table)
-        self.codes = {}
+        kept = sorted(self.keep)
+        self.codes = dict(zip(kept, pmap(lambda b: (*oracle.mx_quantize_rows(data[b][0]),
+                                                    *oracle.mx_quantize_rows(data[b][1])), kept)))
         for b0 in range(0, w.B, chunk):
             ks, vs, seqs, poss = [], [], [], []
             for b in range(b0, min(w.B, b0 + chunk)):
@@ -279,8 +302,6 @@ class BuiltMx:
                 vs.append(v)
                 seqs.append(np.full(len(k), b, np.int32))
                 poss.append(np.arange(len(k), dtype=np.int32))
-                if b in self.keep:
-                    self.codes[b] = (*oracle.mx_quantize_rows(k), *oracle.mx_quantize_rows(v))
             k = np.concatenate(ks)
             if len(k) == 0:
                 continue
@@ -303,14 +324,7 @@ class BuiltMx:
         self.lens += 1
 
     def check_codes(self, seqs):
-        P = planes(self.cache)
-        for b in seqs:
-            pages, slots = sequence_tokens(self.w.page_table[b], int(self.lens[b]))
-            got = P.gather(pages, slots)
-            for g, e, nm in zip(got, self.codes[b], ("k codes", "k scales", "v codes", "v scales")):
-                if not np.array_equal(g, e):
-                    bad = np.argwhere(g != e)[:5]
-                    raise AssertionError(f"seq {b}: {nm} differ at {bad.tolist()}")
+        check_planes(planes(self.cache), self.w.page_table, self.lens, self.codes, seqs)
 
     def decode(self, q: np.ndarray, num_splits=0, dtype=None):
         qd = to_dev(q, dtype or self.w.dtype)

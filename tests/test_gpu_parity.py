@@ -8,7 +8,8 @@ import torch
 
 from decode_attention_nvfp4_amd import api
 from decode_attention_nvfp4_amd import workloads as W
-from gpu_common import TOL, BuiltCmp, BuiltDecode, BuiltMx, check_decode, compare, i32, planes, say, to_dev
+from gpu_common import (THREADS, TOL, BuiltCmp, BuiltDecode, BuiltMx, check_decode, compare, i32, planes,
+                        pmap, say, to_dev)
 from layout import sequence_tokens
 
 pytestmark = pytest.mark.gpu
@@ -495,39 +496,47 @@ PREFILL_CASES = [
 ]
 
 # The prefill path multiplies FP8 operands, as on the pages (K~, V~ = E4M3 of
-# the dequantized cache, Q and P rounded to E4M3).  Each rounding is at most
-# 2^-4 relative.  The V and P roundings move an output by at most 2^-4 * A
-# each, with A = sum_t w_t |v_t| the attention-weighted magnitude of the
-# values; the Q and K roundings perturb the scores and hence the weights,
-# typically by a few percent.  Outputs are held to
-# 2e-2 * max(1, |r|) + 0.2 * A, and the relative L2 error to 8%.  (Over the
-# 33k-key context of the full workload the errors average out and the plain
-# 2e-2 mixed gate holds; see test_config5_prefill_sampled.)
-FP8_LOCAL = 0.2
-FP8_REL_L2 = 0.08
+# the dequantized cache, Q and P rounded to E4M3), each rounding at most 2^-4
+# relative.  Outputs are held to the error model of oracle/bounds.py (the
+# four roundings as independent uniform errors, first order in the scores,
+# weights and values): |o - r| <= 6 sigma + floor + 1e-5 max(1, |r|) per
+# element, and the root mean square of (o - r) / sigma at most 2 (a
+# systematic slip, e.g. an operand scale off by a few percent, moves many
+# elements by several sigma).  Over the 33k-key context of the full workload
+# the errors average out and the plain 2e-2 mixed gate holds as well; see
+# test_config5_prefill_rows.
+FP8_Z = 6.0
+FP8_RMS = 2.0
 
 
-def _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, causal):
+def _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, causal, rows=None):
+    """(reference, (sigma, floor)) for the chunk rows `rows` (default all)."""
+    rows = np.arange(T) if rows is None else np.asarray(rows)
     kc, ks = orc.quantize_rows(k, stk)
     vc, vs = orc.quantize_rows(v, stv)
-    ref = orc.prefill_rows(q, np.arange(T), Hkv, kc, ks, stk, vc, vs, stv, prefix, causal=causal)
-    mag = orc.prefill_rows(q, np.arange(T), Hkv, kc, ks, stk, vc & 7, vs, stv, prefix, causal=causal)
-    return ref, mag
+    ref = orc.prefill_rows(q[rows], rows, Hkv, kc, ks, stk, vc, vs, stv, prefix, causal=causal)
+    from oracle.bounds import fp8_attention_error_model
+    model = fp8_attention_error_model(q[rows], rows, Hkv, orc.dequant_rows(kc, ks, stk),
+                                      orc.dequant_rows(vc, vs, stv), prefix, causal)
+    return ref, model
 
 
-def _prefill_check(out, ref, mag, mode):
-    """FP8 operands: the local bound above and the L2 gate; exact 16-bit
-    operands (only P rounded, 2^-11 relative): the decode gate."""
+def _prefill_check(out, ref, model, mode):
+    """FP8 operands: the error model's per-element bound and its RMS gate;
+    exact 16-bit operands (only P rounded, 2^-11 relative): the 2e-2 gate."""
     err = np.abs(out.astype(np.float64) - ref)
-    if mode == api.PREFILL_FP8:
-        bound = TOL * np.maximum(1.0, np.abs(ref)) + FP8_LOCAL * mag
-    else:
-        bound = TOL * np.maximum(1.0, np.abs(ref))
     ok, st = compare(out, ref)
-    say("   ", st, "worst err/bound", float((err / bound).max()))
-    assert np.all(np.isfinite(out)) and np.all(err <= bound), float((err / bound).max())
     if mode == api.PREFILL_FP8:
-        assert st["rel_l2"] < FP8_REL_L2, st
+        sigma, floor = model
+        bound = FP8_Z * sigma + floor + 1e-5 * np.maximum(1.0, np.abs(ref))
+        rms = float(np.sqrt(np.mean((err / np.maximum(sigma, 1e-30)) ** 2)))
+        st.update(worst_err_over_bound=float((err / bound).max()), rms_err_over_sigma=rms)
+        say("   ", st)
+        assert np.all(np.isfinite(out)) and np.all(err <= bound), st
+        assert rms <= FP8_RMS, st
+    else:
+        say("   ", st)
+        assert ok, st
 
 
 @pytest.mark.parametrize("mode", [0, 1], ids=["fp8", "f16"])
@@ -550,8 +559,8 @@ def test_prefill_parity_small(orc, case, mode):
     q = pw.q()
     say(f"prefill {case} mode {mode}: attention")
     out = api.prefill(cache, to_dev(q, "bf16"), i32(perm), prefix, causal=causal, mode=mode).cpu().numpy()
-    ref, mag = _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, causal)
-    _prefill_check(out, ref, mag, mode)
+    ref, model = _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, causal)
+    _prefill_check(out, ref, model, mode)
 
 
 @pytest.mark.parametrize("mode", [0, 1], ids=["fp8", "f16"])
@@ -581,8 +590,37 @@ def test_prefill_score_range(orc, mode, pattern):
                i32(pt[None]))
     say(f"prefill score range {pattern} mode {mode}")
     out = api.prefill(cache, to_dev(q, "bf16"), i32(pt), prefix, causal=True, mode=mode).cpu().numpy()
-    ref, mag = _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, True)
-    _prefill_check(out, ref, mag, mode)
+    ref, model = _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, True)
+    _prefill_check(out, ref, model, mode)
+
+
+@pytest.mark.parametrize("mode", [0, 1], ids=["fp8", "f16"])
+def test_prefill_structured_weights_and_values(orc, mode):
+    """A tenth of the keys lie along a direction the queries share (they take
+    most of the weight) and carry values near +2, the rest values near -2:
+    the outputs depend visibly on how the weight splits and on the value
+    scale, so a slipped Q, K, P or V scale of a few percent would fail the
+    FP8 error model's gates (shown on the CPU in test_oracle_bounds.py)."""
+    prefix, T, Hq, Hkv = 400, 64, 8, 2
+    total = prefix + T
+    rng = np.random.default_rng(78)
+    u = rng.standard_normal(128)
+    u /= np.linalg.norm(u)
+    hot = rng.random(total) < 0.1
+    k = rng.standard_normal((total, Hkv, 128)) + np.where(hot, 3.0 * np.sqrt(128) * 0.25, 0.0)[:, None, None] * u
+    v = rng.standard_normal((total, Hkv, 128)) + np.where(hot, 2.0, -2.0)[:, None, None]
+    q = 0.5 * rng.standard_normal((T, Hq, 128)) + 2.0 * np.sqrt(128) * 0.25 * u
+    k, v, q = (W.round_bf16(x.astype(np.float32)) for x in (k, v, q))
+    stk, stv = orc.tensor_scale(k), orc.tensor_scale(v)
+    npages = -(-total // 16)
+    perm = np.random.default_rng(79).permutation(npages).astype(np.int32)
+    cache = api.KVCache(npages, Hkv, stk, stv, fill=0xA5)
+    api.append(cache, to_dev(k, "bf16"), to_dev(v, "bf16"), i32(np.zeros(total)), i32(np.arange(total)),
+               i32(perm[None]))
+    say(f"prefill structured mode {mode}")
+    out = api.prefill(cache, to_dev(q, "bf16"), i32(perm), prefix, causal=True, mode=mode).cpu().numpy()
+    ref, model = _prefill_ref(orc, q, T, Hkv, k, v, stk, stv, prefix, True)
+    _prefill_check(out, ref, model, mode)
 
 
 # ------------------------------------------------ full-size configurations
@@ -627,26 +665,33 @@ def test_config3_long_context(orc):
     check_decode(few, ref, mag)
 
 
-def test_config4_paged_sampled(orc):
-    """Batch 128 with ragged lengths and permuted pages, built in full on the
-    device; the oracle checks 6 sequences (shortest, longest, 4 seeded)."""
+def test_config4_paged_all(orc):
+    """Batch 128 with ragged lengths (U[1024, 8192]) and permuted pages, built
+    in full on the device: the codes and scales of every token of every
+    sequence match the oracle's, and so does the decode output of every
+    sequence and head."""
     w = W.decode_workload(4)
-    rng = np.random.default_rng(44)
-    sample = sorted(set([int(np.argmin(w.lens)), int(np.argmax(w.lens))] +
-                        rng.choice(w.B, 4, replace=False).tolist()))
-    built = BuiltDecode(w, orc, keep=sample)
-    built.check_codes(sample)
+    built = BuiltDecode(w, orc)
+    say("config 4: codes of all 128 sequences")
+    built.check_codes(range(w.B))
     q = w.q(0)
-    say(f"config 4 decode, checking {sample}")
+    say("config 4 decode, all sequences")
     out = built.decode(q).cpu().numpy()
-    ref, mag = built.oracle_decode(orc, q, sample)
-    say("   ", check_decode(out[sample], ref, mag))
-    assert np.all(np.isfinite(out))
+    ref, mag = built.oracle_decode(orc, q, range(w.B))
+    say("   ", check_decode(out, ref, mag))
 
 
-def test_config5_prefill_sampled(orc):
-    """Prefix 32768 + causal chunk 2048, 64/8 heads; the chunk is bulk-appended
-    then attended; the oracle checks 12 query rows (first, last, seeded)."""
+# Configuration 5: the chunk's prefill in both operand modes is computed once
+# on the device; the oracle checks 256 seeded rows plus the last 64 (split
+# into four tests, 80 rows each, so each stays well inside a test's time
+# limit) and the codes of every token of the 34,816-token cache.
+CFG5_ROWS = np.unique(np.concatenate([np.random.default_rng(55).choice(2048 - 64, 256, replace=False),
+                                      np.arange(2048 - 64, 2048)]))
+CFG5_PARTS = 4
+
+
+@pytest.fixture(scope="module")
+def cfg5(orc):
     pw = W.PrefillWorkload()
     kp, vp = pw.prefix_kv()
     kc_, vc_ = pw.chunk_kv()
@@ -654,29 +699,56 @@ def test_config5_prefill_sampled(orc):
     v = np.concatenate([vp, vc_])
     stk, stv = orc.tensor_scale(k), orc.tensor_scale(v)
     pt = pw.page_table()
-    cache = api.KVCache(pw.num_pages, pw.Hkv, stk, stv, fill=0)
+    cache = api.KVCache(pw.num_pages, pw.Hkv, stk, stv, fill=0xA5)
     say("config 5: append prefix, then chunk")
     api.append(cache, to_dev(kp, "bf16"), to_dev(vp, "bf16"), i32(np.zeros(pw.prefix)),
                i32(np.arange(pw.prefix)), i32(pt))
     api.append(cache, to_dev(kc_, "bf16"), to_dev(vc_, "bf16"), i32(np.zeros(pw.T)),
                i32(pw.prefix + np.arange(pw.T)), i32(pt))
     q = pw.q()
-    say("config 5: prefill")
-    out = api.prefill(cache, to_dev(q, "bf16"), i32(pt[0]), pw.prefix, causal=True).cpu().numpy()
-    rows = np.unique(np.concatenate([[0, 1, pw.T - 1], np.random.default_rng(55).choice(pw.T, 9, replace=False)]))
-    kc, ks = orc.quantize_rows(k, stk)
-    vc, vs = orc.quantize_rows(v, stv)
-    # the device codes of the chunk are the oracle's (bit-exact)
-    P = planes(cache)
-    pages, slots = sequence_tokens(pt[0], pw.total)
-    sel = np.concatenate([np.arange(0, 64), np.arange(pw.prefix - 8, pw.total)])
-    got = P.gather(pages[sel], slots[sel])
-    for g, e in zip(got, (kc[sel], ks[sel], vc[sel], vs[sel])):
-        assert np.array_equal(g, e)
-    ref = orc.prefill_rows(q[rows], rows, pw.Hkv, kc, ks, stk, vc, vs, stv, pw.prefix, causal=True)
-    ok, st = compare(out[rows], ref)
-    say("   ", st)
-    assert ok, st
+    outs = {}
+    for mode in (api.PREFILL_FP8, api.PREFILL_F16):
+        say(f"config 5: prefill mode {mode}")
+        outs[mode] = api.prefill(cache, to_dev(q, "bf16"), i32(pt[0]), pw.prefix, causal=True,
+                                 mode=mode).cpu().numpy()
+    say("config 5: oracle codes of the whole cache")
+    bounds = np.linspace(0, pw.total, THREADS + 1).astype(int)
+    kq = pmap(lambda i: orc.quantize_rows(k[bounds[i]:bounds[i + 1]], stk), range(THREADS))
+    vq = pmap(lambda i: orc.quantize_rows(v[bounds[i]:bounds[i + 1]], stv), range(THREADS))
+    codes = (np.concatenate([c for c, _ in kq]), np.concatenate([x for _, x in kq]),
+             np.concatenate([c for c, _ in vq]), np.concatenate([x for _, x in vq]))
+    return dict(pw=pw, cache=cache, pt=pt, q=q, outs=outs, codes=codes, stk=stk, stv=stv)
+
+
+def test_config5_codes_of_every_token(cfg5):
+    P = planes(cfg5["cache"])
+    pw = cfg5["pw"]
+    pages, slots = sequence_tokens(cfg5["pt"][0], pw.total)
+    got = P.gather(pages, slots)
+    for g, e, nm in zip(got, cfg5["codes"], ("k codes", "k scales", "v codes", "v scales")):
+        assert np.array_equal(g, e), (nm, np.argwhere(g != e)[:5].tolist())
+
+
+@pytest.mark.parametrize("part", range(CFG5_PARTS))
+def test_config5_prefill_rows(orc, cfg5, part):
+    """Both operand modes on 80 of the 320 checked rows: the 2e-2 mixed gate,
+    and for FP8 operands also the error model's per-element bound."""
+    pw, q = cfg5["pw"], cfg5["q"]
+    rows = CFG5_ROWS[part::CFG5_PARTS]
+    kc, ks, vc, vs = cfg5["codes"]
+    stk, stv = cfg5["stk"], cfg5["stv"]
+    say(f"config 5 rows part {part}: oracle on {len(rows)} rows")
+    ref = orc.prefill_rows(q[rows], rows, pw.Hkv, kc, ks, stk, vc, vs, stv, pw.prefix, causal=True,
+                           threads=THREADS)
+    from oracle.bounds import fp8_attention_error_model
+    model = fp8_attention_error_model(q[rows], rows, pw.Hkv, orc.dequant_rows(kc, ks, stk),
+                                      orc.dequant_rows(vc, vs, stv), pw.prefix, True)
+    for mode in (api.PREFILL_FP8, api.PREFILL_F16):
+        out = cfg5["outs"][mode][rows]
+        ok, st = compare(out, ref)
+        say(f"   mode {mode}", st)
+        assert ok, st
+        _prefill_check(out, ref, model, mode)
 
 
 # ------------------------------------------------ comparison KV formats
@@ -899,38 +971,35 @@ def test_mx_decode_splits_f32_query_and_steps(orc):
     check_decode(built.decode(q2).cpu().numpy(), *built.oracle_decode(orc, q2, range(3)))
 
 
-def test_mx_config4_paged_sampled(orc):
-    """Configuration 4 in MXFP4, built in full on the device; the oracle
-    checks the codes and the attention of 6 sequences."""
+def test_mx_config4_paged_all(orc):
+    """Configuration 4 in MXFP4, built in full on the device: the codes and
+    E8M0 scales of every token and the decode output of every sequence
+    match the oracle's."""
     w = W.decode_workload(4)
-    rng = np.random.default_rng(45)
-    sample = sorted(set([int(np.argmin(w.lens)), int(np.argmax(w.lens))] +
-                        rng.choice(w.B, 4, replace=False).tolist()))
-    built = BuiltMx(w, orc, keep=sample, fill=0)
-    built.check_codes(sample)
+    built = BuiltMx(w, orc, fill=0)
+    say("mx config 4: codes of all 128 sequences")
+    built.check_codes(range(w.B))
     q = w.q(0)
-    say(f"mx config 4 decode, checking {sample}")
+    say("mx config 4 decode, all sequences")
     out = built.decode(q).cpu().numpy()
-    ref, mag = built.oracle_decode(orc, q, sample)
-    say("   ", check_decode(out[sample], ref, mag))
-    assert np.all(np.isfinite(out))
+    ref, mag = built.oracle_decode(orc, q, range(w.B))
+    say("   ", check_decode(out, ref, mag))
 
 
 def test_mse_config2_steps(orc):
     """Configuration 2 (outlier channels) written with the MSE-searched scale,
-    then 3 appended steps: the oracle checks sequence 3's codes and decode
-    (its search over the whole batch takes a minute on the CPU)."""
+    then 3 appended steps: the oracle checks every sequence's codes and
+    decode (its search runs one sequence per host thread)."""
     w = W.decode_workload(2)
-    built = BuiltDecode(w, orc, keep=[3], mse=True)
-    built.check_codes([3])
+    built = BuiltDecode(w, orc, mse=True)
+    built.check_codes(range(w.B))
     for step in range(3):
         built.append_step(step, orc)
-    built.check_codes([3])
+    built.check_codes(range(w.B))
     q = w.q(2)
     say("mse config 2 decode")
     out = built.decode(q).cpu().numpy()
-    check_decode(out[[3]], *built.oracle_decode(orc, q, [3]))
-    assert np.all(np.isfinite(out))
+    check_decode(out, *built.oracle_decode(orc, q, range(w.B)))
 
 
 @pytest.mark.parametrize("kind", ["nvfp4", "mxfp4", "fp8", "bf16"])
@@ -960,18 +1029,16 @@ def test_weighted_ranges_in_64_bits(orc):
     """Two waves per SIMD over more units than 32-bit weighted range
     arithmetic holds (units x (8 R + 5 R) >= 2^32, R the SIMD count), so the
     decode and the merge split the work with 64-bit arithmetic: a batch of
-    160 sequences of 3500 .. 5500 tokens, sampled against the oracle."""
+    160 sequences of 3500 .. 5500 tokens, every sequence against the oracle."""
     rng = np.random.default_rng(45)
     lens = rng.integers(3500, 5501, 160).tolist()
     w = W.custom_decode(31, 160, 32, 8, lens, dtype="bf16")
     sw = two_waves_per_simd()
     units = sum((L + 15) // 16 for L in lens) * 8
     assert units * 13 * (sw // 2) >= 2 ** 32
-    sample = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 77, 159})
-    built = BuiltDecode(w, orc, keep=sample)
+    built = BuiltDecode(w, orc)
     q = w.q(0)
-    say(f"{units} units at {sw} waves, checking {sample}")
+    say(f"{units} units at {sw} waves, checking all 160 sequences")
     out = built.decode(q, num_splits=sw).cpu().numpy()
-    ref, mag = built.oracle_decode(orc, q, sample)
-    say("   ", check_decode(out[sample], ref, mag))
-    assert np.all(np.isfinite(out))
+    ref, mag = built.oracle_decode(orc, q, range(160))
+    say("   ", check_decode(out, ref, mag))
