@@ -31,14 +31,18 @@ _i32p = ctypes.POINTER(ctypes.c_int)
 
 
 def lib():
-    """Load (building first if needed) the oracle shared library."""
+    """Load (building first if needed) the oracle shared library.  The
+    environment variable NVFP4_ORACLE_LIB names another build of the same
+    source to load instead (the sanitized one, see build.py)."""
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_build.LIB) or (
-                    os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC)):
-                _build.build()
-            L = ctypes.CDLL(_build.LIB)
+            path = os.environ.get("NVFP4_ORACLE_LIB")
+            if not path:
+                path = _build.LIB
+                if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+                    _build.build()
+            L = ctypes.CDLL(path)
             L.orc_e2m1_value.restype = ctypes.c_double
             L.orc_e2m1_value.argtypes = [ctypes.c_uint]
             L.orc_e4m3_value.restype = ctypes.c_double
