@@ -112,22 +112,132 @@ def time_region(torch, fn, iters, stream):
     return start.elapsed_time(end) / iters
 
 
+def host_threads():
+    """(threads used, CPUs this process may run on, CPUs the host shows).  A
+    GPU machine's share for one GPU is 16 cores, whatever the host shows."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    return max(1, min(16, affinity)), affinity, os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_decode_cfg(cfg, threads_all):
+    """Oracle decode of a whole decode workload (configurations 1-3): the
+    codes come from the oracle's own quantizer (timed on all threads, as the
+    append), the attention is timed on all threads and on one."""
+    import oracle
+    from decode_attention_nvfp4_amd import workloads as W
+    w = W.decode_workload(cfg)
+    data = [w.kv(b) for b in range(w.B)]
+    k_all = np.concatenate([d[0] for d in data])
+    v_all = np.concatenate([d[1] for d in data])
+    s_tk, s_tv = oracle.tensor_scale(k_all), oracle.tensor_scale(v_all)
+    def quant(x, st):
+        # rows split over the threads (the C calls release the GIL)
+        bounds = np.linspace(0, len(x), threads_all + 1).astype(int)
+        with ThreadPoolExecutor(max_workers=threads_all) as ex:
+            parts = list(ex.map(lambda i: oracle.quantize_rows(x[bounds[i]:bounds[i + 1]], st), range(threads_all)))
+        return np.concatenate([a for a, _ in parts]), np.concatenate([b for _, b in parts])
+
+    t0 = time.perf_counter()
+    codes = [(*quant(k, s_tk), *quant(v, s_tv)) for k, v in data]
+    t_quant = time.perf_counter() - t0
+    q = w.q(0)
+    nbytes = int(w.lens.sum()) * w.Hkv * BYTES_PER_TOKEN_HEAD
+    out = {"cache_mb": round(nbytes / 1e6, 2)}
+    for name, th in (("all", threads_all), ("one", 1)):
+        t0 = time.perf_counter()
+        oracle.decode_batch(q, codes, w.Hkv, s_tk, s_tv, threads=th)
+        dt = time.perf_counter() - t0
+        out[f"decode_s_{name}"] = round(dt, 4)
+        out[f"decode_gbs_{name}"] = round(nbytes / dt / 1e9, 4)
+    n_el = 2 * k_all.size
+    out["quantize_s_all"] = round(t_quant, 3)
+    out["quantize_gbs_all"] = round(n_el * (2 + 0.5625) / t_quant / 1e9, 4)
+    return out
+
+
 def cpu_baseline(w, data, s_tk, s_tv, q, threads):
     """The oracle, untuned, on the same decode step (all 128 sequences; the
-    codes come from the oracle's own quantizer, untimed)."""
+    codes come from the oracle's own quantizer, untimed), on the machine's host
+    threads and on one thread; then the other workloads (configurations 1-3
+    whole, the prefill on a sample of query rows)."""
     import oracle
     sample = list(range(w.B))
     with ThreadPoolExecutor(max_workers=threads) as ex:
         codes = list(ex.map(lambda b: (*oracle.quantize_rows(data[b][0], s_tk),
                                        *oracle.quantize_rows(data[b][1], s_tv)), sample))
+    nbytes = sum(int(w.lens[b]) for b in sample) * w.Hkv * BYTES_PER_TOKEN_HEAD
     t0 = time.perf_counter()
     oracle.decode_batch(q[sample], codes, w.Hkv, s_tk, s_tv, threads=threads)
     dt = time.perf_counter() - t0
-    nbytes = sum(int(w.lens[b]) for b in sample) * w.Hkv * BYTES_PER_TOKEN_HEAD
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"decode attention of the whole step (128 sequences, all heads, full length; "
-                      f"{nbytes / 1e6:.1f} MB of NVFP4 cache), without the append"}
+    one = list(range(0, w.B, 8))                      # every eighth sequence on one thread
+    nb1 = sum(int(w.lens[b]) for b in one) * w.Hkv * BYTES_PER_TOKEN_HEAD
+    t0 = time.perf_counter()
+    oracle.decode_batch(q[one], [codes[b] for b in one], w.Hkv, s_tk, s_tv, threads=1)
+    dt1 = time.perf_counter() - t0
+    used, affinity, visible = host_threads()
+    res = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "seconds": round(dt, 3),
+           "sample": f"decode attention of the whole step (128 sequences, all heads, full length; "
+                     f"{nbytes / 1e6:.1f} MB of NVFP4 cache), without the append",
+           "one_thread_gbs": round(nb1 / dt1 / 1e9, 4),
+           "one_thread_sample": f"16 of the 128 sequences ({nb1 / 1e6:.1f} MB), one thread",
+           "cpu_model": cpu_model(), "host_cpus_allowed": affinity, "host_cpus_visible": visible,
+           "threads_note": "a GPU box's share for one GPU is 16 cores"}
+    per = {}
+    for cfg in (1, 2, 3):
+        per[f"config{cfg}"] = _oracle_decode_cfg(cfg, threads)
+        log(f"oracle config {cfg}: {per[f'config{cfg}']}")
+    per["config5"] = _oracle_prefill_sample(threads)
+    log(f"oracle config 5: {per['config5']}")
+    res["per_config"] = per
+    return res
+
+
+def _oracle_prefill_sample(threads):
+    """Oracle prefill of configuration 5 on a sample of query rows (all 64
+    heads, every visible key): 16 rows on the box's threads, 2 on one."""
+    import oracle
+    from decode_attention_nvfp4_amd import workloads as W
+    pw = W.PrefillWorkload()
+    kp, vp = pw.prefix_kv()
+    kc, vc = pw.chunk_kv()
+    k = np.concatenate([kp, kc])
+    v = np.concatenate([vp, vc])
+    s_tk, s_tv = oracle.tensor_scale(k), oracle.tensor_scale(v)
+    bounds = np.linspace(0, len(k), threads + 1).astype(int)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        kq = list(ex.map(lambda i: oracle.quantize_rows(k[bounds[i]:bounds[i + 1]], s_tk), range(threads)))
+        vq = list(ex.map(lambda i: oracle.quantize_rows(v[bounds[i]:bounds[i + 1]], s_tv), range(threads)))
+    kcodes, kscales = np.concatenate([a for a, _ in kq]), np.concatenate([b for _, b in kq])
+    vcodes, vscales = np.concatenate([a for a, _ in vq]), np.concatenate([b for _, b in vq])
+    q = pw.q()
+    out = {}
+    for name, th, rows in (("all", threads, np.linspace(0, pw.T - 1, 16).astype(np.int32)),
+                           ("one", 1, np.array([0, pw.T - 1], np.int32))):
+        flops = 4.0 * 128 * pw.Hq * float(sum(pw.prefix + int(i) + 1 for i in rows))
+        t0 = time.perf_counter()
+        oracle.prefill_rows(q[rows], rows, pw.Hkv, kcodes, kscales, s_tk, vcodes, vscales, s_tv, pw.prefix,
+                            causal=True, threads=th)
+        dt = time.perf_counter() - t0
+        out[f"rows_{name}"] = len(rows)
+        out[f"seconds_{name}"] = round(dt, 3)
+        out[f"gflops_{name}"] = round(flops / dt / 1e9, 3)
+    out["sample"] = "query rows of the 2048-row chunk, all 64 heads, every visible key (of 2.268 TFLOP in all)"
+    return out
 
 
 def bench_prefill(api, torch, stream, iters=3, modes=None):
@@ -197,12 +307,49 @@ def stream_read_probe(api, torch, stream, gib=1, iters=10):
             "gbs": round((gib << 30) / (t * 1e-3) / 1e9, 1)}
 
 
+def llc_flush(api, torch):
+    """A read of 1 GiB (four times the 256 MB last-level cache) by the
+    library's streaming kernel, so that the next kernel finds the cache full
+    of other, clean lines.  (Filling a buffer instead would leave dirty lines
+    that the next kernel's reads must first write back.)"""
+    buf = torch.ones((1 << 30) // 2, dtype=torch.bfloat16, device="cuda")
+    return lambda: api.abs_max(buf)
+
+
+def time_calls(torch, stream, fn, iters, before=None):
+    """Per-call microseconds of fn() (HIP events on stream), with `before`
+    enqueued ahead of each call outside the timed region."""
+    ts = []
+    for _ in range(iters):
+        if before is not None:
+            before()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        fn()
+        e.record(stream)
+        e.synchronize()
+        ts.append(s.elapsed_time(e) * 1e3)
+    return np.array(ts)
+
+
+def gpu_busy(torch, us=60.0):
+    """A GPU-side spin of about `us` microseconds, enqueued ahead of a timed
+    call so that the call's kernels are queued before the GPU reaches them:
+    the events then time the GPU, not the host's launch latency."""
+    return lambda: torch.cuda._sleep(int(us * 2400))
+
+
+def pct(a):
+    return {"us_median": round(float(np.median(a)), 2), "us_p10": round(float(np.percentile(a, 10)), 2),
+            "us_p90": round(float(np.percentile(a, 90)), 2)}
+
+
 def bench_small_decode(api, torch, stream, cfg, iters=20):
     """Decode of configurations 2 (GQA batch 8, L 4096) and 3 (L 65536), in
     NVFP4 and in the FP8 and BF16 comparison formats built from the same
-    data.  The caches fit in the 256 MB last-level cache; to read from HBM
-    the cold timing rotates over 4 replicas and fills a 512 MB buffer
-    between launches."""
+    data.  The caches fit in the 256 MB last-level cache; the cold timing
+    rotates over 4 replicas and reads 1 GiB between launches (llc_flush)."""
     from decode_attention_nvfp4_amd import workloads as W
     w = W.decode_workload(cfg)
     data = gen_decode(w)
@@ -214,7 +361,7 @@ def bench_small_decode(api, torch, stream, cfg, iters=20):
     out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(1, 2 * api.decode_workspace_bytes(w.B, w.Hq, w.Hkv, L)), dtype=torch.uint8,
                      device="cuda")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = llc_flush(api, torch)
     res = {"workload": f"decode config {cfg}: batch {w.B}, {w.Hq}/{w.Hkv} heads, L {L}",
            "splits": api.decode_num_splits(w.B, w.Hkv, L)}
     reps = [format_caches(api, torch, w, data, (s_tk, s_tv), (amax_k, amax_v)) for _ in range(4)]
@@ -227,32 +374,110 @@ def bench_small_decode(api, torch, stream, cfg, iters=20):
             fn(c, q, pt, lens, L, workspace=ws, out=out)
 
         one(); torch.cuda.synchronize()
-        times = []
-        for _ in range(iters):
-            flush.fill_(1)
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record(stream)
-            one()
-            e.record(stream)
-            e.synchronize()
-            times.append(s.elapsed_time(e))
-        t_cold = float(np.median(times))
+        cold = time_calls(torch, stream, one, iters, before=flush)
+        t_cold = float(np.median(cold)) * 1e-3
         _, c0, pt0, fn0 = reps[0][f]
-        t_warm = time_region(torch, lambda: fn0(c0, q, pt0, lens, L, workspace=ws, out=out), iters, stream)
+        warm = time_calls(torch, stream, lambda: fn0(c0, q, pt0, lens, L, workspace=ws, out=out), iters,
+                          before=gpu_busy(torch))
+        t_warm = float(np.median(warm)) * 1e-3
         nbytes = int(w.lens.sum()) * w.Hkv * FORMAT_BYTES[name]
         entry = {"cache_mb": round(nbytes / 1e6, 2), "cold_us": round(t_cold * 1e3, 2),
                  "cold_gbs": round(nbytes / t_cold / 1e6, 1), "warm_us": round(t_warm * 1e3, 2),
-                 "warm_gbs": round(nbytes / t_warm / 1e6, 1)}
+                 "warm_gbs": round(nbytes / t_warm / 1e6, 1),
+                 "cold_us_p10": round(float(np.percentile(cold, 10)), 2),
+                 "cold_us_p90": round(float(np.percentile(cold, 90)), 2)}
         if name == "nvfp4":
             res.update(entry)
         else:
             res[name] = entry
     for name in ("fp8", "bf16"):
         res[f"nvfp4_speedup_vs_{name}_cold"] = round(res[name]["cold_us"] / res["cold_us"], 3)
+    if cfg == 2:
+        res["steps"] = _cfg2_steps(api, torch, stream, w, reps[0][0][1], reps[0][0][2], flush)
     del reps
     torch.cuda.empty_cache()
     return res
+
+
+def _cfg2_steps(api, torch, stream, w, cache, pt, flush):
+    """Configuration 2's decode loop: 16 steps, each appending one token per
+    sequence (nvfp4_kv_append, 8 rows x 8 KV heads) and then attending over
+    L + step + 1 tokens; per-step microseconds of the append and the decode
+    (HIP events), once warm (a GPU spin ahead of each step, the cache in the
+    LLC) and once with the LLC flushed before each step."""
+    out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device="cuda")
+    bidx = torch.arange(w.B, dtype=torch.int32, device="cuda")
+    new = [tuple(torch.from_numpy(x).to(torch.bfloat16).cuda() for x in w.append_kv(s)) for s in range(w.steps)]
+    qs = [torch.from_numpy(w.q(s)).to(torch.bfloat16).cuda() for s in range(w.steps)]
+    ws = torch.empty(max(1, api.decode_workspace_bytes(w.B, w.Hq, w.Hkv, int(w.lens.max()) + w.steps)),
+                     dtype=torch.uint8, device="cuda")
+    res = {}
+    poss = [torch.from_numpy((w.lens + s).astype(np.int32)).cuda() for s in range(w.steps)]
+    lenss = [torch.from_numpy((w.lens + s + 1).astype(np.int32)).cuda() for s in range(w.steps)]
+    busy = gpu_busy(torch)
+    for mode in ("warm", "cold"):
+        ta, td = [], []
+        for s in range(w.steps):
+            pos, lens = poss[s], lenss[s]
+            L = int(w.lens.max()) + s + 1
+            (flush if mode == "cold" else busy)()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+            api.append(cache, new[s][0], new[s][1], bidx, pos, pt)
+            ev[1].record(stream)
+            api.decode(cache, qs[s], pt, lens, L, workspace=ws, out=out)
+            ev[2].record(stream)
+            ev[2].synchronize()
+            ta.append(ev[0].elapsed_time(ev[1]) * 1e3)
+            td.append(ev[1].elapsed_time(ev[2]) * 1e3)
+        res[mode] = {"append_us_mean": round(float(np.mean(ta)), 2), "decode_us_mean": round(float(np.mean(td)), 2),
+                     "step_us_mean": round(float(np.mean(np.array(ta) + np.array(td))), 2),
+                     "append_us_per_step": [round(x, 2) for x in ta], "decode_us_per_step": [round(x, 2) for x in td]}
+    return res
+
+
+def bench_cfg1(api, torch, stream, iters=50):
+    """Configuration 1 (one sequence, one head, L 1024, FP32 K/V/Q): the
+    decode call's latency in microseconds, warm and after an LLC flush (its
+    147 KB are a latency, not a bandwidth, problem)."""
+    from decode_attention_nvfp4_amd import workloads as W
+    w = W.decode_workload(1)
+    k, v = w.kv(0)
+    s_tk = api.tensor_scale_from_amax(float(np.abs(k).max()))
+    s_tv = api.tensor_scale_from_amax(float(np.abs(v).max()))
+    cache = api.KVCache(w.num_pages, w.Hkv, s_tk, s_tv, fill=0)
+    pt = torch.from_numpy(w.page_table).cuda()
+    api.append(cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+               torch.zeros(len(k), dtype=torch.int32, device="cuda"),
+               torch.arange(len(k), dtype=torch.int32, device="cuda"), pt)
+    q = torch.from_numpy(w.q(0)).cuda()
+    lens = torch.from_numpy(w.lens).cuda()
+    out = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, api.decode_workspace_bytes(1, 1, 1, 1024)), dtype=torch.uint8, device="cuda")
+
+    def call():
+        api.decode(cache, q, pt, lens, 1024, workspace=ws, out=out)
+
+    call(); torch.cuda.synchronize()
+    warm = time_calls(torch, stream, call, iters, before=gpu_busy(torch))
+    cold = time_calls(torch, stream, call, iters, before=llc_flush(api, torch))
+    return {"workload": "decode config 1: 1 sequence, 1/1 heads, L 1024, FP32 K/V/Q",
+            "splits": api.decode_num_splits(1, 1, 1024), "warm": pct(warm), "cold": pct(cold)}
+
+
+def bench_gather_probe(api, torch, stream, cache, pt, lens, L, decode_us, iters=10):
+    """The page-gather ceiling: the decode kernel's own wave ranges, page walk
+    and page loads over the same cache, without the math or the merge
+    (nvfp4_decode_gather_probe)."""
+    sink = api.decode_gather_probe(cache, pt, lens, L)
+    torch.cuda.synchronize()
+    t = time_calls(torch, stream, lambda: api.decode_gather_probe(cache, pt, lens, L, sink=sink), iters,
+                   before=gpu_busy(torch, 200.0))
+    nbytes = int((lens.cpu().numpy()).sum()) * cache.num_kv_heads * BYTES_PER_TOKEN_HEAD
+    med = float(np.median(t))
+    return {"what": "nvfp4_decode_gather_probe on the headline cache", **pct(t),
+            "gbs": round(nbytes / med / 1e3, 1), "frac_hbm_peak": round(nbytes / med / 1e3 / HBM_PEAK_GBS, 4),
+            "decode_frac_of_ceiling": round(med / decode_us, 4)}
 
 
 def bench_formats_cfg4(api, torch, stream, w, data, nv_scales, amax, q_np, iters=10):
@@ -574,7 +799,7 @@ def main():
     api.lib()
     torch.cuda.init()
     stream = torch.cuda.current_stream()
-    threads = min(16, os.cpu_count() or 1)
+    threads = host_threads()[0]
     if args.prefill_only:
         print(json.dumps({"prefill_cfg5": bench_prefill(api, torch, stream, iters=max(1, args.steps))}),
               flush=True)
@@ -658,7 +883,8 @@ def main():
         e[3].record(stream)
     torch.cuda.synchronize()
     t_app = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    t_dec = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    dec_calls = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
+    t_dec = float(np.mean(dec_calls)) * 1e-3
     # decode calls back to back (no append between them) run slower on the
     # boxes measured; reported for reference
     t_dec_b2b = None if args.no_extra else time_region(torch, decode_step, args.steps, stream)
@@ -705,7 +931,7 @@ def main():
             "bytes_per_launch": cache_bytes, "avg_ms": round(t_dec, 5),
         },
         "extra": {
-            "decode_ms": round(t_dec, 5), "append_step_us": round(t_app * 1e3, 2),
+            "decode_ms": round(t_dec, 5), "decode_calls": pct(dec_calls), "append_step_us": round(t_app * 1e3, 2),
             "decode_back_to_back_ms": None if t_dec_b2b is None else round(t_dec_b2b, 5),
             "bulk_append": {"tokens": ntok, "ms": round(t_bulk, 3),
                             "gbs": round(bulk_bytes / (t_bulk * 1e-3) / 1e9, 1),
@@ -714,8 +940,19 @@ def main():
         },
     }
     if not args.no_extra:
+        try:
+            res["extra"]["gather_ceiling"] = bench_gather_probe(api, torch, stream, cache, pt, lens1, Lmax,
+                                                                float(np.median(dec_calls)))
+        except Exception as e:  # noqa: BLE001
+            res["extra"]["gather_ceiling"] = {"error": repr(e)}
+        log(f"gather ceiling: {res['extra']['gather_ceiling']}")
         del cache
         torch.cuda.empty_cache()
+        try:
+            res["extra"]["decode_cfg1"] = bench_cfg1(api, torch, stream)
+        except Exception as e:  # noqa: BLE001
+            res["extra"]["decode_cfg1"] = {"error": repr(e)}
+        log(f"decode config 1: {res['extra']['decode_cfg1']}")
         try:
             probe = stream_read_probe(api, torch, stream)
             probe["decode_frac"] = round(achieved / probe["gbs"], 4)

@@ -80,6 +80,7 @@ _SIGS = {
     "nvfp4_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "nvfp4_decode_attn": (_I32, [_CP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _F, _I32,
                                  _VP, _SZ, _VP, _VP]),
+    "nvfp4_decode_gather_probe": (_I32, [_CP, _I32, _VP, _I32, _VP, _I32, _I32, _VP, _SZ, _VP]),
     "nvfp4_decode_attn_noalloc": (_I32, [_CP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _F, _I32,
                                          _VP, _VP]),
     "nvfp4_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
@@ -306,6 +307,22 @@ def decode(cache: KVCache, q, page_table, seq_lens, max_seq_len: int, softmax_sc
         _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(num_splits), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _ptr(out), _stream(stream)))
     return out
+
+
+def decode_gather_probe(cache: KVCache, page_table, seq_lens, max_seq_len: int, num_splits: int = 0,
+                        sink=None, stream=None):
+    """The decode's page walk and loads without the math (a timing aid)."""
+    _dev(page_table, "page_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    B = seq_lens.numel()
+    if sink is None:
+        w = decode_num_splits(B, cache.num_kv_heads, max_seq_len, num_splits)
+        sink = torch.empty(max(1, w) * 64, dtype=torch.int32, device=page_table.device)
+    cs = cache.struct()
+    _check("nvfp4_decode_gather_probe", lib().nvfp4_decode_gather_probe(
+        ctypes.byref(cs), B, _ptr(page_table), page_table.shape[-1], _ptr(seq_lens), int(max_seq_len),
+        int(num_splits), _ptr(sink), sink.numel() * sink.element_size(), _stream(stream)))
+    return sink
 
 
 NOALLOC_SCRATCH_BYTES = 40 << 20   # NVFP4_DECODE_NOALLOC_SCRATCH_BYTES

@@ -232,6 +232,7 @@ static int32_t append_call(const nvfp4_kv_cache* cache, const void* k_new, const
   a.k_inv6 = inv6(a.k_six_st);
   a.v_inv6 = inv6(a.v_six_st);
   a.hkv = cache->num_kv_heads;
+  a.num_pages = cache->num_pages;
   return append_rows(a, mode, k_new, v_new, dtype, n_tok, tok_seq, tok_pos, page_table, max_pages_per_seq,
                      stream);
 }
@@ -270,6 +271,7 @@ int32_t nvfp4_kv_dequant(const nvfp4_kv_cache* cache, const int32_t* page_table_
   a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
   a.k_scale = cache->k_tensor_scale; a.v_scale = cache->v_tensor_scale;
   a.page_table_row = page_table_row; a.pos0 = pos0; a.n = n; a.hkv = cache->num_kv_heads;
+  a.num_pages = cache->num_pages;
   a.k_out = k_out; a.v_out = v_out;
   return hip_status(launch_dequant(a, out_dtype == NVFP4_DTYPE_F32, (hipStream_t)stream),
                     "dequant launch");
@@ -301,7 +303,7 @@ size_t nvfp4_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
 // Validation and launch shared by the NVFP4 and comparison-format decodes
 // (the cache itself has been checked by the caller).
 static int32_t decode_call(int fmt, const uint8_t* kplane, const uint8_t* kscales, const uint8_t* vplane,
-                           const uint8_t* vscales, float k_scale, float v_scale, int32_t hkv,
+                           const uint8_t* vscales, float k_scale, float v_scale, int32_t hkv, int32_t num_pages,
                            const void* q, int32_t q_dtype, int32_t batch, int32_t num_q_heads,
                            const int32_t* page_table, int32_t max_pages_per_seq,
                            const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
@@ -309,6 +311,8 @@ static int32_t decode_call(int fmt, const uint8_t* kplane, const uint8_t* kscale
                            void* stream, int32_t k_exp = 0, int32_t v_exp = 0,
                            bool fixed_scratch = false) {
   if (!dtype_ok(q_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
+  const int64_t num_slabs = (int64_t)num_pages * hkv;
+  if (num_slabs > (int64_t)UINT32_MAX) return fail(NVFP4_ERR_INVALID_ARG, "num_pages x num_kv_heads too large");
   if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0 || max_pages_per_seq <= 0)
     return fail(NVFP4_ERR_INVALID_ARG, "bad sizes (batch %d, heads %d, max_seq_len %d, splits %d, "
                 "max_pages %d)", batch, num_q_heads, max_seq_len, num_splits, max_pages_per_seq);
@@ -358,6 +362,7 @@ static int32_t decode_call(int fmt, const uint8_t* kplane, const uint8_t* kscale
   a.max_pages = max_pages_per_seq;
   a.batch = batch; a.hq = num_q_heads; a.hkv = hkv; a.group = G;
   a.num_splits = W;
+  a.num_slabs = (uint32_t)num_slabs;
   set_wave_weights(a, fmt, (int64_t)batch * hkv * max_pages_per_seq);
   return hip_status(launch_decode(a, f32q, fmt, (hipStream_t)stream), "decode launch");
 }
@@ -371,9 +376,41 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
   int32_t st = check_cache(cache);
   if (st) return st;
   return decode_call(kFmtNvfp4, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales,
-                     cache->k_tensor_scale, cache->v_tensor_scale, cache->num_kv_heads, q, q_dtype,
+                     cache->k_tensor_scale, cache->v_tensor_scale, cache->num_kv_heads, cache->num_pages, q, q_dtype,
                      batch, num_q_heads, page_table, max_pages_per_seq, seq_lens, max_seq_len,
                      softmax_scale, num_splits, workspace, workspace_bytes, out, stream);
+}
+
+int32_t nvfp4_decode_gather_probe(const nvfp4_kv_cache* cache, int32_t batch, const int32_t* page_table,
+                                  int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                  int32_t num_splits, void* sink, size_t sink_bytes, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  if (batch < 0 || max_seq_len < 0 || num_splits < 0 || max_pages_per_seq <= 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "bad sizes");
+  if ((int64_t)(max_seq_len + NVFP4_PAGE_SIZE - 1) / NVFP4_PAGE_SIZE > max_pages_per_seq)
+    return fail(NVFP4_ERR_INVALID_ARG, "max_seq_len %d needs more than max_pages_per_seq %d pages",
+                max_seq_len, max_pages_per_seq);
+  if (batch == 0) return NVFP4_OK;
+  if (!page_table || !seq_lens || !sink) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer");
+  const int64_t num_slabs = (int64_t)cache->num_pages * cache->num_kv_heads;
+  if (num_slabs * (NVFP4_PAGE_SIZE * NVFP4_HEAD_DIM / 2) > 0x7FFFFFFFll)
+    return fail(NVFP4_ERR_UNSUPPORTED, "the probe takes caches whose planes fit 31-bit offsets");
+  const int32_t W = plan_waves(num_splits, false, batch, cache->num_kv_heads, max_seq_len);
+  if (sink_bytes < (size_t)W * 64 * sizeof(uint32_t))
+    return fail(NVFP4_ERR_WORKSPACE, "the probe needs %zu sink bytes", (size_t)W * 64 * sizeof(uint32_t));
+  DecodeArgs a = {};
+  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
+  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
+  a.page_table = page_table; a.seq_lens = seq_lens;
+  a.out = static_cast<float*>(sink);
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch; a.hkv = cache->num_kv_heads; a.group = 1; a.hq = cache->num_kv_heads;
+  a.num_splits = W;
+  a.num_slabs = (uint32_t)num_slabs;
+  set_wave_weights(a, kFmtNvfp4, (int64_t)batch * a.hkv * max_pages_per_seq);
+  return hip_status(launch_gather_probe(a, (hipStream_t)stream), "probe launch");
 }
 
 int32_t nvfp4_decode_attn_noalloc(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
@@ -385,7 +422,7 @@ int32_t nvfp4_decode_attn_noalloc(const nvfp4_kv_cache* cache, const void* q, in
   int32_t st = check_cache(cache);
   if (st) return st;
   return decode_call(kFmtNvfp4, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales,
-                     cache->k_tensor_scale, cache->v_tensor_scale, cache->num_kv_heads, q, q_dtype,
+                     cache->k_tensor_scale, cache->v_tensor_scale, cache->num_kv_heads, cache->num_pages, q, q_dtype,
                      batch, num_q_heads, page_table, max_pages_per_seq, seq_lens, max_seq_len,
                      softmax_scale, num_splits, nullptr, 0, out, stream, 0, 0, true);
 }
@@ -448,6 +485,7 @@ int32_t nvfp4_cmp_append(const nvfp4_cmp_cache* cache, const void* k_new, const 
   a.tok_seq = tok_seq; a.tok_pos = tok_pos; a.page_table = page_table;
   a.max_pages = max_pages_per_seq; a.n_tok = n_tok; a.hkv = cache->num_kv_heads;
   a.fmt = cache->format == NVFP4_CMP_FP8 ? kFmtFp8 : kFmtBf16;
+  a.num_pages = cache->num_pages;
   return hip_status(launch_cmp_append(a, dtype == NVFP4_DTYPE_F32, (hipStream_t)stream), "append launch");
 }
 
@@ -474,7 +512,8 @@ int32_t nvfp4_cmp_decode_attn(const nvfp4_cmp_cache* cache, const void* q, int32
   const bool fp8 = cache->format == NVFP4_CMP_FP8;
   return decode_call(fp8 ? kFmtFp8 : kFmtBf16, static_cast<const uint8_t*>(cache->k), nullptr,
                      static_cast<const uint8_t*>(cache->v), nullptr, fp8 ? cache->k_scale : 1.0f,
-                     fp8 ? cache->v_scale : 1.0f, cache->num_kv_heads, q, q_dtype, batch, num_q_heads,
+                     fp8 ? cache->v_scale : 1.0f, cache->num_kv_heads, cache->num_pages, q, q_dtype, batch,
+                     num_q_heads,
                      page_table, max_pages_per_seq, seq_lens, max_seq_len, softmax_scale, num_splits,
                      workspace, workspace_bytes, out, stream);
 }
@@ -528,6 +567,7 @@ int32_t nvfp4_mx_append(const nvfp4_mx_cache* cache, const void* k_new, const vo
   a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
   a.k_scale = a.v_scale = 1.0f;
   a.hkv = cache->num_kv_heads;
+  a.num_pages = cache->num_pages;
   return append_rows(a, kAppendMx, k_new, v_new, dtype, n_tok, tok_seq, tok_pos, page_table,
                      max_pages_per_seq, stream);
 }
@@ -552,7 +592,7 @@ int32_t nvfp4_mx_decode_attn(const nvfp4_mx_cache* cache, const void* q, int32_t
   if (st) return st;
   return decode_call(kFmtMxfp4, cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales,
                      std::ldexp(1.0f, cache->k_exp_offset), std::ldexp(1.0f, cache->v_exp_offset),
-                     cache->num_kv_heads, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
+                     cache->num_kv_heads, cache->num_pages, q, q_dtype, batch, num_q_heads, page_table, max_pages_per_seq,
                      seq_lens, max_seq_len, softmax_scale, num_splits, workspace, workspace_bytes, out,
                      stream, cache->k_exp_offset, cache->v_exp_offset);
 }
@@ -615,6 +655,7 @@ int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q
   a.T = num_tokens; a.hq = num_q_heads; a.hkv = hkv; a.group = num_q_heads / hkv;
   a.prefix = prefix_len; a.causal = causal ? 1 : 0; a.total = total;
   a.num_tiles = (total + kPrefillTile - 1) / kPrefillTile;
+  a.num_pages = cache->num_pages;
   return hip_status(launch_prefill(a, q_dtype == NVFP4_DTYPE_F32, (hipStream_t)stream),
                     "prefill launch");
 }

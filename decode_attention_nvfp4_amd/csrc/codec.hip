@@ -306,7 +306,7 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
   int slot = 0;
   uint32_t vw = 0, vsb = 0;
   if (valid) {
-    const int page = p.page_table[(size_t)seq * p.max_pages + pos / kPage];
+    const int page = clamp_page(p.page_table[(size_t)seq * p.max_pages + pos / kPage], p.num_pages);
     slot = pos % kPage;
     uint32_t ksb;
     float x[8];
@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(256) cmp_append_kernel(CmpAppendArgs a) {
   const Raw8 rk = load_raw8<F32IN>(a.k_new, (size_t)row, g);
   const Raw8 rv = load_raw8<F32IN>(a.v_new, (size_t)row, g);
   const int seq = a.tok_seq[tok], pos = a.tok_pos[tok];
-  const int page = a.page_table[(size_t)seq * a.max_pages + pos / kPage];
+  const int page = clamp_page(a.page_table[(size_t)seq * a.max_pages + pos / kPage], a.num_pages);
   const int t = pos % kPage;
   const size_t slab = (size_t)page * a.hkv + head;
   const size_t kelem = slab * kPage * kD + (size_t)t * kD + 8 * g;              // K element index
@@ -453,7 +453,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(DequantArgs p) {
   const int i = (int)(row / p.hkv);
   const int h = (int)(row - (size_t)i * p.hkv);
   const int pos = p.pos0 + i;
-  const int page = p.page_table_row[pos / kPage];
+  const int page = clamp_page(p.page_table_row[pos / kPage], p.num_pages);
   const int slot = pos % kPage;
   const size_t slab = (size_t)page * p.hkv + h;
   for (int kv = 0; kv < 2; ++kv) {

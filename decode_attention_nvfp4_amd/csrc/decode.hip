@@ -94,30 +94,62 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* base)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
 }
 
+// Bytes per (page, head) slab of each plane of a format: K codes (or the
+// comparison formats' K plane), K scales, V codes, V scales.
+template <int FMT> struct SlabBytes;
+template <> struct SlabBytes<kFmtNvfp4> { static constexpr uint32_t k = kSlab, ks = kScaleSlab, v = kSlab, vs = kScaleSlab; };
+template <> struct SlabBytes<kFmtMxfp4> { static constexpr uint32_t k = kSlab, ks = kMxScaleSlab, v = kSlab, vs = kMxScaleSlab; };
+template <> struct SlabBytes<kFmtFp8> { static constexpr uint32_t k = kPage * kD, ks = 0, v = kPage * kD, vs = 0; };
+template <> struct SlabBytes<kFmtBf16> { static constexpr uint32_t k = 2 * kPage * kD, ks = 0, v = 2 * kPage * kD, vs = 0; };
+
+// Buffer resources over whole planes: a page load then only moves the
+// scalar offset (slab x slab bytes), and a load past the plane's end returns
+// zeros.  Used when every plane fits 32-bit offsets (WIDE == false); larger
+// caches build a resource at each slab's base instead.
+struct PlaneRsrc {
+  __amdgpu_buffer_rsrc_t k, ks, v, vs;
+};
+
+template <int FMT>
+__device__ __forceinline__ PlaneRsrc plane_rsrc(const DecodeArgs& p) {
+  using SB = SlabBytes<FMT>;
+  auto mk = [&](const uint8_t* base, uint32_t slab_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
+                                             (int)(p.num_slabs * slab_bytes), 0x00020000);
+  };
+  PlaneRsrc r;
+  r.k = mk(p.k_codes, SB::k);
+  r.v = mk(p.v_codes, SB::v);
+  r.ks = SB::ks ? mk(p.k_scales, SB::ks) : r.k;
+  r.vs = SB::vs ? mk(p.v_scales, SB::vs) : r.v;
+  return r;
+}
+
 // Buffer loads: the slab base lives in scalar registers and the lane offsets
 // are fixed, so a page load needs no vector address temporaries.
-template <int FMT>
-__device__ __forceinline__ void load_page(const DecodeArgs& p, uint32_t slab, const LaneOffsets& o,
-                                          PageRegs<FMT>& r) {
-  if constexpr (FMT == kFmtNvfp4) {
-    r.kq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.k_codes + (size_t)slab * kSlab), o.k, 0, 0);
-    r.ksc = __builtin_amdgcn_raw_buffer_load_b16(page_rsrc(p.k_scales + (size_t)slab * kScaleSlab), o.ks, 0, 0);
-    r.vq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.v_codes + (size_t)slab * kSlab), o.v, 0, 0);
-    r.vsc = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(p.v_scales + (size_t)slab * kScaleSlab), o.vs, 0, 0);
-  } else if constexpr (FMT == kFmtMxfp4) {
-    r.kq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.k_codes + (size_t)slab * kSlab), o.k, 0, 0);
-    r.ksc = __builtin_amdgcn_raw_buffer_load_b8(page_rsrc(p.k_scales + (size_t)slab * kMxScaleSlab), o.ks, 0, 0);
-    r.vq = __builtin_amdgcn_raw_buffer_load_b128(page_rsrc(p.v_codes + (size_t)slab * kSlab), o.v, 0, 0);
-    r.vsc = __builtin_amdgcn_raw_buffer_load_b32(page_rsrc(p.v_scales + (size_t)slab * kMxScaleSlab), o.vs, 0, 0);
+template <int FMT, bool WIDE>
+__device__ __forceinline__ void load_page(const DecodeArgs& p, const PlaneRsrc& pr, uint32_t slab,
+                                          const LaneOffsets& o, PageRegs<FMT>& r) {
+  using SB = SlabBytes<FMT>;
+  // narrow planes: one resource per plane, the slab in the scalar offset
+  const auto rk = WIDE ? page_rsrc(p.k_codes + (size_t)slab * SB::k) : pr.k;
+  const auto rv = WIDE ? page_rsrc(p.v_codes + (size_t)slab * SB::v) : pr.v;
+  const int sk = WIDE ? 0 : (int)(slab * SB::k), sv = WIDE ? 0 : (int)(slab * SB::v);
+  if constexpr (FMT == kFmtNvfp4 || FMT == kFmtMxfp4) {
+    const auto rks = WIDE ? page_rsrc(p.k_scales + (size_t)slab * SB::ks) : pr.ks;
+    const auto rvs = WIDE ? page_rsrc(p.v_scales + (size_t)slab * SB::vs) : pr.vs;
+    const int sks = WIDE ? 0 : (int)(slab * SB::ks), svs = WIDE ? 0 : (int)(slab * SB::vs);
+    r.kq = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k, sk, 0);
+    if constexpr (FMT == kFmtNvfp4) r.ksc = __builtin_amdgcn_raw_buffer_load_b16(rks, o.ks, sks, 0);
+    else r.ksc = __builtin_amdgcn_raw_buffer_load_b8(rks, o.ks, sks, 0);
+    r.vq = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v, sv, 0);
+    r.vsc = __builtin_amdgcn_raw_buffer_load_b32(rvs, o.vs, svs, 0);
   } else {
     constexpr int N = 2 * kElemBytes<FMT>;             // 16-byte loads per lane and operand
-    constexpr size_t S = (size_t)kPage * kD * kElemBytes<FMT>;
-    const auto kr = page_rsrc(p.k_codes + (size_t)slab * S);
-    const auto vr = page_rsrc(p.v_codes + (size_t)slab * S);
 #pragma unroll
-    for (int i = 0; i < N; ++i) r.kq[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, o.k + 16 * i, 0, 0);
+    for (int i = 0; i < N; ++i) r.kq[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k + 16 * i, sk, 0);
 #pragma unroll
-    for (int i = 0; i < N; ++i) r.vq[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, o.v + 16 * i, 0, 0);
+    for (int i = 0; i < N; ++i) r.vq[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v + 16 * i, sv, 0);
   }
 }
 
@@ -523,7 +555,11 @@ __device__ __forceinline__ bool range_fits_u32(const DecodeArgs& p, long long U)
 // the registers of an NVFP4 one).
 template <int FMT> constexpr int kDepth = FMT == kFmtBf16 ? 4 : 8;
 
-template <bool F32Q, int FMT>
+// PROBE: the page-gather ceiling of this kernel's access pattern.  The same
+// wave ranges, page walk and page loads, but every page is consumed by an
+// exclusive or instead of the attention math; nothing is written but one
+// word per wave (p.out), and no merge follows.
+template <bool F32Q, int FMT, bool WIDE, bool PROBE = false>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) decode_kernel(DecodeArgs p) {
   constexpr int kD8 = kDepth<FMT>;
   const int lane = threadIdx.x;
@@ -551,17 +587,17 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   for (int i = 0; i < kHeld; ++i) {
     const int b = 64 * i + lane;
     incl_h[i] = wave_scan(np_h[i], lane);
-    if (wave == 0 && b < B) p.ws_prefix[b] = total_pages + incl_h[i] - np_h[i];
+    if (!PROBE && wave == 0 && b < B) p.ws_prefix[b] = total_pages + incl_h[i] - np_h[i];
     total_pages += __builtin_amdgcn_readlane(incl_h[i], 63);
   }
   for (int c = 64 * kHeld; c < B; c += 64) {
     const int b = c + lane;
     const int np = b < B ? pages_of(seq_len(p, b)) : 0;
     const int incl = wave_scan(np, lane);
-    if (wave == 0 && b < B) p.ws_prefix[b] = total_pages + incl - np;
+    if (!PROBE && wave == 0 && b < B) p.ws_prefix[b] = total_pages + incl - np;
     total_pages += __builtin_amdgcn_readlane(incl, 63);
   }
-  if (wave == 0 && lane == 0) p.ws_prefix[B] = total_pages;
+  if (!PROBE && wave == 0 && lane == 0) p.ws_prefix[B] = total_pages;
   const long long U = (long long)total_pages * Hkv;
   long long u0, u1;
   if (range_fits_u32(p, U)) {
@@ -626,16 +662,24 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   // ---- issue side: the wave's units form one stream of pages; `iw` is
   // the unit issued next and `ipage` its page id, read one issue ahead
   SegPos iw = start;
-  uint32_t ipage = page_id_uniform(p, iw);
+  const ConstI32* irow = (const ConstI32*)p.page_table + (size_t)iw.b * p.max_pages;
+  uint32_t ipage = (uint32_t)irow[iw.pg];
   int issued = 0;
   const LaneOffsets lo = lane_offsets<FMT>(col, kg);
-  // units past the end reload the last one (never consumed)
+  const PlaneRsrc pr = plane_rsrc<FMT>(p);
+  // units past the end reload the last one (never consumed).  A page id
+  // beyond the cache is clamped to its last slab, so a bad page table reads
+  // wrong data but never outside the planes.
   auto issue = [&](PageRegs<FMT>& r) {
-    load_page<FMT>(p, ipage * (uint32_t)Hkv + (uint32_t)iw.kvh, lo, r);
+    const uint32_t slab = min(ipage * (uint32_t)Hkv + (uint32_t)iw.kvh, p.num_slabs - 1u);
+    load_page<FMT, WIDE>(p, pr, slab, lo, r);
     if (issued + 1 < N) {
       ++issued;
-      if (++iw.pg == iw.np) next_segment(p, iw);
-      ipage = page_id_uniform(p, iw);
+      if (++iw.pg == iw.np) {
+        next_segment(p, iw);
+        irow = (const ConstI32*)p.page_table + (size_t)iw.b * p.max_pages;
+      }
+      ipage = (uint32_t)irow[iw.pg];
     }
   };
 
@@ -647,7 +691,13 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   halfx8 qh[4], ql[4];
   float qscale = 0.0f;
   WaveState st;
+  uint32_t probe_sink = 0;
   auto step = [&](const PageRegs<FMT>& r) {
+    if constexpr (PROBE) {
+      if constexpr (FMT == kFmtNvfp4)
+        probe_sink ^= r.kq.x ^ r.kq.y ^ r.kq.z ^ r.kq.w ^ r.vq.x ^ r.vq.y ^ r.vq.z ^ r.vq.w ^ r.ksc ^ r.vsc;
+      return;
+    }
     if (piece_left == 0) {                 // a new piece starts with this page
       if (started) next_segment(p, seg);
       started = true;
@@ -689,6 +739,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  if constexpr (PROBE) reinterpret_cast<uint32_t*>(p.out)[wave * 64 + lane] = probe_sink;
 }
 
 // A segment cut by wave ranges is combined from its pieces:
@@ -818,8 +869,8 @@ __device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMa
 template <int FMT>
 static int occupancy_of(bool f32_q) {
   int n = 0;
-  hipError_t e = f32_q ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<true, FMT>, 64, 0)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<false, FMT>, 64, 0);
+  hipError_t e = f32_q ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<true, FMT, false>, 64, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<false, FMT, false>, 64, 0);
   return e == hipSuccess ? n : 0;
 }
 
@@ -836,10 +887,31 @@ int decode_occupancy(bool f32_q, int fmt) {
   return n;
 }
 
+// Planes whose bytes exceed 32-bit offsets take the kernel that builds a
+// buffer resource at each slab's base.
+template <int FMT>
+static bool wide_planes(uint32_t num_slabs) {
+  using SB = SlabBytes<FMT>;
+  const uint64_t m = SB::k > SB::ks ? SB::k : SB::ks;
+  return (uint64_t)num_slabs * m > 0x7FFFFFFFull;
+}
+
 template <int FMT>
 static void launch_fmt(const DecodeArgs& a, bool f32_q, hipStream_t s) {
-  if (f32_q) decode_kernel<true, FMT><<<a.num_splits, 64, 0, s>>>(a);
-  else decode_kernel<false, FMT><<<a.num_splits, 64, 0, s>>>(a);
+  const bool wide = wide_planes<FMT>(a.num_slabs);
+  if (f32_q) {
+    if (wide) decode_kernel<true, FMT, true><<<a.num_splits, 64, 0, s>>>(a);
+    else decode_kernel<true, FMT, false><<<a.num_splits, 64, 0, s>>>(a);
+  } else {
+    if (wide) decode_kernel<false, FMT, true><<<a.num_splits, 64, 0, s>>>(a);
+    else decode_kernel<false, FMT, false><<<a.num_splits, 64, 0, s>>>(a);
+  }
+}
+
+hipError_t launch_gather_probe(const DecodeArgs& a, hipStream_t s) {
+  if (wide_planes<kFmtNvfp4>(a.num_slabs)) return hipErrorInvalidValue;
+  decode_kernel<false, kFmtNvfp4, false, true><<<a.num_splits, 64, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool f32_q, int fmt, hipStream_t s) {

@@ -36,6 +36,7 @@ struct AppendArgs {
   int32_t max_pages;
   int32_t n_tok;
   int32_t hkv;
+  int32_t num_pages;          // page ids beyond the cache are clamped to its last page
 };
 
 // Append to a comparison-format cache: k / v planes of E4M3 codes of
@@ -53,6 +54,7 @@ struct CmpAppendArgs {
   int32_t n_tok;
   int32_t hkv;
   int32_t fmt;
+  int32_t num_pages;
 };
 
 // NVFP4 -> FP8 conversion of a flat run of 16-element blocks.
@@ -73,6 +75,7 @@ struct DequantArgs {
   float k_scale, v_scale;
   const int32_t* page_table_row;
   int32_t pos0, n, hkv;
+  int32_t num_pages;
   void* k_out;
   void* v_out;
 };
@@ -94,6 +97,7 @@ struct DecodeArgs {
   int32_t max_pages;
   int32_t batch, hq, hkv, group;
   int32_t num_splits;         // W: number of waves (work ranges)
+  uint32_t num_slabs;         // num_pages * hkv: (page, head) slabs of each plane
   int32_t k_exp, v_exp;       // MXFP4: values are taken relative to 2^k_exp, 2^v_exp
   // work weights of the waves: the first first_waves weigh weight_first,
   // the rest weight_rest (equal weights: equal ranges)
@@ -117,7 +121,15 @@ struct PrefillArgs {
   int32_t total;              // prefix + T
   int32_t num_tiles;          // ceil(total / 64)
   int32_t mode;               // kPrefillFP8 or kPrefillF16
+  int32_t num_pages;
 };
+
+// A page id read from a page table, clamped into the cache (ids outside
+// [0, num_pages) are a caller error; clamping keeps every access inside the
+// planes).
+__host__ __device__ __forceinline__ int clamp_page(int page, int num_pages) {
+  return (unsigned)page < (unsigned)num_pages ? page : num_pages - 1;
+}
 
 hipError_t launch_append(const AppendArgs& a, bool f32_in, int mode, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, bool f32_out, hipStream_t s);
@@ -125,6 +137,7 @@ hipError_t launch_to_fp8(const ToFp8Args& a, hipStream_t s);
 hipError_t launch_absmax(const void* x, bool f32_in, int64_t n, float* out, hipStream_t s);
 hipError_t launch_cmp_append(const CmpAppendArgs& a, bool f32_in, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, bool f32_q, int fmt, hipStream_t s);
+hipError_t launch_gather_probe(const DecodeArgs& a, hipStream_t s);
 int decode_occupancy(bool f32_q, int fmt);   // resident decode waves per CU
 hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s);
 

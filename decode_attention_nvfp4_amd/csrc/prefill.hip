@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256) expand_kernel(PrefillArgs p) {
 #pragma unroll
     for (int i = 0; i < 8 * P::EB; ++i) o[i] = 0u;
     if (t < p.total) {
-      const int page = p.page_table_row[t / kPage], slot = t % kPage;
+      const int page = clamp_page(p.page_table_row[t / kPage], p.num_pages), slot = t % kPage;
       const size_t slab = (size_t)page * p.hkv + kvh;
       const u32x4 kq = *reinterpret_cast<const u32x4*>(p.k_codes + slab * kSlab + slot * 64 + q * 16);
       const uint32_t ksc = *reinterpret_cast<const uint16_t*>(p.k_scales + slab * kScaleSlab + slot * kNBlk + q * 2);
@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(256) expand_kernel(PrefillArgs p) {
     u32x4 W = {0u, 0u, 0u, 0u};
     uint32_t sc4 = 0;
     if (t0 < p.total) {
-      const int page = p.page_table_row[t0 / kPage], slot0 = t0 % kPage;
+      const int page = clamp_page(p.page_table_row[t0 / kPage], p.num_pages), slot0 = t0 % kPage;
       const size_t slab = (size_t)page * p.hkv + kvh;
       W = *reinterpret_cast<const u32x4*>(p.v_codes + slab * kSlab + (slot0 >> 2) * 256 + m * 16);
       sc4 = *reinterpret_cast<const uint32_t*>(p.v_scales + slab * kScaleSlab + (m >> 1) * kPage + slot0);

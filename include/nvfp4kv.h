@@ -55,8 +55,11 @@
  *    work is enqueued on it; no call synchronizes.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    failed call enqueues nothing.  Device-resident indices (page tables,
- *    sequence ids, positions, lengths) are trusted: they must lie within the
- *    bounds stated below.
+ *    sequence ids, positions, lengths) are not checked: they must lie within
+ *    the bounds stated below.  Every page id read from a page table must lie
+ *    in [0, num_pages); the kernels clamp an id outside that range to the
+ *    last page, so a bad page table gives wrong results but no access
+ *    outside the cache planes.
  *  - Every entry returns an nvfp4_status.  nvfp4_last_error() describes the
  *    most recent failure on the calling thread.
  */
@@ -185,7 +188,8 @@ int32_t nvfp4_to_fp8(const void* codes, const void* scales, int64_t n, float glo
 
 /* Dequantization (step A10, for checks and fallbacks): positions
  * pos0 .. pos0+n-1 of the sequence whose page-table row is page_table_row
- * (device int32, at least ceil((pos0+n)/16) entries) into k_out and v_out,
+ * (device int32, at least ceil((pos0+n)/16) page ids in [0, num_pages))
+ * into k_out and v_out,
  * each device [n][num_kv_heads][128] of out_dtype.  F32 output is
  * FP32(e2m1 * s_block * s_t); BF16 output is that value rounded to nearest
  * even.  Either output pointer may be NULL to skip it.  n == 0 is a no-op. */
@@ -213,7 +217,9 @@ size_t nvfp4_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t 
  * ([EXPL] §量子化・逆量子化フロー: dequantize, then attention; FP32
  * accumulation as in [TRTL] §Pourquoi FP8 est toujours le sol pour KV cache).
  *   q          : device [batch][num_q_heads][128], F32 or BF16
- *   page_table : device int32 [batch][max_pages_per_seq]
+ *   page_table : device int32 [batch][max_pages_per_seq]; the first
+ *                ceil(seq_lens[b]/16) entries of row b are page ids in
+ *                [0, num_pages)
  *   seq_lens   : device int32 [batch], each in [0, max_seq_len];
  *                ceil(seq_lens[b]/16) <= max_pages_per_seq
  *   max_seq_len: host bound on seq_lens, used by the split planner
@@ -235,6 +241,21 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
                           int32_t max_pages_per_seq, const int32_t* seq_lens,
                           int32_t max_seq_len, float softmax_scale, int32_t num_splits,
                           void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/* Page-gather ceiling of the NVFP4 decode (a measurement aid beside the hot
+ * path): runs the decode kernel's wave ranges, page walk and page loads over
+ * the cache exactly as nvfp4_decode_attn with bf16 queries and these
+ * arguments would, but consumes each page with an exclusive or instead of
+ * the attention math, and runs no merge.  Its time is what the decode's own
+ * access pattern costs without the math.
+ *   page_table, max_pages_per_seq, seq_lens, max_seq_len, num_splits: as for
+ *                nvfp4_decode_attn (same wave ranges)
+ *   sink       : device, >= 256 * (wave count) bytes; one word per lane is
+ *                written (meaningless values)
+ * Planes beyond 2^31 bytes are not supported (NVFP4_ERR_UNSUPPORTED). */
+int32_t nvfp4_decode_gather_probe(const nvfp4_kv_cache* cache, int32_t batch, const int32_t* page_table,
+                                  int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                  int32_t num_splits, void* sink, size_t sink_bytes, void* stream);
 
 /* Bytes of the fixed device scratch of nvfp4_decode_attn_noalloc (40 MiB:
  * every automatic split of up to 8 waves per CU on 256 CUs with up to 16
@@ -278,7 +299,8 @@ size_t nvfp4_prefill_workspace_bytes(int32_t num_tokens, int32_t num_q_heads,
  * an FP32 accumulator; mode NVFP4_PREFILL_F16 keeps the dequantized values
  * exact instead).  The chunk's own K/V must already be appended.
  *   q             : device [num_tokens][num_q_heads][128], F32 or BF16
- *   page_table_row: device int32, ceil((prefix_len+num_tokens)/16) pages
+ *   page_table_row: device int32, ceil((prefix_len+num_tokens)/16) page ids
+ *                   in [0, num_pages)
  *   causal != 0   : query i (absolute position prefix_len + i) attends to
  *                   tokens 0 .. prefix_len + i; causal == 0: to all
  *                   prefix_len + num_tokens tokens
