@@ -777,6 +777,9 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the chunked prefill (both operand modes) and print its record; "
                          "a profiling entry, not the benchmark line")
+    ap.add_argument("--small-decode", action="store_true",
+                    help="time only the decode of configurations 1-3 and print their record; a profiling "
+                         "entry, not the benchmark line")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only configuration 4's decode call on a random-byte cache and print its "
                          "record; a profiling entry, not the benchmark line")
@@ -803,6 +806,12 @@ def main():
     if args.prefill_only:
         print(json.dumps({"prefill_cfg5": bench_prefill(api, torch, stream, iters=max(1, args.steps))}),
               flush=True)
+        return
+    if args.small_decode:
+        rec = {"decode_cfg1": bench_cfg1(api, torch, stream)}
+        for cfg in (2, 3):
+            rec[f"decode_cfg{cfg}"] = bench_small_decode(api, torch, stream, cfg, iters=max(1, args.steps))
+        print(json.dumps(rec), flush=True)
         return
     if args.decode_only:
         print(json.dumps({"decode_cfg4": decode_only(api, torch, stream, max(1, args.steps), args.warmup)}),
