@@ -634,6 +634,46 @@ def bench_to_fp8(api, torch, stream, rows=16384, cols=16384, iters=10):
     return res
 
 
+def append_only(api, torch, stream, steps, warmup):
+    """Configuration 4's bulk append alone: every token of the workload
+    (594,571 x 8 KV heads, positions 0 .. L_b - 1 of each sequence) quantized
+    into an NVFP4 cache and into an MXFP4 cache, from random bf16 K/V drawn on
+    the device, so that profilers see the append kernels after a few seconds.
+    Per-call HIP events on the launch stream: median, p10 and p90."""
+    from decode_attention_nvfp4_amd import workloads as W
+    w = W.decode_workload(4)
+    ntok = int(w.lens.sum())
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    kd = torch.randn((ntok, w.Hkv, 128), device="cuda", generator=gen).to(torch.bfloat16)
+    vd = torch.randn((ntok, w.Hkv, 128), device="cuda", generator=gen).to(torch.bfloat16)
+    seq = torch.from_numpy(np.concatenate([np.full(int(L), b, np.int32) for b, L in enumerate(w.lens)])).cuda()
+    pos = torch.from_numpy(np.concatenate([np.arange(int(L), dtype=np.int32) for L in w.lens])).cuda()
+    pt = torch.from_numpy(w.page_table).cuda()
+    res = {"workload": f"bulk append of configuration 4's tokens ({ntok} x {w.Hkv} heads, bf16 in), random data",
+           "calls": steps}
+    for name in ("nvfp4", "mxfp4"):
+        if name == "mxfp4":
+            c, put, per_elem = api.MxCache(w.num_pages, w.Hkv, 0, 0, fill=0), api.mx_append, 0.53125
+        else:
+            c, put, per_elem = api.KVCache(w.num_pages, w.Hkv, 1.0 / 400, 1.0 / 400, fill=0), api.append, 0.5625
+        for _ in range(max(1, warmup)):
+            put(c, kd, vd, seq, pos, pt, stream=stream)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for s, e in ev:
+            s.record(stream)
+            put(c, kd, vd, seq, pos, pt, stream=stream)
+            e.record(stream)
+        torch.cuda.synchronize()
+        t = np.array([s.elapsed_time(e) for s, e in ev]) * 1e3
+        nbytes = ntok * w.Hkv * 128 * 2 * (2 + per_elem)
+        res[name] = {"bytes": int(nbytes), "us_median": round(float(np.median(t)), 1),
+                     "us_p10": round(float(np.percentile(t, 10)), 1), "us_p90": round(float(np.percentile(t, 90)), 1),
+                     "tbs_median": round(nbytes / float(np.median(t)) / 1e6, 3)}
+        del c
+    return res
+
+
 def decode_only(api, torch, stream, steps, warmup):
     """Configuration 4's decode call alone, on a cache of random bytes (block
     scales drawn from the finite E4M3 codes 0..126) filled on the device: the
@@ -780,6 +820,9 @@ def main():
     ap.add_argument("--small-decode", action="store_true",
                     help="time only the decode of configurations 1-3 and print their record; a profiling "
                          "entry, not the benchmark line")
+    ap.add_argument("--append-only", action="store_true",
+                    help="time only configuration 4's bulk append (NVFP4 and MXFP4) on random data and print "
+                         "its record; a profiling entry, not the benchmark line")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only configuration 4's decode call on a random-byte cache and print its "
                          "record; a profiling entry, not the benchmark line")
@@ -811,6 +854,17 @@ def main():
         rec = {"decode_cfg1": bench_cfg1(api, torch, stream)}
         for cfg in (2, 3):
             rec[f"decode_cfg{cfg}"] = bench_small_decode(api, torch, stream, cfg, iters=max(1, args.steps))
+        print(json.dumps(rec), flush=True)
+        return
+    if args.append_only:
+        rec = {"append_cfg4": append_only(api, torch, stream, max(1, args.steps), args.warmup)}
+        if args.copy_mib:          # the calibration copy for FETCH_SIZE / WRITE_SIZE passes
+            src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            rec["copy_mib"] = args.copy_mib
         print(json.dumps(rec), flush=True)
         return
     if args.decode_only:

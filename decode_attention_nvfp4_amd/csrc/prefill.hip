@@ -264,10 +264,21 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(kt + (tid + NT * i) * 16);
   };
+  // V~^T chunk of thread tid, as (row d, 16-byte column): FP8 rows hold 4
+  // chunks, and 8 consecutive lanes take one column of 8 consecutive rows, so
+  // that their LDS stores (row stride 80 bytes) fall in distinct banks; the
+  // wave still covers 1 KiB of the tile contiguously
+  auto vchunk = [&](int c) -> int2 {
+    if constexpr (EB == 1) return make_int2(8 * (c >> 5) + (c & 7), (c >> 3) & 3);
+    else return make_int2(c / (4 * EB), c % (4 * EB));
+  };
   auto gload_v = [&](int tile, u32x4 r[CPT]) {
     const uint8_t* vt = vx + (size_t)tile * kD * kTile * EB;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(vt + (tid + NT * i) * 16);
+    for (int i = 0; i < CPT; ++i) {
+      const int2 rc = vchunk(tid + NT * i);
+      r[i] = *reinterpret_cast<const u32x4*>(vt + (rc.x * 4 * EB + rc.y) * 16);
+    }
   };
   auto sstore_k = [&](int buf, const u32x4 r[CPT]) {
 #pragma unroll
@@ -279,8 +290,8 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   auto sstore_v = [&](int buf, const u32x4 r[CPT]) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + NT * i;
-      *reinterpret_cast<u32x4*>(&vs[buf][(c / (4 * EB)) * VROW + (c % (4 * EB)) * 16]) = r[i];
+      const int2 rc = vchunk(tid + NT * i);
+      *reinterpret_cast<u32x4*>(&vs[buf][rc.x * VROW + rc.y * 16]) = r[i];
     }
   };
 
@@ -295,23 +306,35 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
 
   // ---- S^T of the tile in ks[buf], two 32-key blocks
   auto qk = [&](int buf, floatx16 s[2]) {
+    if constexpr (MODE == kPrefillFP8) {
+      // all LDS reads first, then the products with the two key blocks'
+      // chains interleaved
+      intx8 a[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t* kr = &ks[buf][(kb * 32 + n) * KROW + h * 64 * EB];
-      floatx16 c;
-      if constexpr (MODE == kPrefillFP8) {
-        c = cbias;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          intx8 a, b;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) b[w] = (int)qw[8 * i + w];
-          *reinterpret_cast<u32x4*>(&a) = *reinterpret_cast<const u32x4*>(kr + 32 * i);
-          *(reinterpret_cast<u32x4*>(&a) + 1) = *reinterpret_cast<const u32x4*>(kr + 32 * i + 16);
-          c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, qscale);
+          const uint8_t* kr = &ks[buf][(kb * 32 + n) * KROW + h * 64 + 32 * i];
+          *reinterpret_cast<u32x4*>(&a[kb][i]) = *reinterpret_cast<const u32x4*>(kr);
+          *(reinterpret_cast<u32x4*>(&a[kb][i]) + 1) = *reinterpret_cast<const u32x4*>(kr + 16);
         }
-      } else {
-        c = floatx16{};
+      __builtin_amdgcn_sched_barrier(0);       // keep the reads ahead of the products
+      s[0] = cbias;
+      s[1] = cbias;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        intx8 b;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) b[w] = (int)qw[8 * i + w];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kb][i], b, s[kb], 0, 0, 0, 127, 0, qscale);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint8_t* kr = &ks[buf][(kb * 32 + n) * KROW + h * 64 * EB];
+        floatx16 c = floatx16{};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const u32x4 av = *reinterpret_cast<const u32x4*>(kr + 16 * i);
@@ -319,8 +342,8 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
           c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, av),
                                                       __builtin_bit_cast(halfx8, bv), c, 0, 0, 0);
         }
+        s[kb] = c;
       }
-      s[kb] = c;
     }
   };
 
@@ -331,6 +354,23 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
     for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.0f;
   // ---- O^T += V~^T P^T with the tile in vs[buf]
   auto pv = [&](int buf, const uint32_t pw[8 * EB]) {
+    if constexpr (MODE == kPrefillFP8) {
+      // all LDS reads first, then four independent products
+      intx8 a[4], b;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint8_t* vr = &vs[buf][(db * 32 + n) * VROW + h * 32];
+        *reinterpret_cast<u32x4*>(&a[db]) = *reinterpret_cast<const u32x4*>(vr);
+        *(reinterpret_cast<u32x4*>(&a[db]) + 1) = *reinterpret_cast<const u32x4*>(vr + 16);
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) b[w] = (int)pw[w];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        acc_o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[db], b, acc_o[db], 0, 0, 0, 127, 0, 127);
+      return;
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const uint8_t* vr = &vs[buf][(db * 32 + n) * VROW];
@@ -356,11 +396,13 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   // the reference max starts finite and far below any score, so that keys
   // masked to -inf give p = 0, never NaN
   float m_ref = -1.0e30f, l_run = 0.0f;
-  // FP8: the row sum of P accumulates on the matrix core.  A 16x16x128 MFMA
-  // with P^T as its B operand and a 0/1 A operand: B column c gathers the
-  // lanes c, c+16, c+32, c+48 (rows c and c+16, both key halves); A rows 0
-  // and 8 select the key blocks of row c, rows 4 and 12 those of row c+16,
-  // so result element 0 of every lane is the sum of its own row.
+  // FP8: the row sum of P accumulates on the matrix core, next to the
+  // product with V~ that consumes the same P (so the softmax interval issues
+  // no matrix instruction and never queues behind the other group's).  A
+  // 16x16x128 MFMA with P^T as its B operand and a 0/1 A operand: B column c
+  // gathers the lanes c, c+16, c+32, c+48 (rows c and c+16, both key halves);
+  // A rows 0 and 8 select the key blocks of row c, rows 4 and 12 those of
+  // row c+16, so result element 0 of every lane is the sum of its own row.
   floatx4 acc_l = {0.0f, 0.0f, 0.0f, 0.0f};
   intx8 ones;
   {
@@ -443,10 +485,6 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
         pw[w] = conv(fast_exp2(s[kb][r0]), fast_exp2(s[kb][r0 + 1]),
                      fast_exp2(s[kb][r0 + 2]), fast_exp2(s[kb][r0 + 3]));
       }
-      intx8 b;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) b[w] = (int)pw[w];
-      acc_l = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, b, acc_l, 0, 0, 0, 127, 0, 127);
     } else {
       // P^T = 2^(s * rowscale - m)
       const float cexp = -m_ref;
@@ -495,7 +533,15 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
     gload_k(tcl(t + 2 + G()), stk[B()]);
     gload_v(tcl(t + 1 + G()), stv[B()]);
     if (t < ntiles) qk(B(), sc);
-    if (t > 0 && t <= ntiles) pv(B() ^ 1, pw);   // the last product is O += V~(ntiles-1) P
+    if (t > 0 && t <= ntiles) {               // the last product is O += V~(ntiles-1) P
+      pv(B() ^ 1, pw);
+      if constexpr (MODE == kPrefillFP8) {
+        intx8 b;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) b[w] = (int)pw[w];
+        acc_l = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, b, acc_l, 0, 0, 0, 127, 0, 127);
+      }
+    }
   };
   auto soft = [&](auto G, auto B, int t) {   // B = (t - 1) & 1, the set to store
     if (t >= 0 && t < ntiles) {
