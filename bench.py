@@ -240,10 +240,10 @@ def _oracle_prefill_sample(threads):
     return out
 
 
-def bench_prefill(api, torch, stream, iters=3, modes=None):
+def bench_prefill(api, torch, stream, iters=3, modes=None, mx=True):
     """Chunked prefill at its full size: the chunk's bulk append and the
     attention, once per operand mode (FP8 as in the pages' flow, then exact
-    16-bit operands)."""
+    16-bit operands), then over an MXFP4 cache of the same data."""
     from decode_attention_nvfp4_amd import workloads as W
     modes = [api.PREFILL_FP8, api.PREFILL_F16] if modes is None else modes
     pw = W.PrefillWorkload()
@@ -291,6 +291,27 @@ def bench_prefill(api, torch, stream, iters=3, modes=None):
             res["f16_operands"] = {"attention_ms": round(t_att, 4), "tflops": round(tf, 2),
                                    "frac_f16_peak": round(tf / F16_PEAK_TFLOPS, 4)}
         del ws
+    if mx:
+        # the same chunk over an MXFP4 cache: FP4 K with its block scales in
+        # the score products, FP8 Q, P and V (V expanded, K read in place)
+        amax = lambda a: float(np.abs(a).max())  # noqa: E731
+        mcache = api.MxCache(pw.num_pages, pw.Hkv, api.mx_exp_offset_from_amax(max(amax(kp), amax(kc))),
+                             api.mx_exp_offset_from_amax(max(amax(vp), amax(vc))), fill=0)
+        api.mx_append(mcache, dev(kp), dev(vp), i32(np.zeros(pw.prefix)), i32(np.arange(pw.prefix)), pt)
+        api.mx_append(mcache, kcd, vcd, seq, pos, pt)
+        ws = torch.empty(api.mx_prefill_workspace_bytes(pw.T, pw.Hq, pw.Hkv, pw.prefix), dtype=torch.uint8,
+                         device="cuda")
+
+        def attend_mx():
+            api.mx_prefill(mcache, q, pt[0], pw.prefix, causal=True, workspace=ws, out=out)
+
+        attend_mx()
+        torch.cuda.synchronize()
+        t_att = time_region(torch, attend_mx, iters, stream)
+        tf = flops / t_att / 1e9
+        res["mxfp4_cache"] = {"attention_ms": round(t_att, 4), "tflops": round(tf, 2),
+                              "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+        del ws, mcache
     return res
 
 

@@ -96,6 +96,8 @@ _SIGS = {
     "nvfp4_mx_exp_offset_from_amax": (_I32, [_F]),
     "nvfp4_mx_append": (_I32, [_MP, _VP, _VP, _I32, _I32, _VP, _VP, _VP, _I32, _VP]),
     "nvfp4_mx_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "nvfp4_mx_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "nvfp4_mx_prefill_attn": (_I32, [_MP, _VP, _I32, _I32, _I32, _VP, _I32, _I32, _F, _VP, _SZ, _VP, _VP]),
     "nvfp4_mx_decode_attn": (_I32, [_MP, _VP, _I32, _I32, _I32, _VP, _I32, _VP, _I32, _F, _I32,
                                     _VP, _SZ, _VP, _VP]),
 }
@@ -528,5 +530,31 @@ def mx_decode(cache: MxCache, q, page_table, seq_lens, max_seq_len: int, softmax
     _check("nvfp4_mx_decode_attn", lib().nvfp4_mx_decode_attn(
         ctypes.byref(cs), _ptr(q), _dtype_code(q), B, Hq, _ptr(page_table), page_table.shape[-1],
         _ptr(seq_lens), int(max_seq_len), float(softmax_scale), int(num_splits), _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _ptr(out), _stream(stream)))
+    return out
+
+
+def mx_prefill_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, prefix_len) -> int:
+    return lib().nvfp4_mx_prefill_workspace_bytes(num_tokens, num_q_heads, num_kv_heads, prefix_len)
+
+
+def mx_prefill(cache: MxCache, q, page_table_row, prefix_len: int, causal: bool = True,
+               softmax_scale=None, workspace=None, out=None, stream=None):
+    """Chunked prefill over an MXFP4 cache: q [T][Hq][128] -> out [T][Hq][128]
+    FP32 (FP4 K operand with its block scales, FP8 Q, P and V)."""
+    _dev(q, "q")
+    _dev(page_table_row, "page_table_row", torch.int32)
+    T, Hq = q.shape[0], q.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((T, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = mx_prefill_workspace_bytes(T, Hq, cache.num_kv_heads, prefix_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    cs = cache.struct()
+    _check("nvfp4_mx_prefill_attn", lib().nvfp4_mx_prefill_attn(
+        ctypes.byref(cs), _ptr(q), _dtype_code(q), T, Hq, _ptr(page_table_row), int(prefix_len),
+        int(bool(causal)), float(softmax_scale), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _ptr(out), _stream(stream)))
     return out

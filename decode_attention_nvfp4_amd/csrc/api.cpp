@@ -600,7 +600,8 @@ int32_t nvfp4_mx_decode_attn(const nvfp4_mx_cache* cache, const void* q, int32_t
 static size_t prefill_ws(int32_t total, int32_t hkv, int32_t mode) {
   const size_t tiles = (size_t)(total + kPrefillTile - 1) / kPrefillTile;
   const size_t eb = mode == NVFP4_PREFILL_F16 ? 2 : 1;
-  return 2 * align256(tiles * kPrefillTile * NVFP4_HEAD_DIM * (size_t)hkv * eb);
+  const size_t one = align256(tiles * kPrefillTile * NVFP4_HEAD_DIM * (size_t)hkv * eb);
+  return mode == kPrefillMx ? one : 2 * one;    // MXFP4: V~ only (K is read from the cache)
 }
 
 size_t nvfp4_prefill_workspace_bytes(int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
@@ -611,21 +612,23 @@ size_t nvfp4_prefill_workspace_bytes(int32_t num_tokens, int32_t num_q_heads, in
   return prefill_ws(prefix_len + num_tokens, num_kv_heads, mode);
 }
 
-int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
-                           int32_t num_tokens, int32_t num_q_heads,
-                           const int32_t* page_table_row, int32_t prefix_len, int32_t causal,
-                           int32_t mode, float softmax_scale, void* workspace,
-                           size_t workspace_bytes, float* out, void* stream) {
-  g_err[0] = 0;
-  int32_t st = check_cache(cache);
-  if (st) return st;
+size_t nvfp4_mx_prefill_workspace_bytes(int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t prefix_len) {
+  (void)num_q_heads;
+  if (num_tokens < 0 || num_kv_heads <= 0 || prefix_len < 0) return 0;
+  return prefill_ws(prefix_len + num_tokens, num_kv_heads, kPrefillMx);
+}
+
+// Shared checks and launch of the prefill entry points; the planes and
+// scales of the cache are in a (its mode set), the rest is checked here.
+static int32_t prefill_call(PrefillArgs a, int32_t hkv, const void* q, int32_t q_dtype, int32_t num_tokens,
+                            int32_t num_q_heads, const int32_t* page_table_row, int32_t prefix_len,
+                            int32_t causal, float softmax_scale, void* workspace, size_t workspace_bytes,
+                            float* out, void* stream) {
   if (!dtype_ok(q_dtype)) return fail(NVFP4_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
-  if (mode != NVFP4_PREFILL_FP8 && mode != NVFP4_PREFILL_F16)
-    return fail(NVFP4_ERR_UNSUPPORTED, "prefill mode %d", mode);
   if (num_tokens < 0 || prefix_len < 0 || num_q_heads <= 0)
     return fail(NVFP4_ERR_INVALID_ARG, "bad sizes (tokens %d, prefix %d, heads %d)", num_tokens,
                 prefix_len, num_q_heads);
-  const int32_t hkv = cache->num_kv_heads;
   if (num_q_heads % hkv != 0)
     return fail(NVFP4_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 num_q_heads, hkv);
@@ -637,27 +640,69 @@ int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q
   if (!q || !page_table_row || !out) return fail(NVFP4_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(NVFP4_ERR_INVALID_ARG, "q / out must be 16-byte aligned");
   const int32_t total = prefix_len + num_tokens;
-  const size_t need = prefill_ws(total, hkv, mode);
+  const size_t need = prefill_ws(total, hkv, a.mode);
   if (!workspace || workspace_bytes < need)
     return fail(NVFP4_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return fail(NVFP4_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  PrefillArgs a;
-  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
-  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
   a.q = q; a.page_table_row = page_table_row; a.out = out;
-  a.kx = static_cast<uint8_t*>(workspace);
-  a.vx = static_cast<uint8_t*>(workspace) + need / 2;
-  a.mode = mode;
-  a.k_scale = cache->k_tensor_scale; a.v_scale = cache->v_tensor_scale;
+  if (a.mode == kPrefillMx) {
+    a.kx = nullptr;
+    a.vx = static_cast<uint8_t*>(workspace);
+  } else {
+    a.kx = static_cast<uint8_t*>(workspace);
+    a.vx = static_cast<uint8_t*>(workspace) + need / 2;
+  }
   a.softmax_scale = softmax_scale;
   a.T = num_tokens; a.hq = num_q_heads; a.hkv = hkv; a.group = num_q_heads / hkv;
   a.prefix = prefix_len; a.causal = causal ? 1 : 0; a.total = total;
   a.num_tiles = (total + kPrefillTile - 1) / kPrefillTile;
-  a.num_pages = cache->num_pages;
   return hip_status(launch_prefill(a, q_dtype == NVFP4_DTYPE_F32, (hipStream_t)stream),
                     "prefill launch");
+}
+
+int32_t nvfp4_prefill_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_dtype,
+                           int32_t num_tokens, int32_t num_q_heads,
+                           const int32_t* page_table_row, int32_t prefix_len, int32_t causal,
+                           int32_t mode, float softmax_scale, void* workspace,
+                           size_t workspace_bytes, float* out, void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_cache(cache);
+  if (st) return st;
+  if (mode != NVFP4_PREFILL_FP8 && mode != NVFP4_PREFILL_F16)
+    return fail(NVFP4_ERR_UNSUPPORTED, "prefill mode %d", mode);
+  PrefillArgs a = {};
+  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
+  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
+  a.mode = mode;
+  a.k_scale = cache->k_tensor_scale; a.v_scale = cache->v_tensor_scale;
+  a.num_pages = cache->num_pages;
+  return prefill_call(a, cache->num_kv_heads, q, q_dtype, num_tokens, num_q_heads, page_table_row, prefix_len,
+                      causal, softmax_scale, workspace, workspace_bytes, out, stream);
+}
+
+int32_t nvfp4_mx_prefill_attn(const nvfp4_mx_cache* cache, const void* q, int32_t q_dtype,
+                              int32_t num_tokens, int32_t num_q_heads,
+                              const int32_t* page_table_row, int32_t prefix_len, int32_t causal,
+                              float softmax_scale, void* workspace, size_t workspace_bytes, float* out,
+                              void* stream) {
+  g_err[0] = 0;
+  int32_t st = check_mx_cache(cache);
+  if (st) return st;
+  PrefillArgs a = {};
+  a.k_codes = cache->k_codes; a.k_scales = cache->k_scales;
+  a.v_codes = cache->v_codes; a.v_scales = cache->v_scales;
+  a.mode = kPrefillMx;
+  // K values are the codes times their E8M0 scales (no tensor scale); V~
+  // holds values relative to 2^v_ref, with the largest block of a tensor
+  // quantized under v_exp_offset (at v_exp_offset + 8) reaching 6 * 2^6
+  a.k_scale = 1.0f;
+  a.v_ref = std::min(cache->v_exp_offset + 2, 125);
+  a.v_scale = std::ldexp(1.0f, a.v_ref);
+  a.num_pages = cache->num_pages;
+  return prefill_call(a, cache->num_kv_heads, q, q_dtype, num_tokens, num_q_heads, page_table_row, prefix_len,
+                      causal, softmax_scale, workspace, workspace_bytes, out, stream);
 }
 
 }  // extern "C"

@@ -19,6 +19,7 @@ constexpr int kAppendMse = 1;      // NVFP4, MSE-searched E4M3 scale
 constexpr int kAppendMx = 2;       // MXFP4, E8M0 floor(log2 amax) - 2
 constexpr int kPrefillFP8 = 0;     // operand precisions of the prefill path
 constexpr int kPrefillF16 = 1;
+constexpr int kPrefillMx = 2;      // MXFP4 cache: FP4 K operand, FP8 V~, Q', P
 
 struct AppendArgs {
   uint8_t* k_codes;
@@ -120,8 +121,9 @@ struct PrefillArgs {
   int32_t prefix, causal;
   int32_t total;              // prefix + T
   int32_t num_tiles;          // ceil(total / 64)
-  int32_t mode;               // kPrefillFP8 or kPrefillF16
+  int32_t mode;               // kPrefillFP8, kPrefillF16 or kPrefillMx
   int32_t num_pages;
+  int32_t v_ref;              // MXFP4: V~ holds values relative to 2^v_ref (v_scale = 2^v_ref)
 };
 
 // A page id read from a page table, clamped into the cache (ids outside

@@ -13,6 +13,13 @@
 //   F16: K~, V~ = e2m1 * s_block exactly (at most 6 significant bits,
 //     magnitudes 2^-10 .. 2688); Q = F16(q * 2^shift_row) (exact for bf16
 //     input in range); P = F16(p); 32x32x16 f16 MFMAs at half the FP8 rate.
+//   MXFP4 (the MXFP4 cache, [EXPL] §MXFP4との比較): K enters the score
+//     MFMAs as the cache's own E2M1 codes with their E8M0 block scales as
+//     the MFMA's per-(row, 32-element) operand scales, read straight from
+//     the paged cache (the 32-element MX block is the MFMA's scale block);
+//     V is expanded to V~ = E4M3(e2m1 * 2^(e - r_V)), r_V = the cache's
+//     v_exp_offset + 2 (the largest block's values reach 384 at most), and
+//     the rest of the path is the FP8 path (Q', P, 32x32x64 MFMAs).
 // The scores and the output take the scale factors back in FP32.
 //
 // The expansion is a separate pass over the sequence's cache (expand_kernel)
@@ -46,11 +53,18 @@ template <> struct Prec<kPrefillFP8> {
   static constexpr int EB = 1;                       // bytes per operand element
   static constexpr float kExpand = 0.125f;           // K~, V~ carry 2^-3
 };
+template <> struct Prec<kPrefillMx> {
+  static constexpr int EB = 1;
+  static constexpr float kExpand = 1.0f;             // K exact; V~ relative to 2^r_V
+};
 template <> struct Prec<kPrefillF16> {
   static constexpr int EB = 2;
   static constexpr float kExpand = 1.0f;
   static constexpr int kQTop = 14;                   // |q| 2^shift in [2^14, 2^15)
 };
+
+// The FP8 and MXFP4 modes share the FP8 operand path (Q', P, V~ in E4M3).
+template <int MODE> constexpr bool kF8Ops = MODE != kPrefillF16;
 
 // Position of key kk (0..63) of a tile inside a V~^T row.
 //  FP8 (K = 64 keys per MFMA): S^T key block kb gives lane half h, element r
@@ -60,7 +74,7 @@ template <> struct Prec<kPrefillF16> {
 //    16u + 8(j/4) + 4h + j%4; the row holds [u][h][j].
 template <int MODE>
 __device__ __forceinline__ int vt_pos(int kk) {
-  if (MODE == kPrefillFP8) {
+  if (kF8Ops<MODE>) {
     const int kb = kk >> 5, rem = kk & 31;
     const int h = (rem >> 2) & 1;
     const int j = 16 * kb + (rem >> 3) * 4 + (rem & 3);
@@ -82,7 +96,7 @@ __device__ __forceinline__ float e2m1_value(uint32_t c) {
 // Operand encoding of a value: E4M3 (nearest even; |v| < 448 here) or F16.
 template <int MODE>
 __device__ __forceinline__ uint32_t encode(float v) {
-  if (MODE == kPrefillFP8) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+  if (kF8Ops<MODE>) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
   _Float16 h = (_Float16)v;
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
@@ -95,8 +109,9 @@ __global__ void __launch_bounds__(256) expand_kernel(PrefillArgs p) {
   const int tile = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
   __shared__ uint8_t vt[kD * kTile * P::EB];
 
-  // K: thread -> key tid/4, elements 32q..32q+31
-  {
+  // K: thread -> key tid/4, elements 32q..32q+31 (MXFP4: K is read from the
+  // cache by the attention kernel)
+  if constexpr (MODE != kPrefillMx) {
     const int kk = tid >> 2, q = tid & 3;
     const int t = tile * kTile + kk;
     uint32_t o[8 * P::EB];
@@ -133,19 +148,30 @@ __global__ void __launch_bounds__(256) expand_kernel(PrefillArgs p) {
       const int page = clamp_page(p.page_table_row[t0 / kPage], p.num_pages), slot0 = t0 % kPage;
       const size_t slab = (size_t)page * p.hkv + kvh;
       W = *reinterpret_cast<const u32x4*>(p.v_codes + slab * kSlab + (slot0 >> 2) * 256 + m * 16);
-      sc4 = *reinterpret_cast<const uint32_t*>(p.v_scales + slab * kScaleSlab + (m >> 1) * kPage + slot0);
+      // the block of elements 8m..8m+7 for the 4 tokens: NVFP4 block m/2 of
+      // 16, MXFP4 block m/4 of 32 (scale planes [block][token 16])
+      if constexpr (MODE == kPrefillMx)
+        sc4 = *reinterpret_cast<const uint32_t*>(p.v_scales + slab * kMxScaleSlab + (m >> 2) * kPage + slot0);
+      else
+        sc4 = *reinterpret_cast<const uint32_t*>(p.v_scales + slab * kScaleSlab + (m >> 1) * kPage + slot0);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {               // token 4tq + j
       const int kk = 4 * tq + j;
       const bool live = t0 + j < p.total;
-      const float sc = e4m3_to_float((sc4 >> (8 * j)) & 0xFFu) * P::kExpand;
+      const uint32_t sb = (sc4 >> (8 * j)) & 0xFFu;
+      // MXFP4: 2^(e - r_V) with e = sb - 127 (a power of two, possibly a
+      // subnormal FP32 or zero far below the tensor's blocks)
+      const float sc = MODE == kPrefillMx ? ldexpf(1.0f, (int)sb - 127 - p.v_ref) : e4m3_to_float(sb) * P::kExpand;
       const int pos = vt_pos<MODE>(kk);
       const int sh = 4 * (j & 1);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {             // element 8m + e
         const uint32_t c = (W[(j >> 1) * 2 + (e >> 2)] >> (8 * (e & 3) + sh)) & 15u;
-        const uint32_t v = live ? encode<MODE>(e2m1_value(c) * sc) : 0u;
+        // (MXFP4: a block above the range the cache's offset was set for
+        // saturates at 448)
+        const float x = MODE == kPrefillMx ? fminf(fmaxf(e2m1_value(c) * sc, -448.0f), 448.0f) : e2m1_value(c) * sc;
+        const uint32_t v = live ? encode<MODE>(x) : 0u;
         if (P::EB == 1) vt[(8 * m + e) * kTile + pos] = (uint8_t)v;
         else reinterpret_cast<uint16_t*>(vt)[(8 * m + e) * kTile + pos] = (uint16_t)v;
       }
@@ -162,7 +188,10 @@ template <int MODE, bool F32Q>
 __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   using P = Prec<MODE>;
   constexpr int EB = P::EB;
-  constexpr int KROW = kD * EB + 16;        // LDS bytes per K~ row (padded)
+  // LDS bytes per K row (padded): the expanded K~, or for MXFP4 the cache's
+  // 64 code bytes, followed (MXFP4) by the 4 block scales of each key
+  constexpr int KROW = MODE == kPrefillMx ? 64 + 16 : kD * EB + 16;
+  constexpr int KBYTES = MODE == kPrefillMx ? kTile * KROW + kTile * 4 : kTile * KROW;
   constexpr int VROW = kTile * EB + 16;     // LDS bytes per V~^T row (padded)
   constexpr int NT = 512;                   // threads: 8 waves of 32 rows
   constexpr int ROWS = NT / 2;              // (query, head) rows per workgroup
@@ -181,17 +210,46 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   const int head = kvh * p.group + (row_ok ? row % p.group : 0);
   const int lim = p.causal ? p.prefix + qi : p.total - 1;    // last key this row sees
 
-  __shared__ __attribute__((aligned(16))) uint8_t ks[2][kTile * KROW];
+  __shared__ __attribute__((aligned(16))) uint8_t ks[2][KBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vs[2][kD * VROW];
 
   // ---- Q^T operand: lane (row n, half h) holds q[64h + e], e = 0..63, in
-  // operand order (byte e for FP8, half e for F16)
+  // operand order (byte e for FP8, half e for F16).  MXFP4: the FP4 A
+  // operand of a 32x32x64 product gives lane (row, half h) the contraction
+  // indices 16h .. 16h+15 (its nibbles 0-15) and 32+16h .. 47+16h (nibbles
+  // 16-31) under one scale, and the lane loads one 32-element MX block of K
+  // (block 2h + i in product i); Q' then holds, for product i and lane half
+  // h, byte e = q[64 (e/16) + 32 i + 16 h + e%16]: the lane keeps the
+  // 16-element chunks q[32 c + 16 h ..] (c = 0..3) as qv[16 c ..]
   uint32_t qw[16 * EB];
   float rowscale = 1.0f;    // F16: scores * rowscale are in log2 units
   int qscale = 127;         // FP8: E8M0 scale of the Q' operand
   {
     float qv[64];
-    if (row_ok) {
+    if (row_ok && MODE == kPrefillMx) {
+      const size_t base = ((size_t)qi * p.hq + head) * kD + h * 16;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (F32Q) {
+          const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + base + 32 * c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float4 v = src[i];
+            float* d = qv + 16 * c + 4 * i;
+            d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+          }
+        } else {
+          const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + base + 32 * c);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            uint4 v = src[i];
+            float* d = qv + 16 * c + 8 * i;
+            d[0] = bf16_lo(v.x); d[1] = bf16_hi(v.x); d[2] = bf16_lo(v.y); d[3] = bf16_hi(v.y);
+            d[4] = bf16_lo(v.z); d[5] = bf16_hi(v.z); d[6] = bf16_lo(v.w); d[7] = bf16_hi(v.w);
+          }
+        }
+      }
+    } else if (row_ok) {
       const size_t off = ((size_t)qi * p.hq + head) * kD + h * 64;
       if (F32Q) {
         const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + off);
@@ -221,7 +279,7 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
     amax = max_across_halves(amax);
     // score scale: (q . K~) * c is the score in log2 units
     const float c = p.k_scale * p.softmax_scale * 1.4426950408889634f / P::kExpand;
-    if constexpr (MODE == kPrefillFP8) {
+    if constexpr (kF8Ops<MODE>) {
       // Q' = E4M3(q c 2^-(ea + ec - 6)) with the row maximum in [64, 256);
       // the MFMA's per-row E8M0 scale on Q' gives back 2^(ea + ec - 6), so
       // the scores come out of the MFMA in log2 units
@@ -231,7 +289,9 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
       qscale = 127 + max(-127, min(127, ea + ec - 6));
 #pragma unroll
       for (int w = 0; w < 16; ++w) {
-        const float* v = qv + 4 * w;
+        // product w / 8, bytes 4 (w % 8) .. +3 (MXFP4: chunk w/8 for the
+        // first 16 bytes, chunk 2 + w/8 for the last 16)
+        const float* v = qv + (MODE == kPrefillMx ? ((w & 4) ? 32 : 0) + 16 * (w >> 3) + 4 * (w & 3) : 4 * w);
         int lo = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -ea) * cn, ldexpf(v[1], -ea) * cn, 0, false);
         qw[w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -ea) * cn, ldexpf(v[3], -ea) * cn, lo, true);
       }
@@ -259,11 +319,6 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
 
   // tile loads: K~ chunk c = key c/(8 EB), 16 bytes at (c % (8 EB)) * 16;
   // V~^T chunk c = d c/(4 EB), 16 bytes at (c % (4 EB)) * 16
-  auto gload_k = [&](int tile, u32x4 r[CPT]) {
-    const uint8_t* kt = kx + (size_t)tile * kTile * kD * EB;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(kt + (tid + NT * i) * 16);
-  };
   // V~^T chunk of thread tid, as (row d, 16-byte column): FP8 rows hold 4
   // chunks, and 8 consecutive lanes take one column of 8 consecutive rows, so
   // that their LDS stores (row stride 80 bytes) fall in distinct banks; the
@@ -271,6 +326,31 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   auto vchunk = [&](int c) -> int2 {
     if constexpr (EB == 1) return make_int2(8 * (c >> 5) + (c & 7), (c >> 3) & 3);
     else return make_int2(c / (4 * EB), c % (4 * EB));
+  };
+  // K tile loads.  MXFP4: thread c < 256 takes 16 code bytes of key
+  // vchunk(c) (row = key, column = 16-byte group; the same bank-spread
+  // lane mapping), thread 256 + u the 16 scale bytes of keys 4u .. 4u+3
+  // ([token][block 4], one page), straight from the paged cache; keys past
+  // the context load zeros
+  auto gload_k = [&](int tile, u32x4 r[CPT]) {
+    if constexpr (MODE == kPrefillMx) {
+      r[0] = u32x4{0u, 0u, 0u, 0u};
+      const int c = tid;
+      if (c < 256 + kTile / 4) {
+        const int key = c < 256 ? vchunk(c).x : 4 * (c - 256);
+        const int t = tile * kTile + key;
+        if (t < p.total) {
+          const int page = clamp_page(p.page_table_row[t / kPage], p.num_pages), slot = t % kPage;
+          const size_t slab = (size_t)page * p.hkv + kvh;
+          r[0] = c < 256 ? *reinterpret_cast<const u32x4*>(p.k_codes + slab * kSlab + slot * 64 + vchunk(c).y * 16)
+                         : *reinterpret_cast<const u32x4*>(p.k_scales + slab * kMxScaleSlab + slot * kMxNBlk);
+        }
+      }
+    } else {
+      const uint8_t* kt = kx + (size_t)tile * kTile * kD * EB;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) r[i] = *reinterpret_cast<const u32x4*>(kt + (tid + NT * i) * 16);
+    }
   };
   auto gload_v = [&](int tile, u32x4 r[CPT]) {
     const uint8_t* vt = vx + (size_t)tile * kD * kTile * EB;
@@ -281,6 +361,16 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
     }
   };
   auto sstore_k = [&](int buf, const u32x4 r[CPT]) {
+    if constexpr (MODE == kPrefillMx) {
+      const int c = tid;
+      if (c < 256) {
+        const int2 rc = vchunk(c);
+        *reinterpret_cast<u32x4*>(&ks[buf][rc.x * KROW + rc.y * 16]) = r[0];
+      } else if (c < 256 + kTile / 4) {
+        *reinterpret_cast<u32x4*>(&ks[buf][kTile * KROW + (c - 256) * 16]) = r[0];
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + NT * i;
@@ -306,7 +396,34 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
 
   // ---- S^T of the tile in ks[buf], two 32-key blocks
   auto qk = [&](int buf, floatx16 s[2]) {
-    if constexpr (MODE == kPrefillFP8) {
+    if constexpr (MODE == kPrefillMx) {
+      // A = the keys' E2M1 codes (16 bytes = one 32-element MX block per
+      // lane) with that block's E8M0 scale; lane half h of product i takes
+      // block 2h + i, in the order of the Q' operand above
+      intx8 a[2][2];
+      int sa[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = kb * 32 + n, blk = 2 * h + i;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&ks[buf][row * KROW + 16 * blk]);
+          a[kb][i] = intx8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          sa[kb][i] = ks[buf][kTile * KROW + row * 4 + blk];
+        }
+      __builtin_amdgcn_sched_barrier(0);       // keep the reads ahead of the products
+      s[0] = cbias;
+      s[1] = cbias;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        intx8 b;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) b[w] = (int)qw[8 * i + w];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[kb][i], b, s[kb], 4, 0, 0, sa[kb][i], 0, qscale);
+      }
+    } else if constexpr (MODE == kPrefillFP8) {
       // all LDS reads first, then the products with the two key blocks'
       // chains interleaved
       intx8 a[2][2];
@@ -354,7 +471,7 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
     for (int r = 0; r < 16; ++r) acc_o[i][r] = 0.0f;
   // ---- O^T += V~^T P^T with the tile in vs[buf]
   auto pv = [&](int buf, const uint32_t pw[8 * EB]) {
-    if constexpr (MODE == kPrefillFP8) {
+    if constexpr (kF8Ops<MODE>) {
       // all LDS reads first, then four independent products
       intx8 a[4], b;
 #pragma unroll
@@ -374,7 +491,7 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const uint8_t* vr = &vs[buf][(db * 32 + n) * VROW];
-      if constexpr (MODE == kPrefillFP8) {
+      if constexpr (kF8Ops<MODE>) {
         intx8 a, b;
 #pragma unroll
         for (int w = 0; w < 8; ++w) b[w] = (int)pw[w];
@@ -439,20 +556,20 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   // over the reference, so p <= 2^kLazy (FP8: p * 2^4 <= 256 stays inside
   // E4M3's range; F16: p <= 256).  A rescale of any row costs the whole
   // wave a pass over its accumulators, so the threshold is kept large
-  constexpr float kLazy = MODE == kPrefillFP8 ? 4.0f : 8.0f;
+  constexpr float kLazy = kF8Ops<MODE> ? 4.0f : 8.0f;
   auto rescale = [&](float mx, floatx16 s[2]) {
     const bool grow = mx > m_ref + kLazy;
     if (__any(grow)) {
       // FP8 keeps the reference max an integer (the conversion scale is a
       // power of two); m >= mx keeps p <= 1 on this tile
-      const float m_new = grow ? (MODE == kPrefillFP8 ? ceilf(mx) : mx) : m_ref;
+      const float m_new = grow ? (kF8Ops<MODE> ? ceilf(mx) : mx) : m_ref;
       const float alpha = fast_exp2(m_ref - m_new);
       m_ref = m_new;
       l_run *= alpha;
       acc_l *= alpha;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc_o[i] *= alpha;
-      if constexpr (MODE == kPrefillFP8) {
+      if constexpr (kF8Ops<MODE>) {
         // move the bias of rows whose max left [-100, 100] (a row still at
         // the initial reference has seen no key yet and keeps it)
         const float shift = (fabsf(m_ref) > 100.0f && m_ref > -1.0e29f) ? m_ref : 0.0f;
@@ -472,7 +589,7 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   };
   // ---- P^T and the row sum
   auto probs = [&](const floatx16 s[2], uint32_t pw[8 * EB]) {
-    if constexpr (MODE == kPrefillFP8) {
+    if constexpr (kF8Ops<MODE>) {
       // P^T = E4M3(2^(s - m + 4)); the factor 2^4 cancels in O / l (weights
       // below 2^-13 of 2^m fall under E4M3's smallest value)
       auto conv = [&](float e0, float e1, float e2, float e3) {
@@ -535,7 +652,7 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
     if (t < ntiles) qk(B(), sc);
     if (t > 0 && t <= ntiles) {               // the last product is O += V~(ntiles-1) P
       pv(B() ^ 1, pw);
-      if constexpr (MODE == kPrefillFP8) {
+      if constexpr (kF8Ops<MODE>) {
         intx8 b;
 #pragma unroll
         for (int w = 0; w < 8; ++w) b[w] = (int)pw[w];
@@ -593,7 +710,7 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
   }
 
   // ---- epilogue: O / l * s_tV, removing the operand scale factors
-  const float l_tot = MODE == kPrefillFP8 ? acc_l[0] : sum_across_halves(l_run);
+  const float l_tot = kF8Ops<MODE> ? acc_l[0] : sum_across_halves(l_run);
   if (row_ok) {
     const float f = l_tot > 0.0f ? p.v_scale / P::kExpand / l_tot : 0.0f;
     float* o = p.out + ((size_t)qi * p.hq + head) * kD;
@@ -621,6 +738,7 @@ static void launch_mode(const PrefillArgs& a, bool f32_q, hipStream_t s) {
 
 hipError_t launch_prefill(const PrefillArgs& a, bool f32_q, hipStream_t s) {
   if (a.mode == kPrefillF16) launch_mode<kPrefillF16>(a, f32_q, s);
+  else if (a.mode == kPrefillMx) launch_mode<kPrefillMx>(a, f32_q, s);
   else launch_mode<kPrefillFP8>(a, f32_q, s);
   return hipGetLastError();
 }

@@ -457,6 +457,32 @@ int32_t nvfp4_mx_decode_attn(const nvfp4_mx_cache* cache, const void* q, int32_t
                              int32_t max_seq_len, float softmax_scale, int32_t num_splits,
                              void* workspace, size_t workspace_bytes, float* out, void* stream);
 
+/* Workspace bytes of nvfp4_mx_prefill_attn (0 for invalid arguments): the
+ * expanded V of the sequence, 1 byte per element (K is not expanded). */
+size_t nvfp4_mx_prefill_workspace_bytes(int32_t num_tokens, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t prefix_len);
+
+/* Chunked-prefill attention over an MXFP4 cache: the operation and arguments
+ * of nvfp4_prefill_attn on FP8-class matrix products ([EXPL]
+ * §量子化・逆量子化フロー; §MXFP4との比較 for the format).  K enters the score
+ * products as the cache's own E2M1 codes with their E8M0 block scales (the
+ * block-scaled FP4 x FP8 matrix instruction; exact K), Q as E4M3 with a
+ * power-of-two scale per (row, head), P as E4M3, and V as E4M3 of
+ * e2m1 * 2^(e - r) with r = min(v_exp_offset + 2, 125): exact for blocks
+ * within [v_exp_offset - 12, v_exp_offset + 8] (the range
+ * nvfp4_mx_exp_offset_from_amax sets for the tensor it was computed from),
+ * rounded below, saturated at 448 * 2^r above.  The chunk's own K/V must
+ * already be appended (nvfp4_mx_append).  Accumulation in FP32.
+ *   page_table_row, causal, q, out: as in nvfp4_prefill_attn
+ *   workspace: device, >= nvfp4_mx_prefill_workspace_bytes(...), 256-byte
+ *              aligned
+ * num_tokens == 0 is a no-op. */
+int32_t nvfp4_mx_prefill_attn(const nvfp4_mx_cache* cache, const void* q, int32_t q_dtype,
+                              int32_t num_tokens, int32_t num_q_heads,
+                              const int32_t* page_table_row, int32_t prefix_len, int32_t causal,
+                              float softmax_scale, void* workspace, size_t workspace_bytes,
+                              float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -140,6 +140,24 @@ def test_mx_sizes_offsets_and_bad_arguments(api):
                                   None, 0, FAKE, None) == 3
     assert api.mx_decode_workspace_bytes(2, 32, 8, 1000, 4) == api.decode_workspace_bytes(2, 32, 8, 1000, 4)
 
+    # MXFP4 prefill: the nvfp4_prefill_attn checks; the workspace holds V~
+    # only (half of the FP8 path's)
+    def mpf(T=16, Hq=64, prefix=100, ws=FAKE, ws_bytes=1 << 30, q_dtype=1, cache=c):
+        return L.nvfp4_mx_prefill_attn(ctypes.byref(cache), FAKE, q_dtype, T, Hq, FAKE, prefix, 1, 0.088, ws,
+                                       ws_bytes, FAKE, None)
+    assert mpf(Hq=60) == 1
+    assert mpf(T=-1) == 1
+    assert mpf(q_dtype=9) == 2
+    assert mpf(ws=None, ws_bytes=0) == 3
+    assert mpf(ws_bytes=100) == 3
+    assert mpf(cache=mx(page_size=8)) == 2
+    assert mpf(cache=mx(v_exp_offset=128)) == 1
+    assert mpf(T=0) == 0
+    assert L.nvfp4_mx_prefill_attn(ctypes.byref(c), FAKE, 1, 16, 64, FAKE, 100, 1, float("nan"), FAKE, 1 << 30,
+                                   FAKE, None) == 1
+    assert 2 * api.mx_prefill_workspace_bytes(2048, 64, 8, 32768) == api.prefill_workspace_bytes(2048, 64, 8, 32768, 0)
+    assert api.mx_prefill_workspace_bytes(16, 8, 0, 10) == 0
+
 
 def test_dequant_rejects_bad_arguments(api):
     L = api.lib()

@@ -986,6 +986,75 @@ def test_mx_config4_paged_all(orc):
     say("   ", check_decode(out, ref, mag))
 
 
+def _mx_prefill_ref(orc, q_rows, rows, Hkv, kh, vh, prefix, causal):
+    """Exact attention (the oracle's dense routine, in double) of the chunk
+    rows over the MXFP4 values kh, vh [Ltot][Hkv][128]."""
+    total = kh.shape[0]
+
+    def one(i):
+        lim = prefix + int(rows[i]) if causal else total - 1
+        return orc.attend_dense(q_rows[i], Hkv, kh[:lim + 1], vh[:lim + 1])
+    return np.stack(pmap(one, range(len(rows))))
+
+
+def _mx_prefill_setup(orc, pw, perm, npages, k, v):
+    cache = api.MxCache(npages, pw.Hkv, api.mx_exp_offset_from_amax(orc.abs_max(k)),
+                        api.mx_exp_offset_from_amax(orc.abs_max(v)), fill=0xA5)
+    api.mx_append(cache, to_dev(k, "bf16"), to_dev(v, "bf16"), i32(np.zeros(pw.total)),
+                  i32(np.arange(pw.total)), i32(perm[None]))
+    kh = orc.mx_dequant_rows(*orc.mx_quantize_rows(k))
+    vh = orc.mx_dequant_rows(*orc.mx_quantize_rows(v))
+    return cache, kh, vh
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: f"p{c[0]}-T{c[1]}-G{c[2] // c[3]}-c{int(c[4])}")
+def test_mx_prefill_parity_small(orc, case):
+    """Chunked prefill over an MXFP4 cache (FP4 K with its block scales in the
+    matrix products, FP8 Q, P and V): the FP8 error model's bound and RMS
+    gate against exact attention over the cache's MXFP4 values (the model
+    also charges K a rounding it does not have here)."""
+    prefix, T, Hq, Hkv, causal = case
+    pw = W.small_prefill(prefix, T, Hq, Hkv, seed_cfg=700 + prefix + T)
+    kp, vp = pw.prefix_kv()
+    kc_, vc_ = pw.chunk_kv()
+    k, v = np.concatenate([kp, kc_]), np.concatenate([vp, vc_])
+    npages = -(-pw.total // 16)
+    perm = np.random.default_rng(prefix + T + 1).permutation(npages + 3)[:npages].astype(np.int32)
+    say(f"mx prefill {case}: append")
+    cache, kh, vh = _mx_prefill_setup(orc, pw, perm, npages + 3, k, v)
+    q = pw.q()
+    out = api.mx_prefill(cache, to_dev(q, "bf16"), i32(perm), prefix, causal=causal).cpu().numpy()
+    rows = np.arange(T)
+    ref = _mx_prefill_ref(orc, q, rows, Hkv, kh, vh, prefix, causal)
+    from oracle.bounds import fp8_attention_error_model
+    model = fp8_attention_error_model(q, rows, Hkv, kh, vh, prefix, causal)
+    _prefill_check(out, ref, model, api.PREFILL_FP8)
+
+
+def test_mx_prefill_config5_rows(orc):
+    """Configuration 5 (2048 causal queries after a 32768-token prefix, 64/8
+    heads) over an MXFP4 cache at full size: 96 rows (the first 32, the last
+    32 and 32 seeded ones) against exact attention, to the FP8 model."""
+    pw = W.PrefillWorkload()
+    kp, vp = pw.prefix_kv()
+    kc_, vc_ = pw.chunk_kv()
+    k, v = np.concatenate([kp, kc_]), np.concatenate([vp, vc_])
+    pt = pw.page_table()
+    say("mx config 5: append")
+    cache, kh, vh = _mx_prefill_setup(orc, pw, pt[0], pw.num_pages, k, v)
+    q = pw.q()
+    say("mx config 5: prefill")
+    out = api.mx_prefill(cache, to_dev(q, "bf16"), i32(pt[0]), pw.prefix, causal=True).cpu().numpy()
+    rng = np.random.default_rng(55)
+    rows = np.unique(np.concatenate([np.arange(32), pw.T - 32 + np.arange(32),
+                                     rng.choice(np.arange(32, pw.T - 32), 32, replace=False)]))
+    say(f"mx config 5: oracle on {len(rows)} rows")
+    ref = _mx_prefill_ref(orc, q[rows], rows, pw.Hkv, kh, vh, pw.prefix, True)
+    from oracle.bounds import fp8_attention_error_model
+    model = fp8_attention_error_model(q[rows], rows, pw.Hkv, kh, vh, pw.prefix, True)
+    _prefill_check(out[rows], ref, model, api.PREFILL_FP8)
+
+
 def test_mse_config2_steps(orc):
     """Configuration 2 (outlier channels) written with the MSE-searched scale,
     then 3 appended steps: the oracle checks every sequence's codes and
