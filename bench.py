@@ -655,6 +655,49 @@ def bench_to_fp8(api, torch, stream, rows=16384, cols=16384, iters=10):
     return res
 
 
+def prefill_sweep(api, torch, stream, iters=5):
+    """Cost of re-expanding the prefix at every chunk: the prefill call of a
+    2048-token chunk (and of a 512-token one) after prefixes of 0 to 131072
+    tokens, 64/8 heads, both operand modes, on caches of random bytes (E4M3
+    block scales drawn from codes 1..126).  Each call runs expand_kernel over
+    all prefix + chunk tokens, then fa_kernel; a kernel trace of this run
+    splits the two (the configurations run in the printed order, `iters`
+    calls each after one untimed call)."""
+    Hq, Hkv = 64, 8
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    rows = []
+    for mode in (api.PREFILL_FP8, api.PREFILL_F16):
+        for prefix, T in ((0, 2048), (4096, 2048), (16384, 2048), (32768, 2048), (65536, 2048), (131072, 2048),
+                          (32768, 512)):
+            total = prefix + T
+            npages = -(-total // 16)
+            cache = api.KVCache(npages, Hkv, 1.0 / 2688, 1.0 / 2688, fill=None)
+            for t in (cache.k_codes, cache.v_codes):
+                t.copy_(torch.randint(0, 256, t.shape, dtype=torch.uint8, device="cuda", generator=gen))
+            for t in (cache.k_scales, cache.v_scales):
+                t.copy_(torch.randint(1, 127, t.shape, dtype=torch.uint8, device="cuda", generator=gen))
+            pt = torch.arange(npages, dtype=torch.int32, device="cuda")
+            q = torch.randn((T, Hq, 128), device="cuda", generator=gen).to(torch.bfloat16)
+            out = torch.empty((T, Hq, 128), dtype=torch.float32, device="cuda")
+            ws = torch.empty(api.prefill_workspace_bytes(T, Hq, Hkv, prefix, mode), dtype=torch.uint8, device="cuda")
+
+            def call():
+                api.prefill(cache, q, pt, prefix, causal=True, workspace=ws, out=out, mode=mode, stream=stream)
+
+            call()
+            torch.cuda.synchronize()
+            t = time_region(torch, call, iters, stream)
+            flops = 4.0 * 128 * Hq * (T * prefix + T * (T + 1) / 2)
+            exp_bytes = total * Hkv * 128 * 2 * (0.5625 + (1 if mode == api.PREFILL_FP8 else 2))
+            rows.append({"mode": "fp8" if mode == api.PREFILL_FP8 else "f16", "prefix": prefix, "chunk": T,
+                         "call_ms": round(t, 4), "tflops": round(flops / t / 1e9, 1),
+                         "expand_bytes": int(exp_bytes)})
+            del cache, ws, out, q
+            torch.cuda.empty_cache()
+    return {"workload": "chunk prefill after prefixes 0..131072 (64/8 heads), random cache bytes",
+            "calls_per_config": iters + 1, "configs": rows}
+
+
 def append_only(api, torch, stream, steps, warmup):
     """Configuration 4's bulk append alone: every token of the workload
     (594,571 x 8 KV heads, positions 0 .. L_b - 1 of each sequence) quantized
@@ -841,6 +884,9 @@ def main():
     ap.add_argument("--small-decode", action="store_true",
                     help="time only the decode of configurations 1-3 and print their record; a profiling "
                          "entry, not the benchmark line")
+    ap.add_argument("--prefill-sweep", action="store_true",
+                    help="time the prefill call over prefix lengths 0..131072 (expansion against attention; "
+                         "split the two kernels with a kernel trace of this run)")
     ap.add_argument("--append-only", action="store_true",
                     help="time only configuration 4's bulk append (NVFP4 and MXFP4) on random data and print "
                          "its record; a profiling entry, not the benchmark line")
@@ -876,6 +922,9 @@ def main():
         for cfg in (2, 3):
             rec[f"decode_cfg{cfg}"] = bench_small_decode(api, torch, stream, cfg, iters=max(1, args.steps))
         print(json.dumps(rec), flush=True)
+        return
+    if args.prefill_sweep:
+        print(json.dumps({"prefill_sweep": prefill_sweep(api, torch, stream, iters=max(1, args.steps))}), flush=True)
         return
     if args.append_only:
         rec = {"append_cfg4": append_only(api, torch, stream, max(1, args.steps), args.warmup)}
