@@ -786,6 +786,17 @@ DECODE_SOURCES = [os.path.join(ROOT, "decode_attention_nvfp4_amd", "csrc", f)
                   for f in ("decode.hip", "common.h", "internal.h", "api.cpp")]
 
 
+def calibration_copy(torch, mib: int):
+    """The device-to-device copy of `mib` MiB whose FETCH_SIZE and WRITE_SIZE
+    scale a counter run's readings to bytes (ideal: mib MiB each way)."""
+    src = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def sources_digest() -> str:
     import hashlib
     h = hashlib.sha256()
@@ -855,7 +866,7 @@ def write_traffic_record(fetch_dir: str, write_dir: str):
     dec_f, dec_w = pick(fetch, "decode_kernel"), pick(write, "decode_kernel")
     mer_f, mer_w = pick(fetch, "merge_kernel"), pick(write, "merge_kernel")
     rec = {
-        "workload": "paged decode, batch 128, 32/8 heads, context U[1024, 8192] (bench.py)",
+        "workload": "paged decode, batch 128, 32/8 heads, context U[1024, 8192] (bench.py --decode-only)",
         "copy_mib": mib, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
         "fetch_factor": fk, "write_factor": wk,
         "decode_kernel_kib": {"fetch": dec_f, "write": dec_w},
@@ -928,18 +939,17 @@ def main():
         return
     if args.append_only:
         rec = {"append_cfg4": append_only(api, torch, stream, max(1, args.steps), args.warmup)}
-        if args.copy_mib:          # the calibration copy for FETCH_SIZE / WRITE_SIZE passes
-            src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
-            dst = torch.empty_like(src)
-            for _ in range(3):
-                dst.copy_(src)
-            torch.cuda.synchronize()
+        if args.copy_mib:
+            calibration_copy(torch, args.copy_mib)
             rec["copy_mib"] = args.copy_mib
         print(json.dumps(rec), flush=True)
         return
     if args.decode_only:
-        print(json.dumps({"decode_cfg4": decode_only(api, torch, stream, max(1, args.steps), args.warmup)}),
-              flush=True)
+        rec = {"decode_cfg4": decode_only(api, torch, stream, max(1, args.steps), args.warmup)}
+        if args.copy_mib:
+            calibration_copy(torch, args.copy_mib)
+            rec["copy_mib"] = args.copy_mib
+        print(json.dumps(rec), flush=True)
         return
 
     # ---- workload: paged large-batch decode
@@ -1023,12 +1033,7 @@ def main():
     t_dec_b2b = None if args.no_extra else time_region(torch, decode_step, args.steps, stream)
 
     if args.copy_mib:
-        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(torch, args.copy_mib)
 
     cache_bytes = int((w.lens + 1).sum()) * w.Hkv * BYTES_PER_TOKEN_HEAD
     q_out_bytes = w.B * w.Hq * 128 * (2 + 4)
