@@ -609,7 +609,10 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
     u0 = rm.start(wave);
     u1 = rm.start(wave + 1);
   }
-  if (u0 >= u1) return;
+  if (u0 >= u1) {                          // no units (more waves than units)
+    if constexpr (PROBE) reinterpret_cast<uint32_t*>(p.out)[wave * 64 + lane] = 0u;
+    return;
+  }
   const int N = (int)(u1 - u0);            // units of this wave
 
   // ---- the segment holding u0: sequence b0 (first sequence whose prefix

@@ -250,8 +250,13 @@ int32_t nvfp4_decode_attn(const nvfp4_kv_cache* cache, const void* q, int32_t q_
  * access pattern costs without the math.
  *   page_table, max_pages_per_seq, seq_lens, max_seq_len, num_splits: as for
  *                nvfp4_decode_attn (same wave ranges)
- *   sink       : device, >= 256 * (wave count) bytes; one word per lane is
- *                written (meaningless values)
+ *   sink       : device, >= 256 * (wave count) bytes; one 32-bit word per
+ *                lane is written: the exclusive or of the words the lane
+ *                loaded (0 for waves without units), so the exclusive or of
+ *                all words is that of every (page, KV head) slab the
+ *                sequences own (K codes and V codes as 32-bit words, K
+ *                scales as 16-bit words; V scales are loaded by lane pairs
+ *                and cancel)
  * Planes beyond 2^31 bytes are not supported (NVFP4_ERR_UNSUPPORTED). */
 int32_t nvfp4_decode_gather_probe(const nvfp4_kv_cache* cache, int32_t batch, const int32_t* page_table,
                                   int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,

@@ -159,6 +159,23 @@ def test_mx_sizes_offsets_and_bad_arguments(api):
     assert api.mx_prefill_workspace_bytes(16, 8, 0, 10) == 0
 
 
+def test_gather_probe_rejects_bad_arguments(api):
+    L = api.lib()
+    c = _fake_cache(api)
+
+    def gp(B=2, maxp=64, max_len=1000, S=4, sink=FAKE, sink_bytes=1 << 20, cache=c):
+        return L.nvfp4_decode_gather_probe(ctypes.byref(cache), B, FAKE, maxp, FAKE, max_len, S, sink, sink_bytes,
+                                           None)
+    assert gp(B=-1) == 1
+    assert gp(S=-1) == 1
+    assert gp(maxp=0) == 1
+    assert gp(max_len=1025, maxp=64) == 1          # 65 pages > 64 per row
+    assert gp(sink=None) == 1
+    assert gp(sink_bytes=4 * 64 * 4 - 1) == 3      # 4 waves need 4 x 64 words
+    assert gp(cache=_fake_cache(api, head_dim=64)) == 2
+    assert gp(B=0, sink=None) == 0
+
+
 def test_dequant_rejects_bad_arguments(api):
     L = api.lib()
     c = _fake_cache(api)

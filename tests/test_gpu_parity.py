@@ -460,6 +460,51 @@ def test_decode_split_sweep_and_determinism(orc):
     assert np.array_equal(again.view(np.uint32), outs[0].view(np.uint32))
 
 
+def test_gather_probe_loads_every_page_once():
+    """nvfp4_decode_gather_probe (the decode's work split, page walk and page
+    loads without the math): every lane XORs the words it loads into its
+    sink entry, so the XOR of all entries is the XOR of every (page, KV
+    head) slab the sequences own (K codes and V codes as 32-bit words, K
+    scales as 16-bit words; the V scales are loaded twice per lane pair and
+    cancel) whatever the number of waves, when each unit is loaded exactly
+    once.  Random cache bytes, ragged lengths, a permuted page table."""
+    rng = np.random.default_rng(31)
+    Hkv, B = 4, 11
+    lens = np.array([1, 16, 17, 300, 0, 1024, 47, 511, 2000, 33, 64], np.int32)
+    maxp = int(-(-lens.max() // 16))
+    npages = int(sum(-(-int(L) // 16) for L in lens)) + 5
+    pt = np.zeros((B, maxp), np.int32)
+    perm = rng.permutation(npages).astype(np.int32)
+    c = 0
+    for b, L in enumerate(lens):
+        n = -(-int(L) // 16)
+        pt[b, :n] = perm[c:c + n]
+        pt[b, n:] = rng.integers(0, npages, maxp - n)     # rows past the length are never read
+        c += n
+    cache = api.KVCache(npages, Hkv, 1.0, 1.0, fill=None)
+    planes_np = []
+    for t in (cache.k_codes, cache.k_scales, cache.v_codes, cache.v_scales):
+        x = rng.integers(0, 256, t.numel(), dtype=np.uint8)
+        t.copy_(torch.from_numpy(x).view(t.shape).cuda())
+        planes_np.append(x)
+    kcodes = planes_np[0].view(np.uint32).reshape(npages * Hkv, 256)
+    kscales = planes_np[1].view(np.uint16).reshape(npages * Hkv, 64)
+    vcodes = planes_np[2].view(np.uint32).reshape(npages * Hkv, 256)
+    expect = np.uint32(0)
+    for b, L in enumerate(lens):
+        for pg in range(-(-int(L) // 16)):
+            for h in range(Hkv):
+                slab = int(pt[b, pg]) * Hkv + h
+                expect ^= np.bitwise_xor.reduce(kcodes[slab]) ^ np.bitwise_xor.reduce(vcodes[slab])
+                expect ^= np.uint32(np.bitwise_xor.reduce(kscales[slab]))
+    ptd, lensd = i32(pt), i32(lens)
+    for S in (0, 1, 7, 64, 5000):
+        say(f"gather probe S={S}")
+        sink = api.decode_gather_probe(cache, ptd, lensd, int(lens.max()), num_splits=S)
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == expect, (S, hex(int(got)), hex(int(expect)))
+
+
 def test_decode_f32_query_bf16_cache(orc):
     w = W.custom_decode(10, 2, 8, 2, [300, 1025], dtype="bf16")
     built = BuiltDecode(w, orc)
