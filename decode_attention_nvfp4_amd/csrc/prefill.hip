@@ -661,13 +661,16 @@ __global__ void __launch_bounds__(512) fa_kernel(PrefillArgs p) {
     }
   };
   auto soft = [&](auto G, auto B, int t) {   // B = (t - 1) & 1, the set to store
+    // the tile stores go first: the matrix waves' operand reads keep LDS
+    // busy, and stores issued ahead of the softmax complete under it
+    // instead of holding up the interval's end
+    const int tk = t + 1 + G(), tv = t + G();
+    if (tk < ntiles) sstore_k(tk & 1, stk[B()]);
+    if (tv >= 0 && tv < ntiles) sstore_v(tv & 1, stv[B()]);
     if (t >= 0 && t < ntiles) {
       rescale(row_max(t, sc), sc);
       probs(sc, pw);
     }
-    const int tk = t + 1 + G(), tv = t + G();
-    if (tk < ntiles) sstore_k(tk & 1, stk[B()]);
-    if (tv >= 0 && tv < ntiles) sstore_v(tv & 1, stv[B()]);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
