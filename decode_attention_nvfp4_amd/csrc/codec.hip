@@ -15,7 +15,8 @@ namespace nvfp4 {
 
 // A lane's 8 input elements (half of one block) as raw bits: 32 bytes of
 // FP32 or 16 bytes of BF16.  Converted to float only when quantized, so that
-// the loads of a row can all be in flight together.
+// the loads of a row can all be in flight together.  The input is read once
+// (non-temporal hint).
 struct Raw8 {
   uint4 a, b;
 };
@@ -25,10 +26,10 @@ __device__ __forceinline__ Raw8 load_raw8(const void* base, size_t row, int lane
   Raw8 r;
   if (F32IN) {
     const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + row * kD + lane16 * 8);
-    r.a = p[0];
-    r.b = p[1];
+    r.a = load_once16(p);
+    r.b = load_once16(p + 1);
   } else {
-    r.a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * kD + lane16 * 8);
+    r.a = load_once16(static_cast<const uint16_t*>(base) + row * kD + lane16 * 8);
     r.b = uint4{0u, 0u, 0u, 0u};
   }
   return r;

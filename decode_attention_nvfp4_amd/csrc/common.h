@@ -32,6 +32,21 @@ typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16 / 8 bytes read or written once: loads and stores with the non-temporal
+// hint (the lines are not kept for reuse)
+__device__ __forceinline__ uint4 load_once16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_once8(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void store_once16(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, static_cast<u32x4*>(p));
+}
 
 // ------------------------------------------------------------ E4M3 decode
 

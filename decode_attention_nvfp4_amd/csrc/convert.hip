@@ -13,7 +13,8 @@
 // 1 KiB LDS table of the 128 x 8 magnitude codes (two IEEE divisions per
 // entry) and the stream then costs a table row per block and one byte
 // permute per four elements: the kernel is bound by HBM (0.5625 bytes in and
-// 1 byte out per element), not by the divisions.
+// 1 byte out per element), not by the divisions.  Every byte is read or
+// written once, so the loads and stores carry the non-temporal hint.
 #include "common.h"
 #include "internal.h"
 
@@ -66,8 +67,8 @@ __global__ void __launch_bounds__(kConvThreads) to_fp8_kernel(ToFp8Args a) {
       w[j] = make_uint2(0u, 0u);
       sc[j] = 0u;
       if (b < a.n_blocks) {
-        w[j] = *reinterpret_cast<const uint2*>(a.codes + 8 * b);
-        sc[j] = a.scales[b] & 0x7Fu;
+        w[j] = load_once8(a.codes + 8 * b);
+        sc[j] = __builtin_nontemporal_load(a.scales + b) & 0x7Fu;
       }
     }
 #pragma unroll
@@ -76,7 +77,7 @@ __global__ void __launch_bounds__(kConvThreads) to_fp8_kernel(ToFp8Args a) {
       if (b < a.n_blocks) {
         const uint32_t lo = table[sc[j]][0], hi = table[sc[j]][1];
         const uint2 r0 = convert8(w[j].x, lo, hi), r1 = convert8(w[j].y, lo, hi);
-        *reinterpret_cast<uint4*>(a.out + 16 * b) = make_uint4(r0.x, r0.y, r1.x, r1.y);
+        store_once16(a.out + 16 * b, make_uint4(r0.x, r0.y, r1.x, r1.y));
       }
     }
   }
