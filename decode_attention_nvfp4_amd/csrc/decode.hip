@@ -125,11 +125,17 @@ __device__ __forceinline__ PlaneRsrc plane_rsrc(const DecodeArgs& p) {
   return r;
 }
 
-// Cache policy of the page loads: non-temporal.  A call reads every page of
-// the cache once, so the lines have no reuse to keep; with the streaming
-// hint the same gather moves 6.5 TB/s instead of 5.7 (configuration-4
-// shape, both measured on the kernel's own access pattern).
-constexpr int kPageLoadPolicy = 2;
+// Cache policy of the page loads.  A call reads every page of the cache
+// once; an NVFP4 or MXFP4 page load instruction covers whole lines (1 KiB of
+// codes, 128 or 64 bytes of scales, contiguous over the wave), so the lines
+// have no reuse to keep, and with the non-temporal hint the same gather
+// moves 6.5 TB/s instead of 5.7 (configuration-4 shape).  The FP8 and BF16
+// pages are read 16 bytes per lane per instruction out of 32 or 64
+// contiguous bytes per lane, so each line is touched by two or four
+// instructions, and non-temporal lines were fetched again (BF16 decode of
+// configuration 4: 656 us against 437): those keep the default policy.
+template <int FMT>
+constexpr int kPageLoadPolicy = (FMT == kFmtNvfp4 || FMT == kFmtMxfp4) ? 2 : 0;
 
 // Buffer loads: the slab base lives in scalar registers and the lane offsets
 // are fixed, so a page load needs no vector address temporaries.
@@ -145,17 +151,17 @@ __device__ __forceinline__ void load_page(const DecodeArgs& p, const PlaneRsrc& 
     const auto rks = WIDE ? page_rsrc(p.k_scales + (size_t)slab * SB::ks) : pr.ks;
     const auto rvs = WIDE ? page_rsrc(p.v_scales + (size_t)slab * SB::vs) : pr.vs;
     const int sks = WIDE ? 0 : (int)(slab * SB::ks), svs = WIDE ? 0 : (int)(slab * SB::vs);
-    r.kq = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k, sk, kPageLoadPolicy);
-    if constexpr (FMT == kFmtNvfp4) r.ksc = __builtin_amdgcn_raw_buffer_load_b16(rks, o.ks, sks, kPageLoadPolicy);
-    else r.ksc = __builtin_amdgcn_raw_buffer_load_b8(rks, o.ks, sks, kPageLoadPolicy);
-    r.vq = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v, sv, kPageLoadPolicy);
-    r.vsc = __builtin_amdgcn_raw_buffer_load_b32(rvs, o.vs, svs, kPageLoadPolicy);
+    r.kq = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k, sk, kPageLoadPolicy<FMT>);
+    if constexpr (FMT == kFmtNvfp4) r.ksc = __builtin_amdgcn_raw_buffer_load_b16(rks, o.ks, sks, kPageLoadPolicy<FMT>);
+    else r.ksc = __builtin_amdgcn_raw_buffer_load_b8(rks, o.ks, sks, kPageLoadPolicy<FMT>);
+    r.vq = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v, sv, kPageLoadPolicy<FMT>);
+    r.vsc = __builtin_amdgcn_raw_buffer_load_b32(rvs, o.vs, svs, kPageLoadPolicy<FMT>);
   } else {
     constexpr int N = 2 * kElemBytes<FMT>;             // 16-byte loads per lane and operand
 #pragma unroll
-    for (int i = 0; i < N; ++i) r.kq[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k + 16 * i, sk, kPageLoadPolicy);
+    for (int i = 0; i < N; ++i) r.kq[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k + 16 * i, sk, kPageLoadPolicy<FMT>);
 #pragma unroll
-    for (int i = 0; i < N; ++i) r.vq[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v + 16 * i, sv, kPageLoadPolicy);
+    for (int i = 0; i < N; ++i) r.vq[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v + 16 * i, sv, kPageLoadPolicy<FMT>);
   }
 }
 
