@@ -376,36 +376,52 @@ __device__ __forceinline__ void process_page(PageRegs<FMT> cur, int pg, int L, i
   }
 }
 
+// A lane's raw query bits (32 elements: FP32 or bf16), loaded apart from
+// their conversion so that a load can be issued ahead of its use.
+template <bool F32Q>
+struct QRaw {
+  uint4 w[F32Q ? 8 : 4];
+};
+
+template <bool F32Q>
+__device__ __forceinline__ QRaw<F32Q> fetch_q(const DecodeArgs& p, int b, int kvh, int col, int kg) {
+  QRaw<F32Q> r;
+  if (col < p.group) {
+    const size_t qoff = ((size_t)b * p.hq + kvh * p.group + col) * kD + kg * 32;
+    const uint4* src = F32Q ? reinterpret_cast<const uint4*>(static_cast<const float*>(p.q) + qoff)
+                            : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff);
+#pragma unroll
+    for (int i = 0; i < (F32Q ? 8 : 4); ++i) r.w[i] = src[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < (F32Q ? 8 : 4); ++i) r.w[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  return r;
+}
+
 // Q of (sequence b, KV head kvh) as the B operand of S^T = K~ Q^T: lane
 // (head col, group kg) holds q[32kg + 8i + j] in element j of qh[i], scaled by
 // 2^shift into FP16 (the max |q| of the head lands in [2^14, 2^15)).
 template <bool F32Q, int FMT>
-__device__ __forceinline__ void load_q(const DecodeArgs& p, int b, int kvh, int col, int kg,
-                                       halfx8 qh[4], halfx8 ql[4], float& qscale) {
+__device__ __forceinline__ void convert_q(const DecodeArgs& p, const QRaw<F32Q>& r, int kg,
+                                          halfx8 qh[4], halfx8 ql[4], float& qscale) {
   float qv[32];
-  if (col < p.group) {
-    const size_t qoff = ((size_t)b * p.hq + kvh * p.group + col) * kD + kg * 32;
-    if (F32Q) {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(p.q) + qoff);
+  if (F32Q) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float4 v = src[i];
-        qv[4 * i] = v.x; qv[4 * i + 1] = v.y; qv[4 * i + 2] = v.z; qv[4 * i + 3] = v.w;
-      }
-    } else {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) + qoff);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 v = src[i];
-        qv[8 * i + 0] = bf16_lo(v.x); qv[8 * i + 1] = bf16_hi(v.x);
-        qv[8 * i + 2] = bf16_lo(v.y); qv[8 * i + 3] = bf16_hi(v.y);
-        qv[8 * i + 4] = bf16_lo(v.z); qv[8 * i + 5] = bf16_hi(v.z);
-        qv[8 * i + 6] = bf16_lo(v.w); qv[8 * i + 7] = bf16_hi(v.w);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = r.w[i];
+      qv[4 * i] = __uint_as_float(v.x); qv[4 * i + 1] = __uint_as_float(v.y);
+      qv[4 * i + 2] = __uint_as_float(v.z); qv[4 * i + 3] = __uint_as_float(v.w);
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) qv[i] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = r.w[i];
+      qv[8 * i + 0] = bf16_lo(v.x); qv[8 * i + 1] = bf16_hi(v.x);
+      qv[8 * i + 2] = bf16_lo(v.y); qv[8 * i + 3] = bf16_hi(v.y);
+      qv[8 * i + 4] = bf16_lo(v.z); qv[8 * i + 5] = bf16_hi(v.z);
+      qv[8 * i + 6] = bf16_lo(v.w); qv[8 * i + 7] = bf16_hi(v.w);
+    }
   }
   if constexpr (FMT == kFmtBf16) {
     // bf16 operands (bit patterns in the half registers): q = hi + lo, with
@@ -440,6 +456,12 @@ __device__ __forceinline__ void load_q(const DecodeArgs& p, int b, int kvh, int 
       ql[i][j] = F32Q ? (_Float16)(v - (float)hv) : (_Float16)0.0f;
     }
   }
+}
+
+template <bool F32Q, int FMT>
+__device__ __forceinline__ void load_q(const DecodeArgs& p, int b, int kvh, int col, int kg,
+                                       halfx8 qh[4], halfx8 ql[4], float& qscale) {
+  convert_q<F32Q, FMT>(p, fetch_q<F32Q>(p, b, kvh, col, kg), kg, qh, ql, qscale);
 }
 
 // Write the state of (b, kvh): the final output when the piece is the whole
@@ -705,6 +727,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   int done = 0;                            // units processed
   halfx8 qh[4], ql[4];
   float qscale = 0.0f;
+  QRaw<F32Q> q_first;
   WaveState st;
   uint32_t probe_sink = 0;
   auto step = [&](const PageRegs<FMT>& r) {
@@ -718,7 +741,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
       started = true;
       piece_left = min(seg.np - seg.pg, N - done);
       whole = seg.pg == 0 && piece_left == seg.np;
-      load_q<F32Q, FMT>(p, seg.b, seg.kvh, col, kg, qh, ql, qscale);
+      if (first_piece) convert_q<F32Q, FMT>(p, q_first, kg, qh, ql, qscale);
+      else load_q<F32Q, FMT>(p, seg.b, seg.kvh, col, kg, qh, ql, qscale);
       reset_state(st);
     }
     process_page<F32Q, FMT>(r, seg.pg, seg.L, kg, qscale, qh, ql, st, p.k_exp, p.v_exp);
@@ -740,6 +764,11 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   // unit), and only the loop's latch exits: every path around the back edge
   // then carries a whole iteration of page loads, which the compiler's waits
   // rely on (an exit in the middle, however rare, gives it a short path).
+  // the first piece's queries load ahead of the first pages: its start then
+  // waits for nothing the first page does not (a query load issued at the
+  // piece start waits behind every page load in flight)
+  if constexpr (!PROBE) q_first = fetch_q<F32Q>(p, start.b, start.kvh, col, kg);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < kD8 - 1; ++i) {
     issue(r[i]);
