@@ -48,19 +48,6 @@ __device__ __forceinline__ void unpack8(const Raw8& r, float x[8]) {
   }
 }
 
-// Returns the packed codes of this lane's 8 elements; *sb gets the block
-// scale code of its block.
-__device__ __forceinline__ uint32_t quantize_half_block(const float x[8], float s_t, float inv6, double six_st,
-                                                        uint32_t* sb) {
-  float a = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
-  a = fmaxf(a, __shfl_xor(a, 1));
-  uint32_t code = block_scale_code_fast(a, inv6, six_st);
-  *sb = code;
-  return encode8(x, code, s_t);
-}
-
 // ------------------------------------------------ MSE-searched block scale
 //
 // The block scale may instead be searched ("NVIDIA解説: NVFP4 KV Cacheで長コン
@@ -135,8 +122,9 @@ __device__ __forceinline__ bool block_sq_error_est(const float xb[16], uint32_t 
   return true;
 }
 
-// quantize_half_block with the searched scale.  The lane pair swaps halves
-// so both hold the block's 16 elements in order; search position k = 0 is
+// A lane's 8 packed codes (half of a block held by a lane pair) under the
+// searched block scale, *sb the scale code.  The lane pair swaps halves so
+// both hold the block's 16 elements in order; search position k = 0 is
 // the amax/6 code, k = 2j - 1 and 2j its neighbours at distance j below and
 // above.  The even lane tries the even positions, the odd lane the odd ones,
 // and the pair keeps the smallest (error, position); an unusable position
@@ -273,8 +261,10 @@ __device__ __forceinline__ void spread_nibbles(uint32_t w, uint32_t* w0, uint32_
   *w1 = sp(w >> 16);
 }
 
-// Workgroup = 16 consecutive tokens of the call x one KV head (grid.y).  The
-// V codes of a token pair (2i, 2i+1) share bytes: when both tokens of a pair
+// The MSE-searched and MXFP4 appends (a block spans a lane pair or quad,
+// which exchange the block's amax or candidates): workgroup = 16 consecutive
+// tokens of the call x one KV head (grid.y).  The V codes of a token pair
+// (2i, 2i+1) share bytes: when both tokens of a pair
 // sit in the same workgroup (consecutive rows, same sequence, positions 2i
 // and 2i+1) the even row writes the whole bytes; a token whose partner is
 // elsewhere updates its nibbles with atomic AND / OR, which commute with the
@@ -317,14 +307,11 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
       kw = quantize_half_block_mse(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
       unpack8<F32IN>(rv, x);
       vw = quantize_half_block_mse(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
-    } else if constexpr (MODE == kAppendMx) {
+    } else {
+      static_assert(MODE == kAppendMx, "the amax/6 append is append_block_kernel");
       kw = quantize_half_block_mx(x, &ksb);
       unpack8<F32IN>(rv, x);
       vw = quantize_half_block_mx(x, &vsb);
-    } else {
-      kw = quantize_half_block(x, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
-      unpack8<F32IN>(rv, x);
-      vw = quantize_half_block(x, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
     }
     slab = (size_t)page * p.hkv + h;
     // K: token-major codes [16][64 B]; the V codes follow below
@@ -365,6 +352,98 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
     atomicOr(dst, a0 << sh);
     atomicAnd(dst + 1, keep);
     atomicOr(dst + 1, a1 << sh);
+  }
+}
+
+// The amax/6 append with one lane per 16-element block: workgroup = 32
+// consecutive tokens of the call x one KV head, 8 lanes per token.  A lane
+// holds its whole block, so the block's amax, scale code and reciprocal are
+// computed once (the lane-pair layout above computes them in both lanes and
+// exchanges the amax); the element rounding is encode8's, so the codes are
+// those of append_kernel.  V pairs as in append_kernel.
+constexpr int kBlockRows = 32;
+
+template <bool F32IN>
+__global__ void __launch_bounds__(256) append_block_kernel(AppendArgs p) {
+  const int j = threadIdx.x & 7, r = threadIdx.x >> 3;      // block j of row r
+  const int tok = blockIdx.x * kBlockRows + r;
+  const int h = blockIdx.y;
+  const bool valid = tok < p.n_tok;
+  __shared__ int s_seq[kBlockRows], s_pos[kBlockRows];
+  __shared__ uint2 s_vw[kBlockRows][8];
+  int seq = -1, pos = 0;
+  Raw8 rk0 = {}, rk1 = {}, rv0 = {}, rv1 = {};
+  const size_t row = (size_t)tok * p.hkv + h;
+  if (valid) {
+    seq = p.tok_seq[tok];
+    pos = p.tok_pos[tok];
+    rk0 = load_raw8<F32IN>(p.k_new, row, 2 * j);
+    rk1 = load_raw8<F32IN>(p.k_new, row, 2 * j + 1);
+    rv0 = load_raw8<F32IN>(p.v_new, row, 2 * j);
+    rv1 = load_raw8<F32IN>(p.v_new, row, 2 * j + 1);
+  }
+  if (j == 0) {
+    s_seq[r] = seq;
+    s_pos[r] = pos;
+  }
+  // the block's codes (elements 0-7, 8-15) and scale code
+  auto quantize = [&](const Raw8& r0, const Raw8& r1, float s_t, float inv6, double six_st, uint32_t* sb) {
+    float x0[8], x1[8];
+    unpack8<F32IN>(r0, x0);
+    unpack8<F32IN>(r1, x1);
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fmaxf(fabsf(x0[e]), fabsf(x1[e])));
+    const uint32_t code = block_scale_code_fast(a, inv6, six_st);
+    *sb = code;
+    return make_uint2(encode8(x0, code, s_t), encode8(x1, code, s_t));
+  };
+  size_t slab = 0;
+  int slot = 0;
+  uint2 vw = make_uint2(0u, 0u);
+  if (valid) {
+    const int page = clamp_page(p.page_table[(size_t)seq * p.max_pages + pos / kPage], p.num_pages);
+    slot = pos % kPage;
+    uint32_t ksb, vsb;
+    const uint2 kw = quantize(rk0, rk1, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
+    vw = quantize(rv0, rv1, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
+    slab = (size_t)page * p.hkv + h;
+    // K: token-major codes [16][64 B], block j at byte 8j; scales K [token
+    // 16][block 8], V [block 8][token 16]
+    *reinterpret_cast<uint2*>(p.k_codes + slab * kSlab + slot * 64 + j * 8) = kw;
+    p.k_scales[slab * kScaleSlab + slot * kNBlk + j] = (uint8_t)ksb;
+    p.v_scales[slab * kScaleSlab + j * kPage + slot] = (uint8_t)vsb;
+  }
+  s_vw[r][j] = vw;
+  __syncthreads();
+  if (!valid) return;
+  const int odd = pos & 1;
+  const int pr = odd ? r - 1 : r + 1;           // the partner's row, if it is here
+  const bool paired = pr >= 0 && pr < kBlockRows && s_seq[pr] == seq && s_pos[pr] == (pos ^ 1);
+  // V: the block's element groups 2j and 2j+1 (8 elements each, 16 bytes apart)
+  uint32_t* dst = reinterpret_cast<uint32_t*>(p.v_codes + slab * kSlab + (slot >> 2) * 256 + j * 32 +
+                                              ((slot >> 1) & 1) * 8);
+  uint32_t a[4];
+  spread_nibbles(vw.x, &a[0], &a[1]);
+  spread_nibbles(vw.y, &a[2], &a[3]);
+  if (paired) {
+    if (odd) return;                            // written by the even row
+    const uint2 pv = s_vw[pr][j];
+    uint32_t b[4];
+    spread_nibbles(pv.x, &b[0], &b[1]);
+    spread_nibbles(pv.y, &b[2], &b[3]);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(a[0] | (b[0] << 4), a[1] | (b[1] << 4));
+    *reinterpret_cast<uint2*>(dst + 4) = make_uint2(a[2] | (b[2] << 4), a[3] | (b[3] << 4));
+  } else {
+    const uint32_t keep = odd ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
+    const int sh = odd ? 4 : 0;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      atomicAnd(dst + 4 * g, keep);
+      atomicOr(dst + 4 * g, a[2 * g] << sh);
+      atomicAnd(dst + 4 * g + 1, keep);
+      atomicOr(dst + 4 * g + 1, a[2 * g + 1] << sh);
+    }
   }
 }
 
@@ -440,7 +519,11 @@ hipError_t launch_append(const AppendArgs& a, bool f32, int mode, hipStream_t s)
   const dim3 grid((unsigned)((a.n_tok + 15) / 16), (unsigned)a.hkv);
   if (mode == kAppendMse) launch_append_mode<kAppendMse>(a, f32, grid, s);
   else if (mode == kAppendMx) launch_append_mode<kAppendMx>(a, f32, grid, s);
-  else launch_append_mode<kAppendAmax6>(a, f32, grid, s);
+  else {
+    const dim3 bgrid((unsigned)((a.n_tok + kBlockRows - 1) / kBlockRows), (unsigned)a.hkv);
+    if (f32) append_block_kernel<true><<<bgrid, 256, 0, s>>>(a);
+    else append_block_kernel<false><<<bgrid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
