@@ -371,32 +371,43 @@ __global__ void __launch_bounds__(256) append_block_kernel(AppendArgs p) {
   const bool valid = tok < p.n_tok;
   __shared__ int s_seq[kBlockRows], s_pos[kBlockRows];
   __shared__ uint2 s_vw[kBlockRows][8];
-  int seq = -1, pos = 0;
-  Raw8 rk0 = {}, rk1 = {}, rv0 = {}, rv1 = {};
-  const size_t row = (size_t)tok * p.hkv + h;
-  if (valid) {
-    seq = p.tok_seq[tok];
-    pos = p.tok_pos[tok];
-    rk0 = load_raw8<F32IN>(p.k_new, row, 2 * j);
-    rk1 = load_raw8<F32IN>(p.k_new, row, 2 * j + 1);
-    rv0 = load_raw8<F32IN>(p.v_new, row, 2 * j);
-    rv1 = load_raw8<F32IN>(p.v_new, row, 2 * j + 1);
-  }
+  // rows past the call's end load the last row (their results are dropped)
+  const int ltok = valid ? tok : p.n_tok - 1;
+  const size_t row = (size_t)ltok * p.hkv + h;
+  const int seq = valid ? p.tok_seq[ltok] : -1;
+  const int pos = p.tok_pos[ltok];
+  const Raw8 rk0 = load_raw8<F32IN>(p.k_new, row, 2 * j), rk1 = load_raw8<F32IN>(p.k_new, row, 2 * j + 1);
+  const Raw8 rv0 = load_raw8<F32IN>(p.v_new, row, 2 * j), rv1 = load_raw8<F32IN>(p.v_new, row, 2 * j + 1);
   if (j == 0) {
     s_seq[r] = seq;
     s_pos[r] = pos;
   }
-  // the block's codes (elements 0-7, 8-15) and scale code
+  // the block's codes (elements 0-7, 8-15) and scale code.  The amax is
+  // the largest magnitude's bit pattern as an integer (the same value for
+  // finite elements; bf16 halves compared two at a time)
   auto quantize = [&](const Raw8& r0, const Raw8& r1, float s_t, float inv6, double six_st, uint32_t* sb) {
+    float a;
+    if constexpr (F32IN) {
+      uint32_t m = 0u;
+      const uint4 w[4] = {r0.a, r0.b, r1.a, r1.b};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m = max(m, max(max(w[i].x & 0x7FFFFFFFu, w[i].y & 0x7FFFFFFFu), max(w[i].z & 0x7FFFFFFFu, w[i].w & 0x7FFFFFFFu)));
+      a = __uint_as_float(m);
+    } else {
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+      const uint32_t w[8] = {r0.a.x, r0.a.y, r0.a.z, r0.a.w, r1.a.x, r1.a.y, r1.a.z, r1.a.w};
+      u16x2 m = {0, 0};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+      a = __uint_as_float((uint32_t)max(m.x, m.y) << 16);
+    }
     float x0[8], x1[8];
     unpack8<F32IN>(r0, x0);
     unpack8<F32IN>(r1, x1);
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a = fmaxf(a, fmaxf(fabsf(x0[e]), fabsf(x1[e])));
     const uint32_t code = block_scale_code_fast(a, inv6, six_st);
     *sb = code;
-    return make_uint2(encode8(x0, code, s_t), encode8(x1, code, s_t));
+    return encode16(x0, x1, code, s_t);
   };
   size_t slab = 0;
   int slot = 0;

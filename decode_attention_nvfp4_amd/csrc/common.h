@@ -149,10 +149,13 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t sb_code, 
   // the midpoint decision below needs |x| - p rounded on its own: a fused
   // |x| - a * s_t would compare a different residual with e
 #pragma clang fp contract(off)
-  uint32_t signs = 0;
+  auto signs = [&]() {
+    uint32_t w = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) signs |= (__float_as_uint(x[j]) >> 31) << (4 * j + 3);
-  if (sb_code == 0u) return signs;                  // zero scale: magnitude 0
+    for (int j = 0; j < 8; ++j) w |= (__float_as_uint(x[j]) >> 31) << (4 * j + 3);
+    return w;
+  };
+  if (sb_code == 0u) return signs();                // zero scale: magnitude 0
   // d = s_block * s_t in FP32 (2^-24 relative) and its hardware reciprocal
   // (1 ulp) give y within ~2^-22 of 1/d; the brackets are 2^-20 wide
   const float df = e4m3_to_float(sb_code) * s_t;
@@ -193,13 +196,65 @@ __device__ __forceinline__ uint32_t encode8(const float x[8], uint32_t sb_code, 
         diff &= ~(15u << sh);
       } while (diff);
     }
-    return (lo & 0x77777777u) | signs;
+    // the conversion keeps the sign of x * y, which is that of x (y > 0;
+    // -0 and an element rounded to zero give the sign bit too, a value
+    // past 6 saturates with its sign)
+    return lo;
   }
   const double d = (double)e4m3_to_float(sb_code) * (double)s_t;   // exact
-  uint32_t w = signs;
+  uint32_t w = signs();
 #pragma unroll
   for (int j = 0; j < 8; ++j) w |= e2m1_mag_exact(x[j], d) << (4 * j);
   return w;
+}
+
+// encode8 for a whole 16-element block (x0: elements 0-7, x1: 8-15): the
+// same rounding, with the block's step, reciprocal and brackets computed
+// once and one check for an undecided element.
+__device__ __forceinline__ uint2 encode16(const float x0[8], const float x1[8], uint32_t sb_code, float s_t) {
+#pragma clang fp contract(off)
+  const float df = e4m3_to_float(sb_code) * s_t;
+  if (sb_code == 0u || !(df >= 0x1p-100f && df <= 0x1p100f))
+    return make_uint2(encode8(x0, sb_code, s_t), encode8(x1, sb_code, s_t));
+  const float y = __builtin_amdgcn_rcpf(df);
+  const float y_lo = y * (1.0f - 0x1p-20f);
+  const float y_hi = y * (1.0f + 0x1p-20f);
+  uint32_t lo[2] = {0u, 0u}, hi[2] = {0u, 0u};
+  // (the conversion's word select must be a literal)
+#define NVFP4_BRACKETS(H, X)                                                                          \
+  lo[H] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo[H], X[0] * y_lo, X[1] * y_lo, 1.0f, 0);          \
+  lo[H] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo[H], X[2] * y_lo, X[3] * y_lo, 1.0f, 1);          \
+  lo[H] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo[H], X[4] * y_lo, X[5] * y_lo, 1.0f, 2);          \
+  lo[H] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo[H], X[6] * y_lo, X[7] * y_lo, 1.0f, 3);          \
+  hi[H] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[H], X[0] * y_hi, X[1] * y_hi, 1.0f, 0);          \
+  hi[H] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[H], X[2] * y_hi, X[3] * y_hi, 1.0f, 1);          \
+  hi[H] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[H], X[4] * y_hi, X[5] * y_hi, 1.0f, 2);          \
+  hi[H] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi[H], X[6] * y_hi, X[7] * y_hi, 1.0f, 3);
+  NVFP4_BRACKETS(0, x0)
+  NVFP4_BRACKETS(1, x1)
+#undef NVFP4_BRACKETS
+  if (((lo[0] ^ hi[0]) | (lo[1] ^ hi[1])) & 0x77777777u) {
+    // an element between its brackets: decided exactly as in encode8
+    const float sbv = e4m3_to_float(sb_code);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float* x = h ? x1 : x0;
+      uint32_t diff = (lo[h] ^ hi[h]) & 0x77777777u;
+      while (diff) {
+        const int sh = (__builtin_ctz(diff) >> 2) << 2;
+        const uint32_t c = (lo[h] >> sh) & 7u;
+        const float t = c < 4u ? 0.25f + 0.5f * (float)c : (c == 4u ? 2.5f : (c == 5u ? 3.5f : 5.0f));
+        const float a = sbv * t;
+        const float pr = a * s_t;
+        const float e = __builtin_fmaf(a, s_t, -pr);
+        const float r = fabsf(x[sh >> 2]) - pr;
+        const bool up = r > e || (r == e && ((c + 1u) & 1u) == 0u);
+        lo[h] = (lo[h] & ~(7u << sh)) | ((c + (up ? 1u : 0u)) << sh);
+        diff &= ~(15u << sh);
+      }
+    }
+  }
+  return make_uint2(lo[0], lo[1]);
 }
 
 // 2^x with the hardware exponential (results below 2^-126 flush to zero,
