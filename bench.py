@@ -112,6 +112,17 @@ def time_region(torch, fn, iters, stream):
     return start.elapsed_time(end) / iters
 
 
+def call_times(torch, fn, iters, stream):
+    """Milliseconds of each of iters calls of fn(), HIP events on stream."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for s, e in ev:
+        s.record(stream)
+        fn()
+        e.record(stream)
+    ev[-1][1].synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
 def host_threads():
     """(threads used, CPUs this process may run on, CPUs the host shows).  A
     GPU machine's share for one GPU is 16 cores, whatever the host shows."""
@@ -972,8 +983,9 @@ def main():
     def bulk():
         api.append(cache, kd, vd, seq, pos, pt)
 
-    bulk(); torch.cuda.synchronize()
-    t_bulk = time_region(torch, bulk, 3, stream)
+    # two warm-up calls, then the median of 7 calls timed one by one
+    bulk(); bulk(); torch.cuda.synchronize()
+    t_bulk = float(np.median(call_times(torch, bulk, 7, stream)))
     bulk_bytes = ntok * w.Hkv * 128 * 2 * (2 + 0.5625) + ntok * 8
     del kd, vd
     q_np = w.q(0)

@@ -346,39 +346,49 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
     spread_nibbles(s_vw[pr][lane16], &b0, &b1);
     *reinterpret_cast<uint2*>(dst) = make_uint2(a0 | (b0 << 4), a1 | (b1 << 4));
   } else {
-    const uint32_t keep = odd ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
+    // the partner's nibbles kept (one 64-bit clear and set, 8-byte aligned)
+    const unsigned long long keep = odd ? 0x0F0F0F0F0F0F0F0Full : 0xF0F0F0F0F0F0F0F0ull;
     const int sh = odd ? 4 : 0;
-    atomicAnd(dst, keep);
-    atomicOr(dst, a0 << sh);
-    atomicAnd(dst + 1, keep);
-    atomicOr(dst + 1, a1 << sh);
+    unsigned long long* d64 = reinterpret_cast<unsigned long long*>(dst);
+    atomicAnd(d64, keep);
+    atomicOr(d64, ((unsigned long long)a0 | ((unsigned long long)a1 << 32)) << sh);
   }
 }
 
-// The amax/6 append with one lane per 16-element block: workgroup = 32
-// consecutive tokens of the call x one KV head, 8 lanes per token.  A lane
-// holds its whole block, so the block's amax, scale code and reciprocal are
-// computed once (the lane-pair layout above computes them in both lanes and
-// exchanges the amax); the element rounding is encode8's, so the codes are
-// those of append_kernel.  V pairs as in append_kernel.
-constexpr int kBlockRows = 32;
-
-template <bool F32IN>
+// The amax/6 append with one lane per 16-element block: workgroup = ROWS
+// consecutive tokens of the call x one KV head.  A lane holds its whole
+// block, so the block's amax, scale code and reciprocal are computed once
+// (the lane-pair layout above computes them in both lanes and exchanges the
+// amax); the element rounding is encode8's, so the codes are those of
+// append_kernel.  V pairs as in append_kernel.  SPLIT = false: 8 lanes per
+// token, each encoding K block j and V block j (bulk appends, where the
+// chip is full and fewer instructions per block count).  SPLIT = true: 16
+// lanes per token, lanes 0-7 take the K blocks and 8-15 the V blocks, half
+// the serial work per lane for appends too small to fill the chip.
+template <bool F32IN, bool SPLIT, int ROWS>
 __global__ void __launch_bounds__(256) append_block_kernel(AppendArgs p) {
-  const int j = threadIdx.x & 7, r = threadIdx.x >> 3;      // block j of row r
-  const int tok = blockIdx.x * kBlockRows + r;
+  constexpr int kLanes = SPLIT ? 16 : 8;
+  static_assert(ROWS * kLanes <= 256, "one workgroup holds ROWS tokens");
+  const int j = threadIdx.x & 7, r = threadIdx.x / kLanes;  // block j of row r
+  const bool vlane = SPLIT && (threadIdx.x & 8);            // SPLIT: a V block
+  const int tok = blockIdx.x * ROWS + r;
   const int h = blockIdx.y;
   const bool valid = tok < p.n_tok;
-  __shared__ int s_seq[kBlockRows], s_pos[kBlockRows];
-  __shared__ uint2 s_vw[kBlockRows][8];
+  __shared__ int s_seq[ROWS], s_pos[ROWS];
+  __shared__ uint2 s_vw[ROWS][8];
   // rows past the call's end load the last row (their results are dropped)
   const int ltok = valid ? tok : p.n_tok - 1;
   const size_t row = (size_t)ltok * p.hkv + h;
   const int seq = valid ? p.tok_seq[ltok] : -1;
   const int pos = p.tok_pos[ltok];
-  const Raw8 rk0 = load_raw8<F32IN>(p.k_new, row, 2 * j), rk1 = load_raw8<F32IN>(p.k_new, row, 2 * j + 1);
-  const Raw8 rv0 = load_raw8<F32IN>(p.v_new, row, 2 * j), rv1 = load_raw8<F32IN>(p.v_new, row, 2 * j + 1);
-  if (j == 0) {
+  const void* src0 = vlane ? p.v_new : p.k_new;
+  const Raw8 rk0 = load_raw8<F32IN>(src0, row, 2 * j), rk1 = load_raw8<F32IN>(src0, row, 2 * j + 1);
+  Raw8 rv0, rv1;
+  if constexpr (!SPLIT) {
+    rv0 = load_raw8<F32IN>(p.v_new, row, 2 * j);
+    rv1 = load_raw8<F32IN>(p.v_new, row, 2 * j + 1);
+  }
+  if (j == 0 && !vlane) {
     s_seq[r] = seq;
     s_pos[r] = pos;
   }
@@ -415,22 +425,35 @@ __global__ void __launch_bounds__(256) append_block_kernel(AppendArgs p) {
   if (valid) {
     const int page = clamp_page(p.page_table[(size_t)seq * p.max_pages + pos / kPage], p.num_pages);
     slot = pos % kPage;
-    uint32_t ksb, vsb;
-    const uint2 kw = quantize(rk0, rk1, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
-    vw = quantize(rv0, rv1, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
     slab = (size_t)page * p.hkv + h;
     // K: token-major codes [16][64 B], block j at byte 8j; scales K [token
     // 16][block 8], V [block 8][token 16]
-    *reinterpret_cast<uint2*>(p.k_codes + slab * kSlab + slot * 64 + j * 8) = kw;
-    p.k_scales[slab * kScaleSlab + slot * kNBlk + j] = (uint8_t)ksb;
-    p.v_scales[slab * kScaleSlab + j * kPage + slot] = (uint8_t)vsb;
+    uint32_t ksb, vsb;
+    uint2 kw;
+    if constexpr (SPLIT) {
+      // one quantize with per-lane parameters: K and V lanes share a wave,
+      // so a branch per plane would run both sides one after the other
+      const float s_t = vlane ? p.v_scale : p.k_scale, inv6 = vlane ? p.v_inv6 : p.k_inv6;
+      const double six_st = vlane ? p.v_six_st : p.k_six_st;
+      kw = quantize(rk0, rk1, s_t, inv6, six_st, &ksb);
+      vw = kw;
+      vsb = ksb;
+    } else {
+      kw = quantize(rk0, rk1, p.k_scale, p.k_inv6, p.k_six_st, &ksb);
+      vw = quantize(rv0, rv1, p.v_scale, p.v_inv6, p.v_six_st, &vsb);
+    }
+    if (!vlane) {
+      *reinterpret_cast<uint2*>(p.k_codes + slab * kSlab + slot * 64 + j * 8) = kw;
+      p.k_scales[slab * kScaleSlab + slot * kNBlk + j] = (uint8_t)ksb;
+    }
+    if (!SPLIT || vlane) p.v_scales[slab * kScaleSlab + j * kPage + slot] = (uint8_t)vsb;
   }
-  s_vw[r][j] = vw;
+  if (!SPLIT || vlane) s_vw[r][j] = vw;
   __syncthreads();
-  if (!valid) return;
+  if (!valid || (SPLIT && !vlane)) return;
   const int odd = pos & 1;
   const int pr = odd ? r - 1 : r + 1;           // the partner's row, if it is here
-  const bool paired = pr >= 0 && pr < kBlockRows && s_seq[pr] == seq && s_pos[pr] == (pos ^ 1);
+  const bool paired = pr >= 0 && pr < ROWS && s_seq[pr] == seq && s_pos[pr] == (pos ^ 1);
   // V: the block's element groups 2j and 2j+1 (8 elements each, 16 bytes apart)
   uint32_t* dst = reinterpret_cast<uint32_t*>(p.v_codes + slab * kSlab + (slot >> 2) * 256 + j * 32 +
                                               ((slot >> 1) & 1) * 8);
@@ -446,14 +469,15 @@ __global__ void __launch_bounds__(256) append_block_kernel(AppendArgs p) {
     *reinterpret_cast<uint2*>(dst) = make_uint2(a[0] | (b[0] << 4), a[1] | (b[1] << 4));
     *reinterpret_cast<uint2*>(dst + 4) = make_uint2(a[2] | (b[2] << 4), a[3] | (b[3] << 4));
   } else {
-    const uint32_t keep = odd ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
+    // the partner's nibbles kept: one 64-bit clear and one 64-bit set per
+    // 8-byte group (8-byte aligned), half the atomics of 32-bit words
+    const unsigned long long keep = odd ? 0x0F0F0F0F0F0F0F0Full : 0xF0F0F0F0F0F0F0F0ull;
     const int sh = odd ? 4 : 0;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      atomicAnd(dst + 4 * g, keep);
-      atomicOr(dst + 4 * g, a[2 * g] << sh);
-      atomicAnd(dst + 4 * g + 1, keep);
-      atomicOr(dst + 4 * g + 1, a[2 * g + 1] << sh);
+      unsigned long long* d64 = reinterpret_cast<unsigned long long*>(dst + 4 * g);
+      atomicAnd(d64, keep);
+      atomicOr(d64, ((unsigned long long)a[2 * g] | ((unsigned long long)a[2 * g + 1] << 32)) << sh);
     }
   }
 }
@@ -526,14 +550,28 @@ static void launch_append_mode(const AppendArgs& a, bool f32, dim3 grid, hipStre
   else append_kernel<false, MODE><<<grid, 256, 0, s>>>(a);
 }
 
+template <bool SPLIT, int ROWS>
+static void launch_block(const AppendArgs& a, bool f32, hipStream_t s) {
+  const dim3 grid((unsigned)((a.n_tok + ROWS - 1) / ROWS), (unsigned)a.hkv);
+  constexpr unsigned threads = ROWS * (SPLIT ? 16 : 8);
+  if (f32) append_block_kernel<true, SPLIT, ROWS><<<grid, threads, 0, s>>>(a);
+  else append_block_kernel<false, SPLIT, ROWS><<<grid, threads, 0, s>>>(a);
+}
+
 hipError_t launch_append(const AppendArgs& a, bool f32, int mode, hipStream_t s) {
   const dim3 grid((unsigned)((a.n_tok + 15) / 16), (unsigned)a.hkv);
   if (mode == kAppendMse) launch_append_mode<kAppendMse>(a, f32, grid, s);
   else if (mode == kAppendMx) launch_append_mode<kAppendMx>(a, f32, grid, s);
   else {
-    const dim3 bgrid((unsigned)((a.n_tok + kBlockRows - 1) / kBlockRows), (unsigned)a.hkv);
-    if (f32) append_block_kernel<true><<<bgrid, 256, 0, s>>>(a);
-    else append_block_kernel<false><<<bgrid, 256, 0, s>>>(a);
+    // amax/6 by (token, head) rows: from 32768 rows (1024 workgroups of 32
+    // tokens) the chip is full and the 8-lane layout's fewer instructions
+    // per block win; below, the call is latency bound and the split layout
+    // halves each lane's serial work, with 16 tokens per workgroup down to
+    // 4096 rows (256 workgroups) and single-wave workgroups of 4 tokens below
+    const long long rows = (long long)a.n_tok * a.hkv;
+    if (rows >= 32768) launch_block<false, 32>(a, f32, s);
+    else if (rows >= 4096) launch_block<true, 16>(a, f32, s);
+    else launch_block<true, 4>(a, f32, s);
   }
   return hipGetLastError();
 }

@@ -138,6 +138,46 @@ def test_append_token_pairs(orc):
             assert np.array_equal(arr[~m], f[~m])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n", [300, 1000, 4500], ids=["rows2400", "rows8000", "rows36000"])
+def test_append_launch_layouts(orc, n, dtype):
+    """The append takes a different workgroup layout by call size (8 KV
+    heads: 300 tokens run 4 tokens per workgroup with K and V blocks on
+    separate lanes, 1000 tokens 16 per workgroup, 4500 tokens 32 per
+    workgroup with one lane per K and V block).  Each is bit-exact with V
+    pairs written together, across workgroup boundaries, in reverse order
+    and alone, and every byte outside the rows keeps its sentinel."""
+    rng = np.random.default_rng(n * 2 + (dtype == "f32"))
+    B, Hkv, max_pages = 4, 8, 80
+    num_pages = B * max_pages + 7
+    pt = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    slots = np.sort(rng.choice(B * max_pages * 16, n, replace=False))
+    # runs of consecutive slots reversed, and a tenth of the order shuffled
+    cut = np.sort(rng.choice(np.arange(1, n), n // 40, replace=False))
+    parts = np.split(slots, cut)
+    slots = np.concatenate([p[::-1] if i % 3 == 1 else p for i, p in enumerate(parts)])
+    sh = rng.choice(n, n // 10, replace=False)
+    slots[sh] = slots[rng.permutation(sh)]
+    seq = (slots // (max_pages * 16)).astype(np.int32)
+    pos = (slots % (max_pages * 16)).astype(np.int32)
+    k = W.random_rows(30 + n, n * Hkv, "mixed", dtype).reshape(n, Hkv, 128)
+    v = W.random_rows(31 + n, n * Hkv, "outlier", dtype).reshape(n, Hkv, 128)
+    stk, stv = orc.tensor_scale(k), orc.tensor_scale(v) * 0.8
+    cache = api.KVCache(num_pages, Hkv, stk, stv, fill=0xA5)
+    say(f"append layouts {dtype} n={n} rows={n * Hkv}")
+    api.append(cache, to_dev(k, dtype), to_dev(v, dtype), i32(seq), i32(pos), i32(pt))
+    P = planes(cache)
+    pages = pt[seq, pos // 16]
+    got = P.gather(pages, pos % 16)
+    exp = (*orc.quantize_rows(k, stk), *orc.quantize_rows(v, stv))
+    for g, e, nm in zip(got, exp, ("k codes", "k scales", "v codes", "v scales")):
+        bad = np.argwhere(g != e)
+        assert bad.size == 0, (nm, bad[:5].tolist())
+    masks = P.touched_mask(pages, pos % 16)
+    for arr, m, f in zip(P.arrays(), masks, P.untouched_fill(0xA5)):
+        assert np.array_equal(arr[~m], f[~m])
+
+
 def test_append_edge_values(orc):
     """Ties, exact grid points, zeros of both signs, saturation beyond the
     calibrated amax, zero and subnormal block scales."""
