@@ -314,10 +314,15 @@ __device__ __forceinline__ void process_page(PageRegs<FMT> cur, int pg, int L, i
     for (int r = 0; r < 4; ++r) acc_s[r] = (tbase + r < L) ? acc_s[r] : -INFINITY;
     drop_v<FMT>(cur, L - tbase);
   }
-  float mx = fmaxf(fmaxf(acc_s[0], acc_s[1]), fmaxf(acc_s[2], acc_s[3]));
-  mx = max_across_rows(mx) * qscale;
-  const bool grow = mx > st.m_run + kLazy;
-  if (__any(grow)) {
+  // A head's page max passes the reference by more than kLazy exactly when
+  // one of its four lane rows does, so the cross-row max is taken only on
+  // that (rare) path.  The NaN-propagating maximum needs no quieting of the
+  // accumulator values first.
+  const float lmx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(acc_s[0], acc_s[1]),
+                                                  __builtin_elementwise_maximum(acc_s[2], acc_s[3]));
+  if (__any(lmx * qscale > st.m_run + kLazy)) {
+    const float mx = max_across_rows(lmx) * qscale;
+    const bool grow = mx > st.m_run + kLazy;
     const float m_new = grow ? mx : st.m_run;
     const float alpha = fast_exp2(st.m_run - m_new);
     st.m_run = m_new;
