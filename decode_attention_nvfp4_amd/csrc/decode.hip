@@ -168,8 +168,16 @@ __device__ __forceinline__ void load_page(const DecodeArgs& p, const PlaneRsrc& 
 struct WaveState {
   floatx4 acc_o[8];   // O^T[d = 8(4kg + r) + i][head col] in acc_o[i][r]
   float m_run;        // reference max (log2 domain) of head col
-  float l_run;        // this lane's share of the running sum
+  float l_run;        // FP8 / BF16 pages: this lane's share of the running sum
+  floatx4 acc_l;      // NVFP4 / MXFP4 pages: the running sum of head col in every row
 };
+
+// For the 4-bit pages the running sum of the weights is taken on the matrix
+// core: a 16x16x16 product of a ones tile with P^T gives every row of head
+// col the sum of its 16 weights, as rounded to FP16 for the PV product.  (The
+// comparison formats keep the VALU sum: their register budget is spent on
+// wider pages.)
+template <int FMT> constexpr bool kSumOnMatrixCore = FMT == kFmtNvfp4 || FMT == kFmtMxfp4;
 
 // Lazy rescaling: the accumulators are rescaled only when a head's max grows
 // by more than kLazy (log2 units) over the reference, so p = 2^(s - m_run)
@@ -183,6 +191,7 @@ __device__ __forceinline__ void reset_state(WaveState& st) {
   for (int i = 0; i < 8; ++i) st.acc_o[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   st.m_run = kNoMax;
   st.l_run = 0.0f;
+  st.acc_l = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 // 2^(byte - 127 - ex) as an FP32, for an E8M0 byte taken relative to 2^ex:
@@ -326,16 +335,18 @@ __device__ __forceinline__ void process_page(PageRegs<FMT> cur, int pg, int L, i
     const float m_new = grow ? mx : st.m_run;
     const float alpha = fast_exp2(st.m_run - m_new);
     st.m_run = m_new;
-    st.l_run *= alpha;
+    if constexpr (kSumOnMatrixCore<FMT>) st.acc_l *= alpha;
+    else st.l_run *= alpha;
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.acc_o[i] *= alpha;
   }
   float pr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(fmaf(acc_s[r], qscale, -st.m_run));
-  st.l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+  if constexpr (!kSumOnMatrixCore<FMT>) st.l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
   if constexpr (FMT == kFmtNvfp4 || FMT == kFmtMxfp4) {
     const halfx4 bp = {(_Float16)pr[0], (_Float16)pr[1], (_Float16)pr[2], (_Float16)pr[3]};
+    st.acc_l = __builtin_amdgcn_mfma_f32_16x16x16f16(halfx4{1.0f16, 1.0f16, 1.0f16, 1.0f16}, bp, st.acc_l, 0, 0, 0);
     // ---- O^T += V~^T P^T: one 16-token MFMA per element of the lane's
     // d run; P^T comes straight from the S^T accumulator layout
     halfx2 v01, v23;
@@ -472,9 +483,10 @@ __device__ __forceinline__ void load_q(const DecodeArgs& p, int b, int kvh, int 
 // Write the state of (b, kvh): the final output when the piece is the whole
 // segment, else a normalized partial (o / l, log2-sum-exp) in workspace slot
 // (wave, slot).
+template <int FMT>
 __device__ __forceinline__ void flush(const DecodeArgs& p, const WaveState& st, int b, int kvh,
                                       int col, int kg, bool complete, int wave, int slot) {
-  const float l_tot = sum_across_rows(st.l_run);
+  const float l_tot = kSumOnMatrixCore<FMT> ? st.acc_l[0] : sum_across_rows(st.l_run);
   if (col >= p.group) return;
   float* dst;
   float f;
@@ -754,7 +766,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
     ++seg.pg;
     ++done;
     if (--piece_left == 0) {
-      flush(p, st, seg.b, seg.kvh, col, kg, whole, wave, first_piece ? 0 : 1);
+      flush<FMT>(p, st, seg.b, seg.kvh, col, kg, whole, wave, first_piece ? 0 : 1);
       first_piece = false;
     }
   };
