@@ -875,25 +875,44 @@ __device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMa
   float (&s_den)[PL] = s_den_h[PER_SEG ? g : 0];
   float m = -INFINITY, den = 0.0f;
   float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-  for (int i = pi; i < n; i += PL) {
-    const int k = piece(i);
-    if (k < 0) continue;
-    const float l = p.ws_lse[k];
-    const float4 v = reinterpret_cast<const float4*>(p.ws_o + (size_t)k * kD)[e];
-    if (l == -INFINITY) continue;             // a piece with no weight
-    if (l > m) {
-      const float r = exp2f(m - l);           // 0 while m is -inf
-      acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
-      den *= r;
-      m = l;
+  // The thread's pieces i = pi, pi + PL, ... in batches of kBatch whose loads
+  // are all issued before the first is used (one memory round trip per
+  // batch); a slot without a piece loads the segment's first piece, which
+  // always exists (wave w0 owns the segment's first unit), and is skipped.
+  constexpr int kBatch = 4;
+  const int k0 = piece(0);
+  for (int i0 = pi; i0 < n; i0 += kBatch * PL) {
+    int ks[kBatch];
+    float ls[kBatch];
+    float4 vs[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * PL;
+      ks[u] = i < n ? piece(i) : -1;
     }
-    const float c = exp2f(l - m);
-    acc.x = fmaf(c, v.x, acc.x);
-    acc.y = fmaf(c, v.y, acc.y);
-    acc.z = fmaf(c, v.z, acc.z);
-    acc.w = fmaf(c, v.w, acc.w);
-    den += c;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int k = ks[u] >= 0 ? ks[u] : k0;
+      ls[u] = p.ws_lse[k];
+      vs[u] = reinterpret_cast<const float4*>(p.ws_o + (size_t)k * kD)[e];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float l = ls[u];
+      if (ks[u] < 0 || l == -INFINITY) continue;   // no piece, or a piece with no weight
+      if (l > m) {
+        const float r = exp2f(m - l);           // 0 while m is -inf
+        acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
+        den *= r;
+        m = l;
+      }
+      const float c = exp2f(l - m);
+      acc.x = fmaf(c, vs[u].x, acc.x);
+      acc.y = fmaf(c, vs[u].y, acc.y);
+      acc.z = fmaf(c, vs[u].z, acc.z);
+      acc.w = fmaf(c, vs[u].w, acc.w);
+      den += c;
+    }
   }
   s_acc[pi][e] = acc;
   if (e == 0) {
