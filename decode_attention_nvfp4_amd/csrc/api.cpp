@@ -74,10 +74,17 @@ int cu_count() {
 // that each wave's fixed cost (query load, partial write and merge) stays
 // small next to its page stream, and at most about kMaxPiecesPerSegment waves
 // per (sequence, KV head) segment, since the merge of a segment's partials
-// grows with their number (few long sequences).  A requested count is used
-// as given.
+// grows with their number (few long sequences).  Work too small to give every
+// SIMD a wave of 16 pages is spread over up to one wave per SIMD with at least
+// kMinPagesSmall pages each instead: such a call is bound by a wave's latency,
+// not by the machine (configuration 1, 64 pages: 16.3 us at 4 waves, 12.1 us
+// at 32; configuration 2, 16384 pages: 20.4 us at 1024 waves against 24.7 at
+// 2048 and 24.1 at 512, measured on MI355X).  A requested count is used as
+// given.
 constexpr int64_t kMinPagesPerWave = 16;
+constexpr int64_t kMinPagesSmall = 2;
 constexpr int64_t kWavesPerCu = 8;
+constexpr int64_t kSimdsPerCu = 4;
 constexpr int64_t kMaxPiecesPerSegment = 128;
 
 int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, int32_t max_seq_len,
@@ -85,8 +92,10 @@ int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, i
   if (num_splits > 0) return num_splits;
   const int64_t slots = (int64_t)cu_count() * std::min<int64_t>(kWavesPerCu, decode_occupancy(f32_q, fmt));
   const int64_t units = (int64_t)batch * hkv * ((max_seq_len + NVFP4_PAGE_SIZE - 1) / NVFP4_PAGE_SIZE);
-  const int64_t want = std::min((units + kMinPagesPerWave - 1) / kMinPagesPerWave,
-                                 std::max<int64_t>(cu_count(), kMaxPiecesPerSegment * batch * hkv));
+  const int64_t simds = kSimdsPerCu * cu_count();
+  int64_t want = (units + kMinPagesPerWave - 1) / kMinPagesPerWave;
+  if (want < simds) want = std::min(simds, (units + kMinPagesSmall - 1) / kMinPagesSmall);
+  want = std::min(want, std::max<int64_t>(cu_count(), kMaxPiecesPerSegment * batch * hkv));
   return (int32_t)std::max<int64_t>(1, std::min(slots, want));
 }
 
@@ -103,7 +112,6 @@ int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, i
 // wave count keeps equal ranges.  The results do not depend on the
 // placement: the decode and the merge kernels derive the same ranges from
 // these weights.
-constexpr int64_t kSimdsPerCu = 4;
 constexpr int32_t kWeightFirst = 8, kWeightRest = 5;
 
 void set_wave_weights(DecodeArgs& a, int fmt, int64_t max_units) {

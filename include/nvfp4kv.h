@@ -198,9 +198,13 @@ int32_t nvfp4_kv_dequant(const nvfp4_kv_cache* cache, const int32_t* page_table_
                          int32_t out_dtype, void* stream);
 
 /* Number of work ranges (waves) the decode planner uses on the current
- * device: num_splits when > 0, else the smaller of the device's resident
- * decode wave slots and ceil(batch * num_kv_heads * ceil(max_seq_len/16) / 16)
- * (at least 16 pages per wave), and at least 1.  0 for invalid arguments. */
+ * device: num_splits when > 0, else, with U = batch * num_kv_heads *
+ * ceil(max_seq_len/16) pages and S = 4 * (compute units) SIMDs,
+ * W = ceil(U / 16) (at least 16 pages per wave), or when that is below S,
+ * min(S, ceil(U / 2)) (latency-bound work: up to one wave per SIMD, at least
+ * 2 pages each); then at most max(compute units, 128 * batch * num_kv_heads)
+ * and at most the device's resident decode wave slots, and at least 1.
+ * 0 for invalid arguments. */
 int32_t nvfp4_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
                                 int32_t num_splits);
 
