@@ -251,14 +251,17 @@ __device__ __forceinline__ uint32_t quantize_half_block_mx(const float x[8], uin
   return w;
 }
 
-// Eight nibbles (element e in bits 4e..4e+3) spread to the low nibbles of
-// eight bytes: elements 0..3 in *w0, 4..7 in *w1.
-__device__ __forceinline__ void spread_nibbles(uint32_t w, uint32_t* w0, uint32_t* w1) {
-  auto sp = [](uint32_t x) {
-    return (x & 0xFu) | ((x & 0xF0u) << 4) | ((x & 0xF00u) << 8) | ((x & 0xF000u) << 12);
-  };
-  *w0 = sp(w & 0xFFFFu);
-  *w1 = sp(w >> 16);
+// The V bytes of a token pair from the two tokens' eight codes each (element
+// e in bits 4e..4e+3 of a for the even token, of b for the odd one): byte e
+// holds element e of a in its low nibble and of b in its high nibble,
+// elements 0..3 in .x and 4..7 in .y.  The even elements 0, 2, 4, 6 and the
+// odd ones 1, 3, 5, 7 are paired up within bytes with masks, then two byte
+// permutes put the bytes in element order.  (b = 0 gives the even token's
+// nibbles alone, a = 0 the odd token's.)
+__device__ __forceinline__ uint2 pair_bytes(uint32_t a, uint32_t b) {
+  const uint32_t even = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);   // bytes: elements 0, 2, 4, 6
+  const uint32_t odd = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);    // bytes: elements 1, 3, 5, 7
+  return make_uint2(__builtin_amdgcn_perm(odd, even, 0x05010400u), __builtin_amdgcn_perm(odd, even, 0x07030602u));
 }
 
 // The MSE-searched and MXFP4 appends (a block spans a lane pair or quad,
@@ -338,20 +341,16 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
   const bool paired = pr >= 0 && pr < 16 && s_seq[pr] == seq && s_pos[pr] == (pos ^ 1);
   uint32_t* dst = reinterpret_cast<uint32_t*>(p.v_codes + slab * kSlab + (slot >> 2) * 256 + lane16 * 16 +
                                               ((slot >> 1) & 1) * 8);
-  uint32_t a0, a1;
-  spread_nibbles(vw, &a0, &a1);
   if (paired) {
     if (odd) return;                            // written by the even row
-    uint32_t b0, b1;
-    spread_nibbles(s_vw[pr][lane16], &b0, &b1);
-    *reinterpret_cast<uint2*>(dst) = make_uint2(a0 | (b0 << 4), a1 | (b1 << 4));
+    *reinterpret_cast<uint2*>(dst) = pair_bytes(vw, s_vw[pr][lane16]);
   } else {
     // the partner's nibbles kept (one 64-bit clear and set, 8-byte aligned)
     const unsigned long long keep = odd ? 0x0F0F0F0F0F0F0F0Full : 0xF0F0F0F0F0F0F0F0ull;
-    const int sh = odd ? 4 : 0;
+    const uint2 own = odd ? pair_bytes(0u, vw) : pair_bytes(vw, 0u);
     unsigned long long* d64 = reinterpret_cast<unsigned long long*>(dst);
     atomicAnd(d64, keep);
-    atomicOr(d64, ((unsigned long long)a0 | ((unsigned long long)a1 << 32)) << sh);
+    atomicOr(d64, (unsigned long long)own.x | ((unsigned long long)own.y << 32));
   }
 }
 
@@ -366,9 +365,9 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs p) {
 // lanes per token, lanes 0-7 take the K blocks and 8-15 the V blocks, half
 // the serial work per lane for appends too small to fill the chip.
 template <bool F32IN, bool SPLIT, int ROWS>
-__global__ void __launch_bounds__(256) append_block_kernel(AppendArgs p) {
+__global__ void __launch_bounds__(ROWS * (SPLIT ? 16 : 8)) append_block_kernel(AppendArgs p) {
   constexpr int kLanes = SPLIT ? 16 : 8;
-  static_assert(ROWS * kLanes <= 256, "one workgroup holds ROWS tokens");
+  static_assert(ROWS * kLanes <= 1024, "one workgroup holds ROWS tokens");
   const int j = threadIdx.x & 7, r = threadIdx.x / kLanes;  // block j of row r
   const bool vlane = SPLIT && (threadIdx.x & 8);            // SPLIT: a V block
   const int tok = blockIdx.x * ROWS + r;
@@ -457,27 +456,22 @@ __global__ void __launch_bounds__(256) append_block_kernel(AppendArgs p) {
   // V: the block's element groups 2j and 2j+1 (8 elements each, 16 bytes apart)
   uint32_t* dst = reinterpret_cast<uint32_t*>(p.v_codes + slab * kSlab + (slot >> 2) * 256 + j * 32 +
                                               ((slot >> 1) & 1) * 8);
-  uint32_t a[4];
-  spread_nibbles(vw.x, &a[0], &a[1]);
-  spread_nibbles(vw.y, &a[2], &a[3]);
   if (paired) {
     if (odd) return;                            // written by the even row
     const uint2 pv = s_vw[pr][j];
-    uint32_t b[4];
-    spread_nibbles(pv.x, &b[0], &b[1]);
-    spread_nibbles(pv.y, &b[2], &b[3]);
-    *reinterpret_cast<uint2*>(dst) = make_uint2(a[0] | (b[0] << 4), a[1] | (b[1] << 4));
-    *reinterpret_cast<uint2*>(dst + 4) = make_uint2(a[2] | (b[2] << 4), a[3] | (b[3] << 4));
+    *reinterpret_cast<uint2*>(dst) = pair_bytes(vw.x, pv.x);
+    *reinterpret_cast<uint2*>(dst + 4) = pair_bytes(vw.y, pv.y);
   } else {
     // the partner's nibbles kept: one 64-bit clear and one 64-bit set per
     // 8-byte group (8-byte aligned), half the atomics of 32-bit words
     const unsigned long long keep = odd ? 0x0F0F0F0F0F0F0F0Full : 0xF0F0F0F0F0F0F0F0ull;
-    const int sh = odd ? 4 : 0;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
+      const uint32_t w = g ? vw.y : vw.x;
+      const uint2 own = odd ? pair_bytes(0u, w) : pair_bytes(w, 0u);
       unsigned long long* d64 = reinterpret_cast<unsigned long long*>(dst + 4 * g);
       atomicAnd(d64, keep);
-      atomicOr(d64, ((unsigned long long)a[2 * g] | ((unsigned long long)a[2 * g + 1] << 32)) << sh);
+      atomicOr(d64, (unsigned long long)own.x | ((unsigned long long)own.y << 32));
     }
   }
 }
@@ -567,9 +561,16 @@ hipError_t launch_append(const AppendArgs& a, bool f32, int mode, hipStream_t s)
     // tokens) the chip is full and the 8-lane layout's fewer instructions
     // per block win; below, the call is latency bound and the split layout
     // halves each lane's serial work, with 16 tokens per workgroup down to
-    // 4096 rows (256 workgroups) and single-wave workgroups of 4 tokens below
+    // 4096 rows (256 workgroups) and single-wave workgroups of 4 tokens below.
+    // From 262144 rows (1024 workgroups of 128 tokens) the windows grow to
+    // 128 tokens: a window whose ends fall inside pages writes partial lines
+    // of those pages' planes, which the neighbouring window writes again, and
+    // wider windows have fewer ends (configuration 4's bulk append, sequences
+    // back to back: 0.855 GB written at 32 tokens, 0.728 GB at 128, against
+    // 0.685 GB of codes and scales; 1.5-2 % faster, measured on MI355X)
     const long long rows = (long long)a.n_tok * a.hkv;
-    if (rows >= 32768) launch_block<false, 32>(a, f32, s);
+    if (rows >= 262144) launch_block<false, 128>(a, f32, s);
+    else if (rows >= 32768) launch_block<false, 32>(a, f32, s);
     else if (rows >= 4096) launch_block<true, 16>(a, f32, s);
     else launch_block<true, 4>(a, f32, s);
   }
