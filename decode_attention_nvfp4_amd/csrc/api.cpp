@@ -116,6 +116,7 @@ constexpr int32_t kWeightFirst = 8, kWeightRest = 5;
 
 void set_wave_weights(DecodeArgs& a, int fmt, int64_t max_units) {
   const int64_t simds = kSimdsPerCu * cu_count();
+  a.shallow = a.num_splits > simds ? 1 : 0;
   a.first_waves = a.num_splits;
   a.weight_first = 1;
   a.weight_rest = 1;

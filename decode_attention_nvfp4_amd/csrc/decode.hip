@@ -603,16 +603,21 @@ __device__ __forceinline__ bool range_fits_u32(const DecodeArgs& p, long long U)
 
 // Register stages of the page pipeline; the planner runs two waves per SIMD,
 // so the register budget is that of two waves (a BF16 page takes three times
-// the registers of an NVFP4 one).
+// the registers of an NVFP4 one).  With two waves on every SIMD the 4-bit
+// formats take kShallow stages (four pages in flight per wave): against eight
+// stages the configuration-4 call ran ~1 % faster (median and p10 over four
+// interleaved runs on MI355X), while a lone wave per SIMD (small batches)
+// keeps the deeper pipeline (configuration 3 ran ~1.5 % slower shallow).
 template <int FMT> constexpr int kDepth = FMT == kFmtBf16 ? 4 : 8;
+constexpr int kShallow = 5;
 
 // PROBE: the page-gather ceiling of this kernel's access pattern.  The same
 // wave ranges, page walk and page loads, but every page is consumed by an
 // exclusive or instead of the attention math; nothing is written but one
 // word per wave (p.out), and no merge follows.
-template <bool F32Q, int FMT, bool WIDE, bool PROBE = false>
+template <bool F32Q, int FMT, bool WIDE, bool PROBE = false, int DEPTH = kDepth<FMT>>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) decode_kernel(DecodeArgs p) {
-  constexpr int kD8 = kDepth<FMT>;
+  constexpr int kD8 = DEPTH;
   const int lane = threadIdx.x;
   const int col = lane & 15, kg = lane >> 4;
   const int wave = blockIdx.x, W = gridDim.x;
@@ -976,21 +981,33 @@ static bool wide_planes(uint32_t num_slabs) {
   return (uint64_t)num_slabs * m > 0x7FFFFFFFull;
 }
 
-template <int FMT>
-static void launch_fmt(const DecodeArgs& a, bool f32_q, hipStream_t s) {
+template <int FMT, int DEPTH>
+static void launch_depth(const DecodeArgs& a, bool f32_q, hipStream_t s) {
   const bool wide = wide_planes<FMT>(a.num_slabs);
   if (f32_q) {
-    if (wide) decode_kernel<true, FMT, true><<<a.num_splits, 64, 0, s>>>(a);
-    else decode_kernel<true, FMT, false><<<a.num_splits, 64, 0, s>>>(a);
+    if (wide) decode_kernel<true, FMT, true, false, DEPTH><<<a.num_splits, 64, 0, s>>>(a);
+    else decode_kernel<true, FMT, false, false, DEPTH><<<a.num_splits, 64, 0, s>>>(a);
   } else {
-    if (wide) decode_kernel<false, FMT, true><<<a.num_splits, 64, 0, s>>>(a);
-    else decode_kernel<false, FMT, false><<<a.num_splits, 64, 0, s>>>(a);
+    if (wide) decode_kernel<false, FMT, true, false, DEPTH><<<a.num_splits, 64, 0, s>>>(a);
+    else decode_kernel<false, FMT, false, false, DEPTH><<<a.num_splits, 64, 0, s>>>(a);
   }
+}
+
+template <int FMT>
+static void launch_fmt(const DecodeArgs& a, bool f32_q, hipStream_t s) {
+  if constexpr (FMT == kFmtNvfp4 || FMT == kFmtMxfp4) {
+    if (a.shallow) {
+      launch_depth<FMT, kShallow>(a, f32_q, s);
+      return;
+    }
+  }
+  launch_depth<FMT, kDepth<FMT>>(a, f32_q, s);
 }
 
 hipError_t launch_gather_probe(const DecodeArgs& a, hipStream_t s) {
   if (wide_planes<kFmtNvfp4>(a.num_slabs)) return hipErrorInvalidValue;
-  decode_kernel<false, kFmtNvfp4, false, true><<<a.num_splits, 64, 0, s>>>(a);
+  if (a.shallow) decode_kernel<false, kFmtNvfp4, false, true, kShallow><<<a.num_splits, 64, 0, s>>>(a);
+  else decode_kernel<false, kFmtNvfp4, false, true><<<a.num_splits, 64, 0, s>>>(a);
   return hipGetLastError();
 }
 

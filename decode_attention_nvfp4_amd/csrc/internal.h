@@ -103,6 +103,9 @@ struct DecodeArgs {
   // work weights of the waves: the first first_waves weigh weight_first,
   // the rest weight_rest (equal weights: equal ranges)
   int32_t first_waves, weight_first, weight_rest;
+  // more than one wave per SIMD: the 4-bit formats take the shallower page
+  // pipeline
+  int32_t shallow;
 };
 
 struct PrefillArgs {
