@@ -86,6 +86,8 @@ constexpr int64_t kMinPagesSmall = 2;
 constexpr int64_t kWavesPerCu = 8;
 constexpr int64_t kSimdsPerCu = 4;
 constexpr int64_t kMaxPiecesPerSegment = 128;
+constexpr int64_t kTailWaves = 1024;
+constexpr int32_t kTailScale = 1;
 
 int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, int32_t max_seq_len,
                    int fmt = kFmtNvfp4) {
@@ -96,7 +98,9 @@ int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, i
   int64_t want = (units + kMinPagesPerWave - 1) / kMinPagesPerWave;
   if (want < simds) want = std::min(simds, (units + kMinPagesSmall - 1) / kMinPagesSmall);
   want = std::min(want, std::max<int64_t>(cu_count(), kMaxPiecesPerSegment * batch * hkv));
-  return (int32_t)std::max<int64_t>(1, std::min(slots, want));
+  want = std::max<int64_t>(1, std::min(slots, want));
+  if ((fmt == kFmtNvfp4 || fmt == kFmtMxfp4) && want == 2 * simds) want += kTailWaves;
+  return (int32_t)want;
 }
 
 // Work weights of the decode waves.  A launch of exactly two waves per SIMD
@@ -118,14 +122,26 @@ void set_wave_weights(DecodeArgs& a, int fmt, int64_t max_units) {
   const int64_t simds = kSimdsPerCu * cu_count();
   a.shallow = a.num_splits > simds ? 1 : 0;
   a.first_waves = a.num_splits;
+  a.tail_start = a.num_splits;
   a.weight_first = 1;
   a.weight_rest = 1;
-  if ((fmt == kFmtNvfp4 || fmt == kFmtMxfp4) && a.num_splits == 2 * simds) {
+  a.weight_tail = 1;
+  if (fmt != kFmtNvfp4 && fmt != kFmtMxfp4) return;
+  if (a.num_splits == 2 * simds) {
     const int64_t T = (kWeightFirst + kWeightRest) * simds;   // sum of the weights
     if (max_units <= (INT64_MAX / 4) / T) {
       a.first_waves = (int32_t)simds;
       a.weight_first = kWeightFirst;
       a.weight_rest = kWeightRest;
+    }
+  } else if (kTailWaves > 0 && a.num_splits == 2 * simds + kTailWaves) {
+    const int64_t T = (int64_t)(kWeightFirst + kWeightRest) * kTailScale * simds + kTailWaves;
+    if (max_units <= (INT64_MAX / 4) / T) {
+      a.first_waves = (int32_t)simds;
+      a.tail_start = (int32_t)(2 * simds);
+      a.weight_first = kWeightFirst * kTailScale;
+      a.weight_rest = kWeightRest * kTailScale;
+      a.weight_tail = 1;
     }
   }
 }

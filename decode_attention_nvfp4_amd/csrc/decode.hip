@@ -564,22 +564,28 @@ __device__ __forceinline__ void next_segment(const DecodeArgs& p, SegPos& s) {
 }
 
 // Wave ranges: wave w takes the units [start(w), start(w + 1)) with
-//   start(w) = floor(U S(w) / S(W)),  S(w) = A min(w, R) + B max(0, w - R),
-// so the first R waves weigh A and the others B (A = B: equal ranges).  The
-// wave owning unit u is the largest w with start(w) <= u, which is the
-// largest w with S(w) <= floor(((u + 1) S(W) - 1) / U) (S grows strictly).
-// I is uint32_t when every product stays below 2^32 (the usual case: 64-bit
-// division is a long software sequence), else int64_t.
+//   start(w) = floor(U S(w) / S(W)),
+//   S(w) = A min(w, R) + B clamp(w - R, 0, R2 - R) + C max(0, w - R2),
+// so the first R waves weigh A, the next R2 - R weigh B and the rest C
+// (A = B = C: equal ranges).  The wave owning unit u is the largest w with
+// start(w) <= u, which is the largest w with S(w) <= floor(((u + 1) S(W) - 1)
+// / U) (S grows strictly).  I is uint32_t when every product stays below
+// 2^32 (the usual case: 64-bit division is a long software sequence), else
+// int64_t.
 template <typename I>
 struct RangeMath {
   I U, T;                                  // units; T = S(W)
-  int R, A, B;
-  __device__ I S(int w) const { return (I)A * (I)min(w, R) + (I)B * (I)max(0, w - R); }
+  int R, R2, A, B, C;
+  __device__ I S(int w) const {
+    return (I)A * (I)min(w, R) + (I)B * (I)max(0, min(w, R2) - R) + (I)C * (I)max(0, w - R2);
+  }
   __device__ long long start(int w) const { return (long long)((I)((I)U * S(w)) / T); }
   __device__ int owner(long long u) const {
     const I smax = (I)((I)(u + 1) * T - 1) / U;
-    const I ar = (I)A * (I)R;
-    return smax < ar ? (int)(smax / (I)A) : R + (int)((smax - ar) / (I)B);
+    const I ar = (I)A * (I)R, br = (I)B * (I)(R2 - R);
+    if (smax < ar) return (int)(smax / (I)A);
+    if (smax - ar < br) return R + (int)((smax - ar) / (I)B);
+    return R2 + (int)((smax - ar - br) / (I)C);
   }
 };
 
@@ -588,8 +594,10 @@ __device__ __forceinline__ RangeMath<I> range_math(const DecodeArgs& p, long lon
   RangeMath<I> rm;
   rm.U = (I)U;
   rm.R = p.first_waves;
+  rm.R2 = p.tail_start;
   rm.A = p.weight_first;
   rm.B = p.weight_rest;
+  rm.C = p.weight_tail;
   rm.T = rm.S(p.num_splits);
   return rm;
 }
@@ -597,7 +605,8 @@ __device__ __forceinline__ RangeMath<I> range_math(const DecodeArgs& p, long lon
 // Every product of the range arithmetic is at most U S(W).
 __device__ __forceinline__ bool range_fits_u32(const DecodeArgs& p, long long U) {
   const long long T = (long long)p.weight_first * p.first_waves +
-                      (long long)p.weight_rest * (p.num_splits - p.first_waves);
+                      (long long)p.weight_rest * (p.tail_start - p.first_waves) +
+                      (long long)p.weight_tail * (p.num_splits - p.tail_start);
   return U * T < (1LL << 32);
 }
 

@@ -101,8 +101,10 @@ struct DecodeArgs {
   uint32_t num_slabs;         // num_pages * hkv: (page, head) slabs of each plane
   int32_t k_exp, v_exp;       // MXFP4: values are taken relative to 2^k_exp, 2^v_exp
   // work weights of the waves: the first first_waves weigh weight_first,
-  // the rest weight_rest (equal weights: equal ranges)
+  // those below tail_start weight_rest, the rest weight_tail (equal weights:
+  // equal ranges)
   int32_t first_waves, weight_first, weight_rest;
+  int32_t tail_start, weight_tail;
   // more than one wave per SIMD: the 4-bit formats take the shallower page
   // pipeline
   int32_t shallow;

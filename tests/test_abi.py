@@ -265,7 +265,10 @@ def test_split_planner_and_workspace(api):
         if want < 4 * 256:
             want = min(4 * 256, -(-units // 2))
         want = min(want, max(256, 128 * B * Hkv))
-        assert auto == max(1, min(8 * 256, want))
+        want = max(1, min(8 * 256, want))
+        # a full launch (two waves per SIMD) gets 1024 small tail ranges that
+        # the dispatcher hands to the first free slots
+        assert auto == (want + 1024 if want == 2 * 4 * 256 else want)
         for req in (1, 2, 7, 64):
             assert api.decode_num_splits(B, Hkv, L, req) == req
         for G in (1, 4, 8):
