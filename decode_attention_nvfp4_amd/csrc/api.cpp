@@ -86,8 +86,15 @@ constexpr int64_t kMinPagesSmall = 2;
 constexpr int64_t kWavesPerCu = 8;
 constexpr int64_t kSimdsPerCu = 4;
 constexpr int64_t kMaxPiecesPerSegment = 128;
+// A full launch of the 4-bit formats (two waves per SIMD) gets kTailWaves
+// more ranges of weight 1 at the end of the stream (~7 % of the work, ~20
+// pages each).  They wait until slots free up, so the dispatcher hands them
+// to the SIMDs whose static ranges finished first: per-wave timestamps of the
+// static launch showed a mean end of 104 us against a span of 114 us
+// (configuration 4).  In interleaved calls 1024 tail ranges ran 8-9 % faster
+// than none; 512, 768 and 1536 gained less, and 2048-4096 finer ranges lost
+// (each range pays the prologue and a partial).
 constexpr int64_t kTailWaves = 1024;
-constexpr int32_t kTailScale = 1;
 
 int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, int32_t max_seq_len,
                    int fmt = kFmtNvfp4) {
@@ -117,6 +124,12 @@ int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, i
 // placement: the decode and the merge kernels derive the same ranges from
 // these weights.
 constexpr int32_t kWeightFirst = 8, kWeightRest = 5;
+// With the tail ranges below the first round weighs 6 : 5 instead: the tail
+// absorbs the waves' spread, and the per-wave timestamps put the span's last
+// waves in the first round (interleaved calls on MI355X: 130-131 us against
+// 142-144 us at 8 : 5 and 137-139 us at 7 : 5; 16 : 10 with a tail of weight
+// 3 ran 148 us).
+constexpr int32_t kTailWeightFirst = 6, kTailWeightRest = 5;
 
 void set_wave_weights(DecodeArgs& a, int fmt, int64_t max_units) {
   const int64_t simds = kSimdsPerCu * cu_count();
@@ -135,12 +148,12 @@ void set_wave_weights(DecodeArgs& a, int fmt, int64_t max_units) {
       a.weight_rest = kWeightRest;
     }
   } else if (kTailWaves > 0 && a.num_splits == 2 * simds + kTailWaves) {
-    const int64_t T = (int64_t)(kWeightFirst + kWeightRest) * kTailScale * simds + kTailWaves;
+    const int64_t T = (int64_t)(kTailWeightFirst + kTailWeightRest) * simds + kTailWaves;
     if (max_units <= (INT64_MAX / 4) / T) {
       a.first_waves = (int32_t)simds;
       a.tail_start = (int32_t)(2 * simds);
-      a.weight_first = kWeightFirst * kTailScale;
-      a.weight_rest = kWeightRest * kTailScale;
+      a.weight_first = kTailWeightFirst;
+      a.weight_rest = kTailWeightRest;
       a.weight_tail = 1;
     }
   }

@@ -203,7 +203,9 @@ int32_t nvfp4_kv_dequant(const nvfp4_kv_cache* cache, const int32_t* page_table_
  * W = ceil(U / 16) (at least 16 pages per wave), or when that is below S,
  * min(S, ceil(U / 2)) (latency-bound work: up to one wave per SIMD, at least
  * 2 pages each); then at most max(compute units, 128 * batch * num_kv_heads)
- * and at most the device's resident decode wave slots, and at least 1.
+ * and at most the device's resident decode wave slots, and at least 1; a
+ * launch of exactly two waves per SIMD (S * 2) of an NVFP4 or MXFP4 cache
+ * adds 1024 small tail ranges that the device dispatches as slots free up.
  * 0 for invalid arguments. */
 int32_t nvfp4_decode_num_splits(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
                                 int32_t num_splits);
