@@ -124,12 +124,16 @@ int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, i
 // placement: the decode and the merge kernels derive the same ranges from
 // these weights.
 constexpr int32_t kWeightFirst = 8, kWeightRest = 5;
-// With the tail ranges below the first round weighs 6 : 5 instead: the tail
-// absorbs the waves' spread, and the per-wave timestamps put the span's last
-// waves in the first round (interleaved calls on MI355X: 130-131 us against
-// 142-144 us at 8 : 5 and 137-139 us at 7 : 5; 16 : 10 with a tail of weight
-// 3 ran 148 us).
-constexpr int32_t kTailWeightFirst = 6, kTailWeightRest = 5;
+// With the tail ranges below the static ranges are equal (5 : 5, the tail
+// ranges weighing 1, ~9 % of the work): the dispatcher does not always place
+// the first round one wave per SIMD (per-wave hardware ids on one box: 91 of
+// 1024 SIMDs held two first-round waves and no second-round one, and their
+// waves ended last), and equal ranges give every SIMD the same static work
+// whatever the placement, while the tail ranges even out the rest.  In
+// interleaved calls on MI355X: 5 : 5 128.9 us, 6 : 5 132.0 us, 4 : 5 133.3 us,
+// 8 : 5 142-144 us; 3 : 3, 4 : 4 and 6 : 6 (tail shares 14, 11 and 8 %) within
+// 1 % of 5 : 5.
+constexpr int32_t kTailWeightFirst = 5, kTailWeightRest = 5;
 
 void set_wave_weights(DecodeArgs& a, int fmt, int64_t max_units) {
   const int64_t simds = kSimdsPerCu * cu_count();
