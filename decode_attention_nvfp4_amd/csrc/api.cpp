@@ -86,15 +86,16 @@ constexpr int64_t kMinPagesSmall = 2;
 constexpr int64_t kWavesPerCu = 8;
 constexpr int64_t kSimdsPerCu = 4;
 constexpr int64_t kMaxPiecesPerSegment = 128;
-// A full launch of the 4-bit formats (two waves per SIMD) gets kTailWaves
-// more ranges of weight 1 at the end of the stream (~7 % of the work, ~20
-// pages each).  They wait until slots free up, so the dispatcher hands them
-// to the SIMDs whose static ranges finished first: per-wave timestamps of the
+// A full launch of the 4-bit formats (two waves per SIMD) gets one more range
+// per SIMD of weight 1 (~9 % of the work, ~26 pages each), interleaved with
+// the static ranges in the stream.  These tail waves come last in the grid,
+// so each is dispatched when a slot frees up: per-wave timestamps of the
 // static launch showed a mean end of 104 us against a span of 114 us
-// (configuration 4).  In interleaved calls 1024 tail ranges ran 8-9 % faster
-// than none; 512, 768 and 1536 gained less, and 2048-4096 finer ranges lost
-// (each range pays the prologue and a partial).
-constexpr int64_t kTailWaves = 1024;
+// (configuration 4).  In interleaved calls 1024 tail ranges (one per SIMD)
+// ran 8-11 % faster than none; 512, 768 and 1536 gained less, and 2048-4096
+// finer ranges lost (each range pays the prologue and a partial).  With the
+// tail ranges at the end of the stream instead, the last sequences' segments
+// were cut into up to 20 pieces and the merge took 9.4 us instead of 6.2.
 
 int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, int32_t max_seq_len,
                    int fmt = kFmtNvfp4) {
@@ -106,7 +107,7 @@ int32_t plan_waves(int32_t num_splits, bool f32_q, int32_t batch, int32_t hkv, i
   if (want < simds) want = std::min(simds, (units + kMinPagesSmall - 1) / kMinPagesSmall);
   want = std::min(want, std::max<int64_t>(cu_count(), kMaxPiecesPerSegment * batch * hkv));
   want = std::max<int64_t>(1, std::min(slots, want));
-  if ((fmt == kFmtNvfp4 || fmt == kFmtMxfp4) && want == 2 * simds) want += kTailWaves;
+  if ((fmt == kFmtNvfp4 || fmt == kFmtMxfp4) && want == 2 * simds) want += simds;
   return (int32_t)want;
 }
 
@@ -151,8 +152,8 @@ void set_wave_weights(DecodeArgs& a, int fmt, int64_t max_units) {
       a.weight_first = kWeightFirst;
       a.weight_rest = kWeightRest;
     }
-  } else if (kTailWaves > 0 && a.num_splits == 2 * simds + kTailWaves) {
-    const int64_t T = (int64_t)(kTailWeightFirst + kTailWeightRest) * simds + kTailWaves;
+  } else if (a.num_splits == 3 * simds) {
+    const int64_t T = (int64_t)(kTailWeightFirst + kTailWeightRest + 1) * simds;
     if (max_units <= (INT64_MAX / 4) / T) {
       a.first_waves = (int32_t)simds;
       a.tail_start = (int32_t)(2 * simds);

@@ -563,30 +563,43 @@ __device__ __forceinline__ void next_segment(const DecodeArgs& p, SegPos& s) {
   }
 }
 
-// Wave ranges: wave w takes the units [start(w), start(w + 1)) with
-//   start(w) = floor(U S(w) / S(W)),
-//   S(w) = A min(w, R) + B clamp(w - R, 0, R2 - R) + C max(0, w - R2),
-// so the first R waves weigh A, the next R2 - R weigh B and the rest C
-// (A = B = C: equal ranges).  The wave owning unit u is the largest w with
-// start(w) <= u, which is the largest w with S(w) <= floor(((u + 1) S(W) - 1)
-// / U) (S grows strictly).  I is uint32_t when every product stays below
-// 2^32 (the usual case: 64-bit division is a long software sequence), else
-// int64_t.
+// Wave ranges.  The ranges follow each other in the stream in the order of
+// a range index v; range v takes the units [start(v), start(v + 1)) with
+//   start(v) = floor(U S(v) / S(V)),
+// S the sum of the weights of the ranges before v.  Two patterns:
+//   - by rounds: v = w, the first R ranges weigh A and the rest B
+//     (A = B: equal ranges);
+//   - interleaved (K > 0, 3K waves): waves w < K, K <= w < 2K and w >= 2K
+//     (the static rounds and the tail ranges, dispatched in that order) take
+//     v = 3(w mod K) + class, with weights A, B and C by class, so that the
+//     small tail ranges lie spread over the whole stream.
+// The range owning unit u is the largest v with start(v) <= u, which is the
+// largest v with S(v) <= floor(((u + 1) S(V) - 1) / U) (S grows strictly).
+// I is uint32_t when every product stays below 2^32 (the usual case: 64-bit
+// division is a long software sequence), else int64_t.
 template <typename I>
 struct RangeMath {
-  I U, T;                                  // units; T = S(W)
-  int R, R2, A, B, C;
-  __device__ I S(int w) const {
-    return (I)A * (I)min(w, R) + (I)B * (I)max(0, min(w, R2) - R) + (I)C * (I)max(0, w - R2);
+  I U, T;                                  // units; T = S(V)
+  int R, A, B, C, K;
+  __device__ I S(int v) const {
+    if (K > 0) {
+      const int j = v % 3;
+      return (I)(v / 3) * (I)(A + B + C) + (I)(j >= 1 ? A : 0) + (I)(j >= 2 ? B : 0);
+    }
+    return (I)A * (I)min(v, R) + (I)B * (I)max(0, v - R);
   }
-  __device__ long long start(int w) const { return (long long)((I)((I)U * S(w)) / T); }
+  __device__ long long start(int v) const { return (long long)((I)((I)U * S(v)) / T); }
   __device__ int owner(long long u) const {
     const I smax = (I)((I)(u + 1) * T - 1) / U;
-    const I ar = (I)A * (I)R, br = (I)B * (I)(R2 - R);
-    if (smax < ar) return (int)(smax / (I)A);
-    if (smax - ar < br) return R + (int)((smax - ar) / (I)B);
-    return R2 + (int)((smax - ar - br) / (I)C);
+    if (K > 0) {
+      const I P = (I)(A + B + C), r = smax % P;
+      return 3 * (int)(smax / P) + (r < (I)A ? 0 : (r < (I)(A + B) ? 1 : 2));
+    }
+    const I ar = (I)A * (I)R;
+    return smax < ar ? (int)(smax / (I)A) : R + (int)((smax - ar) / (I)B);
   }
+  __device__ int v_of(int w) const { return K > 0 ? 3 * (w % K) + w / K : w; }
+  __device__ int w_of(int v) const { return K > 0 ? (v % 3) * K + v / 3 : v; }
 };
 
 template <typename I>
@@ -594,19 +607,20 @@ __device__ __forceinline__ RangeMath<I> range_math(const DecodeArgs& p, long lon
   RangeMath<I> rm;
   rm.U = (I)U;
   rm.R = p.first_waves;
-  rm.R2 = p.tail_start;
   rm.A = p.weight_first;
   rm.B = p.weight_rest;
   rm.C = p.weight_tail;
-  rm.T = rm.S(p.num_splits);
+  rm.K = p.tail_start < p.num_splits ? p.first_waves : 0;
+  rm.T = rm.S(rm.K > 0 ? 3 * rm.K : p.num_splits);
   return rm;
 }
 
 // Every product of the range arithmetic is at most U S(W).
 __device__ __forceinline__ bool range_fits_u32(const DecodeArgs& p, long long U) {
-  const long long T = (long long)p.weight_first * p.first_waves +
-                      (long long)p.weight_rest * (p.tail_start - p.first_waves) +
-                      (long long)p.weight_tail * (p.num_splits - p.tail_start);
+  const long long T = p.tail_start < p.num_splits
+                          ? (long long)(p.weight_first + p.weight_rest + p.weight_tail) * p.first_waves
+                          : (long long)p.weight_first * p.first_waves +
+                                (long long)p.weight_rest * (p.num_splits - p.first_waves);
   return U * T < (1LL << 32);
 }
 
@@ -667,12 +681,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8)))
   long long u0, u1;
   if (range_fits_u32(p, U)) {
     const RangeMath<uint32_t> rm = range_math<uint32_t>(p, U);
-    u0 = rm.start(wave);
-    u1 = rm.start(wave + 1);
+    u0 = rm.start(rm.v_of(wave));
+    u1 = rm.start(rm.v_of(wave) + 1);
   } else {
     const RangeMath<long long> rm = range_math<long long>(p, U);
-    u0 = rm.start(wave);
-    u1 = rm.start(wave + 1);
+    u0 = rm.start(rm.v_of(wave));
+    u1 = rm.start(rm.v_of(wave) + 1);
   }
   if (u0 >= u1) {                          // no units (more waves than units)
     if constexpr (PROBE) reinterpret_cast<uint32_t*>(p.out)[wave * 64 + lane] = 0u;
@@ -868,17 +882,18 @@ __device__ __forceinline__ void merge_segment(const DecodeArgs& p, const RangeMa
                                               long long end, int g, int tid, float* out) {
   const int pi = tid >> 5, e = tid & 31;
   const int G = p.group;
-  const int w0 = rm.owner(a);
-  const int w1 = rm.owner(end - 1);
-  if (w0 == w1) return;                       // finished by one wave
-  const int n = w1 - w0 + 1;
-  // the piece of wave w0 + i: its workspace index, or -1 when w wrote none
+  const int v0 = rm.owner(a);
+  const int v1 = rm.owner(end - 1);
+  if (v0 == v1) return;                       // finished by one wave
+  const int n = v1 - v0 + 1;
+  // the piece of range v0 + i: its workspace index (that of the range's
+  // wave), or -1 when the range is empty
   auto piece = [&](int i) -> int {
-    const int w = w0 + i;
-    const long long sw = rm.start(w);
-    if (sw == rm.start(w + 1)) return -1;
-    const int slot = sw >= a ? 0 : 1;
-    return (w * 2 + slot) * G + g;
+    const int v = v0 + i;
+    const long long sv = rm.start(v);
+    if (sv == rm.start(v + 1)) return -1;
+    const int slot = sv >= a ? 0 : 1;
+    return (rm.w_of(v) * 2 + slot) * G + g;
   };
   // each thread merges its pieces online (running max m, rescaling as it
   // grows); the 8 piece lanes are then combined once

@@ -101,8 +101,10 @@ struct DecodeArgs {
   uint32_t num_slabs;         // num_pages * hkv: (page, head) slabs of each plane
   int32_t k_exp, v_exp;       // MXFP4: values are taken relative to 2^k_exp, 2^v_exp
   // work weights of the waves: the first first_waves weigh weight_first,
-  // those below tail_start weight_rest, the rest weight_tail (equal weights:
-  // equal ranges)
+  // the rest weight_rest (equal weights: equal ranges); or, when tail_start <
+  // num_splits (= 3 first_waves), the three classes of first_waves waves weigh
+  // weight_first, weight_rest and weight_tail with their ranges interleaved
+  // in the stream (RangeMath)
   int32_t first_waves, weight_first, weight_rest;
   int32_t tail_start, weight_tail;
   // more than one wave per SIMD: the 4-bit formats take the shallower page
